@@ -1,0 +1,194 @@
+"""Benchmark of the owner-side Muon step (+ AdamW tail) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = muon_owner_step over the workload's whole bucket of matrices plus
+adamw_tail_step over its packed fp32 tail, inputs already resident in HBM.
+Prints one JSON line.  `value` is Newton-Schulz TFLOP/s with the nominal count
+4 m^2 n + 2 m^3 per iteration and matrix (m = short side); `roofline` is the
+dominant kernel's algorithmic throughput from HIP events recorded around every
+launch of the timed region; `cpu_baseline` is the fp64 oracle timed on the
+host on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Muon owner-step ms + Newton–Schulz TFLOP/s (% bf16 MFMA peak), 1 MI355X"
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3         # MI355X fp32 matrix
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="decoder_layer_h2048")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-phase-timing", action="store_true",
+                    help="time the loop without per-launch events (no roofline object)")
+    ap.add_argument("--profile-only", action="store_true",
+                    help="warmup + timed steps only, no oracle leg (for profilers)")
+    return ap.parse_args()
+
+
+def algorithmic_flops(spec_rows, spec_cols, steps):
+    """Per phase, one launch: Gram m^2 n (one triangle), Poly m^3 (one triangle),
+    Update 2 m^2 n (dense)."""
+    m, n = min(spec_rows, spec_cols), max(spec_rows, spec_cols)
+    return {"gram": float(m) * m * n, "poly": float(m) ** 3, "update": 2.0 * m * m * n}
+
+
+def cpu_baseline(wl, args):
+    """The fp64 oracle on one matrix of each distinct shape + the tail."""
+    import numpy as np
+    from matrix_optimizers_amd import workloads as wlmod
+    from oracle import adamw as oadamw
+    from oracle import muon as omuon
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        cores = max([i.get("num_threads", 1) for i in info] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    seen, sample = set(), []
+    for i, s in enumerate(wl.matrices):
+        if (s.rows, s.cols) not in seen:
+            seen.add((s.rows, s.cols))
+            sample.append(i)
+    flops = 0.0
+    inputs = [wlmod.matrix_inputs(wl, i) for i in sample]
+    t0 = time.perf_counter()
+    for i, x in zip(sample, inputs):
+        omuon.muon_step(x.W, x.G, x.M, wl.hp)
+        s = wl.matrices[i]
+        flops += wlmod.ns_flops_nominal(s.rows, s.cols, wl.hp.ns_steps)
+    if wl.tail_numel:
+        t = wlmod.tail_inputs(wl.seed, wl.tail_numel)
+        a = wl.adamw
+        oadamw.adamw_step(t.p, t.g, t.m, t.v, a.step, a.lr, a.beta1, a.beta2, a.eps, a.weight_decay)
+    dt = time.perf_counter() - t0
+    shapes = ", ".join(f"{wl.matrices[i].rows}x{wl.matrices[i].cols}" for i in sample)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"one matrix of each distinct shape ({shapes})"
+                      + (f" + the {wl.tail_numel}-element AdamW tail" if wl.tail_numel else "")
+                      + f", fp64 numpy, {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the owner step issues no collectives and this "
+              f"build measures one owner's share (--gpus {args.gpus} requested)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import matrix_optimizers_amd as mo
+    from matrix_optimizers_amd import workloads as wlmod
+
+    wl = wlmod.get(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    hp = wl.hp
+    print(f"[bench] workload {wl.key}: {len(wl.matrices)} matrices, tail {wl.tail_numel}",
+          file=sys.stderr, flush=True)
+    mats = [wlmod.torch_matrix_inputs(wl, i, dev) for i in range(len(wl.matrices))]
+    step = mo.MuonOwnerStep(mats, lr=hp.lr, weight_decay=hp.weight_decay, momentum=hp.momentum,
+                            nesterov=hp.nesterov, ns_steps=hp.ns_steps,
+                            ns_coefficients=(hp.ns_a, hp.ns_b, hp.ns_c), eps=hp.eps,
+                            adjust_lr_fn=hp.lr_adjust, ns_dtype=hp.ns_dtype)
+    tail = wlmod.torch_tail_inputs(wl.seed, wl.tail_numel, dev) if wl.tail_numel else None
+    a = wl.adamw
+    t_count = [a.step]
+
+    def one_step():
+        step()
+        if tail is not None:
+            mo.adamw_tail_step(*tail, t_count[0], lr=a.lr, beta1=a.beta1, beta2=a.beta2,
+                               eps=a.eps, weight_decay=a.weight_decay)
+            t_count[0] += 1
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup {args.warmup} done; timing {args.steps} steps", file=sys.stderr, flush=True)
+
+    phase = not args.no_phase_timing
+    if phase:
+        mo.profile_read()           # drop anything recorded before
+        mo.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        one_step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    prof = None
+    if phase:
+        mo.profile_enable(False)
+        prof = mo.profile_read()
+    ms = (t1 - t0) * 1e3 / args.steps
+    print(f"[bench] {ms:.3f} ms/step", file=sys.stderr, flush=True)
+
+    nominal = sum(wlmod.ns_flops_nominal(s.rows, s.cols, hp.ns_steps) for s in wl.matrices)
+    algo = sum(wlmod.ns_flops_algorithmic(s.rows, s.cols, hp.ns_steps) for s in wl.matrices)
+    tflops = nominal / (ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if hp.ns_dtype == "bf16" else PEAK_F32_TFLOPS
+    out = {
+        "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": hp.ns_dtype, "data": "synthetic",
+        "config": {"workload": wl.key, "matrices": len(wl.matrices),
+                   "shapes": sorted({f"{s.rows}x{s.cols}" for s in wl.matrices}),
+                   "tail_elems": wl.tail_numel, "ns_steps": hp.ns_steps,
+                   "w_dtype": wl.w_dtype, "g_dtype": wl.g_dtype, "momentum_dtype": "f32",
+                   "parallelism": "none (one owner's bucket)"},
+        "ns_tflops_nominal": round(tflops, 3),
+        "ns_tflops_algorithmic": round(algo / (ms * 1e-3) / 1e12, 3),
+        "pct_peak_nominal": round(100.0 * tflops / peak, 2),
+    }
+    if prof is not None:
+        per_launch = {}
+        flops_launch = {"gram": 0.0, "poly": 0.0, "update": 0.0}
+        for s in wl.matrices:
+            f = algorithmic_flops(s.rows, s.cols, hp.ns_steps)
+            for k in flops_launch:
+                flops_launch[k] += f[k]
+        for name, (tot, cnt) in prof.items():
+            if cnt:
+                per_launch[name] = {"avg_ms": round(tot / cnt, 5), "launches": int(cnt),
+                                    "ms_per_step": round(tot / args.steps, 5)}
+        out["phases"] = per_launch
+        gemm = {k: v for k, v in per_launch.items() if k in flops_launch}
+        if gemm:
+            dom = max(gemm, key=lambda k: gemm[k]["ms_per_step"])
+            achieved = flops_launch[dom] / (gemm[dom]["avg_ms"] * 1e-3) / 1e12
+            out["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
+                               "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                               "traffic": None,
+                               "algorithmic_per_launch": f"{flops_launch[dom]:.4e} flop"}
+        if "momentum" in per_launch:
+            # momentum kernel: read G (w) + M (4), write M' (4) + U twice in the NS dtype
+            es_g = 2 if wl.g_dtype == "bf16" else 4
+            es_x = 2 if hp.ns_dtype == "bf16" else 4
+            nbytes = sum(s.rows * s.cols for s in wl.matrices) * (es_g + 8 + 2 * es_x)
+            gbs = nbytes / (per_launch["momentum"]["avg_ms"] * 1e-3) / 1e9
+            out["momentum_kernel"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                                      "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    if not args.no_cpu_baseline and not args.profile_only:
+        print("[bench] cpu_baseline (fp64 oracle on host)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, args)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

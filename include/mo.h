@@ -1,0 +1,179 @@
+/*
+ * mo.h - C ABI of the MI355X (gfx950) owner-side Muon step and AdamW tail.
+ *
+ * Sources, cited by page title and section:
+ *   [P] "MatrixFSDP: communication-free matrix optimizers under ZeRO-3 parameter
+ *       sharding" (academ.us article 2607.05895).
+ *   [A] the same paper's abstract excerpt (pith.science record).
+ *
+ * Under owner-shaped ZeRO-3 placement every 2D weight is whole on one owner
+ * rank, and backward reduction leaves the full gradient there, so the optimizer
+ * step on that rank is purely local ([P §3], [P §4.4]).  This library is that
+ * local step: one Muon step over a bucket of whole matrices the caller owns,
+ * and one AdamW step over the packed non-2D tail.  It issues no collectives.
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers (W, G, M, update_out, p, g, m, v, workspace) are device
+ *     pointers on the device that is current for the calling thread; the
+ *     descriptor array and hyperparameter struct are host memory read during
+ *     the call only.  The caller owns every buffer.
+ *   - Matrices are row-major with a row stride `ld_*` in elements (0 means
+ *     "cols").  W, M, p, m, v are updated in place; G and g are only read.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls are asynchronous with respect to the host and ordered on `stream`.
+ *   - Every argument check runs on the host before anything is enqueued.  On
+ *     any error return nothing has been launched and no output is touched.
+ *     Device-side faults are not detected by the call; they surface on the
+ *     caller's next synchronisation.
+ *   - Results are deterministic: the same inputs give bit-identical outputs,
+ *     and a matrix's result does not depend on the other matrices of the bucket.
+ */
+#ifndef MATRIX_OPTIMIZERS_AMD_MO_H
+#define MATRIX_OPTIMIZERS_AMD_MO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t mo_status;
+#define MO_OK                       0
+#define MO_ERR_INVALID_ARG         -1  /* null pointer, negative size, bad stride, bad value */
+#define MO_ERR_UNSUPPORTED         -2  /* dtype / option not implemented, size beyond limits */
+#define MO_ERR_WORKSPACE_TOO_SMALL -3
+#define MO_ERR_ALIAS               -4  /* overlapping tensors that must be disjoint */
+#define MO_ERR_HIP                 -5  /* a HIP runtime call or kernel launch failed */
+
+/* element types */
+#define MO_F32  0
+#define MO_BF16 1
+
+/* learning-rate adjustment, the shape factor on lr (torch.optim.Muon's
+ * adjust_lr_fn; [P §5.1] runs with match_rms_adamw) */
+#define MO_LR_ORIGINAL        0  /* lr * sqrt(max(1, rows/cols)) */
+#define MO_LR_MATCH_RMS_ADAMW 1  /* lr * 0.2 * sqrt(max(rows, cols)) */
+#define MO_LR_NONE            2  /* lr */
+
+/* One whole 2D matrix held by its owner ([P §3]).
+ *   W          rows x cols weight, w_dtype, row stride ld_w; updated in place.
+ *   G          rows x cols gradient, g_dtype, row stride ld_g; read only.  It is
+ *              the already-reduced full gradient: the library neither averages
+ *              nor scales it.
+ *   M          rows x cols fp32 momentum, row stride ld_m; updated in place.
+ *   update_out optional (NULL): rows x cols fp32, row stride ld_u, receives
+ *              lr_eff * O, the orthogonalised update before it meets W.
+ * rows == 0 or cols == 0 marks an empty shard (a non-owner's view of the
+ * matrix, [P §4.4]); it is validated and skipped, its pointers may be NULL. */
+typedef struct mo_matrix {
+    void*       W;
+    const void* G;
+    float*      M;
+    float*      update_out;
+    int64_t     rows, cols;
+    int64_t     ld_w, ld_g, ld_m, ld_u;
+    int32_t     w_dtype, g_dtype;
+} mo_matrix;
+
+/* Muon hyperparameters ([P §5.1] lists lr, weight decay, momentum, the number
+ * of Newton-Schulz steps and the lr adjustment; the quintic coefficients and
+ * eps are torch.optim.Muon's: (3.4445, -4.7750, 2.0315), 1e-7).
+ *   momentum  beta of the EMA  M' = beta*M + (1-beta)*G
+ *   nesterov  nonzero: U = (1-beta)*G + beta*M'; zero: U = M'
+ *   ns_steps  K >= 0 quintic iterations X <- a X + (b A + c A^2) X, A = X X^T,
+ *             on X = U / max(||U||_F, eps) in the short-side frame (U^T when
+ *             rows > cols)
+ *   ns_dtype  MO_BF16: X, A, B are bf16 MFMA operands with fp32 accumulation
+ *             and fp32 epilogues; MO_F32: fp32 throughout
+ * The step is W' = (1 - lr*wd) * W - lr_eff * O with lr_eff per lr_adjust. */
+typedef struct mo_muon_hparams {
+    float   lr, weight_decay, momentum;
+    int32_t nesterov, ns_steps;
+    float   ns_a, ns_b, ns_c, eps;
+    int32_t lr_adjust, ns_dtype;
+} mo_muon_hparams;
+
+/* Bytes of device workspace muon_owner_step needs for this bucket (including
+ * the device copy of the work list and 256 bytes of alignment slack). */
+mo_status muon_workspace_bytes(const mo_matrix* mats, int32_t n_mats,
+                               const mo_muon_hparams* hp, size_t* bytes);
+
+/* The host work list that muon_owner_step uploads, for inspection and tests.
+ * If host_buf is NULL, *bytes_inout receives the size; otherwise *bytes_inout
+ * must hold at least that size and the list is written to host_buf.  The byte
+ * layout (little-endian, packed, version 1):
+ *   header   mo_wl_header (128 bytes)
+ *   matrices mo_wl_mat[n_live] (192 bytes each), one per non-empty descriptor,
+ *            in descriptor order
+ *   items    three arrays of mo_wl_item (8 bytes): Gram, Poly, Update tiles,
+ *            each array starting on a 256-byte boundary
+ * Gram and Poly items are the upper-triangle tiles (ti <= tj) of the m_pad x
+ * m_pad product, Update items all tiles of the m_pad x n_pad product; matrices
+ * appear in descending order of their per-phase work, ties by descriptor
+ * index, tiles of one matrix in row-major order. */
+mo_status muon_build_worklist(const mo_matrix* mats, int32_t n_mats,
+                              const mo_muon_hparams* hp, void* host_buf,
+                              size_t* bytes_inout);
+
+/* One Muon step on every non-empty matrix of the bucket ([P §3], [P §4.4]).
+ * workspace: device memory of at least muon_workspace_bytes() bytes, disjoint
+ * from every tensor; its contents are undefined afterwards and it must not be
+ * shared by calls that may run concurrently.  n_mats == 0 is a no-op.
+ * Errors: MO_ERR_INVALID_ARG (null pointer with numel > 0, negative size,
+ * ld < cols, ns_steps < 0, non-finite hyperparameter, eps <= 0, unknown
+ * lr_adjust), MO_ERR_UNSUPPORTED (dtype not MO_F32/MO_BF16, a side longer than
+ * 2^23), MO_ERR_WORKSPACE_TOO_SMALL, MO_ERR_ALIAS (W, M, update_out of any
+ * matrix overlap any tensor of the bucket or the workspace), MO_ERR_HIP. */
+mo_status muon_owner_step(const mo_matrix* mats, int32_t n_mats,
+                          const mo_muon_hparams* hp, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* One AdamW step on a packed fp32 tail of n elements, in place ([P §3]: the
+ * non-2D tensors stay on the AdamW path; [P §5.1] gives the hyperparameters):
+ *   m' = b1 m + (1-b1) g;  v' = b2 v + (1-b2) g^2;
+ *   p' = p (1 - lr wd) - (lr / (1-b1^t)) m' / (sqrt(v') / sqrt(1-b2^t) + eps)
+ * with the bias corrections formed on the host in fp64.  step t >= 1.
+ * Errors: MO_ERR_INVALID_ARG (null pointer with n > 0, n < 0, step < 1,
+ * non-finite hyperparameter), MO_ERR_ALIAS (p, g, m, v overlap), MO_ERR_HIP. */
+mo_status adamw_tail_step(float* p, const float* g, float* m, float* v, int64_t n,
+                          int64_t step, float lr, float beta1, float beta2, float eps,
+                          float weight_decay, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* mo_status_string(mo_status status);
+
+/* ---- measurement support (not part of the optimizer step) ---------------- */
+
+/* Phase identifiers for per-kernel timing. */
+#define MO_PHASE_MOMENTUM 0   /* momentum + Nesterov + norm partials + NS-frame layout */
+#define MO_PHASE_NORM     1   /* per-matrix norm finalisation */
+#define MO_PHASE_GRAM     2   /* A = X X^T (upper tiles, mirrored) */
+#define MO_PHASE_POLY     3   /* B = b A + c A A */
+#define MO_PHASE_UPDATE   4   /* X <- a X + B X; last step writes W */
+#define MO_PHASE_APPLY    5   /* K == 0 only: W <- (1-lr wd) W - lr_eff X */
+#define MO_PHASE_ADAMW    6
+#define MO_PHASE_COPY     7   /* mo_device_copy */
+#define MO_PHASE_COUNT    8
+
+/* Enable (1) or disable (0) per-launch timing on the calling thread.  While
+ * enabled, every kernel launch is bracketed by HIP events on its own stream;
+ * mo_profile_read() synchronises on them.  Timing costs a few microseconds of
+ * host time per launch and does not change any result. */
+mo_status mo_profile_enable(int32_t enable);
+
+/* Wait for the recorded launches, then add their durations (ms) and counts to
+ * ms[MO_PHASE_COUNT] and launches[MO_PHASE_COUNT] and forget them. */
+mo_status mo_profile_read(double* ms, int64_t* launches);
+
+/* A plain device-to-device copy kernel (16-byte vector loads and stores), used
+ * to calibrate HBM byte counters against a transfer of known size.  dst and
+ * src must not overlap; bytes must be a multiple of 16 and both pointers
+ * 16-byte aligned.  Errors: MO_ERR_INVALID_ARG, MO_ERR_ALIAS, MO_ERR_HIP. */
+mo_status mo_device_copy(void* dst, const void* src, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MATRIX_OPTIMIZERS_AMD_MO_H */

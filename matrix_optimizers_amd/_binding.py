@@ -1,0 +1,307 @@
+"""ctypes binding of ``libmo.so`` (the C ABI declared in ``include/mo.h``).
+
+Argument marshalling only: every step of the optimizer runs in the library's
+HIP kernels.  PyTorch is used for device memory (the workspace) and for the
+current HIP stream.  If the library is missing this module raises; there is no
+fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence, Tuple
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmo.so")
+
+MO_OK = 0
+MO_ERR_INVALID_ARG = -1
+MO_ERR_UNSUPPORTED = -2
+MO_ERR_WORKSPACE_TOO_SMALL = -3
+MO_ERR_ALIAS = -4
+MO_ERR_HIP = -5
+
+MO_F32 = 0
+MO_BF16 = 1
+DTYPES = {"f32": MO_F32, "float32": MO_F32, "bf16": MO_BF16, "bfloat16": MO_BF16}
+
+LR_ADJUST = {"original": 0, "match_rms_adamw": 1, "none": 2}
+
+PHASES = ["momentum", "norm", "gram", "poly", "update", "apply", "adamw", "copy"]
+
+
+class MoError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+class MoMatrix(ctypes.Structure):
+    _fields_ = [("W", ctypes.c_void_p), ("G", ctypes.c_void_p), ("M", ctypes.c_void_p),
+                ("update_out", ctypes.c_void_p),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("ld_w", ctypes.c_int64), ("ld_g", ctypes.c_int64), ("ld_m", ctypes.c_int64),
+                ("ld_u", ctypes.c_int64),
+                ("w_dtype", ctypes.c_int32), ("g_dtype", ctypes.c_int32)]
+
+
+class MoMuonHParams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("weight_decay", ctypes.c_float),
+                ("momentum", ctypes.c_float), ("nesterov", ctypes.c_int32),
+                ("ns_steps", ctypes.c_int32), ("ns_a", ctypes.c_float), ("ns_b", ctypes.c_float),
+                ("ns_c", ctypes.c_float), ("eps", ctypes.c_float), ("lr_adjust", ctypes.c_int32),
+                ("ns_dtype", ctypes.c_int32)]
+
+
+_lib = None
+
+EXPORTS = ["muon_workspace_bytes", "muon_build_worklist", "muon_owner_step", "adamw_tail_step",
+           "mo_status_string", "mo_profile_enable", "mo_profile_read", "mo_device_copy"]
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libmo.so once; raise loudly if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m matrix_optimizers_amd.build`"
+                           " (there is no non-HIP fallback)")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER
+    lib.muon_workspace_bytes.argtypes = [P(MoMatrix), ctypes.c_int32, P(MoMuonHParams),
+                                         P(ctypes.c_size_t)]
+    lib.muon_build_worklist.argtypes = [P(MoMatrix), ctypes.c_int32, P(MoMuonHParams),
+                                        ctypes.c_void_p, P(ctypes.c_size_t)]
+    lib.muon_owner_step.argtypes = [P(MoMatrix), ctypes.c_int32, P(MoMuonHParams),
+                                    ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.adamw_tail_step.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64, ctypes.c_int64] + \
+        [ctypes.c_float] * 5 + [ctypes.c_void_p]
+    lib.mo_status_string.argtypes = [ctypes.c_int32]
+    lib.mo_status_string.restype = ctypes.c_char_p
+    lib.mo_profile_enable.argtypes = [ctypes.c_int32]
+    lib.mo_profile_read.argtypes = [P(ctypes.c_double), P(ctypes.c_int64)]
+    lib.mo_device_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                   ctypes.c_void_p]
+    for name in ("muon_workspace_bytes", "muon_build_worklist", "muon_owner_step",
+                 "adamw_tail_step", "mo_profile_enable", "mo_profile_read", "mo_device_copy"):
+        getattr(lib, name).restype = ctypes.c_int32
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().mo_status_string(int(status)).decode()
+
+
+mo_status_string = status_string
+
+
+def _check(status: int, where: str) -> None:
+    if status != MO_OK:
+        raise MoError(status, where)
+
+
+# ---------------------------------------------------------------------------
+# descriptors
+# ---------------------------------------------------------------------------
+
+def hparams(lr: float = 0.02, weight_decay: float = 0.01, momentum: float = 0.95,
+            nesterov: bool = True, ns_steps: int = 5,
+            ns_coefficients: Tuple[float, float, float] = (3.4445, -4.7750, 2.0315),
+            eps: float = 1e-7, adjust_lr_fn: str = "original",
+            ns_dtype: str = "bf16") -> MoMuonHParams:
+    a, b, c = ns_coefficients
+    return MoMuonHParams(lr=lr, weight_decay=weight_decay, momentum=momentum,
+                         nesterov=1 if nesterov else 0, ns_steps=int(ns_steps), ns_a=a, ns_b=b,
+                         ns_c=c, eps=eps, lr_adjust=LR_ADJUST[adjust_lr_fn],
+                         ns_dtype=DTYPES[ns_dtype])
+
+
+def descriptor(rows: int, cols: int, W: int = 0, G: int = 0, M: int = 0, update_out: int = 0,
+               w_dtype: str = "bf16", g_dtype: str = "bf16", ld_w: int = 0, ld_g: int = 0,
+               ld_m: int = 0, ld_u: int = 0) -> MoMatrix:
+    """A raw descriptor from integer addresses (host-side planning and tests)."""
+    return MoMatrix(W=W or None, G=G or None, M=M or None, update_out=update_out or None,
+                    rows=rows, cols=cols, ld_w=ld_w, ld_g=ld_g, ld_m=ld_m, ld_u=ld_u,
+                    w_dtype=DTYPES[w_dtype] if isinstance(w_dtype, str) else int(w_dtype),
+                    g_dtype=DTYPES[g_dtype] if isinstance(g_dtype, str) else int(g_dtype))
+
+
+def _array(descs: Sequence[MoMatrix]):
+    n = len(descs)
+    arr = (MoMatrix * max(n, 1))()
+    for i, d in enumerate(descs):
+        arr[i] = d
+    return arr, n
+
+
+def workspace_bytes(descs: Sequence[MoMatrix], hp: MoMuonHParams) -> int:
+    lib = load_library()
+    arr, n = _array(descs)
+    out = ctypes.c_size_t(0)
+    _check(lib.muon_workspace_bytes(arr, n, ctypes.byref(hp), ctypes.byref(out)),
+           "muon_workspace_bytes")
+    return int(out.value)
+
+
+def build_worklist(descs: Sequence[MoMatrix], hp: MoMuonHParams) -> bytes:
+    lib = load_library()
+    arr, n = _array(descs)
+    size = ctypes.c_size_t(0)
+    _check(lib.muon_build_worklist(arr, n, ctypes.byref(hp), None, ctypes.byref(size)),
+           "muon_build_worklist")
+    buf = ctypes.create_string_buffer(size.value)
+    _check(lib.muon_build_worklist(arr, n, ctypes.byref(hp), buf, ctypes.byref(size)),
+           "muon_build_worklist")
+    return buf.raw[: size.value]
+
+
+muon_workspace_bytes = workspace_bytes
+muon_build_worklist = build_worklist
+
+
+# ---------------------------------------------------------------------------
+# torch-facing entry points
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return MO_F32
+    if t.dtype == torch.bfloat16:
+        return MO_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _row_stride(t) -> int:
+    if t.dim() != 2:
+        raise ValueError("matrices must be 2D")
+    if t.numel() and t.stride(1) != 1:
+        raise ValueError("matrices must be row-major with unit column stride")
+    return int(t.stride(0)) if t.numel() else 0
+
+
+def tensor_descriptor(W, G, M, update_out=None) -> MoMatrix:
+    torch = _torch()
+    if W.shape != G.shape or W.shape != M.shape:
+        raise ValueError("W, G, M shapes differ")
+    if M.dtype != torch.float32:
+        raise TypeError("momentum buffers are float32")
+    dev = W.device
+    for t in (G, M) + ((update_out,) if update_out is not None else ()):
+        if t.device != dev:
+            raise ValueError("W, G, M, update_out must be on one device")
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a HIP device")
+    rows, cols = W.shape
+    if update_out is not None:
+        if update_out.shape != W.shape or update_out.dtype != torch.float32:
+            raise ValueError("update_out must be float32 and shaped like W")
+    return MoMatrix(W=W.data_ptr() or None, G=G.data_ptr() or None, M=M.data_ptr() or None,
+                    update_out=(update_out.data_ptr() if update_out is not None else None),
+                    rows=rows, cols=cols, ld_w=_row_stride(W), ld_g=_row_stride(G),
+                    ld_m=_row_stride(M), ld_u=_row_stride(update_out) if update_out is not None else 0,
+                    w_dtype=_dtype_code(W), g_dtype=_dtype_code(G))
+
+
+def _stream_handle(stream) -> Optional[int]:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def muon_owner_step(mats: Sequence[Tuple], *, update_out: Optional[Sequence] = None,
+                    workspace=None, stream=None, **hp_kwargs) -> None:
+    """One Muon step over a bucket of (W, G, M) tensors, in place.
+
+    hp_kwargs: lr, weight_decay, momentum, nesterov, ns_steps, ns_coefficients,
+    eps, adjust_lr_fn ("original" | "match_rms_adamw" | "none"), ns_dtype
+    ("bf16" | "f32").  workspace: an optional uint8 device tensor of at least
+    workspace_bytes(); one is allocated when omitted.
+    """
+    torch = _torch()
+    lib = load_library()
+    hp = hparams(**hp_kwargs)
+    ups = list(update_out) if update_out is not None else [None] * len(mats)
+    descs = [tensor_descriptor(W, G, M, u) for (W, G, M), u in zip(mats, ups)]
+    arr, n = _array(descs)
+    need = ctypes.c_size_t(0)
+    _check(lib.muon_workspace_bytes(arr, n, ctypes.byref(hp), ctypes.byref(need)),
+           "muon_workspace_bytes")
+    if workspace is None:
+        dev = mats[0][0].device if mats else torch.device("cuda")
+        workspace = torch.empty(int(need.value), dtype=torch.uint8, device=dev)
+    _check(lib.muon_owner_step(arr, n, ctypes.byref(hp), ctypes.c_void_p(workspace.data_ptr()),
+                               workspace.numel(), ctypes.c_void_p(_stream_handle(stream))),
+           "muon_owner_step")
+
+
+class MuonOwnerStep:
+    """Reusable step over a fixed bucket: descriptors and workspace are prepared
+    once; ``__call__`` launches the step on the current (or given) stream."""
+
+    def __init__(self, mats: Sequence[Tuple], update_out: Optional[Sequence] = None,
+                 **hp_kwargs):
+        torch = _torch()
+        self.lib = load_library()
+        self.hp = hparams(**hp_kwargs)
+        ups = list(update_out) if update_out is not None else [None] * len(mats)
+        self.descs = [tensor_descriptor(W, G, M, u) for (W, G, M), u in zip(mats, ups)]
+        self.arr, self.n = _array(self.descs)
+        self.bytes = workspace_bytes(self.descs, self.hp)
+        dev = mats[0][0].device if mats else torch.device("cuda")
+        self.workspace = torch.empty(self.bytes, dtype=torch.uint8, device=dev)
+        self._keep = (mats, update_out)
+
+    def __call__(self, stream=None) -> None:
+        _check(self.lib.muon_owner_step(self.arr, self.n, ctypes.byref(self.hp),
+                                        ctypes.c_void_p(self.workspace.data_ptr()),
+                                        self.workspace.numel(),
+                                        ctypes.c_void_p(_stream_handle(stream))),
+               "muon_owner_step")
+
+
+def adamw_tail_step(p, g, m, v, step: int, *, lr: float = 1e-3, beta1: float = 0.9,
+                    beta2: float = 0.999, eps: float = 1e-8, weight_decay: float = 1e-2,
+                    stream=None) -> None:
+    """One AdamW step on flat fp32 device tensors p, g, m, v, in place."""
+    torch = _torch()
+    for t in (p, g, m, v):
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.device.type != "cuda":
+            raise ValueError("tail tensors must be contiguous float32 device tensors")
+        if t.numel() != p.numel():
+            raise ValueError("tail tensors differ in length")
+    lib = load_library()
+    _check(lib.adamw_tail_step(ctypes.c_void_p(p.data_ptr()), ctypes.c_void_p(g.data_ptr()),
+                               ctypes.c_void_p(m.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+                               p.numel(), int(step), lr, beta1, beta2, eps, weight_decay,
+                               ctypes.c_void_p(_stream_handle(stream))),
+           "adamw_tail_step")
+
+
+def device_copy(dst, src, stream=None) -> None:
+    lib = load_library()
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("destination too small")
+    _check(lib.mo_device_copy(ctypes.c_void_p(dst.data_ptr()), ctypes.c_void_p(src.data_ptr()),
+                              nbytes, ctypes.c_void_p(_stream_handle(stream))), "mo_device_copy")
+
+
+def profile_enable(on: bool = True) -> None:
+    _check(load_library().mo_profile_enable(1 if on else 0), "mo_profile_enable")
+
+
+def profile_read() -> dict:
+    """Per-phase {name: (total_ms, launches)} of the launches timed since the last read."""
+    ms = (ctypes.c_double * len(PHASES))()
+    cnt = (ctypes.c_int64 * len(PHASES))()
+    _check(load_library().mo_profile_read(ms, cnt), "mo_profile_read")
+    return {name: (ms[i], cnt[i]) for i, name in enumerate(PHASES)}

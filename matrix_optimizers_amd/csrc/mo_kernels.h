@@ -1,0 +1,24 @@
+// Host-side launchers of the gfx950 kernels (defined in the .hip files).
+// Each returns the status of its launch; arguments are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "mo_worklist.h"
+
+// `ws` is the 256-byte-aligned workspace base; the work list sits at ws[0].
+hipError_t mo_launch_momentum(const mo_wl_header& h, uint8_t* ws, float beta, int nesterov,
+                              hipStream_t s);
+hipError_t mo_launch_norm(const mo_wl_header& h, uint8_t* ws, hipStream_t s);
+hipError_t mo_launch_gram(const mo_wl_header& h, uint8_t* ws, int first, int xt_cur,
+                          hipStream_t s);
+hipError_t mo_launch_poly(const mo_wl_header& h, uint8_t* ws, hipStream_t s);
+hipError_t mo_launch_update(const mo_wl_header& h, uint8_t* ws, int first, int last, int xt_cur,
+                            hipStream_t s);
+hipError_t mo_launch_apply(const mo_wl_header& h, uint8_t* ws, hipStream_t s);
+hipError_t mo_launch_adamw(float* p, const float* g, float* m, float* v, int64_t n, float decay,
+                           float beta1, float beta2, float step_size, float inv_sqrt_bc2,
+                           float eps, hipStream_t s);
+hipError_t mo_launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s);

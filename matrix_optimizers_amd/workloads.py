@@ -245,3 +245,41 @@ def ns_flops_algorithmic(rows: int, cols: int, steps: int) -> float:
     B X is dense (2 m^2 n)."""
     m, n = min(rows, cols), max(rows, cols)
     return float(steps) * (3.0 * m * m * n + 1.0 * m ** 3)
+
+
+# ----------------------------------------------------------------------------
+# on-device generation for the multi-GB workloads (benchmarks and full-size
+# property tests); same distributions, torch's Philox stream instead of numpy's
+# ----------------------------------------------------------------------------
+
+def torch_normal(seed: int, index: int, role: int, shape, std: float, dtype: str, device):
+    import torch
+    tdt = torch.bfloat16 if dtype == BF16 else torch.float32
+    if std == 0.0:
+        return torch.zeros(shape, dtype=tdt, device=device)
+    g = torch.Generator(device=device)
+    g.manual_seed(torch_seed(seed, index, role))
+    x = torch.randn(shape, generator=g, dtype=torch.float32, device=device)
+    x.mul_(std)
+    return x.to(tdt)          # round to nearest even into the storage dtype
+
+
+def torch_matrix_inputs(wl: Workload, index: int, device, spec: Optional[MatrixSpec] = None):
+    """(W, G, M) device tensors for matrix `index` of `wl`, drawn on the device."""
+    spec = spec or wl.matrices[index]
+    shape = (spec.rows, spec.cols)
+    W = torch_normal(wl.seed, index, ROLE_W, shape, wl.w_std, wl.w_dtype, device)
+    G = torch_normal(wl.seed, index, ROLE_G, shape, wl.g_std * grad_scale(wl, index),
+                     wl.g_dtype, device)
+    M = torch_normal(wl.seed, index, ROLE_M, shape, wl.m_std, F32, device)
+    return W, G, M
+
+
+def torch_tail_inputs(seed: int, n: int, device):
+    import torch
+    p = torch_normal(seed, 0, ROLE_P, (n,), 0.02, F32, device)
+    g = torch_normal(seed, 0, ROLE_TG, (n,), 1e-3, F32, device)
+    m = torch_normal(seed, 0, ROLE_TM, (n,), 1e-3, F32, device)
+    v = torch_normal(seed, 0, ROLE_TV, (n,), 1e-3, F32, device)
+    v.mul_(v)
+    return p, g, m, v

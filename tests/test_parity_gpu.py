@@ -1,0 +1,190 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Sizes here run the oracle in seconds and span several 128-tiles plus ragged
+edges; the full-size workloads are covered in test_fullsize_gpu.py.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+from matrix_optimizers_amd import workloads as wlmod
+from oracle import adamw as oadamw
+
+from _parity import Case, check_case, random_case, rel, run_gpu, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+BF = wlmod.MuonHP()                         # bf16 Newton-Schulz, torch.optim.Muon defaults
+F32HP = wlmod.MuonHP(ns_dtype="f32")
+
+
+def test_single_256x512_f32_workload(gpu):
+    """The one-matrix fp32 workload in full: fp32 NS, zero momentum, G ~ N(0, 1)."""
+    wl = wlmod.get("single_256x512_f32")
+    x = wlmod.matrix_inputs(wl, 0)
+    c = Case(x.W, x.G, x.M, wl.w_dtype, wl.g_dtype)
+    got = run_gpu([c], wl.hp, gpu)[0]
+    errs = check_case(c, got, wl.hp)
+    print("single_256x512_f32", errs)
+
+
+SHAPES = [(1, 1), (1, 300), (300, 1), (33, 17), (17, 33), (100, 257), (257, 100),
+          (384, 640), (640, 384), (300, 700), (700, 300), (129, 129)]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("ns", ["bf16", "f32"])
+def test_ragged_shapes(gpu, shape, ns):
+    """Tiny, ragged and multi-tile shapes, tall and wide, both NS precisions."""
+    hp = dataclasses.replace(BF, ns_dtype=ns)
+    c = random_case(*shape, "bf16" if ns == "bf16" else "f32", "bf16" if ns == "bf16" else "f32",
+                    seed=hash(shape) & 0xFFFF)
+    errs = check_case(c, run_gpu([c], hp, gpu)[0], hp)
+    print(shape, ns, errs)
+
+
+def test_mixed_bucket_with_empty_shards(gpu):
+    """One grouped launch over differently shaped matrices, with empty shards
+    (a non-owner's view) that must be skipped."""
+    shapes = [(256, 256), (0, 5), (128, 512), (512, 128), (5, 0), (70, 190), (190, 70)]
+    cases = [random_case(r, c, "bf16", "bf16", seed=i + 11) for i, (r, c) in enumerate(shapes)]
+    got = run_gpu(cases, BF, gpu)
+    for c, g in zip(cases, got):
+        print(c.W.shape, check_case(c, g, BF))
+
+
+def test_strided_tensors(gpu):
+    """Row strides larger than the row length (views into wider tensors)."""
+    cases = [random_case(200, 96, "bf16", "bf16", seed=3), random_case(96, 200, "f32", "bf16", seed=4)]
+    got = run_gpu(cases, BF, gpu, strided=True)
+    for c, g in zip(cases, got):
+        print(c.W.shape, check_case(c, g, BF))
+
+
+@pytest.mark.parametrize("w_dtype,g_dtype,ns", [("f32", "bf16", "bf16"), ("bf16", "f32", "f32"),
+                                                 ("f32", "f32", "bf16"), ("bf16", "bf16", "f32")])
+def test_dtype_combinations(gpu, w_dtype, g_dtype, ns):
+    hp = dataclasses.replace(BF, ns_dtype=ns)
+    c = random_case(160, 416, w_dtype, g_dtype, seed=21)
+    print(w_dtype, g_dtype, ns, check_case(c, run_gpu([c], hp, gpu)[0], hp))
+
+
+@pytest.mark.parametrize("variant", [
+    dict(ns_steps=0), dict(ns_steps=1), dict(ns_steps=2, momentum=0.5, lr_adjust="match_rms_adamw"),
+    dict(nesterov=False), dict(lr_adjust="none"), dict(lr_adjust="match_rms_adamw"),
+    dict(weight_decay=0.0), dict(ns_a=1.5, ns_b=-0.5, ns_c=0.0, ns_steps=8),
+])
+def test_hyperparameter_variants(gpu, variant):
+    hp = dataclasses.replace(BF, **variant)
+    cases = [random_case(192, 320, "bf16", "bf16", seed=5), random_case(320, 192, "bf16", "bf16", seed=6)]
+    got = run_gpu(cases, hp, gpu)
+    for c, g in zip(cases, got):
+        print(variant, c.W.shape, check_case(c, g, hp))
+
+
+def test_zero_gradient_and_eps_clamp(gpu):
+    """G = M = 0 gives W' = (1 - lr wd) W exactly; a tiny gradient (||U|| < eps)
+    is divided by eps, not by its norm."""
+    z = random_case(130, 70, "f32", "f32", seed=8)
+    z.G[:] = 0
+    z.M[:] = 0
+    W1, M1, D1 = run_gpu([z], F32HP, gpu)[0]
+    assert not M1.any() and not D1.any()
+    decay = np.float32(1 - np.float32(F32HP.lr) * np.float32(F32HP.weight_decay))
+    np.testing.assert_allclose(W1, (decay * z.W).astype(np.float64), rtol=1e-7, atol=0)
+    tiny = random_case(64, 96, "f32", "f32", seed=9, g_std=1e-12, m_std=0.0)
+    print("tiny", check_case(tiny, run_gpu([tiny], F32HP, gpu)[0], F32HP))
+
+
+def test_without_update_out_is_identical(gpu):
+    """The optional update output does not change what is written to W and M."""
+    cases = [random_case(200, 520, "bf16", "bf16", seed=12), random_case(520, 200, "bf16", "bf16", seed=13)]
+    a = run_gpu(cases, BF, gpu, with_update=True)
+    b = run_gpu(cases, BF, gpu, with_update=False)
+    for (Wa, Ma, _), (Wb, Mb, _) in zip(a, b):
+        np.testing.assert_array_equal(Wa, Wb)
+        np.testing.assert_array_equal(Ma, Mb)
+
+
+def test_deterministic_and_bucket_independent(gpu):
+    """Same inputs give bit-identical outputs; a matrix's result does not depend
+    on the rest of its bucket."""
+    cases = [random_case(256, 768, "bf16", "bf16", seed=14), random_case(384, 128, "bf16", "bf16", seed=15),
+             random_case(1000, 300, "bf16", "bf16", seed=16)]
+    a = run_gpu(cases, BF, gpu)
+    b = run_gpu(cases, BF, gpu)
+    alone = run_gpu([cases[1]], BF, gpu)[0]
+    for x, y in zip(a, b):
+        for u, v in zip(x, y):
+            np.testing.assert_array_equal(u, v)
+    for u, v in zip(a[1], alone):
+        np.testing.assert_array_equal(u, v)
+
+
+def test_power_of_two_scale_invariance_bit_exact(gpu):
+    """NS(alpha X) = NS(X): scaling G and M by 4 scales U, its norm and every
+    partial exactly, so the update is bit-identical."""
+    c = random_case(384, 640, "f32", "f32", seed=17)
+    c4 = Case(c.W.copy(), c.G * 4, c.M * 4, "f32", "f32")
+    a = run_gpu([c], BF, gpu)[0]
+    b = run_gpu([c4], BF, gpu)[0]
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[2], b[2])
+
+
+def test_decoder_layer_bucket_full(gpu):
+    """The hidden-2048 decoder-layer owner bucket in full (7 matrices) plus its
+    AdamW tail."""
+    wl = wlmod.get("decoder_layer_h2048")
+    cases = []
+    for i in range(len(wl.matrices)):
+        x = wlmod.matrix_inputs(wl, i)
+        cases.append(Case(x.W, x.G, x.M, wl.w_dtype, wl.g_dtype))
+    got = run_gpu(cases, wl.hp, gpu)
+    for spec, c, g in zip(wl.matrices, cases, got):
+        print(spec.name, check_case(c, g, wl.hp))
+    check_tail(gpu, wl.seed, wl.tail_numel, wl.adamw)
+
+
+def check_tail(device, seed, n, a: wlmod.AdamWHP):
+    import matrix_optimizers_amd as mo
+    t = wlmod.tail_inputs(seed, n)
+    p, g, m, v = (to_dev(x, "f32", device) for x in (t.p, t.g, t.m, t.v))
+    mo.adamw_tail_step(p, g, m, v, a.step, lr=a.lr, beta1=a.beta1, beta2=a.beta2, eps=a.eps,
+                       weight_decay=a.weight_decay)
+    f = lambda x: float(np.float32(x))
+    po, mo_, vo = oadamw.adamw_step(t.p, t.g, t.m, t.v, a.step, f(a.lr), f(a.beta1), f(a.beta2),
+                                    f(a.eps), f(a.weight_decay))
+    errs = (rel(to_host(p), po), rel(to_host(m), mo_), rel(to_host(v), vo))
+    print("adamw", n, errs)
+    assert max(errs) <= 1e-6, errs
+
+
+@pytest.mark.parametrize("n", [0, 1, 3, 4, 1023, 4096, 32768, 1 << 20])
+def test_adamw_tail(gpu, n):
+    check_tail(gpu, 40 + n % 7, n, wlmod.AdamWHP())
+
+
+@pytest.mark.parametrize("step", [1, 2, 1000])
+def test_adamw_steps(gpu, step):
+    check_tail(gpu, 50, 5000, dataclasses.replace(wlmod.AdamWHP(), step=step))
+
+
+def test_adamw_misaligned_views(gpu):
+    """Tail tensors that start 4 bytes off a 16-byte boundary take the scalar path."""
+    import torch
+    import matrix_optimizers_amd as mo
+    n = 1001
+    t = wlmod.tail_inputs(60, n)
+    bufs = [torch.zeros(n + 1, dtype=torch.float32, device=gpu) for _ in range(4)]
+    views = [b[1:] for b in bufs]
+    for v_, x in zip(views, (t.p, t.g, t.m, t.v)):
+        v_.copy_(torch.from_numpy(x))
+    a = wlmod.AdamWHP()
+    mo.adamw_tail_step(*views, a.step, lr=a.lr, beta1=a.beta1, beta2=a.beta2, eps=a.eps,
+                       weight_decay=a.weight_decay)
+    f = lambda x: float(np.float32(x))
+    po, _, _ = oadamw.adamw_step(t.p, t.g, t.m, t.v, a.step, f(a.lr), f(a.beta1), f(a.beta2),
+                                 f(a.eps), f(a.weight_decay))
+    assert rel(to_host(views[0]), po) <= 1e-6
