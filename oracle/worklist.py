@@ -1,0 +1,141 @@
+"""Independent Python builder of the host work list (test infrastructure).
+
+The work list is this library's own data structure (no page defines it); its
+byte layout is specified in ``include/mo.h`` (muon_build_worklist) and the
+record comments there.  This twin is written from that specification with
+Python's ``struct`` so that the C++ builder can be checked byte for byte.
+
+Layout (little-endian, natural alignment, version 1):
+  header (128 B): magic 'MOWL', version, n_mats, ns_steps, ns_dtype, gemm_tile,
+      mom_tile, elem_bytes, n_mom_items, n_gram_items, n_poly_items,
+      n_upd_items, max_partials, 0, mats_offset, gram_offset, poly_offset,
+      upd_offset, wl_bytes, ws_bytes (u64), ns_a, ns_b, ns_c, eps (f32), 2 x 0
+  matrix record (192 B) per non-empty descriptor, descriptor order: W, G, M,
+      update_out (u64), ld_w, ld_g, ld_m, ld_u (i64; 0 -> cols), off_X,
+      off_Xt0, off_Xt1, off_A, off_B, off_partials, off_scale (u64), rows,
+      cols, m, n, m_pad, n_pad, flags, desc_index, mom_begin, mom_tiles_c,
+      n_partials (u32), lr_eff, decay (f32), 5 x 0
+  items (8 B: u32 matrix record index, u16 ti, u16 tj): Gram, Poly, Update,
+      each list 256-byte aligned
+Workspace regions follow the list, per record: X, Xt0, Xt1 (m_pad*n_pad
+elements each), A, B (m_pad^2), partials (n_partials fp32), scale (16 B); every
+region 256-byte aligned.
+"""
+from __future__ import annotations
+
+import math
+import struct
+from typing import List, Sequence
+
+T = 128       # GEMM tile edge
+MT = 64       # momentum tile edge
+ALIGN = 256
+MAGIC = 0x4C574F4D
+
+F32, BF16 = 0, 1
+LR_ORIGINAL, LR_MATCH, LR_NONE = 0, 1, 2
+
+FLAG_TRANSPOSED, FLAG_HAS_UPDATE, FLAG_W_BF16, FLAG_G_BF16 = 1, 2, 4, 8
+
+
+def _up(x: int, a: int) -> int:
+    return (x + a - 1) // a * a
+
+
+def _f32(x: float) -> float:
+    return struct.unpack("<f", struct.pack("<f", x))[0]
+
+
+def build(descs: Sequence[dict], hp: dict) -> bytes:
+    """descs: dicts with rows, cols, W, G, M, update_out (ints), ld_w, ld_g, ld_m,
+    ld_u, w_dtype, g_dtype.  hp: lr, weight_decay, ns_steps, ns_a, ns_b, ns_c,
+    eps, lr_adjust, ns_dtype (ints for the enums)."""
+    es = 2 if hp["ns_dtype"] == BF16 else 4
+    lr = _f32(hp["lr"])
+    wd = _f32(hp["weight_decay"])
+    recs = []
+    mom = 0
+    max_partials = 0
+    for i, d in enumerate(descs):
+        rows, cols = d["rows"], d["cols"]
+        if rows == 0 or cols == 0:
+            continue
+        tr = rows > cols
+        m, n = min(rows, cols), max(rows, cols)
+        m_pad, n_pad = _up(m, T), _up(n, T)
+        r_pad, c_pad = (n_pad, m_pad) if tr else (m_pad, n_pad)
+        n_part = (r_pad // MT) * (c_pad // MT)
+        if hp["lr_adjust"] == LR_ORIGINAL:
+            factor = math.sqrt(max(1.0, rows / cols))
+        elif hp["lr_adjust"] == LR_MATCH:
+            factor = 0.2 * math.sqrt(float(max(rows, cols)))
+        else:
+            factor = 1.0
+        flags = (FLAG_TRANSPOSED if tr else 0) | (FLAG_HAS_UPDATE if d.get("update_out") else 0) \
+            | (FLAG_W_BF16 if d["w_dtype"] == BF16 else 0) | (FLAG_G_BF16 if d["g_dtype"] == BF16 else 0)
+        recs.append(dict(W=d.get("W", 0), G=d.get("G", 0), M=d.get("M", 0), U=d.get("update_out", 0) or 0,
+                         ld_w=d.get("ld_w", 0) or cols, ld_g=d.get("ld_g", 0) or cols,
+                         ld_m=d.get("ld_m", 0) or cols, ld_u=d.get("ld_u", 0) or cols,
+                         rows=rows, cols=cols, m=m, n=n, m_pad=m_pad, n_pad=n_pad, flags=flags,
+                         desc_index=i, mom_begin=mom, mom_tiles_c=c_pad // MT, n_partials=n_part,
+                         lr_eff=lr * factor, decay=1.0 - lr * wd))
+        mom += n_part
+        max_partials = max(max_partials, n_part)
+
+    def ordered(work):
+        idx = list(range(len(recs)))
+        return sorted(idx, key=lambda j: -work(recs[j]))   # stable: ties keep order
+
+    def upper(r):
+        t = r["m_pad"] // T
+        return t * (t + 1) // 2
+
+    gram, poly, upd = [], [], []
+    for j in ordered(lambda r: upper(r) * r["n_pad"]):
+        t = recs[j]["m_pad"] // T
+        gram += [(j, a, b) for a in range(t) for b in range(a, t)]
+    for j in ordered(lambda r: upper(r) * r["m_pad"]):
+        t = recs[j]["m_pad"] // T
+        poly += [(j, a, b) for a in range(t) for b in range(a, t)]
+    for j in ordered(lambda r: (r["m_pad"] // T) * (r["n_pad"] // T) * r["m_pad"]):
+        tm, tn = recs[j]["m_pad"] // T, recs[j]["n_pad"] // T
+        upd += [(j, a, b) for a in range(tm) for b in range(tn)]
+
+    mats_off = 128
+    gram_off = _up(mats_off + 192 * len(recs), ALIGN)
+    poly_off = _up(gram_off + 8 * len(gram), ALIGN)
+    upd_off = _up(poly_off + 8 * len(poly), ALIGN)
+    wl_bytes = _up(upd_off + 8 * len(upd), ALIGN)
+
+    off = wl_bytes
+    for r in recs:
+        mn, mm = r["m_pad"] * r["n_pad"], r["m_pad"] * r["m_pad"]
+        for key, size in (("off_X", mn * es), ("off_Xt0", mn * es), ("off_Xt1", mn * es),
+                          ("off_A", mm * es), ("off_B", mm * es),
+                          ("off_partials", r["n_partials"] * 4), ("off_scale", 16)):
+            r[key] = off
+            off = _up(off + size, ALIGN)
+    ws_bytes = off
+
+    out = bytearray(wl_bytes)
+    struct.pack_into("<14I6Q4f2I", out, 0, MAGIC, 1, len(recs), hp["ns_steps"], hp["ns_dtype"],
+                     T, MT, es, mom, len(gram), len(poly), len(upd), max_partials, 0,
+                     mats_off, gram_off, poly_off, upd_off, wl_bytes, ws_bytes,
+                     hp["ns_a"], hp["ns_b"], hp["ns_c"], hp["eps"], 0, 0)
+    for k, r in enumerate(recs):
+        struct.pack_into("<4Q4q7Q11I2f5I", out, mats_off + 192 * k,
+                         r["W"], r["G"], r["M"], r["U"], r["ld_w"], r["ld_g"], r["ld_m"], r["ld_u"],
+                         r["off_X"], r["off_Xt0"], r["off_Xt1"], r["off_A"], r["off_B"],
+                         r["off_partials"], r["off_scale"],
+                         r["rows"], r["cols"], r["m"], r["n"], r["m_pad"], r["n_pad"], r["flags"],
+                         r["desc_index"], r["mom_begin"], r["mom_tiles_c"], r["n_partials"],
+                         r["lr_eff"], r["decay"], 0, 0, 0, 0, 0)
+    for base, items in ((gram_off, gram), (poly_off, poly), (upd_off, upd)):
+        for k, (j, a, b) in enumerate(items):
+            struct.pack_into("<IHH", out, base + 8 * k, j, a, b)
+    return bytes(out)
+
+
+def workspace_bytes(descs: Sequence[dict], hp: dict) -> int:
+    wl = build(descs, hp)
+    return struct.unpack_from("<Q", wl, 96)[0] + ALIGN

@@ -141,6 +141,12 @@ def check_case(c: Case, got, hp: wlmod.MuonHP, tol: Optional[float] = None) -> d
         # evaluation can move a value across a binade boundary
         err = np.abs(W1 - want) / bf16_ulp(np.maximum(np.abs(W1), np.abs(want)))
         out["w_ulps"] = float(err.max())
+        if out["w_ulps"] > 1.0 + 1e-6:
+            worst = np.argsort(err.ravel())[-4:]
+            rows = [(int(k) // W1.shape[1], int(k) % W1.shape[1], float(c.W.ravel()[k]),
+                     float(D1.ravel()[k]), float(want.ravel()[k]), float(W1.ravel()[k]))
+                    for k in worst]
+            out["worst(row,col,W,delta,want,got)"] = rows
         assert out["w_ulps"] <= 1.0 + 1e-6, out
     else:
         out["w_rel"] = rel(W1, want)
