@@ -38,7 +38,38 @@ def parse():
                     help="time the loop without per-launch events (no roofline object)")
     ap.add_argument("--profile-only", action="store_true",
                     help="warmup + timed steps only, no oracle leg (for profilers)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the step, time the library's plain copy kernel over "
+                         "MIB mebibytes (HBM ceiling; byte-counter calibration)")
     return ap.parse_args()
+
+
+def copy_calibration(args):
+    """Times mo_device_copy over a buffer of known size: the measured HBM copy
+    ceiling, and the reference transfer for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    import matrix_optimizers_amd as mo
+    nbytes = args.copy_calibration << 20
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").random_(0, 255)
+    dst = torch.empty_like(src)
+    for _ in range(max(args.warmup, 1)):
+        mo.device_copy(dst, src)
+    torch.cuda.synchronize()
+    mo.profile_read()
+    mo.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        mo.device_copy(dst, src)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    mo.profile_enable(False)
+    tot, cnt = mo.profile_read()["copy"]
+    assert torch.equal(dst, src)
+    per = tot / cnt
+    out = {"metric": "device copy bandwidth (read + write)", "bytes_per_launch": 2 * nbytes,
+           "avg_ms": round(per, 5), "GBps": round(2 * nbytes / (per * 1e-3) / 1e9, 1),
+           "wall_ms_per_launch": round((t1 - t0) * 1e3 / args.steps, 5), "peak_GBps": PEAK_HBM_GBS}
+    print(json.dumps(out), flush=True)
 
 
 def algorithmic_flops(spec_rows, spec_cols, steps):
@@ -94,6 +125,8 @@ def main():
     import matrix_optimizers_amd as mo
     from matrix_optimizers_amd import workloads as wlmod
 
+    if args.copy_calibration:
+        return copy_calibration(args)
     wl = wlmod.get(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -24,7 +24,7 @@
 
 namespace {
 
-constexpr int64_t kMaxSide = int64_t(1) << 23;   // 65535 tiles of 128, rounded down
+constexpr int64_t kMaxSide = int64_t(1) << 23;   // 32768 tiles of 256: tile indexes fit 16 bits
 
 inline uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 
@@ -171,22 +171,30 @@ void build_plan(const mo_matrix* mats, int32_t n, const mo_muon_hparams* hp, Pla
         return ks;
     };
     auto upper = [&](const mo_wl_mat& r) { uint64_t t = r.m_pad / T; return t * (t + 1) / 2; };
+    // Tiles of one matrix are emitted in super-blocks of SB_R tile-rows x SB_C
+    // tile-columns (super-blocks row-major, tiles row-major inside), so that
+    // the 32 tiles one XCD runs at a time share 4 row panels and 8 column
+    // panels of their operands in that XCD's L2.
+    constexpr uint32_t SB_R = 4, SB_C = 8;
+    auto emit = [](std::vector<mo_wl_item>& out, uint32_t idx, uint32_t tm, uint32_t tn, bool upper_only) {
+        for (uint32_t bi = 0; bi < tm; bi += SB_R)
+            for (uint32_t bj = 0; bj < tn; bj += SB_C)
+                for (uint32_t a = bi; a < std::min(bi + SB_R, tm); ++a)
+                    for (uint32_t b = bj; b < std::min(bj + SB_C, tn); ++b)
+                        if (!upper_only || a <= b) out.push_back({idx, uint16_t(a), uint16_t(b)});
+    };
     std::vector<mo_wl_item> gram, poly, upd;
     for (const Key& k : order([&](const mo_wl_mat& r) { return upper(r) * r.n_pad; })) {
         const uint32_t t = recs[k.idx].m_pad / T;
-        for (uint32_t a = 0; a < t; ++a)
-            for (uint32_t b = a; b < t; ++b) gram.push_back({k.idx, uint16_t(a), uint16_t(b)});
+        emit(gram, k.idx, t, t, true);
     }
     for (const Key& k : order([&](const mo_wl_mat& r) { return upper(r) * r.m_pad; })) {
         const uint32_t t = recs[k.idx].m_pad / T;
-        for (uint32_t a = 0; a < t; ++a)
-            for (uint32_t b = a; b < t; ++b) poly.push_back({k.idx, uint16_t(a), uint16_t(b)});
+        emit(poly, k.idx, t, t, true);
     }
     for (const Key& k : order([&](const mo_wl_mat& r) {
              return uint64_t(r.m_pad / T) * (r.n_pad / T) * r.m_pad; })) {
-        const uint32_t tm = recs[k.idx].m_pad / T, tn = recs[k.idx].n_pad / T;
-        for (uint32_t a = 0; a < tm; ++a)
-            for (uint32_t b = 0; b < tn; ++b) upd.push_back({k.idx, uint16_t(a), uint16_t(b)});
+        emit(upd, k.idx, recs[k.idx].m_pad / T, recs[k.idx].n_pad / T, false);
     }
 
     mo_wl_header h;

@@ -11,12 +11,12 @@
 #include <stdint.h>
 
 #define MO_WL_MAGIC   0x4C574F4Du  // "MOWL"
-#define MO_WL_VERSION 1u
+#define MO_WL_VERSION 2u
 
 // Tile edge of the Newton-Schulz GEMMs.  Every NS-frame dimension is padded
 // to a multiple of it inside the workspace, with zeros, so the GEMM kernels
 // never test bounds: zero rows/columns of X stay zero through every step.
-#define MO_GEMM_TILE 128
+#define MO_GEMM_TILE 256
 // Tile of the momentum kernel in the weight's own frame.
 #define MO_MOM_TILE 64
 // Alignment of every workspace region.

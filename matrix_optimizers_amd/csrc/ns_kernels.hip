@@ -174,13 +174,17 @@ __global__ __launch_bounds__(MOM_THREADS) void apply_kernel(uint8_t* ws) {
 // NT GEMM family on MFMA:  C[i][j] = sum_k P[i][k] * Q[j][k]
 // ============================================================================
 //
-// Workgroup tile 128 x 128, 256 threads = 4 wavefronts in a 2 x 2 grid, each
-// wavefront owning 64 x 64 = 2 x 2 MFMA blocks of 32 x 32.  K advances by 128
-// bytes per stage (64 bf16 / 32 fp32) through double-buffered LDS; global loads
-// of stage s+1 are in flight while stage s is multiplied.  LDS rows are 128
-// bytes of eight 16-byte chunks, chunk index XOR (row & 7), so both the 16-byte
-// stores of the global->LDS copy and the 16-byte fragment reads of 8 (32)
-// consecutive rows hit distinct banks.
+// Workgroup tile 256 x 256, 256 threads = 4 wavefronts in a 2 x 2 grid; each
+// wavefront owns a 128 x 128 sub-tile = 4 x 4 MFMA blocks of 32 x 32 (256 fp32
+// accumulators per lane, held in AGPRs).  Per K stage every operand row
+// contributes 64 bytes (32 bf16 / 16 fp32): 2 x 256 rows x 64 B = 32 KB, in a
+// ring of four stages in LDS (128 KB of the CU's 160 KB, one workgroup per CU).
+// Global data goes straight to LDS (global_load_lds_dwordx4, no VGPR round
+// trip); stage s+4 is issued right after the barrier that publishes stage s+1,
+// into the slot stage s vacated, so up to three stages are in flight.
+//
+// A direct-to-LDS load writes lane l's 16 bytes at (wave base + 16 l), so each
+// lane fetches the global chunk that belongs at its physical (swizzled) slot.
 //
 // MFMA operands.  bf16: v_mfma_f32_32x32x16_bf16 takes 8 consecutive k per
 // lane; lane l supplies row (l % 32) and k-group (l / 32).  fp32:
@@ -189,20 +193,24 @@ __global__ __launch_bounds__(MOM_THREADS) void apply_kernel(uint8_t* ws) {
 // sum over all k is exact regardless of how k is split among lanes.  The 32 x 32
 // result sits in lane l, register v at row (v/4)*8 + (l/32)*4 + v%4, col l%32.
 //
-// Epilogue.  The fp32 tile is staged in LDS (128 x 132 floats), then written
-// out in the tile's orientation (pass A) and, where the product is needed
-// transposed, in the mirrored orientation (pass B), both as 16-byte chunks.
+// Epilogue, per wavefront and per 32-row block of its sub-tile: the fp32
+// values are staged in a private 16 KB LDS slice (column index XOR-swizzled by
+// row group), then written out as 16-byte chunks in the tile's own orientation
+// (pass A: 16 lanes cover one 128-column row) and, where the transposed
+// product is needed, in the mirrored orientation (pass B).
 
-constexpr int GT = MO_GEMM_TILE;           // 128
+constexpr int GT = MO_GEMM_TILE;           // 256
 constexpr int G_THREADS = 256;
-constexpr int KB = 128;                    // bytes of K per LDS stage and row
+constexpr int KB = 64;                     // bytes of K per LDS stage and row
+constexpr int NSTAGE = 4;                  // LDS ring depth (NSTAGE-1 stages in flight)
 constexpr int OPND_BYTES = GT * KB;        // 16 KB per operand per stage
-constexpr int MAIN_LDS = 4 * OPND_BYTES;   // 2 stages x 2 operands
-constexpr int ST = GT + 4;                 // staging row stride (floats)
-constexpr int EPI_LDS = GT * ST * 4;
-constexpr int GEMM_LDS = MAIN_LDS > EPI_LDS ? MAIN_LDS : EPI_LDS;
+constexpr int STAGE_BYTES = 2 * OPND_BYTES;
+constexpr int GEMM_LDS = NSTAGE * STAGE_BYTES;  // 128 KB
+constexpr int WAVE_ST_BYTES = 32 * 128 * 4;  // per-wave staging slice
 
 enum { KIND_GRAM = 0, KIND_POLY = 1, KIND_UPDATE = 2 };
+
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 template <typename T> struct Mfma;
 template <> struct Mfma<bf16_t> {
@@ -221,7 +229,13 @@ template <> struct Mfma<float> {
     }
 };
 
-MO_DEV int swz(int row, int chunk) { return row * KB + ((chunk ^ (row & 7)) << 4); }
+// 64-byte rows of four 16-byte chunks; logical chunk c of row r sits at
+// c ^ ((r >> 1) & 3), so 8 consecutive rows read at one logical chunk cover all
+// eight 16-byte bank groups.
+MO_DEV int swz(int row, int chunk) { return row * KB + ((chunk ^ ((row >> 1) & 3)) << 4); }
+
+// staging slice index: 128 fp32 columns per row, column bits 3..4 XOR row bits 3..4
+MO_DEV int st_idx(int row, int col) { return row * 128 + (col ^ (((row >> 3) & 3) << 3)); }
 
 // Block index -> logical item.  Consecutive workgroups are dealt round-robin
 // over the 8 XCDs; giving each XCD a contiguous run of items keeps the tiles
@@ -231,9 +245,86 @@ MO_DEV uint32_t xcd_item(uint32_t b, uint32_t nb) {
     return (b & 7) * chunk + (b >> 3);
 }
 
+// Epilogue context of one workgroup tile.
 template <typename T, int KIND>
-__global__ __launch_bounds__(G_THREADS, 2) void gemm_kernel(uint8_t* ws, int first, int last,
-                                                            int xt_cur) {
+struct Epi {
+    const mo_wl_mat* mt;
+    T *X, *Xt_nxt, *A, *B;
+    float alpha, sx, na, nb, nc;
+    int64_t m_pad, n_pad;
+    bool last, trans;
+
+    // pass A: 8 values at tile-orientation position (gi, gj..gj+7)
+    MO_DEV void pass_a(int64_t gi, int64_t gj, f32x8& v, float* slot) const {
+        if (KIND == KIND_GRAM) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v.v[e] *= alpha;
+            store8(A + gi * m_pad + gj, v);
+        } else if (KIND == KIND_POLY) {
+            f32x8 av;
+            load8(A + gi * m_pad + gj, av);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v.v[e] = nc * v.v[e] + nb * av.v[e];
+            store8(B + gi * m_pad + gj, v);
+        } else {
+            f32x8 xv;
+            load8(X + gi * n_pad + gj, xv);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v.v[e] = sx * (na * xv.v[e] + v.v[e]);
+            if (!last) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v.v[e] = quantize<T>(v.v[e]);
+                store8(X + gi * n_pad + gj, v);
+                store8(slot, v);
+            } else if (!trans) {
+                write_w(gi, gj, v);       // weight frame == NS frame
+            } else {
+                store8(slot, v);
+            }
+        }
+    }
+
+    // pass B: 8 values at mirrored position (oj, oi..oi+7)
+    MO_DEV void pass_b(int64_t oj, int64_t oi, f32x8& v) const {
+        if (KIND == KIND_GRAM) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v.v[e] *= alpha;
+            store8(A + oj * m_pad + oi, v);
+        } else if (KIND == KIND_POLY) {
+            f32x8 av;
+            load8(A + oj * m_pad + oi, av);     // A is exactly symmetric
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v.v[e] = nc * v.v[e] + nb * av.v[e];
+            store8(B + oj * m_pad + oi, v);
+        } else if (!last) {
+            store8(Xt_nxt + oj * m_pad + oi, v);
+        } else {
+            write_w(oj, oi, v);            // weight frame is the transpose
+        }
+    }
+
+    // W[r][c..c+7] <- decay * W - lr_eff * O, clipped to the matrix
+    MO_DEV void write_w(int64_t r, int64_t c, const f32x8& o) const {
+        if (r >= mt->rows) return;
+        const bool wbf = mt->flags & MO_WLF_W_BF16;
+        void* W = reinterpret_cast<void*>(mt->W);
+        float* U = reinterpret_cast<float*>(mt->U);
+        const float decay = mt->decay, lr = mt->lr_eff;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if (c + e < mt->cols) {
+                const int64_t wi = r * mt->ld_w + c + e;
+                const float w = load_elem(W, wi, wbf);
+                store_elem(W, wi, decay * w - lr * o.v[e], wbf);
+                if (U) U[r * mt->ld_u + c + e] = lr * o.v[e];
+            }
+        }
+    }
+};
+
+template <typename T, int KIND>
+__global__ __launch_bounds__(G_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_kernel(uint8_t* ws, int first, int last, int xt_cur) {
     __shared__ __align__(16) uint8_t smem[GEMM_LDS];
     const mo_wl_header* h = wl_header(ws);
     const uint32_t n_items = KIND == KIND_GRAM ? h->n_gram_items
@@ -265,193 +356,168 @@ __global__ __launch_bounds__(G_THREADS, 2) void gemm_kernel(uint8_t* ws, int fir
         ld = m_pad; P = B + int64_t(ti) * GT * ld; Q = Xt_cur + int64_t(tj) * GT * ld;
     }
     const int64_t ldb = ld * int64_t(sizeof(T));             // row stride in bytes
-    const int nk = int(ld * int64_t(sizeof(T)) / KB);         // K stages
+    const int nk = int(ldb / KB);                              // K stages
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int r32 = lane & 31, kg = lane >> 5;
 
+    // direct-to-LDS loads: wave w fills rows [64 w, 64 w + 64) of both operands,
+    // 16 rows (1 KB) per instruction; lane l -> row + l/4, physical chunk l%4.
     const uint8_t* Pb = reinterpret_cast<const uint8_t*>(P);
     const uint8_t* Qb = reinterpret_cast<const uint8_t*>(Q);
-    u32x4 rp[4], rq[4];
-    auto gload = [&](int ks) {
+    const int lrow = lane >> 2, pch = lane & 3;
+    int64_t goff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = wave * 64 + i * 16 + lrow;
+        goff[i] = int64_t(row) * ldb + ((pch ^ ((row >> 1) & 3)) << 4);
+    }
+    auto issue = [&](int ks) {
+        uint8_t* sp = smem + (ks % NSTAGE) * STAGE_BYTES + wave * 64 * KB;
+        const int64_t kofs = int64_t(ks) * KB;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int q = tid + G_THREADS * i;
-            const int row = q >> 3, cc = q & 7;
-            const int64_t off = int64_t(row) * ldb + int64_t(ks) * KB + cc * 16;
-            rp[i] = *reinterpret_cast<const u32x4*>(Pb + off);
-            rq[i] = *reinterpret_cast<const u32x4*>(Qb + off);
-        }
-    };
-    auto lstore = [&](int buf) {
-        uint8_t* sp = smem + buf * 2 * OPND_BYTES;
-        uint8_t* sq = sp + OPND_BYTES;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int q = tid + G_THREADS * i;
-            const int row = q >> 3, cc = q & 7;
-            *reinterpret_cast<u32x4*>(sp + swz(row, cc)) = rp[i];
-            *reinterpret_cast<u32x4*>(sq + swz(row, cc)) = rq[i];
+            __builtin_amdgcn_global_load_lds(Pb + goff[i] + kofs, (lds_void_t*)(sp + i * 16 * KB), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(Qb + goff[i] + kofs, (lds_void_t*)(sp + OPND_BYTES + i * 16 * KB),
+                                             16, 0, 0);
         }
     };
 
-    f32x16 acc[2][2];
+    f32x16 acc[4][4];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < 4; ++b)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
 
-    auto compute = [&](int cur) {
-        const uint8_t* sp = smem + cur * 2 * OPND_BYTES;
+    // Fragments of one 16-deep K substep: 4 A and 4 B chunks per lane.
+    auto rd = [&](int ks, int sub, u32x4 (&fa)[4], u32x4 (&fb)[4]) {
+        const uint8_t* sp = smem + (ks % NSTAGE) * STAGE_BYTES;
         const uint8_t* sq = sp + OPND_BYTES;
+        const int chunk = 2 * sub + kg;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int chunk = 2 * s + kg;
-            u32x4 fa[2], fb[2];
+        for (int a = 0; a < 4; ++a)
+            fa[a] = *reinterpret_cast<const u32x4*>(sp + swz(wm * 128 + a * 32 + r32, chunk));
 #pragma unroll
-            for (int a = 0; a < 2; ++a)
-                fa[a] = *reinterpret_cast<const u32x4*>(sp + swz(wm * 64 + a * 32 + r32, chunk));
+        for (int b = 0; b < 4; ++b)
+            fb[b] = *reinterpret_cast<const u32x4*>(sq + swz(wn * 128 + b * 32 + r32, chunk));
+    };
+    auto mm = [&](const u32x4 (&fa)[4], const u32x4 (&fb)[4]) {
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
-                fb[b] = *reinterpret_cast<const u32x4*>(sq + swz(wn * 64 + b * 32 + r32, chunk));
+        for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int a = 0; a < 2; ++a)
-#pragma unroll
-                for (int b = 0; b < 2; ++b) Mfma<T>::run(fa[a], fb[b], acc[a][b]);
-        }
+            for (int b = 0; b < 4; ++b) Mfma<T>::run(fa[a], fb[b], acc[a][b]);
+    };
+    // Workgroup barrier without the release fence of __syncthreads(), which
+    // would also drain the direct-to-LDS loads still in flight for later
+    // stages.  Each thread first waits for its own loads of the stage being
+    // published (explicit vmcnt) and for its LDS reads (lgkmcnt).
+    auto wait_loads = [&](int later) {   // later = stages issued after the one awaited
+        if (later >= 3) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+        else if (later == 2) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        else if (later == 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    };
+    auto barrier = [&]() {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
     };
 
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int ks = 0; ks + 1 < nk; ++ks) {
-        gload(ks + 1);
-        compute(ks & 1);
-        lstore((ks & 1) ^ 1);
-        __syncthreads();
-    }
-    compute((nk - 1) & 1);
-    __syncthreads();
-
-    // ---- stage the fp32 tile in LDS ----
-    float* st = reinterpret_cast<float*>(smem);
+    // Interleave the 8 fragment reads of the next substep with the MFMAs of
+    // the current one (bf16: 1 MFMA then 1 read; fp32 issues 4 MFMAs per chunk).
+    constexpr int MF = sizeof(T) == 2 ? 1 : 4;
+    auto interleave = [&]() {
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int row = wm * 64 + a * 32 + (v >> 2) * 8 + kg * 4 + (v & 3);
-                const int col = wn * 64 + b * 32 + r32;
-                st[row * ST + col] = acc[a][b][v];
-            }
-    __syncthreads();
-
-    const float na = h->ns_a, nb = h->ns_b, nc = h->ns_c;
-    const bool trans = mt.flags & MO_WLF_TRANSPOSED;
-    const int64_t gi0 = int64_t(ti) * GT, gj0 = int64_t(tj) * GT;
-
-    // ---- pass A: the tile in its own orientation ----
-#pragma unroll 2
-    for (int i = 0; i < 8; ++i) {
-        const int q = tid + G_THREADS * i;
-        const int cc = q & 15, row = q >> 4;
-        const int64_t gi = gi0 + row, gj = gj0 + cc * 8;
-        f32x8 v;
-        load8(st + row * ST + cc * 8, v);
-        if (KIND == KIND_GRAM) {
-            const float alpha = first ? scale[1] : 1.0f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v.v[e] *= alpha;
-            store8(A + gi * m_pad + gj, v);
-        } else if (KIND == KIND_POLY) {
-            f32x8 av;
-            load8(A + gi * m_pad + gj, av);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v.v[e] = nc * v.v[e] + nb * av.v[e];
-            store8(B + gi * m_pad + gj, v);
-        } else {
-            const float sx = first ? scale[0] : 1.0f;
-            f32x8 xv;
-            load8(X + gi * n_pad + gj, xv);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v.v[e] = sx * (na * xv.v[e] + v.v[e]);
-            if (!last) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) v.v[e] = quantize<T>(v.v[e]);
-                store8(X + gi * n_pad + gj, v);
-                store8(st + row * ST + cc * 8, v);
-            } else if (!trans) {
-                // weight frame == NS frame: row gi, cols gj..gj+7
-                if (gi < mt.rows) {
-                    const bool wbf = mt.flags & MO_WLF_W_BF16;
-                    void* W = reinterpret_cast<void*>(mt.W);
-                    float* U = reinterpret_cast<float*>(mt.U);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        if (gj + e < mt.cols) {
-                            const int64_t wi = gi * mt.ld_w + gj + e;
-                            const float w = load_elem(W, wi, wbf);
-                            store_elem(W, wi, mt.decay * w - mt.lr_eff * v.v[e], wbf);
-                            if (U) U[gi * mt.ld_u + gj + e] = mt.lr_eff * v.v[e];
-                        }
-                    }
-                }
-            } else {
-                store8(st + row * ST + cc * 8, v);
-            }
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // DS read
         }
-    }
+        __builtin_amdgcn_sched_group_barrier(0x008, 16 * MF - 8 * MF, 0);
+    };
 
-    // ---- pass B: the mirrored orientation ----
-    bool need_b;
-    if (KIND == KIND_UPDATE) {
-        need_b = !last || trans;
-        __syncthreads();   // pass A rewrote the staging tile
-    } else {
-        need_b = ti != tj;
+    // Software pipeline over K (nk >= 8: every padded dimension is >= 256).
+    // Stage s occupies ring slot s % 4.  Entering iteration ks, F0 holds the
+    // fragments of (ks, substep 0).  The barrier sits between the two substeps,
+    // so the MFMAs after it use fragments already in registers while the reads
+    // for the next stage land.
+    u32x4 f0a[4], f0b[4], f1a[4], f1b[4];
+#pragma unroll
+    for (int ks = 0; ks < NSTAGE; ++ks) issue(ks);
+    wait_loads(NSTAGE - 1);
+    barrier();
+    rd(0, 0, f0a, f0b);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int ks = 0; ks + 1 < nk; ++ks) {
+        mm(f0a, f0b);
+        rd(ks, 1, f1a, f1b);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
+        const int issued_last = ks + NSTAGE - 1 < nk - 1 ? ks + NSTAGE - 1 : nk - 1;
+        wait_loads(issued_last - (ks + 1));
+        barrier();   // stage ks+1 visible everywhere; every read of stage ks done
+        if (ks + NSTAGE < nk) issue(ks + NSTAGE);   // refill the slot of stage ks
+        __builtin_amdgcn_sched_barrier(0);
+        mm(f1a, f1b);
+        rd(ks + 1, 0, f0a, f0b);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
     }
-    if (!need_b) return;
+    mm(f0a, f0b);
+    rd(nk - 1, 1, f1a, f1b);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    mm(f1a, f1b);
+    __syncthreads();   // every wave is done with the operand stages
+
+    Epi<T, KIND> ep;
+    ep.mt = &mt;
+    ep.X = X; ep.Xt_nxt = Xt_nxt; ep.A = A; ep.B = B;
+    ep.alpha = (KIND == KIND_GRAM && first) ? scale[1] : 1.0f;
+    ep.sx = (KIND == KIND_UPDATE && first) ? scale[0] : 1.0f;
+    ep.na = h->ns_a; ep.nb = h->ns_b; ep.nc = h->ns_c;
+    ep.m_pad = m_pad; ep.n_pad = n_pad;
+    ep.last = last;
+    ep.trans = mt.flags & MO_WLF_TRANSPOSED;
+    const bool need_b = KIND == KIND_UPDATE ? (!last || ep.trans) : (ti != tj);
+
+    float* st = reinterpret_cast<float*>(smem + wave * WAVE_ST_BYTES);
+    const int64_t gi_w = int64_t(ti) * GT + wm * 128;   // this wave's sub-tile origin
+    const int64_t gj_w = int64_t(tj) * GT + wn * 128;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        // stage rows [32 a, 32 a + 32) of the wave's sub-tile
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                st[st_idx((v >> 2) * 8 + kg * 4 + (v & 3), b * 32 + r32)] = acc[a][b][v];
+        __builtin_amdgcn_wave_barrier();
+        // pass A: 16 lanes per 128-column row, 4 rows per instruction
 #pragma unroll 2
-    for (int i = 0; i < 8; ++i) {
-        const int q = tid + G_THREADS * i;
-        const int j = q & 127, rr = q >> 7;           // output row j, cols rr*8..rr*8+7
-        f32x8 v;
+        for (int t = 0; t < 8; ++t) {
+            const int q = lane + 64 * t;
+            const int cc = q & 15, row = q >> 4;
+            f32x8 v;
+            float* slot = st + st_idx(row, cc * 8);
+            load8(slot, v);
+            ep.pass_a(gi_w + a * 32 + row, gj_w + cc * 8, v, slot);
+        }
+        __builtin_amdgcn_wave_barrier();
+        if (need_b) {
+            // pass B: output row j (a column of the sub-tile), 32 values in 4 chunks
+#pragma unroll 2
+            for (int t = 0; t < 8; ++t) {
+                const int q = lane + 64 * t;
+                const int ic = q & 3, j = q >> 2;
+                f32x8 v;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v.v[e] = st[(rr * 8 + e) * ST + j];
-        const int64_t oj = gj0 + j, oi = gi0 + rr * 8;
-        if (KIND == KIND_GRAM) {
-            const float alpha = first ? scale[1] : 1.0f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v.v[e] *= alpha;
-            store8(A + oj * m_pad + oi, v);
-        } else if (KIND == KIND_POLY) {
-            f32x8 av;
-            load8(A + oj * m_pad + oi, av);     // A is exactly symmetric
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v.v[e] = nc * v.v[e] + nb * av.v[e];
-            store8(B + oj * m_pad + oi, v);
-        } else if (!last) {
-            store8(Xt_nxt + oj * m_pad + oi, v);
-        } else {
-            // weight frame is the transpose: W row oj (< rows = n), cols oi.. (< cols = m)
-            if (oj < mt.rows) {
-                const bool wbf = mt.flags & MO_WLF_W_BF16;
-                void* W = reinterpret_cast<void*>(mt.W);
-                float* U = reinterpret_cast<float*>(mt.U);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    if (oi + e < mt.cols) {
-                        const int64_t wi = oj * mt.ld_w + oi + e;
-                        const float w = load_elem(W, wi, wbf);
-                        store_elem(W, wi, mt.decay * w - mt.lr_eff * v.v[e], wbf);
-                        if (U) U[oj * mt.ld_u + oi + e] = mt.lr_eff * v.v[e];
-                    }
-                }
+                for (int e = 0; e < 8; ++e) v.v[e] = st[st_idx(ic * 8 + e, j)];
+                ep.pass_b(gj_w + j, gi_w + a * 32 + ic * 8, v);
             }
+            __builtin_amdgcn_wave_barrier();
         }
     }
 }

@@ -5,7 +5,7 @@ byte layout is specified in ``include/mo.h`` (muon_build_worklist) and the
 record comments there.  This twin is written from that specification with
 Python's ``struct`` so that the C++ builder can be checked byte for byte.
 
-Layout (little-endian, natural alignment, version 1):
+Layout (little-endian, natural alignment, version 2):
   header (128 B): magic 'MOWL', version, n_mats, ns_steps, ns_dtype, gemm_tile,
       mom_tile, elem_bytes, n_mom_items, n_gram_items, n_poly_items,
       n_upd_items, max_partials, 0, mats_offset, gram_offset, poly_offset,
@@ -16,7 +16,9 @@ Layout (little-endian, natural alignment, version 1):
       cols, m, n, m_pad, n_pad, flags, desc_index, mom_begin, mom_tiles_c,
       n_partials (u32), lr_eff, decay (f32), 5 x 0
   items (8 B: u32 matrix record index, u16 ti, u16 tj): Gram, Poly, Update,
-      each list 256-byte aligned
+      each list 256-byte aligned; matrices by descending work (ties in
+      record order), each matrix's tiles in super-blocks of 4 tile-rows x 8
+      tile-columns (Gram/Poly: only ti <= tj)
 Workspace regions follow the list, per record: X, Xt0, Xt1 (m_pad*n_pad
 elements each), A, B (m_pad^2), partials (n_partials fp32), scale (16 B); every
 region 256-byte aligned.
@@ -27,7 +29,7 @@ import math
 import struct
 from typing import List, Sequence
 
-T = 128       # GEMM tile edge
+T = 256       # GEMM tile edge
 MT = 64       # momentum tile edge
 ALIGN = 256
 MAGIC = 0x4C574F4D
@@ -90,16 +92,27 @@ def build(descs: Sequence[dict], hp: dict) -> bytes:
         t = r["m_pad"] // T
         return t * (t + 1) // 2
 
+    def blocked(j, tm, tn, upper_only):
+        """Tiles in super-blocks of 4 tile-rows x 8 tile-columns, super-blocks
+        row-major, tiles row-major inside each."""
+        out = []
+        for bi in range(0, tm, 4):
+            for bj in range(0, tn, 8):
+                for a in range(bi, min(bi + 4, tm)):
+                    for b in range(bj, min(bj + 8, tn)):
+                        if not upper_only or a <= b:
+                            out.append((j, a, b))
+        return out
+
     gram, poly, upd = [], [], []
     for j in ordered(lambda r: upper(r) * r["n_pad"]):
         t = recs[j]["m_pad"] // T
-        gram += [(j, a, b) for a in range(t) for b in range(a, t)]
+        gram += blocked(j, t, t, True)
     for j in ordered(lambda r: upper(r) * r["m_pad"]):
         t = recs[j]["m_pad"] // T
-        poly += [(j, a, b) for a in range(t) for b in range(a, t)]
+        poly += blocked(j, t, t, True)
     for j in ordered(lambda r: (r["m_pad"] // T) * (r["n_pad"] // T) * r["m_pad"]):
-        tm, tn = recs[j]["m_pad"] // T, recs[j]["n_pad"] // T
-        upd += [(j, a, b) for a in range(tm) for b in range(tn)]
+        upd += blocked(j, recs[j]["m_pad"] // T, recs[j]["n_pad"] // T, False)
 
     mats_off = 128
     gram_off = _up(mats_off + 192 * len(recs), ALIGN)
@@ -118,7 +131,7 @@ def build(descs: Sequence[dict], hp: dict) -> bytes:
     ws_bytes = off
 
     out = bytearray(wl_bytes)
-    struct.pack_into("<14I6Q4f2I", out, 0, MAGIC, 1, len(recs), hp["ns_steps"], hp["ns_dtype"],
+    struct.pack_into("<14I6Q4f2I", out, 0, MAGIC, 2, len(recs), hp["ns_steps"], hp["ns_dtype"],
                      T, MT, es, mom, len(gram), len(poly), len(upd), max_partials, 0,
                      mats_off, gram_off, poly_off, upd_off, wl_bytes, ws_bytes,
                      hp["ns_a"], hp["ns_b"], hp["ns_c"], hp["eps"], 0, 0)

@@ -6,8 +6,9 @@ Tolerances (relative Frobenius norm):
     with fp32 ones;
   * the momentum buffer M': 1e-6 (one fp32 fma chain per element);
   * W': the written weight must equal round(decay * W - delta_gpu) in W's dtype
-    to within one unit in the last place per element (the fp32 evaluation order
-    may differ), and delta_gpu is checked against the oracle above.
+    to within one unit in the last place per element plus the fp32 rounding of
+    the two operands (the fp32 evaluation order may differ, and the operands can
+    cancel), and delta_gpu is checked against the oracle above.
 """
 from __future__ import annotations
 
@@ -137,17 +138,20 @@ def check_case(c: Case, got, hp: wlmod.MuonHP, tol: Optional[float] = None) -> d
     decay = np.float32(1.0 - np.float64(np.float32(hp.lr)) * np.float64(np.float32(hp.weight_decay)))
     want = (decay * c.W.astype(np.float32) - D1.astype(np.float32)).astype(np.float64)
     if c.w_dtype == "bf16":
-        # spacing at the larger magnitude: a 1-ulp difference in the fp32
-        # evaluation can move a value across a binade boundary
-        err = np.abs(W1 - want) / bf16_ulp(np.maximum(np.abs(W1), np.abs(want)))
+        # One bf16 spacing at the larger magnitude (a 1-ulp difference of the
+        # fp32 evaluation can cross a rounding boundary or a binade), plus the
+        # fp32 rounding of the two operands, which dominates when they cancel.
+        op = np.maximum(np.abs(decay * c.W.astype(np.float64)), np.abs(D1))
+        allow = bf16_ulp(np.maximum(np.abs(W1), np.abs(want))) + 4 * 2.0 ** -24 * op
+        err = np.abs(W1 - want) / allow
         out["w_ulps"] = float(err.max())
-        if out["w_ulps"] > 1.0 + 1e-6:
+        if out["w_ulps"] > 1.0:
             worst = np.argsort(err.ravel())[-4:]
             rows = [(int(k) // W1.shape[1], int(k) % W1.shape[1], float(c.W.ravel()[k]),
                      float(D1.ravel()[k]), float(want.ravel()[k]), float(W1.ravel()[k]))
                     for k in worst]
             out["worst(row,col,W,delta,want,got)"] = rows
-        assert out["w_ulps"] <= 1.0 + 1e-6, out
+        assert out["w_ulps"] <= 1.0, out
     else:
         out["w_rel"] = rel(W1, want)
         assert out["w_rel"] <= 1e-6, out
