@@ -102,18 +102,21 @@ mo_status muon_workspace_bytes(const mo_matrix* mats, int32_t n_mats,
 /* The host work list that muon_owner_step uploads, for inspection and tests.
  * If host_buf is NULL, *bytes_inout receives the size; otherwise *bytes_inout
  * must hold at least that size and the list is written to host_buf.  The byte
- * layout (little-endian, natural alignment, version 2):
+ * layout (little-endian, natural alignment, version 3):
  *   header   mo_wl_header (128 bytes)
  *   matrices mo_wl_mat[n_live] (192 bytes each), one per non-empty descriptor,
  *            in descriptor order
- *   items    three arrays of mo_wl_item (8 bytes): Gram, Poly, Update tiles,
- *            each array starting on a 256-byte boundary
- * Gram and Poly items are the upper-triangle tiles (ti <= tj) of the m_pad x
- * m_pad product, Update items all tiles of the m_pad x n_pad product (tiles
- * of 256 x 256); matrices appear in descending order of their per-phase work,
- * ties by descriptor index; the tiles of one matrix come in super-blocks of 4
- * tile-rows x 8 tile-columns, super-blocks row-major and tiles row-major
- * inside each. */
+ *   items    three dispatch lists of mo_wl_item (8 bytes: record index, tile
+ *            row, tile column): Gram, Poly, Update, each starting on a
+ *            256-byte boundary; entry b is the 256 x 256 tile run by workgroup b
+ * Gram and Poly cover the upper-triangle tiles (ti <= tj) of the m_pad x m_pad
+ * product, Update all tiles of the m_pad x n_pad product.  Matrices are taken
+ * in descending order of their per-phase work (ties by descriptor index) and
+ * cut into super-blocks of 4 tile-rows x 8 tile-columns (row-major, tiles
+ * row-major inside); each super-block goes to the one of 8 queues (one per
+ * XCD) with the least K-length x tiles so far, ties to the lowest, and entry
+ * 8 j + x of a list is the j-th tile of queue x, or a pad entry (record index
+ * 0xFFFFFFFF) where queue x is shorter. */
 mo_status muon_build_worklist(const mo_matrix* mats, int32_t n_mats,
                               const mo_muon_hparams* hp, void* host_buf,
                               size_t* bytes_inout);

@@ -171,31 +171,51 @@ void build_plan(const mo_matrix* mats, int32_t n, const mo_muon_hparams* hp, Pla
         return ks;
     };
     auto upper = [&](const mo_wl_mat& r) { uint64_t t = r.m_pad / T; return t * (t + 1) / 2; };
-    // Tiles of one matrix are emitted in super-blocks of SB_R tile-rows x SB_C
-    // tile-columns (super-blocks row-major, tiles row-major inside), so that
-    // the 32 tiles one XCD runs at a time share 4 row panels and 8 column
-    // panels of their operands in that XCD's L2.
-    constexpr uint32_t SB_R = 4, SB_C = 8;
-    auto emit = [](std::vector<mo_wl_item>& out, uint32_t idx, uint32_t tm, uint32_t tn, bool upper_only) {
-        for (uint32_t bi = 0; bi < tm; bi += SB_R)
-            for (uint32_t bj = 0; bj < tn; bj += SB_C)
-                for (uint32_t a = bi; a < std::min(bi + SB_R, tm); ++a)
-                    for (uint32_t b = bj; b < std::min(bj + SB_C, tn); ++b)
-                        if (!upper_only || a <= b) out.push_back({idx, uint16_t(a), uint16_t(b)});
+    // Dispatch lists.  A workgroup's XCD is its block index mod 8 (the
+    // hardware deals consecutive workgroups round-robin over the 8 XCDs), and
+    // each XCD runs its share in block order on its 32 CUs.  The tiles of one
+    // matrix are grouped into super-blocks of SB_R tile-rows x SB_C
+    // tile-columns (super-blocks row-major, tiles row-major inside), so one
+    // super-block is what an XCD runs at once and its tiles share 4 row panels
+    // and 8 column panels of the operands in that XCD's L2.  Super-blocks (in
+    // the matrices' descending-work order) go to the XCD with the least work
+    // so far (K-length x tiles; ties to the lowest XCD), and the list
+    // interleaves the 8 queues: entry 8 j + x is the j-th tile of XCD x, or a
+    // pad entry (matrix index MO_WL_PAD) where that queue is shorter.
+    constexpr uint32_t SB_R = 4, SB_C = 8, NXCD = 8;
+    auto dispatch = [&](std::vector<mo_wl_item>& out, const std::vector<Key>& mats_order,
+                        bool upper_only, bool k_is_n) {
+        std::vector<std::vector<mo_wl_item>> q(NXCD);
+        uint64_t load[NXCD] = {0};
+        for (const Key& k : mats_order) {
+            const mo_wl_mat& r = recs[k.idx];
+            const uint32_t tm = r.m_pad / T, tn = upper_only ? tm : r.n_pad / T;
+            const uint64_t klen = k_is_n ? r.n_pad : r.m_pad;
+            for (uint32_t bi = 0; bi < tm; bi += SB_R)
+                for (uint32_t bj = 0; bj < tn; bj += SB_C) {
+                    std::vector<mo_wl_item> blk;
+                    for (uint32_t a = bi; a < std::min(bi + SB_R, tm); ++a)
+                        for (uint32_t b = bj; b < std::min(bj + SB_C, tn); ++b)
+                            if (!upper_only || a <= b) blk.push_back({k.idx, uint16_t(a), uint16_t(b)});
+                    if (blk.empty()) continue;
+                    uint32_t x = 0;
+                    for (uint32_t y = 1; y < NXCD; ++y)
+                        if (load[y] < load[x]) x = y;
+                    load[x] += klen * blk.size();
+                    q[x].insert(q[x].end(), blk.begin(), blk.end());
+                }
+        }
+        size_t len = 0;
+        for (const auto& v : q) len = std::max(len, v.size());
+        for (size_t j = 0; j < len; ++j)
+            for (uint32_t x = 0; x < NXCD; ++x)
+                out.push_back(j < q[x].size() ? q[x][j] : mo_wl_item{MO_WL_PAD, 0, 0});
     };
     std::vector<mo_wl_item> gram, poly, upd;
-    for (const Key& k : order([&](const mo_wl_mat& r) { return upper(r) * r.n_pad; })) {
-        const uint32_t t = recs[k.idx].m_pad / T;
-        emit(gram, k.idx, t, t, true);
-    }
-    for (const Key& k : order([&](const mo_wl_mat& r) { return upper(r) * r.m_pad; })) {
-        const uint32_t t = recs[k.idx].m_pad / T;
-        emit(poly, k.idx, t, t, true);
-    }
-    for (const Key& k : order([&](const mo_wl_mat& r) {
-             return uint64_t(r.m_pad / T) * (r.n_pad / T) * r.m_pad; })) {
-        emit(upd, k.idx, recs[k.idx].m_pad / T, recs[k.idx].n_pad / T, false);
-    }
+    dispatch(gram, order([&](const mo_wl_mat& r) { return upper(r) * r.n_pad; }), true, true);
+    dispatch(poly, order([&](const mo_wl_mat& r) { return upper(r) * r.m_pad; }), true, false);
+    dispatch(upd, order([&](const mo_wl_mat& r) {
+                 return uint64_t(r.m_pad / T) * (r.n_pad / T) * r.m_pad; }), false, false);
 
     mo_wl_header h;
     std::memset(&h, 0, sizeof(h));

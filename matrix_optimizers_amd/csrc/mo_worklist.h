@@ -11,7 +11,10 @@
 #include <stdint.h>
 
 #define MO_WL_MAGIC   0x4C574F4Du  // "MOWL"
-#define MO_WL_VERSION 2u
+#define MO_WL_VERSION 3u
+
+// matrix index of a padding entry in a dispatch list
+#define MO_WL_PAD 0xFFFFFFFFu
 
 // Tile edge of the Newton-Schulz GEMMs.  Every NS-frame dimension is padded
 // to a multiple of it inside the workspace, with zeros, so the GEMM kernels

@@ -237,14 +237,6 @@ MO_DEV int swz(int row, int chunk) { return row * KB + ((chunk ^ ((row >> 1) & 3
 // staging slice index: 128 fp32 columns per row, column bits 3..4 XOR row bits 3..4
 MO_DEV int st_idx(int row, int col) { return row * 128 + (col ^ (((row >> 3) & 3) << 3)); }
 
-// Block index -> logical item.  Consecutive workgroups are dealt round-robin
-// over the 8 XCDs; giving each XCD a contiguous run of items keeps the tiles
-// that share operand panels on the same L2.
-MO_DEV uint32_t xcd_item(uint32_t b, uint32_t nb) {
-    const uint32_t chunk = nb >> 3;
-    return (b & 7) * chunk + (b >> 3);
-}
-
 // Epilogue context of one workgroup tile.
 template <typename T, int KIND>
 struct Epi {
@@ -254,21 +246,24 @@ struct Epi {
     int64_t m_pad, n_pad;
     bool last, trans;
 
-    // pass A: 8 values at tile-orientation position (gi, gj..gj+7)
-    MO_DEV void pass_a(int64_t gi, int64_t gj, f32x8& v, float* slot) const {
+    // pass A: 8 values at tile-orientation position (gi, gj..gj+7).  `opnd`
+    // is the matching chunk of the epilogue operand (A for Poly, X for Update)
+    // when it was prefetched, else null and it is loaded here.
+    MO_DEV void pass_a(int64_t gi, int64_t gj, f32x8& v, float* slot, const f32x8* opnd) const {
         if (KIND == KIND_GRAM) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) v.v[e] *= alpha;
             store8(A + gi * m_pad + gj, v);
         } else if (KIND == KIND_POLY) {
             f32x8 av;
-            load8(A + gi * m_pad + gj, av);
+            if (opnd) av = *opnd; else load8(A + gi * m_pad + gj, av);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v.v[e] = nc * v.v[e] + nb * av.v[e];
+            for (int e = 0; e < 8; ++e) v.v[e] = quantize<T>(nc * v.v[e] + nb * av.v[e]);
             store8(B + gi * m_pad + gj, v);
+            store8(slot, v);               // the mirrored write re-uses the rounded value
         } else {
             f32x8 xv;
-            load8(X + gi * n_pad + gj, xv);
+            if (opnd) xv = *opnd; else load8(X + gi * n_pad + gj, xv);
 #pragma unroll
             for (int e = 0; e < 8; ++e) v.v[e] = sx * (na * xv.v[e] + v.v[e]);
             if (!last) {
@@ -291,11 +286,7 @@ struct Epi {
             for (int e = 0; e < 8; ++e) v.v[e] *= alpha;
             store8(A + oj * m_pad + oi, v);
         } else if (KIND == KIND_POLY) {
-            f32x8 av;
-            load8(A + oj * m_pad + oi, av);     // A is exactly symmetric
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v.v[e] = nc * v.v[e] + nb * av.v[e];
-            store8(B + oj * m_pad + oi, v);
+            store8(B + oj * m_pad + oi, v);    // B is symmetric: the staged values
         } else if (!last) {
             store8(Xt_nxt + oj * m_pad + oi, v);
         } else {
@@ -327,13 +318,11 @@ __global__ __launch_bounds__(G_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)
 void gemm_kernel(uint8_t* ws, int first, int last, int xt_cur) {
     __shared__ __align__(16) uint8_t smem[GEMM_LDS];
     const mo_wl_header* h = wl_header(ws);
-    const uint32_t n_items = KIND == KIND_GRAM ? h->n_gram_items
-                           : KIND == KIND_POLY ? h->n_poly_items : h->n_upd_items;
     const uint64_t items_off = KIND == KIND_GRAM ? h->gram_offset
                              : KIND == KIND_POLY ? h->poly_offset : h->upd_offset;
-    const uint32_t logical = xcd_item(blockIdx.x, gridDim.x);
-    if (logical >= n_items) return;
-    const mo_wl_item it = reinterpret_cast<const mo_wl_item*>(ws + items_off)[logical];
+    // The grid is exactly the dispatch list; entry b is this workgroup's tile.
+    const mo_wl_item it = reinterpret_cast<const mo_wl_item*>(ws + items_off)[blockIdx.x];
+    if (it.mat == MO_WL_PAD) return;
     const mo_wl_mat& mt = wl_mats(ws)[it.mat];
     const int ti = it.ti, tj = it.tj;
     const int64_t m_pad = mt.m_pad, n_pad = mt.n_pad;
@@ -450,7 +439,30 @@ void gemm_kernel(uint8_t* ws, int first, int last, int xt_cur) {
     barrier();
     rd(0, 0, f0a, f0b);
     __builtin_amdgcn_sched_barrier(0);
-    for (int ks = 0; ks + 1 < nk; ++ks) {
+    // Epilogue operand prefetch (bf16 Poly / Update): the lane's 32 chunks of
+    // A or X that pass A will combine with the product, loaded into registers,
+    // rounds 0-1 while the last K substeps run and rounds 2-3 as the epilogue
+    // starts.  Chunk (round r, task t) sits at sub-tile
+    // row 32 r + 4 t + lane/16, columns 8 (lane % 16) .. + 7.
+    constexpr bool PREF = sizeof(T) == 2 && KIND != KIND_GRAM;
+    const int64_t gi_w = int64_t(ti) * GT + wm * 128;   // this wave's sub-tile origin
+    const int64_t gj_w = int64_t(tj) * GT + wn * 128;
+    u32x4 pre[PREF ? 4 : 1][8];
+    auto prefetch = [&](int r0, int r1) {   // rounds [r0, r1)
+        if constexpr (PREF) {
+            const T* src = KIND == KIND_UPDATE ? X : A;
+            const int64_t lds = KIND == KIND_UPDATE ? n_pad : m_pad;
+            const T* base = src + (gi_w + (lane >> 4)) * lds + gj_w + (lane & 15) * 8;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int t = 0; t < 8; ++t)
+                    if (r >= r0 && r < r1)
+                        pre[r][t] = *reinterpret_cast<const u32x4*>(base + int64_t(32 * r + 4 * t) * lds);
+        }
+    };
+
+    auto step = [&](int ks, bool with_prefetch) {
         mm(f0a, f0b);
         rd(ks, 1, f1a, f1b);
         interleave();
@@ -459,18 +471,21 @@ void gemm_kernel(uint8_t* ws, int first, int last, int xt_cur) {
         wait_loads(issued_last - (ks + 1));
         barrier();   // stage ks+1 visible everywhere; every read of stage ks done
         if (ks + NSTAGE < nk) issue(ks + NSTAGE);   // refill the slot of stage ks
+        if (with_prefetch) prefetch(0, 2);          // no stage load is in flight any more
         __builtin_amdgcn_sched_barrier(0);
         mm(f1a, f1b);
         rd(ks + 1, 0, f0a, f0b);
         interleave();
         __builtin_amdgcn_sched_barrier(0);
-    }
+    };
+    for (int ks = 0; ks + 1 < nk; ++ks) step(ks, ks + 2 == nk);
     mm(f0a, f0b);
     rd(nk - 1, 1, f1a, f1b);
     interleave();
     __builtin_amdgcn_sched_barrier(0);
     mm(f1a, f1b);
     __syncthreads();   // every wave is done with the operand stages
+    prefetch(2, 4);    // the fragment registers are free now
 
     Epi<T, KIND> ep;
     ep.mt = &mt;
@@ -484,26 +499,32 @@ void gemm_kernel(uint8_t* ws, int first, int last, int xt_cur) {
     const bool need_b = KIND == KIND_UPDATE ? (!last || ep.trans) : (ti != tj);
 
     float* st = reinterpret_cast<float*>(smem + wave * WAVE_ST_BYTES);
-    const int64_t gi_w = int64_t(ti) * GT + wm * 128;   // this wave's sub-tile origin
-    const int64_t gj_w = int64_t(tj) * GT + wn * 128;
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-        // stage rows [32 a, 32 a + 32) of the wave's sub-tile
+    // One 32-row block of the wave's sub-tile; called with literal indices so
+    // the accumulator and prefetch arrays are never indexed dynamically.
+    auto round = [&](const int a, const f32x16 (&ac)[4], const u32x4 (&pf)[8]) __attribute__((always_inline)) {
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
             for (int v = 0; v < 16; ++v)
-                st[st_idx((v >> 2) * 8 + kg * 4 + (v & 3), b * 32 + r32)] = acc[a][b][v];
+                st[st_idx((v >> 2) * 8 + kg * 4 + (v & 3), b * 32 + r32)] = ac[b][v];
         __builtin_amdgcn_wave_barrier();
         // pass A: 16 lanes per 128-column row, 4 rows per instruction
-#pragma unroll 2
+#pragma unroll
         for (int t = 0; t < 8; ++t) {
             const int q = lane + 64 * t;
             const int cc = q & 15, row = q >> 4;
             f32x8 v;
             float* slot = st + st_idx(row, cc * 8);
             load8(slot, v);
-            ep.pass_a(gi_w + a * 32 + row, gj_w + cc * 8, v, slot);
+            if constexpr (PREF) {
+                f32x8 o;
+                const bf16x8 raw = __builtin_bit_cast(bf16x8, pf[t]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o.v[e] = (float)raw[e];
+                ep.pass_a(gi_w + a * 32 + row, gj_w + cc * 8, v, slot, &o);
+            } else {
+                ep.pass_a(gi_w + a * 32 + row, gj_w + cc * 8, v, slot, nullptr);
+            }
         }
         __builtin_amdgcn_wave_barrier();
         if (need_b) {
@@ -519,10 +540,14 @@ void gemm_kernel(uint8_t* ws, int first, int last, int xt_cur) {
             }
             __builtin_amdgcn_wave_barrier();
         }
-    }
+    };
+    round(0, acc[0], pre[0]);
+    round(1, acc[1], pre[PREF ? 1 : 0]);
+    round(2, acc[2], pre[PREF ? 2 : 0]);
+    round(3, acc[3], pre[PREF ? 3 : 0]);
 }
 
-inline unsigned grid_for(uint32_t items) { return (items + 7u) / 8u * 8u; }
+inline unsigned grid_for(uint32_t items) { return items; }   // dispatch lists are padded to 8
 
 }  // namespace
 

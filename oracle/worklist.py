@@ -5,7 +5,7 @@ byte layout is specified in ``include/mo.h`` (muon_build_worklist) and the
 record comments there.  This twin is written from that specification with
 Python's ``struct`` so that the C++ builder can be checked byte for byte.
 
-Layout (little-endian, natural alignment, version 2):
+Layout (little-endian, natural alignment, version 3):
   header (128 B): magic 'MOWL', version, n_mats, ns_steps, ns_dtype, gemm_tile,
       mom_tile, elem_bytes, n_mom_items, n_gram_items, n_poly_items,
       n_upd_items, max_partials, 0, mats_offset, gram_offset, poly_offset,
@@ -15,10 +15,9 @@ Layout (little-endian, natural alignment, version 2):
       off_Xt0, off_Xt1, off_A, off_B, off_partials, off_scale (u64), rows,
       cols, m, n, m_pad, n_pad, flags, desc_index, mom_begin, mom_tiles_c,
       n_partials (u32), lr_eff, decay (f32), 5 x 0
-  items (8 B: u32 matrix record index, u16 ti, u16 tj): Gram, Poly, Update,
-      each list 256-byte aligned; matrices by descending work (ties in
-      record order), each matrix's tiles in super-blocks of 4 tile-rows x 8
-      tile-columns (Gram/Poly: only ti <= tj)
+  items (8 B: u32 matrix record index, u16 ti, u16 tj): Gram, Poly, Update
+      dispatch lists (entry b is run by workgroup b), each 256-byte aligned
+      and a multiple of 8 long; see dispatch() below
 Workspace regions follow the list, per record: X, Xt0, Xt1 (m_pad*n_pad
 elements each), A, B (m_pad^2), partials (n_partials fp32), scale (16 B); every
 region 256-byte aligned.
@@ -92,27 +91,36 @@ def build(descs: Sequence[dict], hp: dict) -> bytes:
         t = r["m_pad"] // T
         return t * (t + 1) // 2
 
-    def blocked(j, tm, tn, upper_only):
-        """Tiles in super-blocks of 4 tile-rows x 8 tile-columns, super-blocks
-        row-major, tiles row-major inside each."""
-        out = []
-        for bi in range(0, tm, 4):
-            for bj in range(0, tn, 8):
-                for a in range(bi, min(bi + 4, tm)):
-                    for b in range(bj, min(bj + 8, tn)):
-                        if not upper_only or a <= b:
-                            out.append((j, a, b))
-        return out
+    PAD = 0xFFFFFFFF
 
-    gram, poly, upd = [], [], []
-    for j in ordered(lambda r: upper(r) * r["n_pad"]):
-        t = recs[j]["m_pad"] // T
-        gram += blocked(j, t, t, True)
-    for j in ordered(lambda r: upper(r) * r["m_pad"]):
-        t = recs[j]["m_pad"] // T
-        poly += blocked(j, t, t, True)
-    for j in ordered(lambda r: (r["m_pad"] // T) * (r["n_pad"] // T) * r["m_pad"]):
-        upd += blocked(j, recs[j]["m_pad"] // T, recs[j]["n_pad"] // T, False)
+    def dispatch(mat_order, upper_only, k_is_n):
+        """Super-blocks of 4 tile-rows x 8 tile-columns (row-major, tiles
+        row-major inside) go, in matrix order, to whichever of 8 queues has the
+        least K-length x tiles so far (ties: lowest queue); the list interleaves
+        the queues (entry 8 j + x = j-th tile of queue x, or a pad entry)."""
+        queues = [[] for _ in range(8)]
+        load = [0] * 8
+        for j in mat_order:
+            r = recs[j]
+            tm = r["m_pad"] // T
+            tn = tm if upper_only else r["n_pad"] // T
+            klen = r["n_pad"] if k_is_n else r["m_pad"]
+            for bi in range(0, tm, 4):
+                for bj in range(0, tn, 8):
+                    blk = [(j, a, b) for a in range(bi, min(bi + 4, tm))
+                           for b in range(bj, min(bj + 8, tn)) if not upper_only or a <= b]
+                    if not blk:
+                        continue
+                    x = min(range(8), key=lambda y: (load[y], y))
+                    load[x] += klen * len(blk)
+                    queues[x] += blk
+        longest = max((len(q) for q in queues), default=0)
+        return [queues[x][j] if j < len(queues[x]) else (PAD, 0, 0)
+                for j in range(longest) for x in range(8)]
+
+    gram = dispatch(ordered(lambda r: upper(r) * r["n_pad"]), True, True)
+    poly = dispatch(ordered(lambda r: upper(r) * r["m_pad"]), True, False)
+    upd = dispatch(ordered(lambda r: (r["m_pad"] // T) * (r["n_pad"] // T) * r["m_pad"]), False, False)
 
     mats_off = 128
     gram_off = _up(mats_off + 192 * len(recs), ALIGN)
@@ -131,7 +139,7 @@ def build(descs: Sequence[dict], hp: dict) -> bytes:
     ws_bytes = off
 
     out = bytearray(wl_bytes)
-    struct.pack_into("<14I6Q4f2I", out, 0, MAGIC, 2, len(recs), hp["ns_steps"], hp["ns_dtype"],
+    struct.pack_into("<14I6Q4f2I", out, 0, MAGIC, 3, len(recs), hp["ns_steps"], hp["ns_dtype"],
                      T, MT, es, mom, len(gram), len(poly), len(upd), max_partials, 0,
                      mats_off, gram_off, poly_off, upd_off, wl_bytes, ws_bytes,
                      hp["ns_a"], hp["ns_b"], hp["ns_c"], hp["eps"], 0, 0)

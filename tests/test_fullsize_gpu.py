@@ -1,0 +1,157 @@
+"""Full-size workloads, in the launch configuration bench.py times (one call over
+the whole bucket), checked against the fp64 oracle on sampled matrices and, for
+matrices too large for the oracle, by properties that hold at any size.
+
+Sampled parity: every matrix of a bucket is an independent output, so the
+oracle recomputes a sample of whole matrices from the same stored inputs.
+Properties (large matrices): momentum is elementwise, so sampled rows of M'
+are compared with the oracle's momentum; the orthogonalised update O of a
+Gaussian gradient has every singular value in the band the quintic maps
+[1e-3, 1] into after five steps ([0.4727, 1.2024]); O U^T is symmetric
+positive semidefinite (O = U_s p(S) V^T and U = U_s S V^T); a transposed twin
+of a matrix gets the transposed update; scaling G and M by 4 changes nothing.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+from matrix_optimizers_amd import workloads as wlmod
+from oracle import muon as omuon
+
+from _parity import Case, check_case, hp_f32, hp_kwargs, rel, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def run_bucket(wl, device, mats=None, hp=None):
+    """One muon_owner_step over the whole bucket (update_out for every matrix)."""
+    import torch
+    import matrix_optimizers_amd as mo
+    hp = hp or wl.hp
+    if mats is None:
+        mats = [wlmod.torch_matrix_inputs(wl, i, device) for i in range(len(wl.matrices))]
+    before = [(W.clone(), G, M.clone()) for (W, G, M) in mats]
+    ups = [torch.empty(W.shape, dtype=torch.float32, device=device) for (W, _, _) in mats]
+    mo.muon_owner_step(mats, update_out=ups, **hp_kwargs(hp))
+    torch.cuda.synchronize()
+    return before, mats, ups
+
+
+def host_case(before, k, wl):
+    W0, G, M0 = before[k]
+    return Case(to_host(W0).astype(np.float32), to_host(G).astype(np.float32),
+                to_host(M0).astype(np.float32), wl.w_dtype, wl.g_dtype)
+
+
+def sampled_parity(wl, device, sample):
+    before, after, ups = run_bucket(wl, device)
+    for k in sample:
+        c = host_case(before, k, wl)
+        got = (to_host(after[k][0]), to_host(after[k][2]), to_host(ups[k]))
+        s = wl.matrices[k]
+        print(f"{wl.key} #{k} {s.rows}x{s.cols}", check_case(c, got, wl.hp), flush=True)
+    return before, after, ups
+
+
+def test_batched_1024_sampled(gpu):
+    """128 matrices in one grouped launch; the per-matrix gradient scales span
+    three decades.  Oracle on 3 matrices of each shape."""
+    wl = wlmod.get("batched_1024")
+    sampled_parity(wl, gpu, [0, 31, 63, 64, 100, 127])
+
+
+def momentum_rows(before, after, k, hp, rows):
+    """Sampled rows of M' against the oracle's momentum (elementwise)."""
+    W0, G, M0 = before[k]
+    Mo, _ = omuon.momentum(to_host(G[rows]), to_host(M0[rows]), np.float32(hp.momentum).item(),
+                           hp.nesterov)
+    return rel(to_host(after[k][2][rows]), Mo)
+
+
+def band_and_symmetry(before, up, k, wl):
+    """Singular-value band of O = delta / lr_eff and symmetry of O U^T."""
+    import torch
+    W0, G, M0 = before[k]
+    rows, cols = W0.shape
+    hp = wl.hp
+    lr_eff = np.float32(np.float32(hp.lr) * omuon.lr_multiplier(rows, cols, hp.lr_adjust))
+    O = up / float(lr_eff)
+    beta = float(np.float32(hp.momentum))
+    Gf = G.float()
+    Mn = beta * M0 + (1 - beta) * Gf
+    U = (1 - beta) * Gf + beta * Mn if hp.nesterov else Mn
+    if rows > cols:            # short-side frame
+        O, U = O.t().contiguous(), U.t().contiguous()
+    O, U = O.contiguous(), U.contiguous()
+    m = O.shape[0]
+    gen = torch.Generator(device=O.device)
+    gen.manual_seed(7)
+    u = torch.randn(8, m, generator=gen, device=O.device)
+    u /= u.norm(dim=1, keepdim=True)
+    gains = torch.mm(u, O).norm(dim=1)        # |O^T u| for unit u (fp32, contiguous operands)
+    S = torch.mm(O, U.t().contiguous())
+    asym = float((S - S.t()).norm() / S.norm())
+    evals = torch.linalg.eigvalsh(((S + S.t()) / 2).double().cpu())
+    frob = float(O.norm() ** 2 / m)
+    return float(gains.min()), float(gains.max()), asym, float(evals.min() / evals.max()), frob
+
+
+def test_llama8b_4layers_sampled_and_properties(gpu):
+    """The 4-layer Llama-3-8B-shaped owner share (28 matrices).  Oracle on a
+    1024x4096 and a 4096x4096 matrix; the 14336x4096 / 4096x14336 MLP matrices
+    by momentum rows and the properties."""
+    wl = wlmod.get("llama8b_4layers")
+    before, after, ups = sampled_parity(wl, gpu, [1, 0])
+    for k in (4, 6):          # w_gate (tall) and w_down (wide) of layer 0
+        rows = list(range(0, wl.matrices[k].rows, 997))
+        e = momentum_rows(before, after, k, wl.hp, rows)
+        gmin, gmax, asym, evr, frob = band_and_symmetry(before, ups[k], k, wl)
+        print(f"#{k} momentum {e:.2e} gains [{gmin:.3f}, {gmax:.3f}] asym {asym:.2e} "
+              f"eig_min/max {evr:.2e} |O|^2/m {frob:.3f}", flush=True)
+        assert e <= 1e-6
+        assert 0.40 <= gmin and gmax <= 1.30
+        assert asym <= 3e-2 and evr > -1e-2 and 0.2 <= frob <= 1.5
+
+
+def test_large_single_properties(gpu):
+    """28672x8192, 8192x28672 and the 128256x4096 head in one launch."""
+    wl = wlmod.get("large_single")
+    before, after, ups = run_bucket(wl, gpu)
+    for k in range(3):
+        rows = list(range(0, wl.matrices[k].rows, 4099))
+        e = momentum_rows(before, after, k, wl.hp, rows)
+        gmin, gmax, asym, evr, frob = band_and_symmetry(before, ups[k], k, wl)
+        print(f"large #{k} momentum {e:.2e} gains [{gmin:.3f}, {gmax:.3f}] asym {asym:.2e} "
+              f"eig_min/max {evr:.2e} |O|^2/m {frob:.3f}", flush=True)
+        assert e <= 1e-6
+        assert 0.40 <= gmin and gmax <= 1.30
+        assert asym <= 3e-2 and evr > -1e-2 and 0.2 <= frob <= 1.5
+
+
+def test_large_transposed_twin(gpu):
+    """A 28672x8192 matrix and its transpose in one bucket: the second must get
+    the transpose of the first's update (equal up to the order in which the
+    norm partials are summed; lr adjustment off so the scales agree)."""
+    import torch
+    wl = wlmod.get("large_single")
+    hp = dataclasses.replace(wl.hp, lr_adjust="none")
+    W, G, M = wlmod.torch_matrix_inputs(wl, 0, gpu)
+    mats = [(W, G, M), (W.t().contiguous(), G.t().contiguous(), M.t().contiguous())]
+    before, after, ups = run_bucket(wl, gpu, mats=mats, hp=hp)
+    d = float((ups[1] - ups[0].t()).norm() / ups[0].norm())
+    m = float((after[1][2] - after[0][2].t()).norm() / after[0][2].norm())
+    print(f"twin delta {d:.2e} momentum {m:.2e}", flush=True)
+    assert m == 0.0
+    assert d <= 1e-2
+
+
+def test_head_scale_invariance_bit_exact(gpu):
+    """The 128256x4096 head alone, then with G and M scaled by 4: bit-identical."""
+    import torch
+    wl = wlmod.get("large_single")
+    W, G, M = wlmod.torch_matrix_inputs(wl, 2, gpu)
+    _, a, ua = run_bucket(wl, gpu, mats=[(W.clone(), G, M.clone())])
+    _, b, ub = run_bucket(wl, gpu, mats=[(W.clone(), (G.float() * 4).to(G.dtype), M * 4)])
+    assert torch.equal(a[0][0], b[0][0])
+    assert torch.equal(ua[0], ub[0])
