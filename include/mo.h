@@ -102,7 +102,7 @@ mo_status muon_workspace_bytes(const mo_matrix* mats, int32_t n_mats,
 /* The host work list that muon_owner_step uploads, for inspection and tests.
  * If host_buf is NULL, *bytes_inout receives the size; otherwise *bytes_inout
  * must hold at least that size and the list is written to host_buf.  The byte
- * layout (little-endian, natural alignment, version 3):
+ * layout (little-endian, natural alignment, version 4):
  *   header   mo_wl_header (128 bytes)
  *   matrices mo_wl_mat[n_live] (192 bytes each), one per non-empty descriptor,
  *            in descriptor order
@@ -114,9 +114,11 @@ mo_status muon_workspace_bytes(const mo_matrix* mats, int32_t n_mats,
  * in descending order of their per-phase work (ties by descriptor index) and
  * cut into super-blocks of 4 tile-rows x 8 tile-columns (row-major, tiles
  * row-major inside); each super-block goes to the one of 8 queues (one per
- * XCD) with the least K-length x tiles so far, ties to the lowest, and entry
- * 8 j + x of a list is the j-th tile of queue x, or a pad entry (record index
- * 0xFFFFFFFF) where queue x is shorter. */
+ * XCD) with the least K-length x tiles so far, ties to the lowest; if that
+ * queue is below an even share ceil(total / 8) it takes only the tiles that
+ * reach the share (at least one) and the rest goes on to the next queue.
+ * Entry 8 j + x of a list is the j-th tile of queue x, or a pad entry (record
+ * index 0xFFFFFFFF) where queue x is shorter. */
 mo_status muon_build_worklist(const mo_matrix* mats, int32_t n_mats,
                               const mo_muon_hparams* hp, void* host_buf,
                               size_t* bytes_inout);

@@ -179,31 +179,53 @@ void build_plan(const mo_matrix* mats, int32_t n, const mo_muon_hparams* hp, Pla
     // super-block is what an XCD runs at once and its tiles share 4 row panels
     // and 8 column panels of the operands in that XCD's L2.  Super-blocks (in
     // the matrices' descending-work order) go to the XCD with the least work
-    // so far (K-length x tiles; ties to the lowest XCD), and the list
-    // interleaves the 8 queues: entry 8 j + x is the j-th tile of XCD x, or a
-    // pad entry (matrix index MO_WL_PAD) where that queue is shorter.
+    // so far (K-length x tiles; ties to the lowest XCD), split where that XCD
+    // would pass an even share of the total, and the list interleaves the 8
+    // queues: entry 8 j + x is the j-th tile of XCD x, or a pad entry (matrix
+    // index MO_WL_PAD) where that queue is shorter.
     constexpr uint32_t SB_R = 4, SB_C = 8, NXCD = 8;
     auto dispatch = [&](std::vector<mo_wl_item>& out, const std::vector<Key>& mats_order,
                         bool upper_only, bool k_is_n) {
-        std::vector<std::vector<mo_wl_item>> q(NXCD);
-        uint64_t load[NXCD] = {0};
+        struct Blk { std::vector<mo_wl_item> tiles; uint64_t klen; };
+        std::vector<Blk> blocks;
+        uint64_t total = 0;
         for (const Key& k : mats_order) {
             const mo_wl_mat& r = recs[k.idx];
             const uint32_t tm = r.m_pad / T, tn = upper_only ? tm : r.n_pad / T;
             const uint64_t klen = k_is_n ? r.n_pad : r.m_pad;
             for (uint32_t bi = 0; bi < tm; bi += SB_R)
                 for (uint32_t bj = 0; bj < tn; bj += SB_C) {
-                    std::vector<mo_wl_item> blk;
+                    Blk b{{}, klen};
                     for (uint32_t a = bi; a < std::min(bi + SB_R, tm); ++a)
-                        for (uint32_t b = bj; b < std::min(bj + SB_C, tn); ++b)
-                            if (!upper_only || a <= b) blk.push_back({k.idx, uint16_t(a), uint16_t(b)});
-                    if (blk.empty()) continue;
-                    uint32_t x = 0;
-                    for (uint32_t y = 1; y < NXCD; ++y)
-                        if (load[y] < load[x]) x = y;
-                    load[x] += klen * blk.size();
-                    q[x].insert(q[x].end(), blk.begin(), blk.end());
+                        for (uint32_t c = bj; c < std::min(bj + SB_C, tn); ++c)
+                            if (!upper_only || a <= c) b.tiles.push_back({k.idx, uint16_t(a), uint16_t(c)});
+                    if (b.tiles.empty()) continue;
+                    total += klen * b.tiles.size();
+                    blocks.push_back(std::move(b));
                 }
+        }
+        // A block goes whole to the least-loaded queue while that queue stays
+        // under the even share; otherwise the queue takes only what fills it
+        // (at least one tile) and the rest moves on to the next least-loaded.
+        const uint64_t target = (total + NXCD - 1) / NXCD;
+        std::vector<std::vector<mo_wl_item>> q(NXCD);
+        uint64_t load[NXCD] = {0};
+        for (const Blk& b : blocks) {
+            size_t i = 0;
+            while (i < b.tiles.size()) {
+                uint32_t x = 0;
+                for (uint32_t y = 1; y < NXCD; ++y)
+                    if (load[y] < load[x]) x = y;
+                const size_t rest = b.tiles.size() - i;
+                size_t take = rest;
+                if (load[x] < target) {
+                    const uint64_t fit = (target - load[x] + b.klen - 1) / b.klen;
+                    take = std::min<size_t>(rest, std::max<uint64_t>(1, fit));
+                }
+                q[x].insert(q[x].end(), b.tiles.begin() + i, b.tiles.begin() + i + take);
+                load[x] += b.klen * take;
+                i += take;
+            }
         }
         size_t len = 0;
         for (const auto& v : q) len = std::max(len, v.size());

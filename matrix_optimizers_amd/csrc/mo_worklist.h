@@ -11,7 +11,7 @@
 #include <stdint.h>
 
 #define MO_WL_MAGIC   0x4C574F4Du  // "MOWL"
-#define MO_WL_VERSION 3u
+#define MO_WL_VERSION 4u
 
 // matrix index of a padding entry in a dispatch list
 #define MO_WL_PAD 0xFFFFFFFFu

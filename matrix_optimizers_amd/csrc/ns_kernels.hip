@@ -230,21 +230,23 @@ template <> struct Mfma<float> {
 };
 
 // 64-byte rows of four 16-byte chunks; logical chunk c of row r sits at
-// c ^ ((r >> 1) & 3), so 8 consecutive rows read at one logical chunk cover all
-// eight 16-byte bank groups.
-MO_DEV int swz(int row, int chunk) { return row * KB + ((chunk ^ ((row >> 1) & 3)) << 4); }
+// c ^ ((r >> 2) & 3).  The LDS serves 16 lanes x 16 bytes per clock from 64
+// banks; 16 consecutive rows read at one logical chunk then fall on 16
+// distinct 16-byte bank groups (four rows per 256-byte bank line, each at a
+// different chunk).
+MO_DEV int swz(int row, int chunk) { return row * KB + ((chunk ^ ((row >> 2) & 3)) << 4); }
 
 // staging slice index: 128 fp32 columns per row, column bits 3..4 XOR row bits 3..4
 MO_DEV int st_idx(int row, int col) { return row * 128 + (col ^ (((row >> 3) & 3) << 3)); }
 
 // Epilogue context of one workgroup tile.
-template <typename T, int KIND>
+template <typename T, int KIND, bool LAST>
 struct Epi {
     const mo_wl_mat* mt;
     T *X, *Xt_nxt, *A, *B;
     float alpha, sx, na, nb, nc;
     int64_t m_pad, n_pad;
-    bool last, trans;
+    bool trans;
 
     // pass A: 8 values at tile-orientation position (gi, gj..gj+7).  `opnd`
     // is the matching chunk of the epilogue operand (A for Poly, X for Update)
@@ -266,7 +268,7 @@ struct Epi {
             if (opnd) xv = *opnd; else load8(X + gi * n_pad + gj, xv);
 #pragma unroll
             for (int e = 0; e < 8; ++e) v.v[e] = sx * (na * xv.v[e] + v.v[e]);
-            if (!last) {
+            if (!LAST) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) v.v[e] = quantize<T>(v.v[e]);
                 store8(X + gi * n_pad + gj, v);
@@ -287,7 +289,7 @@ struct Epi {
             store8(A + oj * m_pad + oi, v);
         } else if (KIND == KIND_POLY) {
             store8(B + oj * m_pad + oi, v);    // B is symmetric: the staged values
-        } else if (!last) {
+        } else if (!LAST) {
             store8(Xt_nxt + oj * m_pad + oi, v);
         } else {
             write_w(oj, oi, v);            // weight frame is the transpose
@@ -313,9 +315,12 @@ struct Epi {
     }
 };
 
-template <typename T, int KIND>
+// LAST (Update only): the final Newton-Schulz step, whose epilogue writes W in
+// the weight's frame instead of the next X / X^T; a separate instantiation
+// keeps the weight-write code out of the common kernel.
+template <typename T, int KIND, bool LAST>
 __global__ __launch_bounds__(G_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gemm_kernel(uint8_t* ws, int first, int last, int xt_cur) {
+void gemm_kernel(uint8_t* ws, int first, int xt_cur) {
     __shared__ __align__(16) uint8_t smem[GEMM_LDS];
     const mo_wl_header* h = wl_header(ws);
     const uint64_t items_off = KIND == KIND_GRAM ? h->gram_offset
@@ -360,7 +365,7 @@ void gemm_kernel(uint8_t* ws, int first, int last, int xt_cur) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int row = wave * 64 + i * 16 + lrow;
-        goff[i] = int64_t(row) * ldb + ((pch ^ ((row >> 1) & 3)) << 4);
+        goff[i] = int64_t(row) * ldb + ((pch ^ ((row >> 2) & 3)) << 4);
     }
     auto issue = [&](int ks) {
         uint8_t* sp = smem + (ks % NSTAGE) * STAGE_BYTES + wave * 64 * KB;
@@ -441,7 +446,7 @@ void gemm_kernel(uint8_t* ws, int first, int last, int xt_cur) {
     __builtin_amdgcn_sched_barrier(0);
     // Epilogue operand prefetch (bf16 Poly / Update): the lane's 32 chunks of
     // A or X that pass A will combine with the product, loaded into registers,
-    // rounds 0-1 while the last K substeps run and rounds 2-3 as the epilogue
+    // round 0 while the last K substeps run and rounds 1-3 as the epilogue
     // starts.  Chunk (round r, task t) sits at sub-tile
     // row 32 r + 4 t + lane/16, columns 8 (lane % 16) .. + 7.
     constexpr bool PREF = sizeof(T) == 2 && KIND != KIND_GRAM;
@@ -471,7 +476,7 @@ void gemm_kernel(uint8_t* ws, int first, int last, int xt_cur) {
         wait_loads(issued_last - (ks + 1));
         barrier();   // stage ks+1 visible everywhere; every read of stage ks done
         if (ks + NSTAGE < nk) issue(ks + NSTAGE);   // refill the slot of stage ks
-        if (with_prefetch) prefetch(0, 2);          // no stage load is in flight any more
+        if (with_prefetch) prefetch(0, 1);          // no stage load is in flight any more
         __builtin_amdgcn_sched_barrier(0);
         mm(f1a, f1b);
         rd(ks + 1, 0, f0a, f0b);
@@ -485,18 +490,17 @@ void gemm_kernel(uint8_t* ws, int first, int last, int xt_cur) {
     __builtin_amdgcn_sched_barrier(0);
     mm(f1a, f1b);
     __syncthreads();   // every wave is done with the operand stages
-    prefetch(2, 4);    // the fragment registers are free now
+    prefetch(1, 4);    // the fragment registers are free now
 
-    Epi<T, KIND> ep;
+    Epi<T, KIND, LAST> ep;
     ep.mt = &mt;
     ep.X = X; ep.Xt_nxt = Xt_nxt; ep.A = A; ep.B = B;
     ep.alpha = (KIND == KIND_GRAM && first) ? scale[1] : 1.0f;
     ep.sx = (KIND == KIND_UPDATE && first) ? scale[0] : 1.0f;
     ep.na = h->ns_a; ep.nb = h->ns_b; ep.nc = h->ns_c;
     ep.m_pad = m_pad; ep.n_pad = n_pad;
-    ep.last = last;
     ep.trans = mt.flags & MO_WLF_TRANSPOSED;
-    const bool need_b = KIND == KIND_UPDATE ? (!last || ep.trans) : (ti != tj);
+    const bool need_b = KIND == KIND_UPDATE ? (!LAST || ep.trans) : (ti != tj);
 
     float* st = reinterpret_cast<float*>(smem + wave * WAVE_ST_BYTES);
     // One 32-row block of the wave's sub-tile; called with literal indices so
@@ -580,26 +584,27 @@ hipError_t mo_launch_apply(const mo_wl_header& h, uint8_t* ws, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int KIND>
+template <int KIND, bool LAST>
 static hipError_t launch_gemm(const mo_wl_header& h, uint32_t items, uint8_t* ws, int first,
-                              int last, int xt_cur, hipStream_t s) {
+                              int xt_cur, hipStream_t s) {
     if (items == 0) return hipSuccess;
     if (h.ns_dtype == MO_BF16)
-        hipLaunchKernelGGL((gemm_kernel<bf16_t, KIND>), dim3(grid_for(items)), dim3(G_THREADS), 0, s,
-                           ws, first, last, xt_cur);
+        hipLaunchKernelGGL((gemm_kernel<bf16_t, KIND, LAST>), dim3(grid_for(items)), dim3(G_THREADS), 0, s,
+                           ws, first, xt_cur);
     else
-        hipLaunchKernelGGL((gemm_kernel<float, KIND>), dim3(grid_for(items)), dim3(G_THREADS), 0, s,
-                           ws, first, last, xt_cur);
+        hipLaunchKernelGGL((gemm_kernel<float, KIND, LAST>), dim3(grid_for(items)), dim3(G_THREADS), 0, s,
+                           ws, first, xt_cur);
     return hipGetLastError();
 }
 
 hipError_t mo_launch_gram(const mo_wl_header& h, uint8_t* ws, int first, int xt_cur, hipStream_t s) {
-    return launch_gemm<KIND_GRAM>(h, h.n_gram_items, ws, first, 0, xt_cur, s);
+    return launch_gemm<KIND_GRAM, false>(h, h.n_gram_items, ws, first, xt_cur, s);
 }
 hipError_t mo_launch_poly(const mo_wl_header& h, uint8_t* ws, hipStream_t s) {
-    return launch_gemm<KIND_POLY>(h, h.n_poly_items, ws, 0, 0, 0, s);
+    return launch_gemm<KIND_POLY, false>(h, h.n_poly_items, ws, 0, 0, s);
 }
 hipError_t mo_launch_update(const mo_wl_header& h, uint8_t* ws, int first, int last, int xt_cur,
                             hipStream_t s) {
-    return launch_gemm<KIND_UPDATE>(h, h.n_upd_items, ws, first, last, xt_cur, s);
+    return last ? launch_gemm<KIND_UPDATE, true>(h, h.n_upd_items, ws, first, xt_cur, s)
+                : launch_gemm<KIND_UPDATE, false>(h, h.n_upd_items, ws, first, xt_cur, s);
 }

@@ -5,7 +5,7 @@ byte layout is specified in ``include/mo.h`` (muon_build_worklist) and the
 record comments there.  This twin is written from that specification with
 Python's ``struct`` so that the C++ builder can be checked byte for byte.
 
-Layout (little-endian, natural alignment, version 3):
+Layout (little-endian, natural alignment, version 4):
   header (128 B): magic 'MOWL', version, n_mats, ns_steps, ns_dtype, gemm_tile,
       mom_tile, elem_bytes, n_mom_items, n_gram_items, n_poly_items,
       n_upd_items, max_partials, 0, mats_offset, gram_offset, poly_offset,
@@ -95,11 +95,13 @@ def build(descs: Sequence[dict], hp: dict) -> bytes:
 
     def dispatch(mat_order, upper_only, k_is_n):
         """Super-blocks of 4 tile-rows x 8 tile-columns (row-major, tiles
-        row-major inside) go, in matrix order, to whichever of 8 queues has the
-        least K-length x tiles so far (ties: lowest queue); the list interleaves
-        the queues (entry 8 j + x = j-th tile of queue x, or a pad entry)."""
-        queues = [[] for _ in range(8)]
-        load = [0] * 8
+        row-major inside), in matrix order, each costing K-length per tile.  A
+        block goes to the least-loaded of 8 queues (ties: lowest); if that
+        queue is under target = ceil(total / 8), it takes only
+        max(1, ceil((target - load) / K-length)) tiles and the rest of the block
+        goes on to the next least-loaded queue.  The list interleaves the queues
+        (entry 8 j + x = j-th tile of queue x, or a pad entry)."""
+        blocks = []
         for j in mat_order:
             r = recs[j]
             tm = r["m_pad"] // T
@@ -109,11 +111,23 @@ def build(descs: Sequence[dict], hp: dict) -> bytes:
                 for bj in range(0, tn, 8):
                     blk = [(j, a, b) for a in range(bi, min(bi + 4, tm))
                            for b in range(bj, min(bj + 8, tn)) if not upper_only or a <= b]
-                    if not blk:
-                        continue
-                    x = min(range(8), key=lambda y: (load[y], y))
-                    load[x] += klen * len(blk)
-                    queues[x] += blk
+                    if blk:
+                        blocks.append((blk, klen))
+        total = sum(len(b) * k for b, k in blocks)
+        target = (total + 7) // 8
+        queues = [[] for _ in range(8)]
+        load = [0] * 8
+        for blk, klen in blocks:
+            i = 0
+            while i < len(blk):
+                x = min(range(8), key=lambda y: (load[y], y))
+                take = len(blk) - i
+                if load[x] < target:
+                    fit = (target - load[x] + klen - 1) // klen
+                    take = min(take, max(1, fit))
+                queues[x] += blk[i:i + take]
+                load[x] += klen * take
+                i += take
         longest = max((len(q) for q in queues), default=0)
         return [queues[x][j] if j < len(queues[x]) else (PAD, 0, 0)
                 for j in range(longest) for x in range(8)]
@@ -139,7 +153,7 @@ def build(descs: Sequence[dict], hp: dict) -> bytes:
     ws_bytes = off
 
     out = bytearray(wl_bytes)
-    struct.pack_into("<14I6Q4f2I", out, 0, MAGIC, 3, len(recs), hp["ns_steps"], hp["ns_dtype"],
+    struct.pack_into("<14I6Q4f2I", out, 0, MAGIC, 4, len(recs), hp["ns_steps"], hp["ns_dtype"],
                      T, MT, es, mom, len(gram), len(poly), len(upd), max_partials, 0,
                      mats_off, gram_off, poly_off, upd_off, wl_bytes, ws_bytes,
                      hp["ns_a"], hp["ns_b"], hp["ns_c"], hp["eps"], 0, 0)
