@@ -191,9 +191,10 @@ def main():
     }
     if prof is not None:
         per_launch = {}
-        flops_launch = {"gram": 0.0, "poly": 0.0, "update": 0.0}
+        flops_launch = {"gram": 0.0, "poly": 0.0, "update": 0.0, "update_last": 0.0}
         for s in wl.matrices:
             f = algorithmic_flops(s.rows, s.cols, hp.ns_steps)
+            f["update_last"] = f["update"]
             for k in flops_launch:
                 flops_launch[k] += f[k]
         for name, (tot, cnt) in prof.items():
@@ -205,10 +206,19 @@ def main():
         if gemm:
             dom = max(gemm, key=lambda k: gemm[k]["ms_per_step"])
             achieved = flops_launch[dom] / (gemm[dom]["avg_ms"] * 1e-3) / 1e12
+            # HBM bytes per launch from the committed rocprofv3 counter summary,
+            # only if it was taken on the current kernel sources
+            from matrix_optimizers_amd import profiling
+            tr = profiling.read_traffic(os.path.join(ROOT, "profiles"), wl.key,
+                                        f"{dom}[{hp.ns_dtype}]")
             out["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                                "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                               "traffic": None,
+                               "traffic": None if tr is None else round(tr["read_bytes"] + tr["write_bytes"]),
                                "algorithmic_per_launch": f"{flops_launch[dom]:.4e} flop"}
+            if tr is not None:
+                out["roofline"]["traffic_detail"] = {
+                    "read_bytes": round(tr["read_bytes"]), "write_bytes": round(tr["write_bytes"]),
+                    "profile": tr["source"], "profile_avg_ms": round(tr["avg_ns"] / 1e6, 5)}
         if "momentum" in per_launch:
             # momentum kernel: read G (w) + M (4), write M' (4) + U twice in the NS dtype
             es_g = 2 if wl.g_dtype == "bf16" else 4

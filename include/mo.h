@@ -157,11 +157,12 @@ const char* mo_status_string(mo_status status);
 #define MO_PHASE_NORM     1   /* per-matrix norm finalisation */
 #define MO_PHASE_GRAM     2   /* A = X X^T (upper tiles, mirrored) */
 #define MO_PHASE_POLY     3   /* B = b A + c A A */
-#define MO_PHASE_UPDATE   4   /* X <- a X + B X; last step writes W */
+#define MO_PHASE_UPDATE   4   /* X <- a X + B X (every step but the last) */
 #define MO_PHASE_APPLY    5   /* K == 0 only: W <- (1-lr wd) W - lr_eff X */
 #define MO_PHASE_ADAMW    6
 #define MO_PHASE_COPY     7   /* mo_device_copy */
-#define MO_PHASE_COUNT    8
+#define MO_PHASE_UPDATE_LAST 8 /* last Newton-Schulz step: O = a X + B X, W written */
+#define MO_PHASE_COUNT    9
 
 /* Enable (1) or disable (0) per-launch timing on the calling thread.  While
  * enabled, every kernel launch is bracketed by HIP events on its own stream;

@@ -27,7 +27,7 @@ DTYPES = {"f32": MO_F32, "float32": MO_F32, "bf16": MO_BF16, "bfloat16": MO_BF16
 
 LR_ADJUST = {"original": 0, "match_rms_adamw": 1, "none": 2}
 
-PHASES = ["momentum", "norm", "gram", "poly", "update", "apply", "adamw", "copy"]
+PHASES = ["momentum", "norm", "gram", "poly", "update", "apply", "adamw", "copy", "update_last"]
 
 
 class MoError(RuntimeError):

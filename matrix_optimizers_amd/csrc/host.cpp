@@ -440,7 +440,8 @@ mo_status muon_owner_step(const mo_matrix* mats, int32_t n, const mo_muon_hparam
             return MO_ERR_HIP;
         if (timed_launch(MO_PHASE_POLY, s, [&] { return mo_launch_poly(h, ws, s); }) != hipSuccess)
             return MO_ERR_HIP;
-        if (timed_launch(MO_PHASE_UPDATE, s, [&] { return mo_launch_update(h, ws, first, last, xt, s); }) != hipSuccess)
+        if (timed_launch(last ? MO_PHASE_UPDATE_LAST : MO_PHASE_UPDATE, s,
+                         [&] { return mo_launch_update(h, ws, first, last, xt, s); }) != hipSuccess)
             return MO_ERR_HIP;
         xt ^= 1;
     }

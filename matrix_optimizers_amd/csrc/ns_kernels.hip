@@ -296,31 +296,47 @@ struct Epi {
         }
     }
 
-    // W[r][c..c+7] <- decay * W - lr_eff * O, clipped to the matrix
+    // W[r][c..c+7] <- decay * W - lr_eff * O, clipped to the matrix; 16-byte
+    // vector accesses when the chunk is whole and the rows are aligned.
+    bool vec_w, vec_u;
     MO_DEV void write_w(int64_t r, int64_t c, const f32x8& o) const {
         if (r >= mt->rows) return;
         const bool wbf = mt->flags & MO_WLF_W_BF16;
         void* W = reinterpret_cast<void*>(mt->W);
         float* U = reinterpret_cast<float*>(mt->U);
         const float decay = mt->decay, lr = mt->lr_eff;
+        const int64_t wi = r * mt->ld_w + c;
+        if (c + 8 <= mt->cols && vec_w) {
+            f32x8 w;
+            if (wbf) load8(reinterpret_cast<const bf16_t*>(W) + wi, w);
+            else load8(reinterpret_cast<const float*>(W) + wi, w);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            if (c + e < mt->cols) {
-                const int64_t wi = r * mt->ld_w + c + e;
-                const float w = load_elem(W, wi, wbf);
-                store_elem(W, wi, decay * w - lr * o.v[e], wbf);
-                if (U) U[r * mt->ld_u + c + e] = lr * o.v[e];
+            for (int e = 0; e < 8; ++e) w.v[e] = decay * w.v[e] - lr * o.v[e];
+            if (wbf) store8(reinterpret_cast<bf16_t*>(W) + wi, w);
+            else store8(reinterpret_cast<float*>(W) + wi, w);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (c + e < mt->cols) store_elem(W, wi + e, decay * load_elem(W, wi + e, wbf) - lr * o.v[e], wbf);
+        }
+        if (U) {
+            const int64_t ui = r * mt->ld_u + c;
+            if (c + 8 <= mt->cols && vec_u) {
+                f32x8 u;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) u.v[e] = lr * o.v[e];
+                store8(U + ui, u);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (c + e < mt->cols) U[ui + e] = lr * o.v[e];
             }
         }
     }
 };
 
-// LAST (Update only): the final Newton-Schulz step, whose epilogue writes W in
-// the weight's frame instead of the next X / X^T; a separate instantiation
-// keeps the weight-write code out of the common kernel.
 template <typename T, int KIND, bool LAST>
-__global__ __launch_bounds__(G_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gemm_kernel(uint8_t* ws, int first, int xt_cur) {
+__device__ __forceinline__ void gemm_tile(uint8_t* ws, int first, int xt_cur) {
     __shared__ __align__(16) uint8_t smem[GEMM_LDS];
     const mo_wl_header* h = wl_header(ws);
     const uint64_t items_off = KIND == KIND_GRAM ? h->gram_offset
@@ -500,6 +516,11 @@ void gemm_kernel(uint8_t* ws, int first, int xt_cur) {
     ep.na = h->ns_a; ep.nb = h->ns_b; ep.nc = h->ns_c;
     ep.m_pad = m_pad; ep.n_pad = n_pad;
     ep.trans = mt.flags & MO_WLF_TRANSPOSED;
+    {
+        const int64_t wes = (mt.flags & MO_WLF_W_BF16) ? 2 : 4;
+        ep.vec_w = ((mt.W | uint64_t(mt.ld_w * wes)) & 15) == 0;
+        ep.vec_u = ((mt.U | uint64_t(mt.ld_u * 4)) & 15) == 0;
+    }
     const bool need_b = KIND == KIND_UPDATE ? (!LAST || ep.trans) : (ti != tj);
 
     float* st = reinterpret_cast<float*>(smem + wave * WAVE_ST_BYTES);
@@ -553,6 +574,20 @@ void gemm_kernel(uint8_t* ws, int first, int xt_cur) {
 
 inline unsigned grid_for(uint32_t items) { return items; }   // dispatch lists are padded to 8
 
+// One plainly named kernel per (phase, NS dtype), so profiles name them unambiguously.
+#define MO_GEMM_KERNEL(name, T, KIND, LAST)                                               \
+    __global__ __launch_bounds__(G_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))    \
+    void name(uint8_t* ws, int first, int xt_cur) { gemm_tile<T, KIND, LAST>(ws, first, xt_cur); }
+MO_GEMM_KERNEL(gram_bf16, bf16_t, KIND_GRAM, false)
+MO_GEMM_KERNEL(gram_f32, float, KIND_GRAM, false)
+MO_GEMM_KERNEL(poly_bf16, bf16_t, KIND_POLY, false)
+MO_GEMM_KERNEL(poly_f32, float, KIND_POLY, false)
+MO_GEMM_KERNEL(update_bf16, bf16_t, KIND_UPDATE, false)
+MO_GEMM_KERNEL(update_f32, float, KIND_UPDATE, false)
+MO_GEMM_KERNEL(update_last_bf16, bf16_t, KIND_UPDATE, true)
+MO_GEMM_KERNEL(update_last_f32, float, KIND_UPDATE, true)
+#undef MO_GEMM_KERNEL
+
 }  // namespace
 
 // ============================================================================
@@ -584,27 +619,24 @@ hipError_t mo_launch_apply(const mo_wl_header& h, uint8_t* ws, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int KIND, bool LAST>
-static hipError_t launch_gemm(const mo_wl_header& h, uint32_t items, uint8_t* ws, int first,
-                              int xt_cur, hipStream_t s) {
+typedef void (*gemm_fn)(uint8_t*, int, int);
+
+static hipError_t launch_gemm(const mo_wl_header& h, uint32_t items, gemm_fn bf, gemm_fn f32,
+                              uint8_t* ws, int first, int xt_cur, hipStream_t s) {
     if (items == 0) return hipSuccess;
-    if (h.ns_dtype == MO_BF16)
-        hipLaunchKernelGGL((gemm_kernel<bf16_t, KIND, LAST>), dim3(grid_for(items)), dim3(G_THREADS), 0, s,
-                           ws, first, xt_cur);
-    else
-        hipLaunchKernelGGL((gemm_kernel<float, KIND, LAST>), dim3(grid_for(items)), dim3(G_THREADS), 0, s,
-                           ws, first, xt_cur);
+    hipLaunchKernelGGL((h.ns_dtype == MO_BF16 ? bf : f32), dim3(grid_for(items)), dim3(G_THREADS), 0, s,
+                       ws, first, xt_cur);
     return hipGetLastError();
 }
 
 hipError_t mo_launch_gram(const mo_wl_header& h, uint8_t* ws, int first, int xt_cur, hipStream_t s) {
-    return launch_gemm<KIND_GRAM, false>(h, h.n_gram_items, ws, first, xt_cur, s);
+    return launch_gemm(h, h.n_gram_items, gram_bf16, gram_f32, ws, first, xt_cur, s);
 }
 hipError_t mo_launch_poly(const mo_wl_header& h, uint8_t* ws, hipStream_t s) {
-    return launch_gemm<KIND_POLY, false>(h, h.n_poly_items, ws, 0, 0, s);
+    return launch_gemm(h, h.n_poly_items, poly_bf16, poly_f32, ws, 0, 0, s);
 }
 hipError_t mo_launch_update(const mo_wl_header& h, uint8_t* ws, int first, int last, int xt_cur,
                             hipStream_t s) {
-    return last ? launch_gemm<KIND_UPDATE, true>(h, h.n_upd_items, ws, first, xt_cur, s)
-                : launch_gemm<KIND_UPDATE, false>(h, h.n_upd_items, ws, first, xt_cur, s);
+    return last ? launch_gemm(h, h.n_upd_items, update_last_bf16, update_last_f32, ws, first, xt_cur, s)
+                : launch_gemm(h, h.n_upd_items, update_bf16, update_f32, ws, first, xt_cur, s);
 }

@@ -1,0 +1,158 @@
+"""Summaries of rocprofv3 output for the committed profiles, and the HBM
+traffic figure bench.py reports.
+
+    python -m matrix_optimizers_amd.profiling summarize TRACE_DIR COUNTER_DIR \\
+        COPY_DIR OUT.md --command "..." --workload NAME
+
+TRACE_DIR holds a ``--kernel-trace --stats -f csv`` run; COUNTER_DIR holds one
+subdirectory per ``--pmc`` pass (FETCH_SIZE/, WRITE_SIZE/) of the same command;
+COPY_DIR holds the same two passes over ``bench.py --copy-calibration`` (the
+library's plain copy of a known number of bytes), which fixes the factor
+between each counter and true bytes.  The summary states the per-kernel
+durations, per-launch HBM bytes, and the SHA-256 of the kernel sources the
+counters were taken on; bench.py reports the traffic only while that hash
+still matches the sources.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import os
+import re
+from collections import defaultdict
+from typing import Dict, Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = ["csrc/ns_kernels.hip", "csrc/tail_kernels.hip", "csrc/device_common.h",
+                  "csrc/mo_worklist.h", "csrc/host.cpp"]
+
+
+def sources_sha256() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(HERE, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def short_name(kernel: str) -> Optional[str]:
+    """Library kernel -> phase name (None for kernels that are not ours)."""
+    m = re.search(r"\b(gram|poly|update_last|update)_(bf16|f32)\b", kernel)
+    if m:
+        return f"{m.group(1)}[{m.group(2)}]"
+    for key, name in (("momentum_kernel", "momentum"), ("norm_kernel", "norm"),
+                      ("apply_kernel", "apply"), ("adamw", "adamw")):
+        if key in kernel:
+            return name
+    if kernel.startswith("(anonymous namespace)::copy_kernel") or "::copy_kernel(" in kernel:
+        return "copy"
+    return None
+
+
+def kernel_stats(trace_dir: str) -> Dict[str, dict]:
+    """Per-phase calls / total / average (ns) from the kernel trace."""
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    out: Dict[str, dict] = defaultdict(lambda: {"calls": 0, "total_ns": 0.0})
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            name = short_name(r["Kernel_Name"])
+            if name is None:
+                continue
+            d = out[name]
+            d["calls"] += 1
+            d["total_ns"] += float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    for d in out.values():
+        d["avg_ns"] = d["total_ns"] / d["calls"]
+    return dict(out)
+
+
+def counter_means(pass_dir: str, counter: str) -> Dict[str, float]:
+    """Mean value of `counter` per dispatch, per phase."""
+    vals: Dict[str, list] = defaultdict(list)
+    for f in glob.glob(os.path.join(pass_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter:
+                continue
+            name = short_name(r["Kernel_Name"])
+            if name is not None:
+                vals[name].append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in vals.items()}
+
+
+def copy_factor(copy_dir: str, counter: str, copied_bytes: int) -> float:
+    """True bytes per counter unit, from the copy kernel: it reads and writes
+    copied_bytes each."""
+    m = counter_means(os.path.join(copy_dir), counter).get("copy")
+    if not m:
+        raise RuntimeError(f"no copy-kernel {counter} samples in {copy_dir}")
+    return copied_bytes / m
+
+
+def summarize(trace_dir, counter_dir, copy_dirs, out_md, command, workload, copied_mib=1024):
+    stats = kernel_stats(trace_dir)
+    copied = copied_mib << 20
+    fetch = counter_means(os.path.join(counter_dir, "FETCH_SIZE"), "FETCH_SIZE")
+    write = counter_means(os.path.join(counter_dir, "WRITE_SIZE"), "WRITE_SIZE")
+    ff = copy_factor(copy_dirs["FETCH_SIZE"], "FETCH_SIZE", copied)
+    wf = copy_factor(copy_dirs["WRITE_SIZE"], "WRITE_SIZE", copied)
+    lines = [f"# rocprofv3 summary: {workload}", "",
+             "Commands (run from the repository root on one MI355X):", "",
+             "```", command, "```", "",
+             f"Kernel sources SHA-256: `{sources_sha256()}`", "",
+             f"Byte-counter calibration with the library's copy kernel ({copied_mib} MiB read + written): "
+             f"FETCH_SIZE x {ff:.4g} B, WRITE_SIZE x {wf:.4g} B.", "",
+             "| phase | launches | avg (us) | total (ms) | HBM read / launch (MB) | HBM write / launch (MB) |",
+             "|---|---|---|---|---|---|"]
+    for name, d in sorted(stats.items(), key=lambda kv: -kv[1]["total_ns"]):
+        rd = fetch.get(name)
+        wr = write.get(name)
+        lines.append(f"| {name} | {d['calls']} | {d['avg_ns'] / 1e3:.2f} | {d['total_ns'] / 1e6:.3f} | "
+                     f"{'' if rd is None else f'{rd * ff / 1e6:.1f}'} | "
+                     f"{'' if wr is None else f'{wr * wf / 1e6:.1f}'} |")
+    lines += ["", "Machine-readable (bench.py reads these lines):", ""]
+    for name, d in sorted(stats.items()):
+        rd, wr = fetch.get(name), write.get(name)
+        if rd is not None and wr is not None:
+            lines.append(f"traffic {workload} {name} {rd * ff:.0f} {wr * wf:.0f} {d['avg_ns']:.0f} "
+                         f"{sources_sha256()}")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return out_md
+
+
+def read_traffic(profiles_dir: str, workload: str, phase: str) -> Optional[dict]:
+    """HBM bytes per launch of `phase` measured on the current kernel sources,
+    or None if no summary matches them."""
+    sha = sources_sha256()
+    for f in sorted(glob.glob(os.path.join(profiles_dir, "*.md"))):
+        for line in open(f):
+            p = line.split()
+            if len(p) == 7 and p[0] == "traffic" and p[1] == workload and p[2] == phase and p[6] == sha:
+                return {"read_bytes": float(p[3]), "write_bytes": float(p[4]), "avg_ns": float(p[5]),
+                        "source": os.path.basename(f)}
+    return None
+
+
+def _main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("summarize")
+    s.add_argument("trace_dir")
+    s.add_argument("counter_dir")
+    s.add_argument("copy_dir", help="directory with copy_FETCH_SIZE/ and copy_WRITE_SIZE/")
+    s.add_argument("out_md")
+    s.add_argument("--command", required=True)
+    s.add_argument("--workload", required=True)
+    s.add_argument("--copy-mib", type=int, default=1024)
+    a = ap.parse_args()
+    summarize(a.trace_dir, a.counter_dir,
+              {"FETCH_SIZE": os.path.join(a.copy_dir, "copy_FETCH_SIZE"),
+               "WRITE_SIZE": os.path.join(a.copy_dir, "copy_WRITE_SIZE")},
+              a.out_md, a.command, a.workload, a.copy_mib)
+    print("wrote", a.out_md)
+
+
+if __name__ == "__main__":
+    _main()

@@ -173,9 +173,18 @@ def test_copy_and_worklist_argument_checks():
     assert lib.muon_workspace_bytes(arr, n, ctypes.byref(hp), None) == INVALID
 
 
+def test_phase_list_matches_header():
+    text = open(HEADER).read()
+    ids = {m.group(1).lower(): int(m.group(2))
+           for m in re.finditer(r"#define MO_PHASE_(\w+)\s+(\d+)", text)}
+    assert ids.pop("count") == len(B.PHASES)
+    for name, i in ids.items():
+        assert B.PHASES[i] == name
+
+
 def test_profile_read_empty():
-    ms = (ctypes.c_double * 8)()
-    cnt = (ctypes.c_int64 * 8)()
+    ms = (ctypes.c_double * len(B.PHASES))()
+    cnt = (ctypes.c_int64 * len(B.PHASES))()
     lib = mo.load_library()
     assert lib.mo_profile_read(ms, cnt) == OK
     assert lib.mo_profile_read(None, cnt) == INVALID
