@@ -383,15 +383,13 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ws, int first, int xt_cur) {
         const int row = wave * 64 + i * 16 + lrow;
         goff[i] = int64_t(row) * ldb + ((pch ^ ((row >> 2) & 3)) << 4);
     }
-    auto issue = [&](int ks) {
-        uint8_t* sp = smem + (ks % NSTAGE) * STAGE_BYTES + wave * 64 * KB;
-        const int64_t kofs = int64_t(ks) * KB;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            __builtin_amdgcn_global_load_lds(Pb + goff[i] + kofs, (lds_void_t*)(sp + i * 16 * KB), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(Qb + goff[i] + kofs, (lds_void_t*)(sp + OPND_BYTES + i * 16 * KB),
-                                             16, 0, 0);
-        }
+    // Load instruction i (0..7) of stage ks: rows 64 wave + 16 (i / 2) + lane/4
+    // of operand P (i even) or Q (i odd).
+    auto issue1 = [&](int ks, int i) __attribute__((always_inline)) {
+        uint8_t* sp = smem + (ks % NSTAGE) * STAGE_BYTES + (i & 1) * OPND_BYTES + wave * 64 * KB +
+                      (i >> 1) * 16 * KB;
+        const uint8_t* g = ((i & 1) ? Qb : Pb) + goff[i >> 1] + int64_t(ks) * KB;
+        __builtin_amdgcn_global_load_lds(g, (lds_void_t*)sp, 16, 0, 0);
     };
 
     f32x16 acc[4][4];
@@ -402,63 +400,67 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ws, int first, int xt_cur) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
 
-    // Fragments of one 16-deep K substep: 4 A and 4 B chunks per lane.
-    auto rd = [&](int ks, int sub, u32x4 (&fa)[4], u32x4 (&fb)[4]) {
+    // Fragment i of one 16-deep K substep: A chunk i (i < 4) or B chunk i - 4.
+    auto rd1 = [&](int ks, int sub, int i, u32x4 (&fa)[4], u32x4 (&fb)[4]) __attribute__((always_inline)) {
         const uint8_t* sp = smem + (ks % NSTAGE) * STAGE_BYTES;
-        const uint8_t* sq = sp + OPND_BYTES;
         const int chunk = 2 * sub + kg;
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-            fa[a] = *reinterpret_cast<const u32x4*>(sp + swz(wm * 128 + a * 32 + r32, chunk));
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-            fb[b] = *reinterpret_cast<const u32x4*>(sq + swz(wn * 128 + b * 32 + r32, chunk));
-    };
-    auto mm = [&](const u32x4 (&fa)[4], const u32x4 (&fb)[4]) {
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int b = 0; b < 4; ++b) Mfma<T>::run(fa[a], fb[b], acc[a][b]);
+        if (i < 4) fa[i] = *reinterpret_cast<const u32x4*>(sp + swz(wm * 128 + i * 32 + r32, chunk));
+        else fb[i - 4] = *reinterpret_cast<const u32x4*>(sp + OPND_BYTES + swz(wn * 128 + (i - 4) * 32 + r32, chunk));
     };
     // Workgroup barrier without the release fence of __syncthreads(), which
     // would also drain the direct-to-LDS loads still in flight for later
     // stages.  Each thread first waits for its own loads of the stage being
     // published (explicit vmcnt) and for its LDS reads (lgkmcnt).
     auto wait_loads = [&](int later) {   // later = stages issued after the one awaited
-        if (later >= 3) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+        if (later >= 4) asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
+        else if (later == 3) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
         else if (later == 2) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
         else if (later == 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
         else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     };
+    // lgkmcnt(0) through the builtin (gfx9 encoding: vmcnt and expcnt at their
+    // maxima), so the compiler knows every fragment read has landed and adds
+    // no wait of its own after the barrier.
     auto barrier = [&]() {
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0xC07F);
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
     };
 
-    // Interleave the 8 fragment reads of the next substep with the MFMAs of
-    // the current one (bf16: 1 MFMA then 1 read; fp32 issues 4 MFMAs per chunk).
-    constexpr int MF = sizeof(T) == 2 ? 1 : 4;
-    auto interleave = [&]() {
+    // The 16 MFMAs of one substep on (fa, fb).  After each of the first 8
+    // comes one fragment read of the next substep (stage rks, substep rsub,
+    // into na / nb) and, when iks >= 0, one load instruction of stage iks; the
+    // order is fixed (sched_barrier), so reads and loads stream out between
+    // the MFMAs instead of in bursts the matrix core would wait behind.
+    auto substep = [&](const u32x4 (&fa)[4], const u32x4 (&fb)[4], bool do_read, int rks, int rsub,
+                       u32x4 (&na)[4], u32x4 (&nb)[4], int iks) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);   // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // DS read
+        for (int i = 0; i < 16; ++i) {
+            Mfma<T>::run(fa[i >> 2], fb[i & 3], acc[i >> 2][i & 3]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (i < 8) {
+                if (do_read) rd1(rks, rsub, i, na, nb);
+                if (iks >= 0) issue1(iks, i);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 16 * MF - 8 * MF, 0);
     };
 
     // Software pipeline over K (nk >= 8: every padded dimension is >= 256).
-    // Stage s occupies ring slot s % 4.  Entering iteration ks, F0 holds the
-    // fragments of (ks, substep 0).  The barrier sits between the two substeps,
-    // so the MFMAs after it use fragments already in registers while the reads
-    // for the next stage land.
+    // Stage s occupies ring slot s % NSTAGE.  Entering iteration ks, F0 holds
+    // the fragments of (ks, substep 0).  The barrier sits between the two
+    // substeps, so the MFMAs after it use fragments already in registers while
+    // the reads for the next stage land.  Stage ks + NSTAGE refills the slot of
+    // stage ks once the barrier has shown every wave done with it.
     u32x4 f0a[4], f0b[4], f1a[4], f1b[4];
 #pragma unroll
-    for (int ks = 0; ks < NSTAGE; ++ks) issue(ks);
+    for (int ks = 0; ks < NSTAGE; ++ks)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) issue1(ks, i);
     wait_loads(NSTAGE - 1);
     barrier();
-    rd(0, 0, f0a, f0b);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) rd1(0, 0, i, f0a, f0b);
     __builtin_amdgcn_sched_barrier(0);
     // Epilogue operand prefetch (bf16 Poly / Update): the lane's 32 chunks of
     // A or X that pass A will combine with the product, loaded into registers,
@@ -483,28 +485,20 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ws, int first, int xt_cur) {
         }
     };
 
-    auto step = [&](int ks, bool with_prefetch) {
-        mm(f0a, f0b);
-        rd(ks, 1, f1a, f1b);
-        interleave();
-        __builtin_amdgcn_sched_barrier(0);
+    auto step = [&](int ks, bool refill, bool with_prefetch) __attribute__((always_inline)) {
+        substep(f0a, f0b, true, ks, 1, f1a, f1b, -1);
         const int issued_last = ks + NSTAGE - 1 < nk - 1 ? ks + NSTAGE - 1 : nk - 1;
         wait_loads(issued_last - (ks + 1));
         barrier();   // stage ks+1 visible everywhere; every read of stage ks done
-        if (ks + NSTAGE < nk) issue(ks + NSTAGE);   // refill the slot of stage ks
         if (with_prefetch) prefetch(0, 1);          // no stage load is in flight any more
         __builtin_amdgcn_sched_barrier(0);
-        mm(f1a, f1b);
-        rd(ks + 1, 0, f0a, f0b);
-        interleave();
-        __builtin_amdgcn_sched_barrier(0);
+        substep(f1a, f1b, true, ks + 1, 0, f0a, f0b, refill ? ks + NSTAGE : -1);
     };
-    for (int ks = 0; ks + 1 < nk; ++ks) step(ks, ks + 2 == nk);
-    mm(f0a, f0b);
-    rd(nk - 1, 1, f1a, f1b);
-    interleave();
-    __builtin_amdgcn_sched_barrier(0);
-    mm(f1a, f1b);
+    int ks = 0;
+    for (; ks + NSTAGE < nk; ++ks) step(ks, true, false);
+    for (; ks + 1 < nk; ++ks) step(ks, false, ks + 2 == nk);
+    substep(f0a, f0b, true, nk - 1, 1, f1a, f1b, -1);
+    substep(f1a, f1b, false, 0, 0, f0a, f0b, -1);
     __syncthreads();   // every wave is done with the operand stages
     prefetch(1, 4);    // the fragment registers are free now
 
