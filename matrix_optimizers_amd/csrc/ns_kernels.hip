@@ -236,10 +236,23 @@ template <> struct Mfma<float> {
 // different chunk).
 MO_DEV int swz(int row, int chunk) { return row * KB + ((chunk ^ ((row >> 2) & 3)) << 4); }
 
-// staging slice index: 128 fp32 columns per row, column bits 3..4 XOR row bits 3..4
-MO_DEV int st_idx(int row, int col) { return row * 128 + (col ^ (((row >> 3) & 3) << 3)); }
+// Staging slice of one wave (16 KB): the fp32 results of one 32-row block of
+// its 128 x 128 sub-tile, stored by column.  Value (column j, row i) sits in
+// the 256-byte line j / 2, in 16-byte group G (rows i & ~3 .. + 3 of the
+// column); G XORs the group's position in the line with bits of j so that
+// the three access patterns (16-byte accumulator writes of 16 consecutive
+// columns, 16-byte reads of 4 columns x 4 row groups, and 4-byte reads of 16
+// columns 8 apart x 4 rows) each hit distinct banks.
+MO_DEV int st_off(int j, int i) {
+    const int p = j >> 1;
+    const int g = ((j & 1) | ((i >> 2) << 1)) ^ (((p & 7) << 1) ^ ((p >> 3) & 7));
+    return p * 256 + g * 16 + (i & 3) * 4;
+}
 
-// Epilogue context of one workgroup tile.
+// Epilogue context of one workgroup tile.  The mirrored pass ("pass B": for
+// a sub-tile column j, 8 consecutive rows) runs first and forms the final
+// values; the tile pass ("pass A": for a sub-tile row, 8 consecutive columns)
+// writes them in the tile's own orientation.
 template <typename T, int KIND, bool LAST>
 struct Epi {
     const mo_wl_mat* mt;
@@ -248,52 +261,39 @@ struct Epi {
     int64_t m_pad, n_pad;
     bool trans;
 
-    // pass A: 8 values at tile-orientation position (gi, gj..gj+7).  `opnd`
-    // is the matching chunk of the epilogue operand (A for Poly, X for Update)
-    // when it was prefetched, else null and it is loaded here.
-    MO_DEV void pass_a(int64_t gi, int64_t gj, f32x8& v, float* slot, const f32x8* opnd) const {
+    // Final values from the product v and the epilogue operand o (A[i][j] for
+    // Poly, X[i][j] for Update; unused for Gram).
+    MO_DEV void combine(f32x8& v, const f32x8& o) const {
         if (KIND == KIND_GRAM) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) v.v[e] *= alpha;
-            store8(A + gi * m_pad + gj, v);
         } else if (KIND == KIND_POLY) {
-            f32x8 av;
-            if (opnd) av = *opnd; else load8(A + gi * m_pad + gj, av);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v.v[e] = quantize<T>(nc * v.v[e] + nb * av.v[e]);
-            store8(B + gi * m_pad + gj, v);
-            store8(slot, v);               // the mirrored write re-uses the rounded value
+            for (int e = 0; e < 8; ++e) v.v[e] = quantize<T>(nc * v.v[e] + nb * o.v[e]);
         } else {
-            f32x8 xv;
-            if (opnd) xv = *opnd; else load8(X + gi * n_pad + gj, xv);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v.v[e] = sx * (na * xv.v[e] + v.v[e]);
+            for (int e = 0; e < 8; ++e) v.v[e] = sx * (na * o.v[e] + v.v[e]);
             if (!LAST) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) v.v[e] = quantize<T>(v.v[e]);
-                store8(X + gi * n_pad + gj, v);
-                store8(slot, v);
-            } else if (!trans) {
-                write_w(gi, gj, v);       // weight frame == NS frame
-            } else {
-                store8(slot, v);
             }
         }
     }
 
-    // pass B: 8 values at mirrored position (oj, oi..oi+7)
-    MO_DEV void pass_b(int64_t oj, int64_t oi, f32x8& v) const {
-        if (KIND == KIND_GRAM) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v.v[e] *= alpha;
-            store8(A + oj * m_pad + oi, v);
-        } else if (KIND == KIND_POLY) {
-            store8(B + oj * m_pad + oi, v);    // B is symmetric: the staged values
-        } else if (!LAST) {
-            store8(Xt_nxt + oj * m_pad + oi, v);
-        } else {
-            write_w(oj, oi, v);            // weight frame is the transpose
-        }
+    // pass B output: 8 values at mirrored position (row oj, columns oi..oi+7)
+    MO_DEV void mirror(int64_t oj, int64_t oi, const f32x8& v) const {
+        if (KIND == KIND_GRAM) store8(A + oj * m_pad + oi, v);
+        else if (KIND == KIND_POLY) store8(B + oj * m_pad + oi, v);   // B is symmetric
+        else if (!LAST) store8(Xt_nxt + oj * m_pad + oi, v);
+        else write_w(oj, oi, v);                                       // weight frame is the transpose
+    }
+
+    // pass A output: 8 values at tile position (row gi, columns gj..gj+7)
+    MO_DEV void tile(int64_t gi, int64_t gj, const f32x8& v) const {
+        if (KIND == KIND_GRAM) store8(A + gi * m_pad + gj, v);
+        else if (KIND == KIND_POLY) store8(B + gi * m_pad + gj, v);
+        else if (!LAST) store8(X + gi * n_pad + gj, v);
+        else write_w(gi, gj, v);                                       // weight frame == NS frame
     }
 
     // W[r][c..c+7] <- decay * W - lr_eff * O, clipped to the matrix; 16-byte
@@ -368,7 +368,8 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ws, int first, int xt_cur) {
     const int64_t ldb = ld * int64_t(sizeof(T));             // row stride in bytes
     const int nk = int(ldb / KB);                              // K stages
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int wm = wave >> 1, wn = wave & 1;
     const int r32 = lane & 31, kg = lane >> 5;
 
@@ -462,45 +463,52 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ws, int first, int xt_cur) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) rd1(0, 0, i, f0a, f0b);
     __builtin_amdgcn_sched_barrier(0);
-    // Epilogue operand prefetch (bf16 Poly / Update): the lane's 32 chunks of
-    // A or X that pass A will combine with the product, loaded into registers,
-    // round 0 while the last K substeps run and rounds 1-3 as the epilogue
-    // starts.  Chunk (round r, task t) sits at sub-tile
-    // row 32 r + 4 t + lane/16, columns 8 (lane % 16) .. + 7.
-    constexpr bool PREF = sizeof(T) == 2 && KIND != KIND_GRAM;
+    // Epilogue operand capture (bf16 Poly / Update).  The Q operand holds the
+    // values the epilogue combines with the product: X[i][j] = X^T[j][i] for
+    // Update, A[i][j] = A[j][i] for Poly.  K stage 8 ti + 4 wm + r covers rows
+    // 32 r .. 32 r + 31 of this wave's sub-tile, so while that stage is in LDS
+    // each lane copies the 8 chunks its mirrored-pass tasks of round r need
+    // (task t: column j = lane / 4 + 16 t, rows 8 (lane % 4) .. + 7) into
+    // registers, and the epilogue reads nothing from global memory.
+    constexpr bool CAP = sizeof(T) == 2 && KIND != KIND_GRAM;
     const int64_t gi_w = int64_t(ti) * GT + wm * 128;   // this wave's sub-tile origin
     const int64_t gj_w = int64_t(tj) * GT + wn * 128;
-    u32x4 pre[PREF ? 4 : 1][8];
-    auto prefetch = [&](int r0, int r1) {   // rounds [r0, r1)
-        if constexpr (PREF) {
-            const T* src = KIND == KIND_UPDATE ? X : A;
-            const int64_t lds = KIND == KIND_UPDATE ? n_pad : m_pad;
-            const T* base = src + (gi_w + (lane >> 4)) * lds + gj_w + (lane & 15) * 8;
+    u32x4 pre[CAP ? 4 : 1][8];
+    const int cap0 = ti * (GT * int(sizeof(T)) / KB) + wm * 4;
+    auto capture = [&](int ks) __attribute__((always_inline)) {
+        if constexpr (CAP) {
+            const int r = ks - cap0;   // wave-uniform
+            if (r >= 0 && r < 4) {
+                // Register selects rather than pre[r][t] = ..., which would
+                // index the array dynamically and move it to scratch memory.
+                const uint8_t* sq = smem + (ks % NSTAGE) * STAGE_BYTES + OPND_BYTES;
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
+                for (int t = 0; t < 8; ++t) {
+                    const u32x4 c = *reinterpret_cast<const u32x4*>(
+                        sq + swz(wn * 128 + (lane >> 2) + 16 * t, lane & 3));
 #pragma unroll
-                for (int t = 0; t < 8; ++t)
-                    if (r >= r0 && r < r1)
-                        pre[r][t] = *reinterpret_cast<const u32x4*>(base + int64_t(32 * r + 4 * t) * lds);
+                    for (int rr = 0; rr < 4; ++rr) pre[rr][t] = r == rr ? c : pre[rr][t];
+                }
+            }
         }
     };
 
-    auto step = [&](int ks, bool refill, bool with_prefetch) __attribute__((always_inline)) {
+    auto step = [&](int ks, bool refill) __attribute__((always_inline)) {
         substep(f0a, f0b, true, ks, 1, f1a, f1b, -1);
+        capture(ks);   // stage ks is still resident until the barrier below
         const int issued_last = ks + NSTAGE - 1 < nk - 1 ? ks + NSTAGE - 1 : nk - 1;
         wait_loads(issued_last - (ks + 1));
         barrier();   // stage ks+1 visible everywhere; every read of stage ks done
-        if (with_prefetch) prefetch(0, 1);          // no stage load is in flight any more
         __builtin_amdgcn_sched_barrier(0);
         substep(f1a, f1b, true, ks + 1, 0, f0a, f0b, refill ? ks + NSTAGE : -1);
     };
     int ks = 0;
-    for (; ks + NSTAGE < nk; ++ks) step(ks, true, false);
-    for (; ks + 1 < nk; ++ks) step(ks, false, ks + 2 == nk);
+    for (; ks + NSTAGE < nk; ++ks) step(ks, true);
+    for (; ks + 1 < nk; ++ks) step(ks, false);
     substep(f0a, f0b, true, nk - 1, 1, f1a, f1b, -1);
+    capture(nk - 1);
     substep(f1a, f1b, false, 0, 0, f0a, f0b, -1);
     __syncthreads();   // every wave is done with the operand stages
-    prefetch(1, 4);    // the fragment registers are free now
 
     Epi<T, KIND, LAST> ep;
     ep.mt = &mt;
@@ -515,55 +523,82 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ws, int first, int xt_cur) {
         ep.vec_w = ((mt.W | uint64_t(mt.ld_w * wes)) & 15) == 0;
         ep.vec_u = ((mt.U | uint64_t(mt.ld_u * 4)) & 15) == 0;
     }
-    const bool need_b = KIND == KIND_UPDATE ? (!LAST || ep.trans) : (ti != tj);
+    // Which passes write where.  Gram and Poly write the mirror of an
+    // off-diagonal tile; Update writes X^T (or, last, W when the weight is the
+    // transposed frame).  The tile pass writes everything except the last
+    // Update of a transposed weight.  Gram scales in each pass; the other
+    // kinds form their values in the mirrored pass and hand them to the tile
+    // pass through the staging slice.
+    const bool off_diag = ti != tj;
+    const bool run_b = KIND == KIND_GRAM ? off_diag : true;
+    const bool write_b = KIND == KIND_UPDATE ? (!LAST || ep.trans) : off_diag;
+    const bool run_a = !(KIND == KIND_UPDATE && LAST && ep.trans);
+    const bool hand_over = KIND != KIND_GRAM && run_a;
 
-    float* st = reinterpret_cast<float*>(smem + wave * WAVE_ST_BYTES);
+    uint8_t* st = smem + wave * WAVE_ST_BYTES;
     // One 32-row block of the wave's sub-tile; called with literal indices so
-    // the accumulator and prefetch arrays are never indexed dynamically.
+    // the accumulator and capture arrays are never indexed dynamically.
     auto round = [&](const int a, const f32x16 (&ac)[4], const u32x4 (&pf)[8]) __attribute__((always_inline)) {
+        // accumulators: lane holds column 32 b + lane % 32, rows 8 g + 4 (lane / 32) .. + 3
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
-            for (int v = 0; v < 16; ++v)
-                st[st_idx((v >> 2) * 8 + kg * 4 + (v & 3), b * 32 + r32)] = ac[b][v];
-        __builtin_amdgcn_wave_barrier();
-        // pass A: 16 lanes per 128-column row, 4 rows per instruction
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const int q = lane + 64 * t;
-            const int cc = q & 15, row = q >> 4;
-            f32x8 v;
-            float* slot = st + st_idx(row, cc * 8);
-            load8(slot, v);
-            if constexpr (PREF) {
-                f32x8 o;
-                const bf16x8 raw = __builtin_bit_cast(bf16x8, pf[t]);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) o.v[e] = (float)raw[e];
-                ep.pass_a(gi_w + a * 32 + row, gj_w + cc * 8, v, slot, &o);
-            } else {
-                ep.pass_a(gi_w + a * 32 + row, gj_w + cc * 8, v, slot, nullptr);
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 v4 = {ac[b][4 * g], ac[b][4 * g + 1], ac[b][4 * g + 2], ac[b][4 * g + 3]};
+                *reinterpret_cast<f32x4*>(st + st_off(b * 32 + r32, g * 8 + kg * 4)) = v4;
             }
-        }
         __builtin_amdgcn_wave_barrier();
-        if (need_b) {
-            // pass B: output row j (a column of the sub-tile), 32 values in 4 chunks
-#pragma unroll 2
+        if (run_b) {
+            // mirrored pass: column j of the sub-tile, rows 8 ic .. 8 ic + 7
+#pragma unroll
             for (int t = 0; t < 8; ++t) {
-                const int q = lane + 64 * t;
-                const int ic = q & 3, j = q >> 2;
+                const int j = (lane >> 2) + 16 * t, ic = lane & 3;
+                f32x4* s0 = reinterpret_cast<f32x4*>(st + st_off(j, ic * 8));
+                f32x4* s1 = reinterpret_cast<f32x4*>(st + st_off(j, ic * 8 + 4));
+                const f32x4 lo = *s0, hi = *s1;
+                f32x8 v, o;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) { v.v[e] = lo[e]; v.v[4 + e] = hi[e]; }
+                const int64_t oj = gj_w + j, oi = gi_w + a * 32 + ic * 8;
+                if constexpr (CAP) {
+                    const bf16x8 raw = __builtin_bit_cast(bf16x8, pf[t]);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) o.v[e] = (float)raw[e];
+                } else if (KIND == KIND_POLY) {
+                    load8(A + oj * m_pad + oi, o);          // A[i][j] = A[j][i]
+                } else if (KIND == KIND_UPDATE) {
+                    load8(Xt_cur + oj * m_pad + oi, o);     // X[i][j] = X^T[j][i]
+                }
+                ep.combine(v, o);
+                if (write_b) ep.mirror(oj, oi, v);
+                if (hand_over) {
+                    *s0 = f32x4{v.v[0], v.v[1], v.v[2], v.v[3]};
+                    *s1 = f32x4{v.v[4], v.v[5], v.v[6], v.v[7]};
+                }
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+        if (run_a) {
+            // tile pass: row of the sub-tile, columns 8 cc .. 8 cc + 7 (16 lanes per row)
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int cc = lane & 15, row = (lane >> 4) + 4 * t;
                 f32x8 v;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v.v[e] = st[st_idx(ic * 8 + e, j)];
-                ep.pass_b(gj_w + j, gi_w + a * 32 + ic * 8, v);
+                for (int e = 0; e < 8; ++e) v.v[e] = *reinterpret_cast<const float*>(st + st_off(cc * 8 + e, row));
+                if (KIND == KIND_GRAM) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v.v[e] *= ep.alpha;
+                }
+                ep.tile(gi_w + a * 32 + row, gj_w + cc * 8, v);
             }
             __builtin_amdgcn_wave_barrier();
         }
     };
     round(0, acc[0], pre[0]);
-    round(1, acc[1], pre[PREF ? 1 : 0]);
-    round(2, acc[2], pre[PREF ? 2 : 0]);
-    round(3, acc[3], pre[PREF ? 3 : 0]);
+    round(1, acc[1], pre[CAP ? 1 : 0]);
+    round(2, acc[2], pre[CAP ? 2 : 0]);
+    round(3, acc[3], pre[CAP ? 3 : 0]);
 }
 
 inline unsigned grid_for(uint32_t items) { return items; }   // dispatch lists are padded to 8
