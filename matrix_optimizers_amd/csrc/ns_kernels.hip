@@ -202,10 +202,10 @@ __global__ __launch_bounds__(MOM_THREADS) void apply_kernel(uint8_t* ws) {
 constexpr int GT = MO_GEMM_TILE;           // 256
 constexpr int G_THREADS = 256;
 constexpr int KB = 64;                     // bytes of K per LDS stage and row
-constexpr int NSTAGE = 4;                  // LDS ring depth (NSTAGE-1 stages in flight)
+constexpr int NSTAGE = 5;                  // LDS ring depth
 constexpr int OPND_BYTES = GT * KB;        // 16 KB per operand per stage
 constexpr int STAGE_BYTES = 2 * OPND_BYTES;
-constexpr int GEMM_LDS = NSTAGE * STAGE_BYTES;  // 128 KB
+constexpr int GEMM_LDS = NSTAGE * STAGE_BYTES;  // 160 KB, all of the CU's LDS
 constexpr int WAVE_ST_BYTES = 32 * 128 * 4;  // per-wave staging slice
 
 enum { KIND_GRAM = 0, KIND_POLY = 1, KIND_UPDATE = 2 };
@@ -375,22 +375,20 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ws, int first, int xt_cur) {
 
     // direct-to-LDS loads: wave w fills rows [64 w, 64 w + 64) of both operands,
     // 16 rows (1 KB) per instruction; lane l -> row + l/4, physical chunk l%4.
+    // The rows of one instruction start at a wave-uniform address (SGPRs); the
+    // lane's part, the same for every instruction since the swizzle depends on
+    // the row modulo 16 only, is one 32-bit offset (16 rows of at most 32 MB).
     const uint8_t* Pb = reinterpret_cast<const uint8_t*>(P);
     const uint8_t* Qb = reinterpret_cast<const uint8_t*>(Q);
     const int lrow = lane >> 2, pch = lane & 3;
-    int64_t goff[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = wave * 64 + i * 16 + lrow;
-        goff[i] = int64_t(row) * ldb + ((pch ^ ((row >> 2) & 3)) << 4);
-    }
+    const uint32_t voff = uint32_t(lrow) * uint32_t(ldb) + uint32_t((pch ^ ((lrow >> 2) & 3)) << 4);
     // Load instruction i (0..7) of stage ks: rows 64 wave + 16 (i / 2) + lane/4
     // of operand P (i even) or Q (i odd).
     auto issue1 = [&](int ks, int i) __attribute__((always_inline)) {
         uint8_t* sp = smem + (ks % NSTAGE) * STAGE_BYTES + (i & 1) * OPND_BYTES + wave * 64 * KB +
                       (i >> 1) * 16 * KB;
-        const uint8_t* g = ((i & 1) ? Qb : Pb) + goff[i >> 1] + int64_t(ks) * KB;
-        __builtin_amdgcn_global_load_lds(g, (lds_void_t*)sp, 16, 0, 0);
+        const uint8_t* g = ((i & 1) ? Qb : Pb) + int64_t(wave * 64 + (i >> 1) * 16) * ldb + int64_t(ks) * KB;
+        __builtin_amdgcn_global_load_lds(g + voff, (lds_void_t*)sp, 16, 0, 0);
     };
 
     f32x16 acc[4][4];
@@ -411,12 +409,12 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ws, int first, int xt_cur) {
     // Workgroup barrier without the release fence of __syncthreads(), which
     // would also drain the direct-to-LDS loads still in flight for later
     // stages.  Each thread first waits for its own loads of the stage being
-    // published (explicit vmcnt) and for its LDS reads (lgkmcnt).
-    auto wait_loads = [&](int later) {   // later = stages issued after the one awaited
-        if (later >= 4) asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
-        else if (later == 3) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
-        else if (later == 2) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-        else if (later == 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    // published (explicit vmcnt: the number of its load instructions issued
+    // after that stage's last one) and for its LDS reads (lgkmcnt).
+    auto wait_loads = [&](int after) {
+        if (after == 17) asm volatile("s_waitcnt vmcnt(17)" ::: "memory");
+        else if (after == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        else if (after == 1) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
         else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     };
     // lgkmcnt(0) through the builtin (gfx9 encoding: vmcnt and expcnt at their
@@ -430,35 +428,43 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ws, int first, int xt_cur) {
 
     // The 16 MFMAs of one substep on (fa, fb).  After each of the first 8
     // comes one fragment read of the next substep (stage rks, substep rsub,
-    // into na / nb) and, when iks >= 0, one load instruction of stage iks; the
-    // order is fixed (sched_barrier), so reads and loads stream out between
-    // the MFMAs instead of in bursts the matrix core would wait behind.
+    // into na / nb); when ia >= 0, MFMA i is also followed by load instruction
+    // i / 2 of stage ia (i even) or ia + 1 (i odd).  The order is fixed
+    // (sched_barrier), so reads and loads stream out between the MFMAs instead
+    // of in bursts the matrix core would wait behind.
     auto substep = [&](const u32x4 (&fa)[4], const u32x4 (&fb)[4], bool do_read, int rks, int rsub,
-                       u32x4 (&na)[4], u32x4 (&nb)[4], int iks) __attribute__((always_inline)) {
+                       u32x4 (&na)[4], u32x4 (&nb)[4], int ia) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             Mfma<T>::run(fa[i >> 2], fb[i & 3], acc[i >> 2][i & 3]);
             __builtin_amdgcn_sched_barrier(0);
-            if (i < 8) {
-                if (do_read) rd1(rks, rsub, i, na, nb);
-                if (iks >= 0) issue1(iks, i);
-            }
+            if (i < 8 && do_read) rd1(rks, rsub, i, na, nb);
+            if (ia >= 0) issue1(ia + (i & 1), i >> 1);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
 
-    // Software pipeline over K (nk >= 8: every padded dimension is >= 256).
-    // Stage s occupies ring slot s % NSTAGE.  Entering iteration ks, F0 holds
-    // the fragments of (ks, substep 0).  The barrier sits between the two
-    // substeps, so the MFMAs after it use fragments already in registers while
-    // the reads for the next stage land.  Stage ks + NSTAGE refills the slot of
-    // stage ks once the barrier has shown every wave done with it.
+    // Software pipeline over K (nk >= 8 and even: every padded dimension is a
+    // multiple of 256).  Stage s occupies ring slot s % NSTAGE.  Entering step
+    // ks, F0 holds the fragments of (ks, substep 0).  The barrier sits between
+    // the two substeps, so the MFMAs after it use fragments already in
+    // registers while the reads for the next stage land.
+    //
+    // Stages are loaded in pairs (2p, 2p + 1), whose 64-byte row pieces are
+    // the two halves of the same 128-byte lines, with the two stages'
+    // instructions alternating so both halves of a line are requested back to
+    // back.  The pair (ks + 4, ks + 5) goes out after the barrier of even step
+    // ks, into the slots of stages ks - 1 and ks, which every wave has then
+    // finished reading.  At the barrier of step ks, stage ks + 1 must have
+    // landed: for even ks it is the second of its pair and the 16 loads of the
+    // next pair came after it; for odd ks it is the first of its pair and one
+    // more load of its partner also follows.
     u32x4 f0a[4], f0b[4], f1a[4], f1b[4];
 #pragma unroll
-    for (int ks = 0; ks < NSTAGE; ++ks)
+    for (int p = 0; p < 4; p += 2)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) issue1(ks, i);
-    wait_loads(NSTAGE - 1);
+        for (int i = 0; i < 16; ++i) issue1(p + (i & 1), i >> 1);
+    wait_loads(17);
     barrier();
 #pragma unroll
     for (int i = 0; i < 8; ++i) rd1(0, 0, i, f0a, f0b);
@@ -493,18 +499,21 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ws, int first, int xt_cur) {
         }
     };
 
-    auto step = [&](int ks, bool refill) __attribute__((always_inline)) {
+    auto step = [&](int ks, int after, int pair) __attribute__((always_inline)) {
         substep(f0a, f0b, true, ks, 1, f1a, f1b, -1);
         capture(ks);   // stage ks is still resident until the barrier below
-        const int issued_last = ks + NSTAGE - 1 < nk - 1 ? ks + NSTAGE - 1 : nk - 1;
-        wait_loads(issued_last - (ks + 1));
-        barrier();   // stage ks+1 visible everywhere; every read of stage ks done
+        wait_loads(after);
+        barrier();     // stage ks+1 visible everywhere; every read of stage ks done
         __builtin_amdgcn_sched_barrier(0);
-        substep(f1a, f1b, true, ks + 1, 0, f0a, f0b, refill ? ks + NSTAGE : -1);
+        substep(f1a, f1b, true, ks + 1, 0, f0a, f0b, pair);
     };
     int ks = 0;
-    for (; ks + NSTAGE < nk; ++ks) step(ks, true);
-    for (; ks + 1 < nk; ++ks) step(ks, false);
+    for (; ks + 6 <= nk; ks += 2) {
+        step(ks, 16, ks + 4);
+        step(ks + 1, 17, -1);
+    }
+    // ks == nk - 4: the last pair (nk - 2, nk - 1) is in flight
+    for (; ks + 1 < nk; ++ks) step(ks, ks + 4 == nk ? 16 : ks + 3 == nk ? 1 : 0, -1);
     substep(f0a, f0b, true, nk - 1, 1, f1a, f1b, -1);
     capture(nk - 1);
     substep(f1a, f1b, false, 0, 0, f0a, f0b, -1);
