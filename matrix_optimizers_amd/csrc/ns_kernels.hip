@@ -414,6 +414,7 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ws, int first, int xt_cur) {
     auto wait_loads = [&](int after) {
         if (after == 17) asm volatile("s_waitcnt vmcnt(17)" ::: "memory");
         else if (after == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        else if (after == 9) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
         else if (after == 1) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
         else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     };
@@ -428,18 +429,23 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ws, int first, int xt_cur) {
 
     // The 16 MFMAs of one substep on (fa, fb).  After each of the first 8
     // comes one fragment read of the next substep (stage rks, substep rsub,
-    // into na / nb); when ia >= 0, MFMA i is also followed by load instruction
-    // i / 2 of stage ia (i even) or ia + 1 (i odd).  The order is fixed
-    // (sched_barrier), so reads and loads stream out between the MFMAs instead
-    // of in bursts the matrix core would wait behind.
+    // into na / nb).  When ia >= 0, every fourth MFMA is also followed by one
+    // load of the pair (ia, ia + 1): quarter q, loads 4 q .. 4 q + 3 of its 16,
+    // load L being instruction L / 2 of stage ia + (L & 1).  The order is fixed
+    // (sched_barrier), so reads and loads stream out evenly between the MFMAs
+    // instead of in bursts that would stall instruction issue behind a full
+    // load queue.
     auto substep = [&](const u32x4 (&fa)[4], const u32x4 (&fb)[4], bool do_read, int rks, int rsub,
-                       u32x4 (&na)[4], u32x4 (&nb)[4], int ia) __attribute__((always_inline)) {
+                       u32x4 (&na)[4], u32x4 (&nb)[4], int ia, int q) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             Mfma<T>::run(fa[i >> 2], fb[i & 3], acc[i >> 2][i & 3]);
             __builtin_amdgcn_sched_barrier(0);
             if (i < 8 && do_read) rd1(rks, rsub, i, na, nb);
-            if (ia >= 0) issue1(ia + (i & 1), i >> 1);
+            if (ia >= 0 && (i & 3) == 3) {
+                const int L = q * 4 + (i >> 2);
+                issue1(ia + (L & 1), L >> 1);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -453,12 +459,14 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ws, int first, int xt_cur) {
     // Stages are loaded in pairs (2p, 2p + 1), whose 64-byte row pieces are
     // the two halves of the same 128-byte lines, with the two stages'
     // instructions alternating so both halves of a line are requested back to
-    // back.  The pair (ks + 4, ks + 5) goes out after the barrier of even step
-    // ks, into the slots of stages ks - 1 and ks, which every wave has then
-    // finished reading.  At the barrier of step ks, stage ks + 1 must have
-    // landed: for even ks it is the second of its pair and the 16 loads of the
-    // next pair came after it; for odd ks it is the first of its pair and one
-    // more load of its partner also follows.
+    // back.  The pair (ks + 4, ks + 5) goes into the slots of stages ks - 1 and
+    // ks, which every wave has finished reading once the barrier of even step
+    // ks has passed; its 16 loads are spread in quarters over the four
+    // substeps that follow (second of step ks, both of ks + 1, first of
+    // ks + 2).  At the barrier of step ks, stage ks + 1 must have landed: for
+    // even ks it is the second of its pair and all 16 loads of the next pair
+    // came after it; for odd ks it is the first of its pair, followed by one
+    // load of its partner and the first half of the next pair.
     u32x4 f0a[4], f0b[4], f1a[4], f1b[4];
 #pragma unroll
     for (int p = 0; p < 4; p += 2)
@@ -499,24 +507,31 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ws, int first, int xt_cur) {
         }
     };
 
-    auto step = [&](int ks, int after, int pair) __attribute__((always_inline)) {
-        substep(f0a, f0b, true, ks, 1, f1a, f1b, -1);
+    // (pa, qa): pair and quarter of loads issued in this step's first
+    // substep; (pb, qb) in its second (pair -1: none).
+    auto step = [&](int ks, int after, int pa, int qa, int pb, int qb) __attribute__((always_inline)) {
+        substep(f0a, f0b, true, ks, 1, f1a, f1b, pa, qa);
         capture(ks);   // stage ks is still resident until the barrier below
         wait_loads(after);
         barrier();     // stage ks+1 visible everywhere; every read of stage ks done
         __builtin_amdgcn_sched_barrier(0);
-        substep(f1a, f1b, true, ks + 1, 0, f0a, f0b, pair);
+        substep(f1a, f1b, true, ks + 1, 0, f0a, f0b, pb, qb);
     };
-    int ks = 0;
+    // the prologue issued pairs (0, 1) and (2, 3) whole
+    step(0, 16, -1, 0, 4, 0);
+    step(1, 9, 4, 1, 4, 2);
+    int ks = 2;
     for (; ks + 6 <= nk; ks += 2) {
-        step(ks, 16, ks + 4);
-        step(ks + 1, 17, -1);
+        step(ks, 16, ks + 2, 3, ks + 4, 0);
+        step(ks + 1, 9, ks + 4, 1, ks + 4, 2);
     }
-    // ks == nk - 4: the last pair (nk - 2, nk - 1) is in flight
-    for (; ks + 1 < nk; ++ks) step(ks, ks + 4 == nk ? 16 : ks + 3 == nk ? 1 : 0, -1);
-    substep(f0a, f0b, true, nk - 1, 1, f1a, f1b, -1);
+    // ks == nk - 4: the last pair (nk - 2, nk - 1) lacks its last quarter
+    step(ks, 16, ks + 2, 3, -1, 0);
+    step(ks + 1, 1, -1, 0, -1, 0);
+    step(ks + 2, 0, -1, 0, -1, 0);
+    substep(f0a, f0b, true, nk - 1, 1, f1a, f1b, -1, 0);
     capture(nk - 1);
-    substep(f1a, f1b, false, 0, 0, f0a, f0b, -1);
+    substep(f1a, f1b, false, 0, 0, f0a, f0b, -1, 0);
     __syncthreads();   // every wave is done with the operand stages
 
     Epi<T, KIND, LAST> ep;
