@@ -41,7 +41,44 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the step, time the library's plain copy kernel over "
                          "MIB mebibytes (HBM ceiling; byte-counter calibration)")
+    ap.add_argument("--adamw-sweep", action="store_true",
+                    help="instead of the step, time adamw_tail_step over n = 2^24 .. 2^28 "
+                         "fp32 elements (28 bytes moved per element) and print one JSON line per n")
     return ap.parse_args()
+
+
+def adamw_sweep(args):
+    """HBM throughput of the AdamW tail kernel at sizes where it is bandwidth-bound
+    (the workloads' own tails are a few thousand elements and launch-bound)."""
+    import torch
+    import matrix_optimizers_amd as mo
+    from matrix_optimizers_amd import workloads as wlmod
+    a = wlmod.AdamWHP()
+    for e in range(24, 29):
+        n = 1 << e
+        gen = torch.Generator(device="cuda").manual_seed(e)
+        p = torch.randn(n, device="cuda", generator=gen) * 0.02
+        g = torch.randn(n, device="cuda", generator=gen) * 1e-3
+        m = torch.randn(n, device="cuda", generator=gen) * 1e-3
+        v = (torch.randn(n, device="cuda", generator=gen) * 1e-3) ** 2
+        for w in range(max(args.warmup, 1)):
+            mo.adamw_tail_step(p, g, m, v, w + 1, lr=a.lr, beta1=a.beta1, beta2=a.beta2, eps=a.eps,
+                               weight_decay=a.weight_decay)
+        torch.cuda.synchronize()
+        mo.profile_read()
+        mo.profile_enable(True)
+        for k in range(args.steps):
+            mo.adamw_tail_step(p, g, m, v, k + 10, lr=a.lr, beta1=a.beta1, beta2=a.beta2, eps=a.eps,
+                               weight_decay=a.weight_decay)
+        torch.cuda.synchronize()
+        mo.profile_enable(False)
+        tot, cnt = mo.profile_read()["adamw"]
+        per = tot / cnt
+        gbs = 28.0 * n / (per * 1e-3) / 1e9
+        print(json.dumps({"metric": "AdamW tail HBM throughput", "n": n, "bytes_per_launch": 28 * n,
+                          "avg_ms": round(per, 5), "GBps": round(gbs, 1),
+                          "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}), flush=True)
+        del p, g, m, v
 
 
 def copy_calibration(args):
@@ -127,6 +164,8 @@ def main():
 
     if args.copy_calibration:
         return copy_calibration(args)
+    if args.adamw_sweep:
+        return adamw_sweep(args)
     wl = wlmod.get(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

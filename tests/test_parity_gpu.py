@@ -161,7 +161,9 @@ def check_tail(device, seed, n, a: wlmod.AdamWHP):
     assert max(errs) <= 1e-6, errs
 
 
-@pytest.mark.parametrize("n", [0, 1, 3, 4, 1023, 4096, 32768, 1 << 20])
+# 517 and 2051: a last partial group of 16-byte accesses plus ragged elements;
+# 2^25 + 4099: more elements than one grid-stride pass covers at the grid cap.
+@pytest.mark.parametrize("n", [0, 1, 3, 4, 517, 1023, 2051, 4096, 32768, 1 << 20, (1 << 25) + 4099])
 def test_adamw_tail(gpu, n):
     check_tail(gpu, 40 + n % 7, n, wlmod.AdamWHP())
 
@@ -188,3 +190,17 @@ def test_adamw_misaligned_views(gpu):
     po, _, _ = oadamw.adamw_step(t.p, t.g, t.m, t.v, a.step, f(a.lr), f(a.beta1), f(a.beta2),
                                  f(a.eps), f(a.weight_decay))
     assert rel(to_host(views[0]), po) <= 1e-6
+
+
+@pytest.mark.parametrize("nbytes", [16, 48, 4096 + 16, 3 * 4096 * 16 + 1008, (64 << 20) + 4080])
+def test_device_copy(gpu, nbytes):
+    """The copy that calibrates the byte counters copies every byte, including
+    a last partial group of 16-byte accesses."""
+    import torch
+    import matrix_optimizers_amd as mo
+    gen = torch.Generator(device=gpu).manual_seed(nbytes % 1000)
+    src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device=gpu, generator=gen)
+    dst = torch.zeros_like(src)
+    mo.device_copy(dst, src)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, src)
