@@ -178,10 +178,10 @@ __global__ __launch_bounds__(MOM_THREADS) void apply_kernel(uint8_t* ws) {
 // wavefront owns a 128 x 128 sub-tile = 4 x 4 MFMA blocks of 32 x 32 (256 fp32
 // accumulators per lane, held in AGPRs).  Per K stage every operand row
 // contributes 64 bytes (32 bf16 / 16 fp32): 2 x 256 rows x 64 B = 32 KB, in a
-// ring of four stages in LDS (128 KB of the CU's 160 KB, one workgroup per CU).
-// Global data goes straight to LDS (global_load_lds_dwordx4, no VGPR round
-// trip); stage s+4 is issued right after the barrier that publishes stage s+1,
-// into the slot stage s vacated, so up to three stages are in flight.
+// ring of five stages in LDS (all 160 KB of the CU's LDS, one workgroup per
+// CU).  Global data goes straight to LDS (global_load_lds_dwordx4, no VGPR
+// round trip), two stages at a time, spread between the MFMAs (see the main
+// loop below).
 //
 // A direct-to-LDS load writes lane l's 16 bytes at (wave base + 16 l), so each
 // lane fetches the global chunk that belongs at its physical (swizzled) slot.
@@ -194,10 +194,10 @@ __global__ __launch_bounds__(MOM_THREADS) void apply_kernel(uint8_t* ws) {
 // result sits in lane l, register v at row (v/4)*8 + (l/32)*4 + v%4, col l%32.
 //
 // Epilogue, per wavefront and per 32-row block of its sub-tile: the fp32
-// values are staged in a private 16 KB LDS slice (column index XOR-swizzled by
-// row group), then written out as 16-byte chunks in the tile's own orientation
-// (pass A: 16 lanes cover one 128-column row) and, where the transposed
-// product is needed, in the mirrored orientation (pass B).
+// values are staged by column in a private 16 KB LDS slice, then written out
+// as 16-byte chunks in the mirrored orientation (pass B, where the transposed
+// product is needed; it also forms the final values) and in the tile's own
+// orientation (pass A: 16 lanes cover one 128-column row).
 
 constexpr int GT = MO_GEMM_TILE;           // 256
 constexpr int G_THREADS = 256;
