@@ -102,13 +102,15 @@ mo_status muon_workspace_bytes(const mo_matrix* mats, int32_t n_mats,
 /* The host work list that muon_owner_step uploads, for inspection and tests.
  * If host_buf is NULL, *bytes_inout receives the size; otherwise *bytes_inout
  * must hold at least that size and the list is written to host_buf.  The byte
- * layout (little-endian, natural alignment, version 4):
+ * layout (little-endian, natural alignment, version 5):
  *   header   mo_wl_header (128 bytes)
  *   matrices mo_wl_mat[n_live] (192 bytes each), one per non-empty descriptor,
  *            in descriptor order
- *   items    three dispatch lists of mo_wl_item (8 bytes: record index, tile
- *            row, tile column): Gram, Poly, Update, each starting on a
- *            256-byte boundary; entry b is the 256 x 256 tile run by workgroup b
+ *   items    three dispatch lists of mo_wl_item (16 bytes: record index, tile
+ *            row ti, tile column tj, width nb in {4, 2, 1}; the tile covers
+ *            rows 256 ti .. +256 and columns 64 nb tj .. +64 nb): Gram, Poly,
+ *            Update, each starting on a 256-byte boundary; entry b is the tile
+ *            run by workgroup b
  * Gram and Poly cover the upper-triangle tiles (ti <= tj) of the m_pad x m_pad
  * product, Update all tiles of the m_pad x n_pad product.  Matrices are taken
  * in descending order of their per-phase work (ties by descriptor index) and
@@ -117,8 +119,13 @@ mo_status muon_workspace_bytes(const mo_matrix* mats, int32_t n_mats,
  * XCD) with the least K-length x tiles so far, ties to the lowest; if that
  * queue is below an even share ceil(total / 8) it takes only the tiles that
  * reach the share (at least one) and the rest goes on to the next queue.
- * Entry 8 j + x of a list is the j-th tile of queue x, or a pad entry (record
- * index 0xFFFFFFFF) where queue x is shorter. */
+ * Then, where full tiles would leave CUs idle, tiles are split by columns: a
+ * queue of n <= 32 tiles (32 CUs per XCD) has every tile split, a longer one
+ * the n % 32 tiles of its last round, into S = 4 quarter-width (nb = 1) or
+ * S = 2 half-width (nb = 2) tiles, the largest S with S x (tiles split) <= 32;
+ * the parts take the tile's place in the queue, in column order.  Entry 8 j + x
+ * of a list is the j-th tile of queue x, or a pad entry (record index
+ * 0xFFFFFFFF) where queue x is shorter. */
 mo_status muon_build_worklist(const mo_matrix* mats, int32_t n_mats,
                               const mo_muon_hparams* hp, void* host_buf,
                               size_t* bytes_inout);

@@ -183,7 +183,7 @@ void build_plan(const mo_matrix* mats, int32_t n, const mo_muon_hparams* hp, Pla
     // would pass an even share of the total, and the list interleaves the 8
     // queues: entry 8 j + x is the j-th tile of XCD x, or a pad entry (matrix
     // index MO_WL_PAD) where that queue is shorter.
-    constexpr uint32_t SB_R = 4, SB_C = 8, NXCD = 8;
+    constexpr uint32_t SB_R = 4, SB_C = 8, NXCD = 8, CU_PER_XCD = 32;
     auto dispatch = [&](std::vector<mo_wl_item>& out, const std::vector<Key>& mats_order,
                         bool upper_only, bool k_is_n) {
         struct Blk { std::vector<mo_wl_item> tiles; uint64_t klen; };
@@ -198,7 +198,7 @@ void build_plan(const mo_matrix* mats, int32_t n, const mo_muon_hparams* hp, Pla
                     Blk b{{}, klen};
                     for (uint32_t a = bi; a < std::min(bi + SB_R, tm); ++a)
                         for (uint32_t c = bj; c < std::min(bj + SB_C, tn); ++c)
-                            if (!upper_only || a <= c) b.tiles.push_back({k.idx, uint16_t(a), uint16_t(c)});
+                            if (!upper_only || a <= c) b.tiles.push_back({k.idx, a, c, 4u});
                     if (b.tiles.empty()) continue;
                     total += klen * b.tiles.size();
                     blocks.push_back(std::move(b));
@@ -227,11 +227,29 @@ void build_plan(const mo_matrix* mats, int32_t n, const mo_muon_hparams* hp, Pla
                 i += take;
             }
         }
+        // Narrow tiles where full ones would leave an XCD's CUs idle: a queue of
+        // n <= 32 tiles (one partial round) has every tile split, and a longer
+        // queue the n % 32 tiles of its last round, into S = 4 quarter-width
+        // or S = 2 half-width tiles, the largest S that still fits the 32 CUs
+        // (none if even halves do not).  Split tiles keep their place in the
+        // queue, the S parts in column order.
+        for (auto& v : q) {
+            const size_t n = v.size();
+            if (n == 0) continue;
+            const size_t first = n <= CU_PER_XCD ? 0 : n - n % CU_PER_XCD;
+            const size_t r = n - first;
+            const uint32_t S = r == 0 ? 1 : 4 * r <= CU_PER_XCD ? 4 : 2 * r <= CU_PER_XCD ? 2 : 1;
+            if (S == 1) continue;
+            std::vector<mo_wl_item> w(v.begin(), v.begin() + first);
+            for (size_t k = first; k < n; ++k)
+                for (uint32_t p = 0; p < S; ++p) w.push_back({v[k].mat, v[k].ti, v[k].tj * S + p, 4 / S});
+            v.swap(w);
+        }
         size_t len = 0;
         for (const auto& v : q) len = std::max(len, v.size());
         for (size_t j = 0; j < len; ++j)
             for (uint32_t x = 0; x < NXCD; ++x)
-                out.push_back(j < q[x].size() ? q[x][j] : mo_wl_item{MO_WL_PAD, 0, 0});
+                out.push_back(j < q[x].size() ? q[x][j] : mo_wl_item{MO_WL_PAD, 0, 0, 0});
     };
     std::vector<mo_wl_item> gram, poly, upd;
     dispatch(gram, order([&](const mo_wl_mat& r) { return upper(r) * r.n_pad; }), true, true);

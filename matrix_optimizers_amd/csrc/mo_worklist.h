@@ -11,7 +11,7 @@
 #include <stdint.h>
 
 #define MO_WL_MAGIC   0x4C574F4Du  // "MOWL"
-#define MO_WL_VERSION 4u
+#define MO_WL_VERSION 5u
 
 // matrix index of a padding entry in a dispatch list
 #define MO_WL_PAD 0xFFFFFFFFu
@@ -60,14 +60,18 @@ struct mo_wl_mat {
     uint32_t reserved[5];
 };
 
+// One GEMM tile: rows [256 ti, 256 ti + 256) and columns [64 nb tj, 64 nb tj +
+// 64 nb) of the phase's product; nb = 4 is the full 256 x 256 tile, 2 and 1 the
+// half and quarter widths.
 struct mo_wl_item {
     uint32_t mat;
-    uint16_t ti, tj;
+    uint32_t ti, tj;
+    uint32_t nb;
 };
 
 static_assert(sizeof(mo_wl_header) == 128, "header layout");
 static_assert(sizeof(mo_wl_mat) == 192, "matrix record layout");
-static_assert(sizeof(mo_wl_item) == 8, "item layout");
+static_assert(sizeof(mo_wl_item) == 16, "item layout");
 static_assert(offsetof(mo_wl_header, mats_offset) == 56, "header layout");
 static_assert(offsetof(mo_wl_header, ns_a) == 104, "header layout");
 static_assert(offsetof(mo_wl_mat, off_X) == 64, "matrix record layout");

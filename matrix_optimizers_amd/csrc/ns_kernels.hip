@@ -204,9 +204,7 @@ constexpr int G_THREADS = 256;
 constexpr int KB = 64;                     // bytes of K per LDS stage and row
 constexpr int NSTAGE = 5;                  // LDS ring depth
 constexpr int OPND_BYTES = GT * KB;        // 16 KB per operand per stage
-constexpr int STAGE_BYTES = 2 * OPND_BYTES;
-constexpr int GEMM_LDS = NSTAGE * STAGE_BYTES;  // 160 KB, all of the CU's LDS
-constexpr int WAVE_ST_BYTES = 32 * 128 * 4;  // per-wave staging slice
+constexpr int GEMM_LDS = NSTAGE * 2 * OPND_BYTES;  // 160 KB at full width, all of the CU's LDS
 
 enum { KIND_GRAM = 0, KIND_POLY = 1, KIND_UPDATE = 2 };
 
@@ -335,17 +333,23 @@ struct Epi {
     }
 };
 
-template <typename T, int KIND, bool LAST>
-__device__ __forceinline__ void gemm_tile(uint8_t* ws, int first, int xt_cur) {
-    __shared__ __align__(16) uint8_t smem[GEMM_LDS];
+// One 256 x TN tile, TN = 64 NB (NB = 4: the full 256 x 256 tile; 2 and 1:
+// the half and quarter widths the host uses where full tiles would leave CUs
+// idle).  Each wavefront owns 128 x (TN / 2) = 4 x NB blocks of 32 x 32.  A
+// narrower tile accumulates every output element over the same K in the same
+// order, so its results are bit-identical to the full tile's.
+template <typename T, int KIND, bool LAST, int NB>
+__device__ __forceinline__ void gemm_tile(uint8_t* smem, uint8_t* ws, const mo_wl_item& it, int first,
+                                          int xt_cur) {
+    constexpr int TN = 64 * NB;                  // tile columns = rows of Q
+    constexpr int SBYTES = OPND_BYTES + TN * KB; // one stage: P (256 rows) then Q (TN rows)
+    constexpr int LS = 4 + NB;                   // load instructions per stage and wave
+    constexpr int LP = 2 * LS;                   // ... per pair of stages
+    constexpr int MF = 4 * NB;                   // MFMA blocks per wave and substep
+    constexpr int NR = 4 + NB;                   // fragment reads per substep
     const mo_wl_header* h = wl_header(ws);
-    const uint64_t items_off = KIND == KIND_GRAM ? h->gram_offset
-                             : KIND == KIND_POLY ? h->poly_offset : h->upd_offset;
-    // The grid is exactly the dispatch list; entry b is this workgroup's tile.
-    const mo_wl_item it = reinterpret_cast<const mo_wl_item*>(ws + items_off)[blockIdx.x];
-    if (it.mat == MO_WL_PAD) return;
     const mo_wl_mat& mt = wl_mats(ws)[it.mat];
-    const int ti = it.ti, tj = it.tj;
+    const int ti = int(it.ti), tj = int(it.tj);
     const int64_t m_pad = mt.m_pad, n_pad = mt.n_pad;
 
     T* X = reinterpret_cast<T*>(ws + mt.off_X);
@@ -359,11 +363,11 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ws, int first, int xt_cur) {
     const T* Q;
     int64_t ld;
     if (KIND == KIND_GRAM) {
-        ld = n_pad; P = X + int64_t(ti) * GT * ld; Q = X + int64_t(tj) * GT * ld;
+        ld = n_pad; P = X + int64_t(ti) * GT * ld; Q = X + int64_t(tj) * TN * ld;
     } else if (KIND == KIND_POLY) {
-        ld = m_pad; P = A + int64_t(ti) * GT * ld; Q = A + int64_t(tj) * GT * ld;
+        ld = m_pad; P = A + int64_t(ti) * GT * ld; Q = A + int64_t(tj) * TN * ld;
     } else {
-        ld = m_pad; P = B + int64_t(ti) * GT * ld; Q = Xt_cur + int64_t(tj) * GT * ld;
+        ld = m_pad; P = B + int64_t(ti) * GT * ld; Q = Xt_cur + int64_t(tj) * TN * ld;
     }
     const int64_t ldb = ld * int64_t(sizeof(T));             // row stride in bytes
     const int nk = int(ldb / KB);                              // K stages
@@ -373,38 +377,45 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ws, int first, int xt_cur) {
     const int wm = wave >> 1, wn = wave & 1;
     const int r32 = lane & 31, kg = lane >> 5;
 
-    // direct-to-LDS loads: wave w fills rows [64 w, 64 w + 64) of both operands,
-    // 16 rows (1 KB) per instruction; lane l -> row + l/4, physical chunk l%4.
-    // The rows of one instruction start at a wave-uniform address (SGPRs); the
-    // lane's part, the same for every instruction since the swizzle depends on
-    // the row modulo 16 only, is one 32-bit offset (16 rows of at most 32 MB).
+    // direct-to-LDS loads: wave w fills rows [64 w, 64 w + 64) of P and rows
+    // [TN/4 w, TN/4 (w + 1)) of Q, 16 rows (1 KB) per instruction; lane l ->
+    // row + l/4, physical chunk l%4.  The rows of one instruction start at a
+    // wave-uniform address (SGPRs); the lane's part, the same for every
+    // instruction since the swizzle depends on the row modulo 16 only, is one
+    // 32-bit offset (16 rows of at most 32 MB).
     const uint8_t* Pb = reinterpret_cast<const uint8_t*>(P);
     const uint8_t* Qb = reinterpret_cast<const uint8_t*>(Q);
     const int lrow = lane >> 2, pch = lane & 3;
     const uint32_t voff = uint32_t(lrow) * uint32_t(ldb) + uint32_t((pch ^ ((lrow >> 2) & 3)) << 4);
-    // Load instruction i (0..7) of stage ks: rows 64 wave + 16 (i / 2) + lane/4
-    // of operand P (i even) or Q (i odd).
+    // Load instruction i (0 .. LS-1) of stage ks: P rows 64 wave + 16 i (i < 4),
+    // else Q rows TN/4 wave + 16 (i - 4).
     auto issue1 = [&](int ks, int i) __attribute__((always_inline)) {
-        uint8_t* sp = smem + (ks % NSTAGE) * STAGE_BYTES + (i & 1) * OPND_BYTES + wave * 64 * KB +
-                      (i >> 1) * 16 * KB;
-        const uint8_t* g = ((i & 1) ? Qb : Pb) + int64_t(wave * 64 + (i >> 1) * 16) * ldb + int64_t(ks) * KB;
-        __builtin_amdgcn_global_load_lds(g + voff, (lds_void_t*)sp, 16, 0, 0);
+        uint8_t* sp = smem + (ks % NSTAGE) * SBYTES;
+        const uint8_t* g;
+        if (i < 4) {
+            sp += (wave * 64 + i * 16) * KB;
+            g = Pb + int64_t(wave * 64 + i * 16) * ldb;
+        } else {
+            sp += OPND_BYTES + (wave * (TN / 4) + (i - 4) * 16) * KB;
+            g = Qb + int64_t(wave * (TN / 4) + (i - 4) * 16) * ldb;
+        }
+        __builtin_amdgcn_global_load_lds(g + int64_t(ks) * KB + voff, (lds_void_t*)sp, 16, 0, 0);
     };
 
-    f32x16 acc[4][4];
+    f32x16 acc[4][NB];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
 
     // Fragment i of one 16-deep K substep: A chunk i (i < 4) or B chunk i - 4.
-    auto rd1 = [&](int ks, int sub, int i, u32x4 (&fa)[4], u32x4 (&fb)[4]) __attribute__((always_inline)) {
-        const uint8_t* sp = smem + (ks % NSTAGE) * STAGE_BYTES;
+    auto rd1 = [&](int ks, int sub, int i, u32x4 (&fa)[4], u32x4 (&fb)[NB]) __attribute__((always_inline)) {
+        const uint8_t* sp = smem + (ks % NSTAGE) * SBYTES;
         const int chunk = 2 * sub + kg;
         if (i < 4) fa[i] = *reinterpret_cast<const u32x4*>(sp + swz(wm * 128 + i * 32 + r32, chunk));
-        else fb[i - 4] = *reinterpret_cast<const u32x4*>(sp + OPND_BYTES + swz(wn * 128 + (i - 4) * 32 + r32, chunk));
+        else fb[i - 4] = *reinterpret_cast<const u32x4*>(sp + OPND_BYTES + swz(wn * (TN / 2) + (i - 4) * 32 + r32, chunk));
     };
     // Workgroup barrier without the release fence of __syncthreads(), which
     // would also drain the direct-to-LDS loads still in flight for later
@@ -414,7 +425,13 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ws, int first, int xt_cur) {
     auto wait_loads = [&](int after) {
         if (after == 17) asm volatile("s_waitcnt vmcnt(17)" ::: "memory");
         else if (after == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        else if (after == 13) asm volatile("s_waitcnt vmcnt(13)" ::: "memory");
+        else if (after == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+        else if (after == 11) asm volatile("s_waitcnt vmcnt(11)" ::: "memory");
+        else if (after == 10) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
         else if (after == 9) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+        else if (after == 7) asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
+        else if (after == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
         else if (after == 1) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
         else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     };
@@ -427,25 +444,34 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ws, int first, int xt_cur) {
         asm volatile("" ::: "memory");
     };
 
-    // The 16 MFMAs of one substep on (fa, fb).  After each of the first 8
-    // comes one fragment read of the next substep (stage rks, substep rsub,
-    // into na / nb).  When ia >= 0, every fourth MFMA is also followed by one
-    // load of the pair (ia, ia + 1): quarter q, loads 4 q .. 4 q + 3 of its 16,
-    // load L being instruction L / 2 of stage ia + (L & 1).  The order is fixed
-    // (sched_barrier), so reads and loads stream out evenly between the MFMAs
-    // instead of in bursts that would stall instruction issue behind a full
-    // load queue.
-    auto substep = [&](const u32x4 (&fa)[4], const u32x4 (&fb)[4], bool do_read, int rks, int rsub,
-                       u32x4 (&na)[4], u32x4 (&nb)[4], int ia, int q) __attribute__((always_inline)) {
+    // The MF MFMAs of one substep on (fa, fb).  The NR fragment reads of the
+    // next substep (stage rks, substep rsub, into na / nb) follow the first
+    // MFMAs, one each (the surplus after the last when NR > MF).  When ia >= 0,
+    // quarter q of the LP loads of the pair (ia, ia + 1) is spread evenly over
+    // the MFMAs, load l being instruction l / 2 of stage ia + (l & 1).  The
+    // order is fixed (sched_barrier), so reads and loads stream out between
+    // the MFMAs instead of in bursts that would stall instruction issue behind
+    // a full load queue.
+    auto substep = [&](const u32x4 (&fa)[4], const u32x4 (&fb)[NB], bool do_read, int rks, int rsub,
+                       u32x4 (&na)[4], u32x4 (&nb)[NB], int ia, int q) __attribute__((always_inline)) {
+        const int l0 = q * LP / 4, nl = (q + 1) * LP / 4 - l0;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            Mfma<T>::run(fa[i >> 2], fb[i & 3], acc[i >> 2][i & 3]);
+        for (int i = 0; i < MF; ++i) {
+            Mfma<T>::run(fa[i / NB], fb[i % NB], acc[i / NB][i % NB]);
             __builtin_amdgcn_sched_barrier(0);
-            if (i < 8 && do_read) rd1(rks, rsub, i, na, nb);
-            if (ia >= 0 && (i & 3) == 3) {
-                const int L = q * 4 + (i >> 2);
-                issue1(ia + (L & 1), L >> 1);
+            if (do_read) {
+                if (i < NR) rd1(rks, rsub, i, na, nb);
+                if (i == MF - 1)
+#pragma unroll
+                    for (int r = MF; r < NR; ++r) rd1(rks, rsub, r, na, nb);
             }
+            if (ia >= 0)
+#pragma unroll
+                for (int j = 0; j < nl; ++j)
+                    if ((j + 1) * MF / nl - 1 == i) {
+                        const int l = l0 + j;
+                        issue1(ia + (l & 1), l >> 1);
+                    }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -461,33 +487,35 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ws, int first, int xt_cur) {
     // instructions alternating so both halves of a line are requested back to
     // back.  The pair (ks + 4, ks + 5) goes into the slots of stages ks - 1 and
     // ks, which every wave has finished reading once the barrier of even step
-    // ks has passed; its 16 loads are spread in quarters over the four
+    // ks has passed; its LP loads are spread in quarters over the four
     // substeps that follow (second of step ks, both of ks + 1, first of
     // ks + 2).  At the barrier of step ks, stage ks + 1 must have landed: for
-    // even ks it is the second of its pair and all 16 loads of the next pair
+    // even ks it is the second of its pair and all LP loads of the next pair
     // came after it; for odd ks it is the first of its pair, followed by one
     // load of its partner and the first half of the next pair.
-    u32x4 f0a[4], f0b[4], f1a[4], f1b[4];
+    constexpr int W_EVEN = LP, W_ODD = 1 + LP / 2, W_FIRST = 1 + LP;
+    u32x4 f0a[4], f0b[NB], f1a[4], f1b[NB];
 #pragma unroll
     for (int p = 0; p < 4; p += 2)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) issue1(p + (i & 1), i >> 1);
-    wait_loads(17);
+        for (int l = 0; l < LP; ++l) issue1(p + (l & 1), l >> 1);
+    wait_loads(W_FIRST);
     barrier();
 #pragma unroll
-    for (int i = 0; i < 8; ++i) rd1(0, 0, i, f0a, f0b);
+    for (int i = 0; i < NR; ++i) rd1(0, 0, i, f0a, f0b);
     __builtin_amdgcn_sched_barrier(0);
     // Epilogue operand capture (bf16 Poly / Update).  The Q operand holds the
     // values the epilogue combines with the product: X[i][j] = X^T[j][i] for
     // Update, A[i][j] = A[j][i] for Poly.  K stage 8 ti + 4 wm + r covers rows
     // 32 r .. 32 r + 31 of this wave's sub-tile, so while that stage is in LDS
-    // each lane copies the 8 chunks its mirrored-pass tasks of round r need
+    // each lane copies the 2 NB chunks its mirrored-pass tasks of round r need
     // (task t: column j = lane / 4 + 16 t, rows 8 (lane % 4) .. + 7) into
     // registers, and the epilogue reads nothing from global memory.
     constexpr bool CAP = sizeof(T) == 2 && KIND != KIND_GRAM;
+    constexpr int NT = 2 * NB;                           // epilogue tasks per lane and pass
     const int64_t gi_w = int64_t(ti) * GT + wm * 128;   // this wave's sub-tile origin
-    const int64_t gj_w = int64_t(tj) * GT + wn * 128;
-    u32x4 pre[CAP ? 4 : 1][8];
+    const int64_t gj_w = int64_t(tj) * TN + wn * (TN / 2);
+    u32x4 pre[CAP ? 4 : 1][NT];
     const int cap0 = ti * (GT * int(sizeof(T)) / KB) + wm * 4;
     auto capture = [&](int ks) __attribute__((always_inline)) {
         if constexpr (CAP) {
@@ -495,11 +523,11 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ws, int first, int xt_cur) {
             if (r >= 0 && r < 4) {
                 // Register selects rather than pre[r][t] = ..., which would
                 // index the array dynamically and move it to scratch memory.
-                const uint8_t* sq = smem + (ks % NSTAGE) * STAGE_BYTES + OPND_BYTES;
+                const uint8_t* sq = smem + (ks % NSTAGE) * SBYTES + OPND_BYTES;
 #pragma unroll
-                for (int t = 0; t < 8; ++t) {
+                for (int t = 0; t < NT; ++t) {
                     const u32x4 c = *reinterpret_cast<const u32x4*>(
-                        sq + swz(wn * 128 + (lane >> 2) + 16 * t, lane & 3));
+                        sq + swz(wn * (TN / 2) + (lane >> 2) + 16 * t, lane & 3));
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr) pre[rr][t] = r == rr ? c : pre[rr][t];
                 }
@@ -518,15 +546,15 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ws, int first, int xt_cur) {
         substep(f1a, f1b, true, ks + 1, 0, f0a, f0b, pb, qb);
     };
     // the prologue issued pairs (0, 1) and (2, 3) whole
-    step(0, 16, -1, 0, 4, 0);
-    step(1, 9, 4, 1, 4, 2);
+    step(0, W_EVEN, -1, 0, 4, 0);
+    step(1, W_ODD, 4, 1, 4, 2);
     int ks = 2;
     for (; ks + 6 <= nk; ks += 2) {
-        step(ks, 16, ks + 2, 3, ks + 4, 0);
-        step(ks + 1, 9, ks + 4, 1, ks + 4, 2);
+        step(ks, W_EVEN, ks + 2, 3, ks + 4, 0);
+        step(ks + 1, W_ODD, ks + 4, 1, ks + 4, 2);
     }
     // ks == nk - 4: the last pair (nk - 2, nk - 1) lacks its last quarter
-    step(ks, 16, ks + 2, 3, -1, 0);
+    step(ks, W_EVEN, ks + 2, 3, -1, 0);
     step(ks + 1, 1, -1, 0, -1, 0);
     step(ks + 2, 0, -1, 0, -1, 0);
     substep(f0a, f0b, true, nk - 1, 1, f1a, f1b, -1, 0);
@@ -553,19 +581,19 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ws, int first, int xt_cur) {
     // Update of a transposed weight.  Gram scales in each pass; the other
     // kinds form their values in the mirrored pass and hand them to the tile
     // pass through the staging slice.
-    const bool off_diag = ti != tj;
+    const bool off_diag = ti != tj * TN / GT;
     const bool run_b = KIND == KIND_GRAM ? off_diag : true;
     const bool write_b = KIND == KIND_UPDATE ? (!LAST || ep.trans) : off_diag;
     const bool run_a = !(KIND == KIND_UPDATE && LAST && ep.trans);
     const bool hand_over = KIND != KIND_GRAM && run_a;
 
-    uint8_t* st = smem + wave * WAVE_ST_BYTES;
+    uint8_t* st = smem + wave * (32 * (TN / 2) * 4);   // 32 rows x TN/2 columns of fp32
     // One 32-row block of the wave's sub-tile; called with literal indices so
     // the accumulator and capture arrays are never indexed dynamically.
-    auto round = [&](const int a, const f32x16 (&ac)[4], const u32x4 (&pf)[8]) __attribute__((always_inline)) {
+    auto round = [&](const int a, const f32x16 (&ac)[NB], const u32x4 (&pf)[NT]) __attribute__((always_inline)) {
         // accumulators: lane holds column 32 b + lane % 32, rows 8 g + 4 (lane / 32) .. + 3
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const f32x4 v4 = {ac[b][4 * g], ac[b][4 * g + 1], ac[b][4 * g + 2], ac[b][4 * g + 3]};
@@ -575,7 +603,7 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ws, int first, int xt_cur) {
         if (run_b) {
             // mirrored pass: column j of the sub-tile, rows 8 ic .. 8 ic + 7
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
+            for (int t = 0; t < NT; ++t) {
                 const int j = (lane >> 2) + 16 * t, ic = lane & 3;
                 f32x4* s0 = reinterpret_cast<f32x4*>(st + st_off(j, ic * 8));
                 f32x4* s1 = reinterpret_cast<f32x4*>(st + st_off(j, ic * 8 + 4));
@@ -603,10 +631,10 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ws, int first, int xt_cur) {
             __builtin_amdgcn_wave_barrier();
         }
         if (run_a) {
-            // tile pass: row of the sub-tile, columns 8 cc .. 8 cc + 7 (16 lanes per row)
+            // tile pass: row of the sub-tile, columns 8 cc .. 8 cc + 7 (4 NB lanes per row)
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const int cc = lane & 15, row = (lane >> 4) + 4 * t;
+            for (int t = 0; t < NT; ++t) {
+                const int cc = lane % (4 * NB), row = lane / (4 * NB) + (16 / NB) * t;
                 f32x8 v;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) v.v[e] = *reinterpret_cast<const float*>(st + st_off(cc * 8 + e, row));
@@ -627,10 +655,25 @@ __device__ __forceinline__ void gemm_tile(uint8_t* ws, int first, int xt_cur) {
 
 inline unsigned grid_for(uint32_t items) { return items; }   // dispatch lists are padded to 8
 
+// Entry b of the phase's dispatch list is workgroup b's tile; the tile width
+// (NB) is uniform per workgroup.
+template <typename T, int KIND, bool LAST>
+__device__ __forceinline__ void gemm_entry(uint8_t* ws, int first, int xt_cur) {
+    __shared__ __align__(16) uint8_t smem[GEMM_LDS];
+    const mo_wl_header* h = wl_header(ws);
+    const uint64_t items_off = KIND == KIND_GRAM ? h->gram_offset
+                             : KIND == KIND_POLY ? h->poly_offset : h->upd_offset;
+    const mo_wl_item it = reinterpret_cast<const mo_wl_item*>(ws + items_off)[blockIdx.x];
+    if (it.mat == MO_WL_PAD) return;
+    if (it.nb == 4) gemm_tile<T, KIND, LAST, 4>(smem, ws, it, first, xt_cur);
+    else if (it.nb == 2) gemm_tile<T, KIND, LAST, 2>(smem, ws, it, first, xt_cur);
+    else gemm_tile<T, KIND, LAST, 1>(smem, ws, it, first, xt_cur);
+}
+
 // One plainly named kernel per (phase, NS dtype), so profiles name them unambiguously.
 #define MO_GEMM_KERNEL(name, T, KIND, LAST)                                               \
     __global__ __launch_bounds__(G_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))    \
-    void name(uint8_t* ws, int first, int xt_cur) { gemm_tile<T, KIND, LAST>(ws, first, xt_cur); }
+    void name(uint8_t* ws, int first, int xt_cur) { gemm_entry<T, KIND, LAST>(ws, first, xt_cur); }
 MO_GEMM_KERNEL(gram_bf16, bf16_t, KIND_GRAM, false)
 MO_GEMM_KERNEL(gram_f32, float, KIND_GRAM, false)
 MO_GEMM_KERNEL(poly_bf16, bf16_t, KIND_POLY, false)

@@ -5,7 +5,7 @@ byte layout is specified in ``include/mo.h`` (muon_build_worklist) and the
 record comments there.  This twin is written from that specification with
 Python's ``struct`` so that the C++ builder can be checked byte for byte.
 
-Layout (little-endian, natural alignment, version 4):
+Layout (little-endian, natural alignment, version 5):
   header (128 B): magic 'MOWL', version, n_mats, ns_steps, ns_dtype, gemm_tile,
       mom_tile, elem_bytes, n_mom_items, n_gram_items, n_poly_items,
       n_upd_items, max_partials, 0, mats_offset, gram_offset, poly_offset,
@@ -15,9 +15,10 @@ Layout (little-endian, natural alignment, version 4):
       off_Xt0, off_Xt1, off_A, off_B, off_partials, off_scale (u64), rows,
       cols, m, n, m_pad, n_pad, flags, desc_index, mom_begin, mom_tiles_c,
       n_partials (u32), lr_eff, decay (f32), 5 x 0
-  items (8 B: u32 matrix record index, u16 ti, u16 tj): Gram, Poly, Update
-      dispatch lists (entry b is run by workgroup b), each 256-byte aligned
-      and a multiple of 8 long; see dispatch() below
+  items (16 B: u32 matrix record index, tile row ti, tile column tj, width
+      nb; the tile covers rows 256 ti .. +256 and columns 64 nb tj .. +64 nb):
+      Gram, Poly, Update dispatch lists (entry b is run by workgroup b), each
+      256-byte aligned and a multiple of 8 long; see dispatch() below
 Workspace regions follow the list, per record: X, Xt0, Xt1 (m_pad*n_pad
 elements each), A, B (m_pad^2), partials (n_partials fp32), scale (16 B); every
 region 256-byte aligned.
@@ -109,7 +110,7 @@ def build(descs: Sequence[dict], hp: dict) -> bytes:
             klen = r["n_pad"] if k_is_n else r["m_pad"]
             for bi in range(0, tm, 4):
                 for bj in range(0, tn, 8):
-                    blk = [(j, a, b) for a in range(bi, min(bi + 4, tm))
+                    blk = [(j, a, b, 4) for a in range(bi, min(bi + 4, tm))
                            for b in range(bj, min(bj + 8, tn)) if not upper_only or a <= b]
                     if blk:
                         blocks.append((blk, klen))
@@ -128,8 +129,21 @@ def build(descs: Sequence[dict], hp: dict) -> bytes:
                 queues[x] += blk[i:i + take]
                 load[x] += klen * take
                 i += take
+        # Queues of at most 32 tiles (32 CUs per XCD) have every tile split,
+        # longer ones the len % 32 tiles of the last round: into S = 4 quarter
+        # or S = 2 half-width tiles, the largest S with S * (tiles split) <= 32.
+        for x, q in enumerate(queues):
+            n = len(q)
+            if n == 0:
+                continue
+            first = 0 if n <= 32 else n - n % 32
+            r = n - first
+            S = 1 if r == 0 else 4 if 4 * r <= 32 else 2 if 2 * r <= 32 else 1
+            if S > 1:
+                queues[x] = q[:first] + [(j, a, b * S + p, 4 // S) for (j, a, b, _) in q[first:]
+                                         for p in range(S)]
         longest = max((len(q) for q in queues), default=0)
-        return [queues[x][j] if j < len(queues[x]) else (PAD, 0, 0)
+        return [queues[x][j] if j < len(queues[x]) else (PAD, 0, 0, 0)
                 for j in range(longest) for x in range(8)]
 
     gram = dispatch(ordered(lambda r: upper(r) * r["n_pad"]), True, True)
@@ -138,9 +152,9 @@ def build(descs: Sequence[dict], hp: dict) -> bytes:
 
     mats_off = 128
     gram_off = _up(mats_off + 192 * len(recs), ALIGN)
-    poly_off = _up(gram_off + 8 * len(gram), ALIGN)
-    upd_off = _up(poly_off + 8 * len(poly), ALIGN)
-    wl_bytes = _up(upd_off + 8 * len(upd), ALIGN)
+    poly_off = _up(gram_off + 16 * len(gram), ALIGN)
+    upd_off = _up(poly_off + 16 * len(poly), ALIGN)
+    wl_bytes = _up(upd_off + 16 * len(upd), ALIGN)
 
     off = wl_bytes
     for r in recs:
@@ -153,7 +167,7 @@ def build(descs: Sequence[dict], hp: dict) -> bytes:
     ws_bytes = off
 
     out = bytearray(wl_bytes)
-    struct.pack_into("<14I6Q4f2I", out, 0, MAGIC, 4, len(recs), hp["ns_steps"], hp["ns_dtype"],
+    struct.pack_into("<14I6Q4f2I", out, 0, MAGIC, 5, len(recs), hp["ns_steps"], hp["ns_dtype"],
                      T, MT, es, mom, len(gram), len(poly), len(upd), max_partials, 0,
                      mats_off, gram_off, poly_off, upd_off, wl_bytes, ws_bytes,
                      hp["ns_a"], hp["ns_b"], hp["ns_c"], hp["eps"], 0, 0)
@@ -166,8 +180,8 @@ def build(descs: Sequence[dict], hp: dict) -> bytes:
                          r["desc_index"], r["mom_begin"], r["mom_tiles_c"], r["n_partials"],
                          r["lr_eff"], r["decay"], 0, 0, 0, 0, 0)
     for base, items in ((gram_off, gram), (poly_off, poly), (upd_off, upd)):
-        for k, (j, a, b) in enumerate(items):
-            struct.pack_into("<IHH", out, base + 8 * k, j, a, b)
+        for k, item in enumerate(items):
+            struct.pack_into("<4I", out, base + 16 * k, *item)
     return bytes(out)
 
 

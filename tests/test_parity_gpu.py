@@ -11,7 +11,7 @@ import pytest
 from matrix_optimizers_amd import workloads as wlmod
 from oracle import adamw as oadamw
 
-from _parity import Case, check_case, random_case, rel, run_gpu, to_dev, to_host
+from _parity import Case, check_case, hp_kwargs, random_case, rel, run_gpu, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -204,3 +204,45 @@ def test_device_copy(gpu, nbytes):
     mo.device_copy(dst, src)
     torch.cuda.synchronize()
     assert torch.equal(dst, src)
+
+
+def _widths(shapes, hp, mat):
+    """Tile widths (nb -> count) of matrix `mat` in each phase's dispatch list."""
+    import collections
+    import matrix_optimizers_amd as mo
+    from worklist_cases import parse_worklist
+    descs = [mo.descriptor(r, c, W=(1 << 40) + 3 * i * (1 << 34), G=(1 << 40) + (3 * i + 1) * (1 << 34),
+                           M=(1 << 40) + (3 * i + 2) * (1 << 34)) for i, (r, c) in enumerate(shapes)]
+    wl = mo.build_worklist(descs, mo.hparams(**hp_kwargs(hp)))
+    _, lists = parse_worklist(wl)
+    return [dict(collections.Counter(nb for m, _, _, nb in items if m == mat)) for items in lists]
+
+
+@pytest.mark.parametrize("shape,count,in_bucket,alone", [
+    ((1024, 1024), 30, [{4: 10}, {4: 10}, {4: 16}], [{1: 40}, {1: 40}, {1: 64}]),
+    ((3072, 1024), 12, [{2: 20}, {2: 20}, {4: 48}], [{1: 40}, {1: 40}, {1: 192}]),
+])
+def test_tile_widths_give_bit_identical_results(gpu, shape, count, in_bucket, alone):
+    """Where full tiles would leave CUs idle the host splits them into half or
+    quarter widths.  Matrix 0 runs at full / half width inside a large bucket and
+    at quarter width alone; every output element is summed over the same K in
+    the same order either way, so the results are bit-identical."""
+    assert _widths([shape] * count, BF, 0) == in_bucket
+    assert _widths([shape], BF, 0) == alone
+    cases = [random_case(shape[0], shape[1], "bf16", "bf16", seed=70 + i) for i in range(count)]
+    a = run_gpu(cases, BF, gpu)[0]
+    b = run_gpu([cases[0]], BF, gpu)[0]
+    for u, v in zip(a, b):
+        np.testing.assert_array_equal(u, v)
+    print(shape, check_case(cases[0], b, BF))
+
+
+@pytest.mark.parametrize("ns", ["bf16", "f32"])
+def test_half_width_tiles_parity(gpu, ns):
+    """Eight 1024 x 1024 matrices: every phase runs half-width tiles."""
+    hp = dataclasses.replace(BF, ns_dtype=ns)
+    assert _widths([(1024, 1024)] * 8, hp, 3) == [{2: 20}, {2: 20}, {2: 32}]
+    cases = [random_case(1024, 1024, "bf16", "bf16", seed=90 + i) for i in range(8)]
+    got = run_gpu(cases, hp, gpu)
+    for k in (0, 5):
+        print(ns, k, check_case(cases[k], got[k], hp))

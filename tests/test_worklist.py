@@ -13,7 +13,7 @@ from oracle import worklist as twin
 HERE = os.path.dirname(os.path.abspath(__file__))
 GOLDEN = os.path.join(HERE, "golden", "worklist_digests.json")
 
-from worklist_cases import ADJ, CASES, DT, fake_descs, hp_dict
+from worklist_cases import ADJ, CASES, DT, fake_descs, hp_dict, parse_worklist as _parse
 
 
 def c_build(descs, hp: wlmod.MuonHP):
@@ -60,3 +60,58 @@ def test_side_beyond_limit_is_unsupported():
     with pytest.raises(mo.MoError) as e:
         c_build(fake_descs([(1, (1 << 23) + 1)]), wlmod.MuonHP())
     assert e.value.status == -2
+
+
+@pytest.mark.parametrize("key", list(CASES))
+def test_dispatch_lists_cover_every_tile_once(key):
+    """Every Gram / Poly upper-triangle tile and every Update tile is covered by
+    its parts exactly once, parts have a width of 4, 2 or 1 column blocks of 64,
+    and only pad entries carry the pad index."""
+    descs, hp = CASES[key]
+    wl, _ = c_build(descs, hp)
+    recs, lists = _parse(wl)
+    for phase, items in zip(("gram", "poly", "update"), lists):
+        assert len(items) % 8 == 0
+        cover = {}
+        for mat, ti, tj, nb in items:
+            if mat == 0xFFFFFFFF:
+                assert (ti, tj, nb) == (0, 0, 0)
+                continue
+            assert nb in (1, 2, 4)
+            c0 = 64 * nb * tj
+            m_pad, n_pad = recs[mat]
+            width = m_pad if phase != "update" else n_pad
+            assert 256 * ti < m_pad and c0 + 64 * nb <= width
+            for c in range(c0 // 64, c0 // 64 + nb):
+                keyc = (mat, ti, c)
+                assert keyc not in cover, (phase, keyc)
+                cover[keyc] = True
+        want = set()
+        for mat, (m_pad, n_pad) in enumerate(recs):
+            tm = m_pad // 256
+            for ti in range(tm):
+                if phase == "update":
+                    cols = range(n_pad // 64)
+                else:
+                    cols = [c for tj in range(ti, tm) for c in range(4 * tj, 4 * tj + 4)]
+                want.update((mat, ti, c) for c in cols)
+        assert set(cover) == want, phase
+
+
+def test_underfilled_launch_uses_narrow_tiles():
+    """A bucket with few tiles per XCD queue splits them (quarter width when the
+    parts still fit the XCD's 32 CUs).  In the decoder-layer bucket the Update
+    queues (98 tiles each) split only the 2 tiles of their last round, the Poly
+    queues (31-32 tiles) none, and the Gram queues that the K-length balance
+    left short (the long-K tiles) split all of theirs."""
+    descs, hp = CASES["ragged_not_tile_multiple"]
+    _, lists = _parse(c_build(descs, hp)[0])
+    for items in lists:
+        assert {nb for m, _, _, nb in items if m != 0xFFFFFFFF} == {1}
+    descs, hp = CASES["decoder_layer_h2048"]
+    _, lists = _parse(c_build(descs, hp)[0])
+    upd = [nb for m, _, _, nb in lists[2] if m != 0xFFFFFFFF]
+    assert upd.count(4) == 768 and upd.count(1) == 64 and len(upd) == 832
+    assert {nb for m, _, _, nb in lists[1] if m != 0xFFFFFFFF} == {4}
+    gram = [(m, nb) for m, _, _, nb in lists[0] if m != 0xFFFFFFFF]
+    assert {nb for _, nb in gram} == {1, 2, 4}

@@ -1,6 +1,8 @@
 """Work-list test cases: the workloads and the edge cases, as descriptors with
 made-up addresses.  No library or binding import (the golden-digest script uses
 this with the Python twin only)."""
+import struct
+
 from matrix_optimizers_amd import workloads as wlmod
 
 DT = {"f32": 0, "bf16": 1}
@@ -52,3 +54,18 @@ def all_cases():
 
 
 CASES = all_cases()
+
+
+def parse_worklist(wl: bytes):
+    """Header fields, matrix records (m_pad, n_pad) and the three item lists."""
+    hdr = struct.unpack_from("<14I6Q4f2I", wl, 0)
+    n_mats = hdr[2]
+    counts = hdr[9:12]
+    mats_off, offs = hdr[14], hdr[15:18]
+    recs = []
+    for k in range(n_mats):
+        rec = struct.unpack_from("<4Q4q7Q11I2f5I", wl, mats_off + 192 * k)
+        recs.append((rec[19], rec[20]))   # m_pad, n_pad
+    lists = [[struct.unpack_from("<4I", wl, off + 16 * i) for i in range(cnt)]
+             for off, cnt in zip(offs, counts)]
+    return recs, lists
