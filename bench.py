@@ -116,8 +116,16 @@ def algorithmic_flops(spec_rows, spec_cols, steps):
     return {"gram": float(m) * m * n, "poly": float(m) ** 3, "update": 2.0 * m * m * n}
 
 
+CPU_BUDGET_S = 20.0          # oracle work per bench run
+ORACLE_TFLOPS_GUESS = 0.5    # fp64 numpy on a GPU machine's host, for sizing the sample only
+
+
 def cpu_baseline(wl, args):
-    """The fp64 oracle on one matrix of each distinct shape + the tail."""
+    """The fp64 oracle on a bounded sample of the workload: one matrix of each
+    distinct shape, smallest first, while the estimated time stays within
+    CPU_BUDGET_S (at least one matrix; if even the smallest would overrun, it
+    runs with fewer Newton-Schulz steps), plus the AdamW tail."""
+    import dataclasses
     import numpy as np
     from matrix_optimizers_amd import workloads as wlmod
     from oracle import adamw as oadamw
@@ -128,26 +136,40 @@ def cpu_baseline(wl, args):
         cores = max([i.get("num_threads", 1) for i in info] or [1])
     except Exception:
         cores = os.cpu_count() or 1
-    seen, sample = set(), []
+    seen, shapes = set(), []
     for i, s in enumerate(wl.matrices):
         if (s.rows, s.cols) not in seen:
             seen.add((s.rows, s.cols))
-            sample.append(i)
+            shapes.append(i)
+    per = lambda i, k: wlmod.ns_flops_nominal(wl.matrices[i].rows, wl.matrices[i].cols, k)
+    shapes.sort(key=lambda i: per(i, wl.hp.ns_steps))
+    sample, est = [], 0.0
+    for i in shapes:
+        t = per(i, wl.hp.ns_steps) / (ORACLE_TFLOPS_GUESS * 1e12)
+        if sample and est + t > CPU_BUDGET_S:
+            break
+        sample.append(i)
+        est += t
+    hp = wl.hp
+    if est > CPU_BUDGET_S and hp.ns_steps > 1:
+        k = max(1, int(hp.ns_steps * CPU_BUDGET_S / est))
+        hp = dataclasses.replace(hp, ns_steps=k)
     flops = 0.0
     inputs = [wlmod.matrix_inputs(wl, i) for i in sample]
     t0 = time.perf_counter()
     for i, x in zip(sample, inputs):
-        omuon.muon_step(x.W, x.G, x.M, wl.hp)
-        s = wl.matrices[i]
-        flops += wlmod.ns_flops_nominal(s.rows, s.cols, wl.hp.ns_steps)
+        omuon.muon_step(x.W, x.G, x.M, hp)
+        flops += per(i, hp.ns_steps)
     if wl.tail_numel:
         t = wlmod.tail_inputs(wl.seed, wl.tail_numel)
         a = wl.adamw
         oadamw.adamw_step(t.p, t.g, t.m, t.v, a.step, a.lr, a.beta1, a.beta2, a.eps, a.weight_decay)
     dt = time.perf_counter() - t0
-    shapes = ", ".join(f"{wl.matrices[i].rows}x{wl.matrices[i].cols}" for i in sample)
+    desc = ", ".join(f"{wl.matrices[i].rows}x{wl.matrices[i].cols}" for i in sample)
+    what = "one matrix of each distinct shape" if len(sample) == len(shapes) else "a bounded sample of matrices"
+    steps = "" if hp.ns_steps == wl.hp.ns_steps else f" with {hp.ns_steps} of {wl.hp.ns_steps} NS steps"
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"one matrix of each distinct shape ({shapes})"
+            "sample": f"{what} ({desc}){steps}"
                       + (f" + the {wl.tail_numel}-element AdamW tail" if wl.tail_numel else "")
                       + f", fp64 numpy, {dt:.2f} s"}
 
