@@ -187,6 +187,65 @@ mo_status mo_profile_read(double* ms, int64_t* launches);
  * 16-byte aligned.  Errors: MO_ERR_INVALID_ARG, MO_ERR_ALIAS, MO_ERR_HIP. */
 mo_status mo_device_copy(void* dst, const void* src, size_t bytes, void* stream);
 
+/* ---- owner planner (host only) --------------------------------------------
+ * The step upstream of a bucket: which data-parallel rank owns each role
+ * ([P §4.1]).  Every FSDP block contributes one role per 2D matrix and one
+ * packed tail role for its non-2D tensors ([P §3]).  The greedy load is the
+ * role's owner-resident numel, a proxy for its resident bytes and optimizer
+ * work ([P §4.1]).  The pages describe the policies but do not print the
+ * algorithm, so the readings below are this library's:
+ *   MO_PLAN_ROLE_GREEDY   blocks in increasing block index; within a block,
+ *                         roles by decreasing numel (ties: array order), each
+ *                         to the rank with the least numel assigned so far over
+ *                         all blocks (ties: lowest rank).  The default.
+ *   MO_PLAN_SCOPE_GREEDY  all roles of all blocks pooled, by decreasing numel
+ *                         (ties: array order), each to the least-loaded rank.
+ *   MO_PLAN_COST_AWARE    the scope plan if its largest per-block owner share
+ *                         max_{B,r} O_{B,r} (the numel one rank must send to
+ *                         materialize block B, which sets C_owner of [P §4.2])
+ *                         is at most block_cap, else the role plan; block_cap
+ *                         0 means the role plan's own largest share.
+ * All functions only read host arrays and run no device work. */
+#define MO_ROLE_MATRIX 0
+#define MO_ROLE_TAIL   1
+#define MO_PLAN_ROLE_GREEDY  0
+#define MO_PLAN_SCOPE_GREEDY 1
+#define MO_PLAN_COST_AWARE   2
+
+typedef struct {
+    int32_t block;   /* FSDP block index, >= 0 */
+    int32_t kind;    /* MO_ROLE_MATRIX or MO_ROLE_TAIL */
+    int64_t rows;    /* matrix rows; for a tail, its numel */
+    int64_t cols;    /* matrix cols; for a tail, 1 */
+} mo_role;
+
+/* owner_out[i] in [0, world) for each of the n_roles roles.  Errors:
+ * MO_ERR_INVALID_ARG (null pointer with n_roles > 0, world < 1, n_roles < 0,
+ * negative block, size or cap, a tail with cols != 1, unknown kind or
+ * policy). */
+mo_status mo_plan_owners(const mo_role* roles, int32_t n_roles, int32_t world, int32_t policy,
+                         int64_t block_cap, int32_t* owner_out);
+
+/* Resource scorer of a plan.  Per rank (arrays of `world`): rank_numel = its
+ * owner-resident numel; rank_flops = nominal Newton-Schulz flops of one
+ * iteration over its matrices, sum of 4 m^2 n + 2 m^3 with m = min(rows, cols),
+ * n = max (tails count 0).  Per block (arrays of n_blocks = 1 + largest block
+ * index; may be NULL): block_gamma = max_r O_{B,r} / (P_B / world), the owner
+ * imbalance gamma_B of [P §4.2] (0 for an empty block), and block_owner_comm =
+ * (world - 1) max_r O_{B,r}, its materialization volume C_owner in elements.
+ * Errors as mo_plan_owners, plus an owner outside [0, world). */
+mo_status mo_plan_score(const mo_role* roles, int32_t n_roles, int32_t world, const int32_t* owner,
+                        double* rank_numel, double* rank_flops, int32_t n_blocks,
+                        double* block_gamma, double* block_owner_comm);
+
+/* Block-local layout of a plan: every rank keeps, per block, one flat buffer
+ * holding the roles it owns, in role-array order and back to back; a role the
+ * rank does not own has an empty segment there ([P §4.1]'s one contiguous
+ * local segment per parameter).  offset_out[i] is role i's element offset in
+ * its owner's buffer for its block.  Errors as mo_plan_score. */
+mo_status mo_plan_layout(const mo_role* roles, int32_t n_roles, int32_t world, const int32_t* owner,
+                         int64_t* offset_out);
+
 #ifdef __cplusplus
 }
 #endif

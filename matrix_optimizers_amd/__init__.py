@@ -14,8 +14,9 @@ The library is loaded on first use; if it has not been built
 (``python -m matrix_optimizers_amd.build``) every entry point raises.
 """
 from ._binding import (  # noqa: F401
-    MoError, MoMatrix, MoMuonHParams, MuonOwnerStep, PHASES, adamw_tail_step, build_worklist,
-    descriptor, device_copy, hparams, load_library, mo_status_string, muon_build_worklist,
-    muon_owner_step, muon_workspace_bytes, profile_enable, profile_read, status_string,
-    tensor_descriptor, workspace_bytes,
+    PLAN_POLICIES, ROLE_MATRIX, ROLE_TAIL, MoError, MoMatrix, MoMuonHParams, MoRole, MuonOwnerStep,
+    PHASES, adamw_tail_step, build_worklist, descriptor, device_copy, hparams, load_library,
+    mo_status_string, muon_build_worklist, muon_owner_step, muon_workspace_bytes, plan_layout,
+    plan_owners, plan_score, profile_enable, profile_read, status_string, tensor_descriptor,
+    workspace_bytes,
 )

@@ -56,7 +56,17 @@ class MoMuonHParams(ctypes.Structure):
 _lib = None
 
 EXPORTS = ["muon_workspace_bytes", "muon_build_worklist", "muon_owner_step", "adamw_tail_step",
-           "mo_status_string", "mo_profile_enable", "mo_profile_read", "mo_device_copy"]
+           "mo_status_string", "mo_profile_enable", "mo_profile_read", "mo_device_copy",
+           "mo_plan_owners", "mo_plan_score", "mo_plan_layout"]
+
+ROLE_MATRIX, ROLE_TAIL = 0, 1
+PLAN_POLICIES = {"role_greedy": 0, "scope_greedy": 1, "cost_aware": 2}
+
+
+class MoRole(ctypes.Structure):
+    """mo_role of include/mo.h."""
+    _fields_ = [("block", ctypes.c_int32), ("kind", ctypes.c_int32),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -83,8 +93,16 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mo_profile_read.argtypes = [P(ctypes.c_double), P(ctypes.c_int64)]
     lib.mo_device_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                    ctypes.c_void_p]
+    lib.mo_plan_owners.argtypes = [P(MoRole), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_int64, P(ctypes.c_int32)]
+    lib.mo_plan_score.argtypes = [P(MoRole), ctypes.c_int32, ctypes.c_int32, P(ctypes.c_int32),
+                                  P(ctypes.c_double), P(ctypes.c_double), ctypes.c_int32,
+                                  P(ctypes.c_double), P(ctypes.c_double)]
+    lib.mo_plan_layout.argtypes = [P(MoRole), ctypes.c_int32, ctypes.c_int32, P(ctypes.c_int32),
+                                   P(ctypes.c_int64)]
     for name in ("muon_workspace_bytes", "muon_build_worklist", "muon_owner_step",
-                 "adamw_tail_step", "mo_profile_enable", "mo_profile_read", "mo_device_copy"):
+                 "adamw_tail_step", "mo_profile_enable", "mo_profile_read", "mo_device_copy",
+                 "mo_plan_owners", "mo_plan_score", "mo_plan_layout"):
         getattr(lib, name).restype = ctypes.c_int32
     _lib = lib
     return lib
@@ -305,3 +323,47 @@ def profile_read() -> dict:
     cnt = (ctypes.c_int64 * len(PHASES))()
     _check(load_library().mo_profile_read(ms, cnt), "mo_profile_read")
     return {name: (ms[i], cnt[i]) for i, name in enumerate(PHASES)}
+
+
+# ---- owner planner (host only) ----------------------------------------------
+
+def _roles(roles):
+    """roles: sequence of (block, kind, rows, cols); kind ROLE_MATRIX / ROLE_TAIL."""
+    arr = (MoRole * max(len(roles), 1))()
+    for i, (b, k, r, c) in enumerate(roles):
+        arr[i] = MoRole(int(b), int(k), int(r), int(c))
+    return arr, len(roles)
+
+
+def plan_owners(roles, world: int, policy: str = "role_greedy", block_cap: int = 0) -> list:
+    """Owner rank of each role (mo_plan_owners)."""
+    if policy not in PLAN_POLICIES:
+        raise ValueError(f"unknown policy {policy!r}")
+    arr, n = _roles(roles)
+    out = (ctypes.c_int32 * max(n, 1))()
+    _check(load_library().mo_plan_owners(arr, n, int(world), PLAN_POLICIES[policy], int(block_cap), out),
+           "mo_plan_owners")
+    return list(out[:n])
+
+
+def plan_score(roles, world: int, owner) -> dict:
+    """Per-rank numel and NS flops, per-block gamma_B and C_owner (mo_plan_score)."""
+    arr, n = _roles(roles)
+    own = (ctypes.c_int32 * max(n, 1))(*owner)
+    nb = 1 + max((int(r[0]) for r in roles), default=-1)
+    rn = (ctypes.c_double * world)()
+    rf = (ctypes.c_double * world)()
+    bg = (ctypes.c_double * max(nb, 1))()
+    bc = (ctypes.c_double * max(nb, 1))()
+    _check(load_library().mo_plan_score(arr, n, int(world), own, rn, rf, nb, bg, bc), "mo_plan_score")
+    return {"rank_numel": list(rn), "rank_flops": list(rf), "block_gamma": list(bg[:nb]),
+            "block_owner_comm": list(bc[:nb])}
+
+
+def plan_layout(roles, world: int, owner) -> list:
+    """Element offset of each role in its owner's block-local buffer (mo_plan_layout)."""
+    arr, n = _roles(roles)
+    own = (ctypes.c_int32 * max(n, 1))(*owner)
+    out = (ctypes.c_int64 * max(n, 1))()
+    _check(load_library().mo_plan_layout(arr, n, int(world), own, out), "mo_plan_layout")
+    return list(out[:n])

@@ -145,8 +145,58 @@ WORKLOADS = _build()
 WORKLOAD_ORDER = ["single_256x512_f32", "decoder_layer_h2048", "batched_1024",
                   "llama8b_4layers", "large_single"]
 
+# The paper's timing and ablation model (§5.1 Setup): Qwen-style decoder layers,
+# hidden 4096, intermediate 16384, 32 heads; per layer 4 square attention
+# matrices, the MLP up (16384 x 4096) and down (4096 x 16384) matrices, and the
+# layer's two hidden-size norm vectors packed into its tail role (§3).  16 layers
+# give the 3.2B model of §5.2, 64 the 12.9B model of §5.6.
+PAPER_LAYER = ((4096, 4096, "q"), (4096, 4096, "k"), (4096, 4096, "v"), (4096, 4096, "o"),
+               (16384, 4096, "up"), (4096, 16384, "down"))
+PAPER_LAYER_TAIL = 2 * 4096
+ROLE_MATRIX, ROLE_TAIL = 0, 1
+
+
+def paper_model_roles(layers: int) -> List[Tuple[int, int, int, int]]:
+    """Planner roles (block, kind, rows, cols) of the paper's model, one block per layer."""
+    roles = []
+    for b in range(layers):
+        roles += [(b, ROLE_MATRIX, r, c) for r, c, _ in PAPER_LAYER]
+        roles.append((b, ROLE_TAIL, PAPER_LAYER_TAIL, 1))
+    return roles
+
+
+def planned_max_rank(layers: int, world: int, policy: str = "role_greedy") -> Workload:
+    """The bucket of the rank with the most Newton-Schulz work when the library's
+    owner planner places the paper's model over `world` ranks: the step time of
+    the whole data-parallel group is that rank's.  Paper settings (§5.1)."""
+    from . import _binding as B   # the C++ planner of libmo.so
+    roles = paper_model_roles(layers)
+    owner = B.plan_owners(roles, world, policy)
+    flops = B.plan_score(roles, world, owner)["rank_flops"]
+    top = max(range(world), key=lambda r: (flops[r], -r))
+    names = {(b, k): name for b in range(layers) for k, (_, _, name) in enumerate(PAPER_LAYER)}
+    mats, tail, k_in_block = [], [], {}
+    for i, ((b, kind, rows, cols), o) in enumerate(zip(roles, owner)):
+        if kind == ROLE_MATRIX:
+            k = k_in_block.get(b, 0)
+            k_in_block[b] = k + 1
+            if o == top:
+                mats.append(MatrixSpec(rows, cols, f"L{b}.{names[(b, k)]}"))
+        elif o == top:
+            tail.append(rows)
+    return Workload(
+        key=f"paper_planned_max_rank", seed=7, matrices=tuple(mats), w_dtype=BF16, g_dtype=BF16,
+        hp=MuonHP(lr=1e-3, weight_decay=1e-2, momentum=0.5, ns_steps=2, lr_adjust="match_rms_adamw"),
+        tail=tuple(tail),
+        description=f"rank {top}'s bucket (most NS work) of the paper's {layers}-layer model over "
+                    f"{world} ranks, {policy} owner plan, paper settings")
+
 
 def get(key: str) -> Workload:
+    if key == "paper_planned_max_rank":
+        if key not in WORKLOADS:
+            WORKLOADS[key] = planned_max_rank(16, 8)
+        return WORKLOADS[key]
     return WORKLOADS[key]
 
 
