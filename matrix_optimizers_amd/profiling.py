@@ -135,6 +135,55 @@ def read_traffic(profiles_dir: str, workload: str, phase: str) -> Optional[dict]
     return None
 
 
+# Counter groups of the executed-work summary; each is one rocprofv3 --pmc pass
+# (per-block limits: 8 SQ, 4 TCC, 4 TCP counters).
+COUNTER_PASSES = [
+    ["SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES",
+     "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "GRBM_GUI_ACTIVE"],
+    ["TCC_HIT_sum", "TCC_MISS_sum", "TCC_EA0_RDREQ_sum"],
+    ["TCP_TCC_READ_REQ_sum", "TCP_TCC_READ_REQ_LATENCY_sum", "TCP_PENDING_STALL_CYCLES_sum"],
+]
+XCDS, SIMDS, CUS = 8, 1024, 256     # MI355X: SQ and GRBM counters below are summed over these
+
+
+def counters_summary(pass_dirs, trace_dir, out_md, command, workload, flops_per_launch=None):
+    """Executed-work summary per GEMM phase from the counter passes:
+    MFMA instructions, MFMA-busy share of SIMD cycles, the shader clock implied
+    by the cycle counters and the kernel duration, L2 hit rate, mean L1->L2
+    read latency."""
+    stats = kernel_stats(trace_dir)
+    vals = {}
+    for d in pass_dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                name = short_name(r["Kernel_Name"])
+                if name is not None:
+                    vals.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    mean = {k: {c: sum(v) / len(v) for c, v in d.items()} for k, d in vals.items()}
+    lines = [f"# rocprofv3 counters: {workload}", "", "Commands (run from the repository root on one MI355X):", "",
+             "```", command, "```", "", f"Kernel sources SHA-256: `{sources_sha256()}`", "",
+             "Per launch, averaged over the profiled launches. GRBM_GUI_ACTIVE counts GPU-busy cycles per XCD "
+             f"(summed over {XCDS}); dividing by the traced duration gives the shader clock under load. "
+             f"SQ_VALU_MFMA_BUSY_CYCLES is summed over the {SIMDS} SIMDs.", "",
+             "| phase | avg (us) | MFMA instr | MFMA busy / SIMD-cycle | clock (GHz) | L2 hit | mean L1->L2 read latency (cycles) |",
+             "|---|---|---|---|---|---|---|"]
+    for name in sorted(mean, key=lambda k: -stats.get(k, {}).get("total_ns", 0.0)):
+        c = mean[name]
+        if "SQ_INSTS_MFMA" not in c or c["SQ_INSTS_MFMA"] == 0:
+            continue
+        avg_ns = stats.get(name, {}).get("avg_ns")
+        cyc = c.get("GRBM_GUI_ACTIVE", 0.0) / XCDS
+        clock = cyc / avg_ns if avg_ns else float("nan")
+        busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / SIMDS / cyc if cyc else float("nan")
+        hit = c.get("TCC_HIT_sum", 0.0) / max(c.get("TCC_HIT_sum", 0.0) + c.get("TCC_MISS_sum", 0.0), 1.0)
+        lat = c.get("TCP_TCC_READ_REQ_LATENCY_sum", 0.0) / max(c.get("TCP_TCC_READ_REQ_sum", 0.0), 1.0)
+        lines.append(f"| {name} | {avg_ns / 1e3 if avg_ns else float('nan'):.1f} | {c['SQ_INSTS_MFMA']:.4g} | "
+                     f"{busy:.3f} | {clock:.2f} | {hit:.3f} | {lat:.0f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return out_md
+
+
 def _main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -146,7 +195,17 @@ def _main():
     s.add_argument("--command", required=True)
     s.add_argument("--workload", required=True)
     s.add_argument("--copy-mib", type=int, default=1024)
+    c = sub.add_parser("counters")
+    c.add_argument("trace_dir")
+    c.add_argument("out_md")
+    c.add_argument("pass_dirs", nargs="+")
+    c.add_argument("--command", required=True)
+    c.add_argument("--workload", required=True)
     a = ap.parse_args()
+    if a.cmd == "counters":
+        counters_summary(a.pass_dirs, a.trace_dir, a.out_md, a.command, a.workload)
+        print("wrote", a.out_md)
+        return
     summarize(a.trace_dir, a.counter_dir,
               {"FETCH_SIZE": os.path.join(a.copy_dir, "copy_FETCH_SIZE"),
                "WRITE_SIZE": os.path.join(a.copy_dir, "copy_WRITE_SIZE")},
