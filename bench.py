@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the step, time the library's plain copy kernel over "
                          "MIB mebibytes (HBM ceiling; byte-counter calibration)")
+    ap.add_argument("--optimizer", default="muon", choices=["muon", "shampoo"],
+                    help="shampoo: time the Shampoo owner step instead (workload "
+                         "shampoo_decoder_layer_h2048 unless --workload names another Shampoo one)")
     ap.add_argument("--adamw-sweep", action="store_true",
                     help="instead of the step, time adamw_tail_step over n = 2^24 .. 2^28 "
                          "fp32 elements (28 bytes moved per element) and print one JSON line per n")
@@ -174,6 +177,105 @@ def cpu_baseline(wl, args):
                       + f", fp64 numpy, {dt:.2f} s"}
 
 
+SHAMPOO_METRIC = "Shampoo owner-step ms + fp32 TFLOP/s (algorithmic, % fp32 MFMA peak), 1 MI355X"
+
+
+def shampoo_cpu_baseline(wl):
+    """The fp64 oracle's Shampoo step on the workload's smallest matrix (its
+    coupled Newton roots are 8 m^3 flops per step and side, plain matmuls)."""
+    import numpy as np
+    from matrix_optimizers_amd import workloads as wlmod
+    from oracle import shampoo as osh
+    try:
+        import threadpoolctl
+        cores = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    i = min(range(len(wl.matrices)), key=lambda k: wl.matrices[k].rows * wl.matrices[k].cols)
+    W, G, L, R = wlmod.shampoo_inputs(wl, i)
+    hp = wl.hp
+    r, c = G.shape
+    t0 = time.perf_counter()
+    osh.shampoo_step(W, G, L, R, hp.lr, hp.weight_decay, "newton", hp.root_iters)
+    dt = time.perf_counter() - t0
+    f = wlmod.shampoo_flops_algorithmic(r, c, hp.root_iters)
+    flops = sum(f.values())
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"one {r}x{c} matrix of the bucket, {hp.root_iters} coupled Newton steps per root, "
+                      f"fp64 numpy, {dt:.2f} s (same algorithmic flop count as the GPU line)"}
+
+
+def shampoo_main(args):
+    import torch
+    import matrix_optimizers_amd as mo
+    from matrix_optimizers_amd import workloads as wlmod
+    key = args.workload if args.workload in wlmod.SHAMPOO_WORKLOADS else "shampoo_decoder_layer_h2048"
+    wl = wlmod.SHAMPOO_WORKLOADS[key]
+    hp = wl.hp
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] shampoo workload {wl.key}: {len(wl.matrices)} matrices", file=sys.stderr, flush=True)
+    mats = []
+    for i, sp in enumerate(wl.matrices):
+        W = wlmod.torch_normal(wl.seed, i, wlmod.ROLE_W, (sp.rows, sp.cols), wl.w_std, wl.w_dtype, dev)
+        G = wlmod.torch_normal(wl.seed, i, wlmod.ROLE_G, (sp.rows, sp.cols), wl.g_std, wl.g_dtype, dev)
+        L = torch.eye(sp.rows, device=dev) * hp.eps
+        R = torch.eye(sp.cols, device=dev) * hp.eps
+        mats.append((W, G, L, R))
+    step = mo.ShampooOwnerStep(mats, lr=hp.lr, weight_decay=hp.weight_decay, root_iters=hp.root_iters)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup {args.warmup} done; timing {args.steps} steps", file=sys.stderr, flush=True)
+    mo.profile_read()
+    mo.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    mo.profile_enable(False)
+    prof = mo.profile_read()
+    ms = (t1 - t0) * 1e3 / args.steps
+    print(f"[bench] {ms:.3f} ms/step", file=sys.stderr, flush=True)
+    flops = {"stats": 0.0, "root": 0.0, "left": 0.0, "right": 0.0}
+    for sp in wl.matrices:
+        for k, v in wlmod.shampoo_flops_algorithmic(sp.rows, sp.cols, hp.root_iters).items():
+            flops[k] += v
+    total = sum(flops.values())
+    tflops = total / (ms * 1e-3) / 1e12
+    per_launch = {name: {"avg_ms": round(tot / cnt, 5), "launches": int(cnt), "ms_per_step": round(tot / args.steps, 5)}
+                  for name, (tot, cnt) in prof.items() if cnt}
+    out = {
+        "metric": SHAMPOO_METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.key, "matrices": len(wl.matrices),
+                   "shapes": sorted({f"{s.rows}x{s.cols}" for s in wl.matrices}),
+                   "root_iters": hp.root_iters, "eps": hp.eps, "w_dtype": wl.w_dtype,
+                   "g_dtype": wl.g_dtype, "parallelism": "none (one owner's bucket)"},
+        "pct_peak": round(100.0 * tflops / PEAK_F32_TFLOPS, 2),
+        "phases": per_launch,
+    }
+    phase_of = {"stats": "sh_stats", "root": "sh_root", "left": "sh_left", "right": "sh_right"}
+    timed = {k: per_launch[v] for k, v in phase_of.items() if v in per_launch}
+    if timed:
+        dom = max(timed, key=lambda k: timed[k]["ms_per_step"])
+        launches = timed[dom]["launches"] / args.steps
+        achieved = flops[dom] / (timed[dom]["ms_per_step"] * 1e-3) / 1e12
+        out["roofline"] = {"kernel": f"sh_gemm_f32 ({phase_of[dom]})", "bound": "mfma",
+                           "achieved": round(achieved, 2), "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(achieved / PEAK_F32_TFLOPS, 4), "traffic": None,
+                           "algorithmic_per_launch": f"{flops[dom] / launches:.4e} flop (mean over "
+                                                     f"{launches:.0f} launches per step)"}
+    if not args.no_cpu_baseline and not args.profile_only:
+        print("[bench] cpu_baseline (fp64 oracle on host)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = shampoo_cpu_baseline(wl)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -188,6 +290,8 @@ def main():
         return copy_calibration(args)
     if args.adamw_sweep:
         return adamw_sweep(args)
+    if args.optimizer == "shampoo":
+        return shampoo_main(args)
     wl = wlmod.get(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

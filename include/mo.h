@@ -1,5 +1,6 @@
 /*
- * mo.h - C ABI of the MI355X (gfx950) owner-side Muon step and AdamW tail.
+ * mo.h - C ABI of the MI355X (gfx950) owner-side Muon step, AdamW tail and
+ * Shampoo step.
  *
  * Sources, cited by page title and section:
  *   [P] "MatrixFSDP: communication-free matrix optimizers under ZeRO-3 parameter
@@ -169,7 +170,13 @@ const char* mo_status_string(mo_status status);
 #define MO_PHASE_ADAMW    6
 #define MO_PHASE_COPY     7   /* mo_device_copy */
 #define MO_PHASE_UPDATE_LAST 8 /* last Newton-Schulz step: O = a X + B X, W written */
-#define MO_PHASE_COUNT    9
+#define MO_PHASE_SH_LAYOUT   9  /* Shampoo: padded G and G^T */
+#define MO_PHASE_SH_STATS   10  /* Shampoo: L' = L + G G^T, R' = R + G^T G */
+#define MO_PHASE_SH_ROOTPREP 11 /* Shampoo: norms, X_0, H_1 (three small launches) */
+#define MO_PHASE_SH_ROOT    12  /* Shampoo: coupled Newton products */
+#define MO_PHASE_SH_LEFT    13  /* Shampoo: T = H_L G */
+#define MO_PHASE_SH_RIGHT   14  /* Shampoo: W <- decay W - lr T H_R */
+#define MO_PHASE_COUNT    15
 
 /* Enable (1) or disable (0) per-launch timing on the calling thread.  While
  * enabled, every kernel launch is bracketed by HIP events on its own stream;
@@ -186,6 +193,76 @@ mo_status mo_profile_read(double* ms, int64_t* launches);
  * src must not overlap; bytes must be a multiple of 16 and both pointers
  * 16-byte aligned.  Errors: MO_ERR_INVALID_ARG, MO_ERR_ALIAS, MO_ERR_HIP. */
 mo_status mo_device_copy(void* dst, const void* src, size_t bytes, void* stream);
+
+/* ---- Shampoo owner step --------------------------------------------------
+ * [P §5.7]: with every 2D matrix whole on its owner, the owner can run any
+ * single-device matrix optimizer; the paper swaps owner-Muon for Shampoo with
+ * full left / right preconditioners and an inverse fourth root, in float32.
+ * The pages name the method without its formulas; this library's readings:
+ *   statistics  L' = L + G G^T and R' = R + G^T G, the published Shampoo
+ *               update of a matrix (Gupta, Koren and Singer, 2018); the caller
+ *               starts them at eps I and keeps them between steps
+ *   roots       H ~ S'^{-1/4} for S' = L', R': root_iters steps of the coupled
+ *               Newton iteration for the inverse p-th root (Guo and Higham,
+ *               2006), p = 4, with the Frobenius scaling of Anil et al. (2020):
+ *               z = (p + 1) / (2 ||S'||_F), M = z S', H = z^{1/p} I; each step
+ *               X = ((p + 1) I - M) / p, H <- H X, M <- X^p M
+ *   update      W' = (1 - lr wd) W - lr H_L G H_R (decoupled decay, as the
+ *               Muon path of the same owner)
+ * Statistics, roots and products are fp32 (fp32 MFMA, fp32 accumulation); W
+ * and G may be bf16.  There is no momentum, grafting or root-reuse schedule.
+ * The statistics and the X^2, X^4 and M products are symmetric: the library
+ * computes one triangle and mirrors it, and it reads L[j][i] for L'[i][j] (the
+ * same value for the symmetric L it always writes).  The H products are
+ * computed whole and the final H is applied by its rows on both sides
+ * (H_L^T G H_R), which keeps fp32 rounding in the near-null directions of a
+ * rank-deficient S' away from the update.  S' must be positive definite; a
+ * zero S' (eps = 0 and G = 0) gives non-finite results. */
+
+/* One whole matrix with its statistics.
+ *   W          rows x cols, w_dtype, row stride ld_w; updated in place
+ *   G          rows x cols, g_dtype, row stride ld_g; read only
+ *   L          rows x rows fp32, row stride ld_l; updated in place (L')
+ *   R          cols x cols fp32, row stride ld_r; updated in place (R')
+ *   update_out optional (NULL): rows x cols fp32, row stride ld_u, receives
+ *              lr H_L G H_R
+ * rows == 0 or cols == 0 marks an empty shard (skipped; pointers may be NULL).
+ * Strides of 0 mean the natural ones (cols, rows for L, cols for R). */
+typedef struct mo_shampoo_matrix {
+    void*       W;
+    const void* G;
+    float*      L;
+    float*      R;
+    float*      update_out;
+    int64_t     rows, cols;
+    int64_t     ld_w, ld_g, ld_l, ld_r, ld_u;
+    int32_t     w_dtype, g_dtype;
+} mo_shampoo_matrix;
+
+/* lr, weight decay, and the number of coupled Newton steps (1 .. 100). */
+typedef struct mo_shampoo_hparams {
+    float   lr, weight_decay;
+    int32_t root_iters;
+} mo_shampoo_hparams;
+
+/* Bytes of device workspace shampoo_owner_step needs for this bucket: per
+ * matrix three fp32 buffers of r_pad x c_pad, per root seven of m_pad x m_pad
+ * (x_pad = x rounded up to 256), plus the work list and 256 bytes of slack. */
+mo_status shampoo_workspace_bytes(const mo_shampoo_matrix* mats, int32_t n_mats,
+                                  const mo_shampoo_hparams* hp, size_t* bytes);
+
+/* One Shampoo step on every non-empty matrix of the bucket: at most
+ * 3 root_iters + 1 grouped GEMM launches plus four small ones, each covering
+ * every matrix of the bucket.
+ * Workspace, stream and error conventions as muon_owner_step: MO_ERR_INVALID_ARG
+ * (null pointer with numel > 0, negative size, a stride below its row length,
+ * root_iters outside 1 .. 100, non-finite lr or weight decay),
+ * MO_ERR_UNSUPPORTED (dtype not MO_F32/MO_BF16, a side longer than 2^23),
+ * MO_ERR_WORKSPACE_TOO_SMALL, MO_ERR_ALIAS (W, L, R, update_out of any matrix
+ * overlap any tensor of the bucket or the workspace), MO_ERR_HIP. */
+mo_status shampoo_owner_step(const mo_shampoo_matrix* mats, int32_t n_mats,
+                             const mo_shampoo_hparams* hp, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 /* ---- owner planner (host only) --------------------------------------------
  * The step upstream of a bucket: which data-parallel rank owns each role

@@ -27,7 +27,8 @@ DTYPES = {"f32": MO_F32, "float32": MO_F32, "bf16": MO_BF16, "bfloat16": MO_BF16
 
 LR_ADJUST = {"original": 0, "match_rms_adamw": 1, "none": 2}
 
-PHASES = ["momentum", "norm", "gram", "poly", "update", "apply", "adamw", "copy", "update_last"]
+PHASES = ["momentum", "norm", "gram", "poly", "update", "apply", "adamw", "copy", "update_last",
+          "sh_layout", "sh_stats", "sh_rootprep", "sh_root", "sh_left", "sh_right"]
 
 
 class MoError(RuntimeError):
@@ -53,11 +54,28 @@ class MoMuonHParams(ctypes.Structure):
                 ("ns_dtype", ctypes.c_int32)]
 
 
+class MoShampooMatrix(ctypes.Structure):
+    """mo_shampoo_matrix of include/mo.h."""
+    _fields_ = [("W", ctypes.c_void_p), ("G", ctypes.c_void_p), ("L", ctypes.c_void_p),
+                ("R", ctypes.c_void_p), ("update_out", ctypes.c_void_p),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("ld_w", ctypes.c_int64), ("ld_g", ctypes.c_int64), ("ld_l", ctypes.c_int64),
+                ("ld_r", ctypes.c_int64), ("ld_u", ctypes.c_int64),
+                ("w_dtype", ctypes.c_int32), ("g_dtype", ctypes.c_int32)]
+
+
+class MoShampooHParams(ctypes.Structure):
+    """mo_shampoo_hparams of include/mo.h."""
+    _fields_ = [("lr", ctypes.c_float), ("weight_decay", ctypes.c_float),
+                ("root_iters", ctypes.c_int32)]
+
+
 _lib = None
 
 EXPORTS = ["muon_workspace_bytes", "muon_build_worklist", "muon_owner_step", "adamw_tail_step",
            "mo_status_string", "mo_profile_enable", "mo_profile_read", "mo_device_copy",
-           "mo_plan_owners", "mo_plan_score", "mo_plan_layout"]
+           "mo_plan_owners", "mo_plan_score", "mo_plan_layout", "shampoo_workspace_bytes",
+           "shampoo_owner_step"]
 
 ROLE_MATRIX, ROLE_TAIL = 0, 1
 PLAN_POLICIES = {"role_greedy": 0, "scope_greedy": 1, "cost_aware": 2}
@@ -100,9 +118,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                   P(ctypes.c_double), P(ctypes.c_double)]
     lib.mo_plan_layout.argtypes = [P(MoRole), ctypes.c_int32, ctypes.c_int32, P(ctypes.c_int32),
                                    P(ctypes.c_int64)]
+    lib.shampoo_workspace_bytes.argtypes = [P(MoShampooMatrix), ctypes.c_int32, P(MoShampooHParams),
+                                            P(ctypes.c_size_t)]
+    lib.shampoo_owner_step.argtypes = [P(MoShampooMatrix), ctypes.c_int32, P(MoShampooHParams),
+                                       ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     for name in ("muon_workspace_bytes", "muon_build_worklist", "muon_owner_step",
                  "adamw_tail_step", "mo_profile_enable", "mo_profile_read", "mo_device_copy",
-                 "mo_plan_owners", "mo_plan_score", "mo_plan_layout"):
+                 "mo_plan_owners", "mo_plan_score", "mo_plan_layout", "shampoo_workspace_bytes",
+                 "shampoo_owner_step"):
         getattr(lib, name).restype = ctypes.c_int32
     _lib = lib
     return lib
@@ -284,6 +307,114 @@ class MuonOwnerStep:
                                         self.workspace.numel(),
                                         ctypes.c_void_p(_stream_handle(stream))),
                "muon_owner_step")
+
+
+# ---------------------------------------------------------------------------
+# Shampoo
+# ---------------------------------------------------------------------------
+
+def shampoo_hparams(lr: float = 1e-3, weight_decay: float = 0.0, root_iters: int = 20) -> MoShampooHParams:
+    return MoShampooHParams(lr=lr, weight_decay=weight_decay, root_iters=int(root_iters))
+
+
+def shampoo_descriptor(rows: int, cols: int, W: int = 0, G: int = 0, L: int = 0, R: int = 0,
+                       update_out: int = 0, w_dtype="f32", g_dtype="f32", ld_w: int = 0,
+                       ld_g: int = 0, ld_l: int = 0, ld_r: int = 0, ld_u: int = 0) -> MoShampooMatrix:
+    """A raw descriptor from integer addresses (host-side planning and tests)."""
+    code = lambda d: DTYPES[d] if isinstance(d, str) else int(d)
+    return MoShampooMatrix(W=W or None, G=G or None, L=L or None, R=R or None,
+                           update_out=update_out or None, rows=rows, cols=cols, ld_w=ld_w, ld_g=ld_g,
+                           ld_l=ld_l, ld_r=ld_r, ld_u=ld_u, w_dtype=code(w_dtype), g_dtype=code(g_dtype))
+
+
+def shampoo_tensor_descriptor(W, G, L, R, update_out=None) -> MoShampooMatrix:
+    torch = _torch()
+    if W.shape != G.shape:
+        raise ValueError("W and G shapes differ")
+    rows, cols = W.shape
+    if tuple(L.shape) != (rows, rows) or tuple(R.shape) != (cols, cols):
+        raise ValueError("L must be rows x rows and R cols x cols")
+    if L.dtype != torch.float32 or R.dtype != torch.float32:
+        raise TypeError("statistics are float32")
+    dev = W.device
+    for t in (G, L, R) + ((update_out,) if update_out is not None else ()):
+        if t.device != dev:
+            raise ValueError("W, G, L, R, update_out must be on one device")
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a HIP device")
+    if update_out is not None and (update_out.shape != W.shape or update_out.dtype != torch.float32):
+        raise ValueError("update_out must be float32 and shaped like W")
+    return MoShampooMatrix(W=W.data_ptr() or None, G=G.data_ptr() or None, L=L.data_ptr() or None,
+                           R=R.data_ptr() or None,
+                           update_out=(update_out.data_ptr() if update_out is not None else None),
+                           rows=rows, cols=cols, ld_w=_row_stride(W), ld_g=_row_stride(G),
+                           ld_l=_row_stride(L), ld_r=_row_stride(R),
+                           ld_u=_row_stride(update_out) if update_out is not None else 0,
+                           w_dtype=_dtype_code(W), g_dtype=_dtype_code(G))
+
+
+def _sh_array(descs: Sequence[MoShampooMatrix]):
+    n = len(descs)
+    arr = (MoShampooMatrix * max(n, 1))()
+    for i, d in enumerate(descs):
+        arr[i] = d
+    return arr, n
+
+
+def shampoo_workspace_bytes(descs: Sequence[MoShampooMatrix], hp: MoShampooHParams) -> int:
+    lib = load_library()
+    arr, n = _sh_array(descs)
+    out = ctypes.c_size_t(0)
+    _check(lib.shampoo_workspace_bytes(arr, n, ctypes.byref(hp), ctypes.byref(out)),
+           "shampoo_workspace_bytes")
+    return int(out.value)
+
+
+class ShampooOwnerStep:
+    """Reusable Shampoo step over a fixed bucket of (W, G, L, R) tensors:
+    descriptors and workspace are prepared once; ``__call__`` launches the step
+    (W, L, R updated in place) on the current (or given) stream."""
+
+    def __init__(self, mats: Sequence[Tuple], update_out: Optional[Sequence] = None, **hp_kwargs):
+        torch = _torch()
+        self.lib = load_library()
+        self.hp = shampoo_hparams(**hp_kwargs)
+        ups = list(update_out) if update_out is not None else [None] * len(mats)
+        self.descs = [shampoo_tensor_descriptor(W, G, L, R, u) for (W, G, L, R), u in zip(mats, ups)]
+        self.arr, self.n = _sh_array(self.descs)
+        self.bytes = shampoo_workspace_bytes(self.descs, self.hp)
+        dev = mats[0][0].device if mats else torch.device("cuda")
+        self.workspace = torch.empty(self.bytes, dtype=torch.uint8, device=dev)
+        self._keep = (mats, update_out)
+
+    def __call__(self, stream=None) -> None:
+        _check(self.lib.shampoo_owner_step(self.arr, self.n, ctypes.byref(self.hp),
+                                           ctypes.c_void_p(self.workspace.data_ptr()),
+                                           self.workspace.numel(),
+                                           ctypes.c_void_p(_stream_handle(stream))),
+               "shampoo_owner_step")
+
+
+def shampoo_owner_step(mats: Sequence[Tuple], *, update_out: Optional[Sequence] = None,
+                       workspace=None, stream=None, **hp_kwargs) -> None:
+    """One Shampoo step over a bucket of (W, G, L, R) tensors, in place.
+
+    hp_kwargs: lr, weight_decay, root_iters.  L and R are the float32
+    statistics (rows x rows, cols x cols), started by the caller at eps I.
+    """
+    torch = _torch()
+    lib = load_library()
+    hp = shampoo_hparams(**hp_kwargs)
+    ups = list(update_out) if update_out is not None else [None] * len(mats)
+    descs = [shampoo_tensor_descriptor(W, G, L, R, u) for (W, G, L, R), u in zip(mats, ups)]
+    arr, n = _sh_array(descs)
+    need = shampoo_workspace_bytes(descs, hp)
+    if workspace is None:
+        dev = mats[0][0].device if mats else torch.device("cuda")
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check(lib.shampoo_owner_step(arr, n, ctypes.byref(hp), ctypes.c_void_p(workspace.data_ptr()),
+                                  workspace.numel(), ctypes.c_void_p(_stream_handle(stream))),
+           "shampoo_owner_step")
 
 
 def adamw_tail_step(p, g, m, v, step: int, *, lr: float = 1e-3, beta1: float = 0.9,

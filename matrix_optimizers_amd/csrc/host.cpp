@@ -20,28 +20,11 @@
 
 #include "../../include/mo.h"
 #include "mo_kernels.h"
+#include "host_common.h"
 #include "mo_worklist.h"
+#include "tile_dispatch.h"
 
-namespace {
-
-constexpr int64_t kMaxSide = int64_t(1) << 23;   // 32768 tiles of 256: tile indexes fit 16 bits
-
-inline uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
-
-struct Range {
-    uintptr_t lo, hi;   // [lo, hi)
-    int writable;
-};
-
-inline int64_t elem_size(int32_t dt) { return dt == MO_BF16 ? 2 : 4; }
-
-// Byte range touched by a rows x cols row-major matrix with stride ld.
-inline Range matrix_range(const void* p, int64_t rows, int64_t cols, int64_t ld, int64_t es,
-                          int writable) {
-    uintptr_t lo = reinterpret_cast<uintptr_t>(p);
-    uintptr_t hi = lo + uintptr_t(((rows - 1) * ld + cols) * es);
-    return Range{lo, hi, writable};
-}
+namespace mo_host {
 
 // Any overlap between a writable range and any other range?
 bool ranges_conflict(std::vector<Range>& rs) {
@@ -64,7 +47,67 @@ bool ranges_conflict(std::vector<Range>& rs) {
     return false;
 }
 
-inline bool finite(float x) { return std::isfinite(x); }
+
+// ---- pinned staging for the work-list upload -----------------------------------
+// The list is copied host->device on the caller's stream.  The source is a
+// pinned buffer owned by the calling thread and reused by its next call once
+// the previous copy has completed (an event marks that); it lives until the
+// process ends.
+struct Staging {
+    void* buf = nullptr;
+    size_t cap = 0;
+    hipEvent_t ev = nullptr;
+    int dev = -1;
+    bool pending = false;
+};
+namespace {
+thread_local Staging g_stage;
+}  // namespace
+
+hipError_t upload(const void* src, size_t bytes, void* dst, hipStream_t s) {
+    hipError_t e;
+    int dev = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    if (g_stage.pending) {
+        if ((e = hipEventSynchronize(g_stage.ev)) != hipSuccess) return e;
+        g_stage.pending = false;
+    }
+    if (g_stage.dev != dev) {
+        if (g_stage.ev) (void)hipEventDestroy(g_stage.ev);
+        g_stage.ev = nullptr;
+        if ((e = hipEventCreateWithFlags(&g_stage.ev, hipEventDisableTiming)) != hipSuccess) return e;
+        g_stage.dev = dev;
+    }
+    if (g_stage.cap < bytes) {
+        if (g_stage.buf) (void)hipHostFree(g_stage.buf);
+        g_stage.buf = nullptr;
+        g_stage.cap = 0;
+        if ((e = hipHostMalloc(&g_stage.buf, bytes, hipHostMallocDefault)) != hipSuccess) return e;
+        g_stage.cap = bytes;
+    }
+    std::memcpy(g_stage.buf, src, bytes);
+    if ((e = hipMemcpyAsync(dst, g_stage.buf, bytes, hipMemcpyHostToDevice, s)) != hipSuccess)
+        return e;
+    if ((e = hipEventRecord(g_stage.ev, s)) != hipSuccess) return e;
+    g_stage.pending = true;
+    return hipSuccess;
+}
+
+// ---- optional per-launch timing --------------------------------------------------
+struct Timed { int phase; hipEvent_t a, b; };
+thread_local bool g_prof_on = false;
+thread_local std::vector<Timed> g_prof;
+
+bool profiling_on() { return g_prof_on; }
+void profile_push(int phase, hipEvent_t a, hipEvent_t b) { g_prof.push_back(Timed{phase, a, b}); }
+
+}  // namespace mo_host
+
+using namespace mo_host;
+
+namespace {
+
+constexpr int64_t kMaxSide = int64_t(1) << 23;   // 32768 tiles of 256: tile indexes fit 16 bits
 
 mo_status validate_hparams(const mo_muon_hparams* hp) {
     if (!hp) return MO_ERR_INVALID_ARG;
@@ -171,91 +214,22 @@ void build_plan(const mo_matrix* mats, int32_t n, const mo_muon_hparams* hp, Pla
         return ks;
     };
     auto upper = [&](const mo_wl_mat& r) { uint64_t t = r.m_pad / T; return t * (t + 1) / 2; };
-    // Dispatch lists.  A workgroup's XCD is its block index mod 8 (the
-    // hardware deals consecutive workgroups round-robin over the 8 XCDs), and
-    // each XCD runs its share in block order on its 32 CUs.  The tiles of one
-    // matrix are grouped into super-blocks of SB_R tile-rows x SB_C
-    // tile-columns (super-blocks row-major, tiles row-major inside), so one
-    // super-block is what an XCD runs at once and its tiles share 4 row panels
-    // and 8 column panels of the operands in that XCD's L2.  Super-blocks (in
-    // the matrices' descending-work order) go to the XCD with the least work
-    // so far (K-length x tiles; ties to the lowest XCD), split where that XCD
-    // would pass an even share of the total, and the list interleaves the 8
-    // queues: entry 8 j + x is the j-th tile of XCD x, or a pad entry (matrix
-    // index MO_WL_PAD) where that queue is shorter.
-    constexpr uint32_t SB_R = 4, SB_C = 8, NXCD = 8, CU_PER_XCD = 32;
-    auto dispatch = [&](std::vector<mo_wl_item>& out, const std::vector<Key>& mats_order,
-                        bool upper_only, bool k_is_n) {
-        struct Blk { std::vector<mo_wl_item> tiles; uint64_t klen; };
-        std::vector<Blk> blocks;
-        uint64_t total = 0;
+    auto jobs = [&](const std::vector<Key>& mats_order, bool upper_only, bool k_is_n) {
+        std::vector<mo_gemm_job> js;
         for (const Key& k : mats_order) {
             const mo_wl_mat& r = recs[k.idx];
-            const uint32_t tm = r.m_pad / T, tn = upper_only ? tm : r.n_pad / T;
-            const uint64_t klen = k_is_n ? r.n_pad : r.m_pad;
-            for (uint32_t bi = 0; bi < tm; bi += SB_R)
-                for (uint32_t bj = 0; bj < tn; bj += SB_C) {
-                    Blk b{{}, klen};
-                    for (uint32_t a = bi; a < std::min(bi + SB_R, tm); ++a)
-                        for (uint32_t c = bj; c < std::min(bj + SB_C, tn); ++c)
-                            if (!upper_only || a <= c) b.tiles.push_back({k.idx, a, c, 4u});
-                    if (b.tiles.empty()) continue;
-                    total += klen * b.tiles.size();
-                    blocks.push_back(std::move(b));
-                }
+            js.push_back({k.idx, uint32_t(r.m_pad / T), uint32_t((upper_only ? r.m_pad : r.n_pad) / T),
+                          upper_only, k_is_n ? r.n_pad : r.m_pad});
         }
-        // A block goes whole to the least-loaded queue while that queue stays
-        // under the even share; otherwise the queue takes only what fills it
-        // (at least one tile) and the rest moves on to the next least-loaded.
-        const uint64_t target = (total + NXCD - 1) / NXCD;
-        std::vector<std::vector<mo_wl_item>> q(NXCD);
-        uint64_t load[NXCD] = {0};
-        for (const Blk& b : blocks) {
-            size_t i = 0;
-            while (i < b.tiles.size()) {
-                uint32_t x = 0;
-                for (uint32_t y = 1; y < NXCD; ++y)
-                    if (load[y] < load[x]) x = y;
-                const size_t rest = b.tiles.size() - i;
-                size_t take = rest;
-                if (load[x] < target) {
-                    const uint64_t fit = (target - load[x] + b.klen - 1) / b.klen;
-                    take = std::min<size_t>(rest, std::max<uint64_t>(1, fit));
-                }
-                q[x].insert(q[x].end(), b.tiles.begin() + i, b.tiles.begin() + i + take);
-                load[x] += b.klen * take;
-                i += take;
-            }
-        }
-        // Narrow tiles where full ones would leave an XCD's CUs idle: a queue of
-        // n <= 32 tiles (one partial round) has every tile split, and a longer
-        // queue the n % 32 tiles of its last round, into S = 4 quarter-width
-        // or S = 2 half-width tiles, the largest S that still fits the 32 CUs
-        // (none if even halves do not).  Split tiles keep their place in the
-        // queue, the S parts in column order.
-        for (auto& v : q) {
-            const size_t n = v.size();
-            if (n == 0) continue;
-            const size_t first = n <= CU_PER_XCD ? 0 : n - n % CU_PER_XCD;
-            const size_t r = n - first;
-            const uint32_t S = r == 0 ? 1 : 4 * r <= CU_PER_XCD ? 4 : 2 * r <= CU_PER_XCD ? 2 : 1;
-            if (S == 1) continue;
-            std::vector<mo_wl_item> w(v.begin(), v.begin() + first);
-            for (size_t k = first; k < n; ++k)
-                for (uint32_t p = 0; p < S; ++p) w.push_back({v[k].mat, v[k].ti, v[k].tj * S + p, 4 / S});
-            v.swap(w);
-        }
-        size_t len = 0;
-        for (const auto& v : q) len = std::max(len, v.size());
-        for (size_t j = 0; j < len; ++j)
-            for (uint32_t x = 0; x < NXCD; ++x)
-                out.push_back(j < q[x].size() ? q[x][j] : mo_wl_item{MO_WL_PAD, 0, 0, 0});
+        return js;
     };
+    // Dispatch lists: tiles to XCD queues (tile_dispatch.h).
     std::vector<mo_wl_item> gram, poly, upd;
-    dispatch(gram, order([&](const mo_wl_mat& r) { return upper(r) * r.n_pad; }), true, true);
-    dispatch(poly, order([&](const mo_wl_mat& r) { return upper(r) * r.m_pad; }), true, false);
-    dispatch(upd, order([&](const mo_wl_mat& r) {
-                 return uint64_t(r.m_pad / T) * (r.n_pad / T) * r.m_pad; }), false, false);
+    mo_dispatch_tiles(jobs(order([&](const mo_wl_mat& r) { return upper(r) * r.n_pad; }), true, true), gram);
+    mo_dispatch_tiles(jobs(order([&](const mo_wl_mat& r) { return upper(r) * r.m_pad; }), true, false), poly);
+    mo_dispatch_tiles(jobs(order([&](const mo_wl_mat& r) {
+                               return uint64_t(r.m_pad / T) * (r.n_pad / T) * r.m_pad; }), false, false),
+                      upd);
 
     mo_wl_header h;
     std::memset(&h, 0, sizeof(h));
@@ -307,68 +281,6 @@ void build_plan(const mo_matrix* mats, int32_t n, const mo_muon_hparams* hp, Pla
         std::memcpy(plan->bytes.data() + h.poly_offset, poly.data(), poly.size() * sizeof(mo_wl_item));
     if (!upd.empty())
         std::memcpy(plan->bytes.data() + h.upd_offset, upd.data(), upd.size() * sizeof(mo_wl_item));
-}
-
-// ---- pinned staging for the work-list upload -----------------------------------
-// The list is copied host->device on the caller's stream.  The source is a
-// pinned buffer owned by the calling thread and reused by its next call once
-// the previous copy has completed (an event marks that); it lives until the
-// process ends.
-struct Staging {
-    void* buf = nullptr;
-    size_t cap = 0;
-    hipEvent_t ev = nullptr;
-    int dev = -1;
-    bool pending = false;
-};
-thread_local Staging g_stage;
-
-hipError_t upload(const void* src, size_t bytes, void* dst, hipStream_t s) {
-    hipError_t e;
-    int dev = 0;
-    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
-    if (g_stage.pending) {
-        if ((e = hipEventSynchronize(g_stage.ev)) != hipSuccess) return e;
-        g_stage.pending = false;
-    }
-    if (g_stage.dev != dev) {
-        if (g_stage.ev) (void)hipEventDestroy(g_stage.ev);
-        g_stage.ev = nullptr;
-        if ((e = hipEventCreateWithFlags(&g_stage.ev, hipEventDisableTiming)) != hipSuccess) return e;
-        g_stage.dev = dev;
-    }
-    if (g_stage.cap < bytes) {
-        if (g_stage.buf) (void)hipHostFree(g_stage.buf);
-        g_stage.buf = nullptr;
-        g_stage.cap = 0;
-        if ((e = hipHostMalloc(&g_stage.buf, bytes, hipHostMallocDefault)) != hipSuccess) return e;
-        g_stage.cap = bytes;
-    }
-    std::memcpy(g_stage.buf, src, bytes);
-    if ((e = hipMemcpyAsync(dst, g_stage.buf, bytes, hipMemcpyHostToDevice, s)) != hipSuccess)
-        return e;
-    if ((e = hipEventRecord(g_stage.ev, s)) != hipSuccess) return e;
-    g_stage.pending = true;
-    return hipSuccess;
-}
-
-// ---- optional per-launch timing --------------------------------------------------
-struct Timed { int phase; hipEvent_t a, b; };
-thread_local bool g_prof_on = false;
-thread_local std::vector<Timed> g_prof;
-
-template <typename F>
-hipError_t timed_launch(int phase, hipStream_t s, F&& launch) {
-    if (!g_prof_on) return launch();
-    Timed t{phase, nullptr, nullptr};
-    hipError_t e;
-    if ((e = hipEventCreate(&t.a)) != hipSuccess) return e;
-    if ((e = hipEventCreate(&t.b)) != hipSuccess) return e;
-    if ((e = hipEventRecord(t.a, s)) != hipSuccess) return e;
-    hipError_t le = launch();
-    if ((e = hipEventRecord(t.b, s)) != hipSuccess) return e;
-    g_prof.push_back(t);
-    return le;
 }
 
 }  // namespace

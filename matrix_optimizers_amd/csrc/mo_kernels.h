@@ -22,3 +22,9 @@ hipError_t mo_launch_adamw(float* p, const float* g, float* m, float* v, int64_t
                            float beta1, float beta2, float step_size, float inv_sqrt_bc2,
                            float eps, hipStream_t s);
 hipError_t mo_launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
+
+// Shampoo step (shampoo_kernels.hip); `ws` holds the Shampoo work list.
+struct mo_sh_header;
+hipError_t mo_launch_sh_layout(const mo_sh_header& h, uint8_t* ws, hipStream_t s);
+hipError_t mo_launch_sh_rootprep(const mo_sh_header& h, uint8_t* ws, hipStream_t s);
+hipError_t mo_launch_sh_gemm(const mo_sh_header& h, uint8_t* ws, int list, int k, hipStream_t s);

@@ -201,6 +201,74 @@ def get(key: str) -> Workload:
 
 
 # ----------------------------------------------------------------------------
+# Shampoo on the owners (§5.7)
+# ----------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class ShampooHP:
+    """Shampoo settings.  The pages run Shampoo on the owners in float32 (§5.7)
+    without printing its settings; the plain reading used here: lr 1e-3 (the
+    paper's Muon timing lr), no weight decay, statistics started at eps I with
+    eps = 1e-6 (about 1e-4 of the largest eigenvalue of G G^T for N(0, 1e-3^2)
+    gradients with a side of 1024 to 2048), and 20 coupled Newton steps per
+    inverse root."""
+    lr: float = 1e-3
+    weight_decay: float = 0.0
+    eps: float = 1e-6
+    root_iters: int = 20
+
+
+@dataclasses.dataclass(frozen=True)
+class ShampooWorkload:
+    key: str
+    seed: int
+    matrices: Tuple[MatrixSpec, ...]
+    w_dtype: str = F32
+    g_dtype: str = F32
+    hp: ShampooHP = ShampooHP()
+    w_std: float = 0.02
+    g_std: float = 1e-3
+    description: str = ""
+
+
+SHAMPOO_WORKLOADS = {
+    "shampoo_mixed_small": ShampooWorkload(
+        key="shampoo_mixed_small", seed=11,
+        matrices=(MatrixSpec(256, 512, "a"), MatrixSpec(300, 200, "b"), MatrixSpec(77, 1000, "c"),
+                  MatrixSpec(513, 513, "d"), MatrixSpec(1, 300, "e")),
+        description="five small fp32 matrices with ragged sides (tiles, tails and a single row)"),
+    "shampoo_decoder_layer_h2048": ShampooWorkload(
+        key="shampoo_decoder_layer_h2048", seed=12, matrices=tuple(_decoder_layer(2048, 5632, 2048)),
+        description="one decoder-layer owner bucket, hidden 2048, FFN 5632, fp32 weights and gradients"),
+}
+
+
+def shampoo_inputs(wl: ShampooWorkload, index: int):
+    """(W, G) for matrix `index` (fp32 arrays holding the storage dtype's values)
+    and the initial statistics eps I_rows, eps I_cols."""
+    spec = wl.matrices[index]
+    shape = (spec.rows, spec.cols)
+    W = normal(wl.seed, index, ROLE_W, shape, wl.w_std, wl.w_dtype)
+    G = normal(wl.seed, index, ROLE_G, shape, wl.g_std, wl.g_dtype)
+    L = (wl.hp.eps * np.eye(spec.rows)).astype(np.float32)
+    R = (wl.hp.eps * np.eye(spec.cols)).astype(np.float32)
+    return W, G, L, R
+
+
+def shampoo_flops_algorithmic(rows: int, cols: int, root_iters: int) -> dict:
+    """Per product kind, the flops one step spends on one matrix as the library
+    computes it: one triangle of a symmetric product (m^3 for an m x m root
+    product, m^2 k for a statistics product with K extent k), 2 m n k for a
+    full one.  Per root and coupled Newton step after the first: S2, S4 and M
+    symmetric, H full (5 m^3)."""
+    out = {"stats": float(rows) ** 2 * cols + float(cols) ** 2 * rows,
+           "root": 0.0, "left": 2.0 * rows * rows * cols, "right": 2.0 * rows * cols * cols}
+    for m in (rows, cols):
+        out["root"] += 5.0 * (root_iters - 1) * float(m) ** 3
+    return out
+
+
+# ----------------------------------------------------------------------------
 # value generation
 # ----------------------------------------------------------------------------
 
