@@ -227,8 +227,9 @@ def shampoo_main(args):
         step()
     torch.cuda.synchronize()
     print(f"[bench] warmup {args.warmup} done; timing {args.steps} steps", file=sys.stderr, flush=True)
+    timing = not args.no_phase_timing
     mo.profile_read()
-    mo.profile_enable(True)
+    mo.profile_enable(timing)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -265,11 +266,20 @@ def shampoo_main(args):
         dom = max(timed, key=lambda k: timed[k]["ms_per_step"])
         launches = timed[dom]["launches"] / args.steps
         achieved = flops[dom] / (timed[dom]["ms_per_step"] * 1e-3) / 1e12
+        # HBM bytes per launch of this role from the committed rocprofv3 summary,
+        # only if it was taken on the current kernel sources
+        from matrix_optimizers_amd import profiling
+        tr = profiling.read_traffic(os.path.join(ROOT, "profiles"), wl.key, f"sh_gemm[{dom}]")
         out["roofline"] = {"kernel": f"sh_gemm_f32 ({phase_of[dom]})", "bound": "mfma",
                            "achieved": round(achieved, 2), "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s",
-                           "frac": round(achieved / PEAK_F32_TFLOPS, 4), "traffic": None,
+                           "frac": round(achieved / PEAK_F32_TFLOPS, 4),
+                           "traffic": None if tr is None else round(tr["read_bytes"] + tr["write_bytes"]),
                            "algorithmic_per_launch": f"{flops[dom] / launches:.4e} flop (mean over "
                                                      f"{launches:.0f} launches per step)"}
+        if tr is not None:
+            out["roofline"]["traffic_detail"] = {
+                "read_bytes": round(tr["read_bytes"]), "write_bytes": round(tr["write_bytes"]),
+                "profile": tr["source"], "profile_avg_ms": round(tr["avg_ns"] / 1e6, 5)}
     if not args.no_cpu_baseline and not args.profile_only:
         print("[bench] cpu_baseline (fp64 oracle on host)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = shampoo_cpu_baseline(wl)

@@ -26,7 +26,9 @@ from typing import Dict, Optional
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ["csrc/ns_kernels.hip", "csrc/tail_kernels.hip", "csrc/device_common.h",
-                  "csrc/mo_worklist.h", "csrc/host.cpp"]
+                  "csrc/mo_worklist.h", "csrc/host.cpp", "csrc/gemm_core.h", "csrc/tile_dispatch.h",
+                  "csrc/host_common.h", "csrc/shampoo_kernels.hip", "csrc/sh_worklist.h",
+                  "csrc/shampoo.cpp"]
 
 
 def sources_sha256() -> str:
@@ -37,8 +39,15 @@ def sources_sha256() -> str:
     return h.hexdigest()
 
 
+SH_KERNELS = (("sh_gemm_f32", "sh_gemm"), ("sh_layout_kernel", "sh_layout"), ("sh_sumsq_kernel", "sh_sumsq"),
+              ("sh_norm_kernel", "sh_norm"), ("sh_init_kernel", "sh_init"))
+
+
 def short_name(kernel: str) -> Optional[str]:
     """Library kernel -> phase name (None for kernels that are not ours)."""
+    for key, name in SH_KERNELS:
+        if key in kernel:
+            return name
     m = re.search(r"\b(gram|poly|update_last|update)_(bf16|f32)\b", kernel)
     if m:
         return f"{m.group(1)}[{m.group(2)}]"
@@ -51,13 +60,39 @@ def short_name(kernel: str) -> Optional[str]:
     return None
 
 
+def shampoo_roles(names):
+    """The Shampoo GEMM launches of a dispatch sequence, by role: in each step
+    (which starts with the layout launch) the first GEMM launch forms the
+    statistics, the last two are the left and right products, the others
+    are coupled Newton (root) products.  Returns one name per entry."""
+    out = list(names)
+    step = []
+    def close():
+        for n, i in enumerate(step):
+            out[i] = ("sh_gemm[stats]" if n == 0 else "sh_gemm[right]" if n == len(step) - 1
+                      else "sh_gemm[left]" if n == len(step) - 2 else "sh_gemm[root]")
+    for i, n in enumerate(names):
+        if n == "sh_layout":
+            close()
+            step = []
+        elif n == "sh_gemm":
+            step.append(i)
+    close()
+    return out
+
+
+def _ordered(rows, key):
+    rows = sorted(rows, key=lambda r: float(r[key]))
+    names = shampoo_roles([short_name(r["Kernel_Name"]) for r in rows])
+    return list(zip(rows, names))
+
+
 def kernel_stats(trace_dir: str) -> Dict[str, dict]:
     """Per-phase calls / total / average (ns) from the kernel trace."""
     files = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
     out: Dict[str, dict] = defaultdict(lambda: {"calls": 0, "total_ns": 0.0})
     for f in files:
-        for r in csv.DictReader(open(f)):
-            name = short_name(r["Kernel_Name"])
+        for r, name in _ordered(list(csv.DictReader(open(f))), "Start_Timestamp"):
             if name is None:
                 continue
             d = out[name]
@@ -72,10 +107,8 @@ def counter_means(pass_dir: str, counter: str) -> Dict[str, float]:
     """Mean value of `counter` per dispatch, per phase."""
     vals: Dict[str, list] = defaultdict(list)
     for f in glob.glob(os.path.join(pass_dir, "**", "*counter_collection.csv"), recursive=True):
-        for r in csv.DictReader(open(f)):
-            if r["Counter_Name"] != counter:
-                continue
-            name = short_name(r["Kernel_Name"])
+        rows = [r for r in csv.DictReader(open(f)) if r["Counter_Name"] == counter]
+        for r, name in _ordered(rows, "Dispatch_Id"):
             if name is not None:
                 vals[name].append(float(r["Counter_Value"]))
     return {k: sum(v) / len(v) for k, v in vals.items()}
