@@ -20,6 +20,9 @@ AdamW step on the packed non-2D tail):
   muon.muon_bucket       the owner step over a bucket            [P §3, §4.4]
   adamw.adamw_step       decoupled-decay Adam on the tail        [P §3, §5.1]
   worklist.build         byte-exact twin of the host work list   (no page defines it)
+  planner.plan/score     owner planner and its bandwidth model    [P §4.1, §4.2]
+  shampoo.shampoo_step   Shampoo on the owners (coupled Newton)   [P §5.7]
+  soap.soap_step         SOAP on the owners (Adam, eigenbasis)    [P §5.7]
 
 Every function is pinned by tests under ``tests/`` against something other than
 itself (SVD brute force, closed forms, invariants, library witnesses); the pins are
