@@ -42,14 +42,18 @@ hipError_t upload(const void* src, size_t bytes, void* dst, hipStream_t s);
 // thread, and the record of one launch bracketed by events a and b.
 bool profiling_on();
 void profile_push(int phase, hipEvent_t a, hipEvent_t b);
+// A timing event on the current device, reused from the thread's pool when
+// one is free (events return to the pool when mo_profile_read has read them),
+// so timing adds two event records per launch and no event creation.
+hipError_t profile_event(hipEvent_t* ev);
 
 template <typename F>
 hipError_t timed_launch(int phase, hipStream_t s, F&& launch) {
     if (!profiling_on()) return launch();
     hipEvent_t a = nullptr, b = nullptr;
     hipError_t e;
-    if ((e = hipEventCreate(&a)) != hipSuccess) return e;
-    if ((e = hipEventCreate(&b)) != hipSuccess) return e;
+    if ((e = profile_event(&a)) != hipSuccess) return e;
+    if ((e = profile_event(&b)) != hipSuccess) return e;
     if ((e = hipEventRecord(a, s)) != hipSuccess) return e;
     hipError_t le = launch();
     if ((e = hipEventRecord(b, s)) != hipSuccess) return e;
