@@ -138,7 +138,9 @@ mo_status muon_build_worklist(const mo_matrix* mats, int32_t n_mats,
  * Errors: MO_ERR_INVALID_ARG (null pointer with numel > 0, negative size,
  * ld < cols, ns_steps < 0, non-finite hyperparameter, eps <= 0, unknown
  * lr_adjust), MO_ERR_UNSUPPORTED (dtype not MO_F32/MO_BF16, a side longer than
- * 2^23), MO_ERR_WORKSPACE_TOO_SMALL, MO_ERR_ALIAS (W, M, update_out of any
+ * 2^23, more than 2^36 elements in one matrix, more than 2^26 tiles of 256 x 256
+ * in the bucket), MO_ERR_WORKSPACE_TOO_SMALL,
+ * MO_ERR_ALIAS (W, M, update_out of any
  * matrix overlap any tensor of the bucket or the workspace), MO_ERR_HIP. */
 mo_status muon_owner_step(const mo_matrix* mats, int32_t n_mats,
                           const mo_muon_hparams* hp, void* workspace,
@@ -257,8 +259,10 @@ mo_status shampoo_workspace_bytes(const mo_shampoo_matrix* mats, int32_t n_mats,
  * Workspace, stream and error conventions as muon_owner_step: MO_ERR_INVALID_ARG
  * (null pointer with numel > 0, negative size, a stride below its row length,
  * root_iters outside 1 .. 100, non-finite lr or weight decay),
- * MO_ERR_UNSUPPORTED (dtype not MO_F32/MO_BF16, a side longer than 2^23),
- * MO_ERR_WORKSPACE_TOO_SMALL, MO_ERR_ALIAS (W, L, R, update_out of any matrix
+ * MO_ERR_UNSUPPORTED (dtype not MO_F32/MO_BF16, a side longer than 2^16: each
+ * side is also a root's; more than 2^26 tiles of 256 x 256 over the bucket's
+ * roots and matrices), MO_ERR_WORKSPACE_TOO_SMALL, MO_ERR_ALIAS (W, L, R,
+ * update_out of any matrix
  * overlap any tensor of the bucket or the workspace), MO_ERR_HIP. */
 mo_status shampoo_owner_step(const mo_shampoo_matrix* mats, int32_t n_mats,
                              const mo_shampoo_hparams* hp, void* workspace,

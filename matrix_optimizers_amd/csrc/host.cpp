@@ -31,6 +31,9 @@ using namespace mo_host;
 namespace {
 
 constexpr int64_t kMaxSide = int64_t(1) << 23;   // 32768 tiles of 256: tile indexes fit 16 bits
+// Elements per matrix: bounds the work list (at most 2^20 tiles per phase and
+// matrix) and the host memory the planner needs to build it.
+constexpr int64_t kMaxElems = int64_t(1) << 36;
 
 mo_status validate_hparams(const mo_muon_hparams* hp) {
     if (!hp) return MO_ERR_INVALID_ARG;
@@ -46,10 +49,15 @@ mo_status validate_hparams(const mo_muon_hparams* hp) {
     return MO_OK;
 }
 
+// Tiles of 256 x 256 in all Update products of a bucket (the largest phase):
+// bounds the work list and the host memory that builds it.
+constexpr int64_t kMaxTiles = int64_t(1) << 26;
+
 // Checks every descriptor; collects the byte ranges of live tensors.
 mo_status validate_mats(const mo_matrix* mats, int32_t n, std::vector<Range>* ranges) {
     if (n < 0) return MO_ERR_INVALID_ARG;
     if (n > 0 && !mats) return MO_ERR_INVALID_ARG;
+    int64_t tiles = 0;
     for (int32_t i = 0; i < n; ++i) {
         const mo_matrix& d = mats[i];
         if (d.rows < 0 || d.cols < 0) return MO_ERR_INVALID_ARG;
@@ -63,6 +71,9 @@ mo_status validate_mats(const mo_matrix* mats, int32_t n, std::vector<Range>* ra
         if (ldw < d.cols || ldg < d.cols || ldm < d.cols || ldu < d.cols)
             return MO_ERR_INVALID_ARG;
         if (d.rows > kMaxSide || d.cols > kMaxSide) return MO_ERR_UNSUPPORTED;
+        if (d.rows * d.cols > kMaxElems) return MO_ERR_UNSUPPORTED;
+        tiles += ((d.rows + 255) / 256) * ((d.cols + 255) / 256);
+        if (tiles > kMaxTiles) return MO_ERR_UNSUPPORTED;
         if (ranges) {
             ranges->push_back(matrix_range(d.W, d.rows, d.cols, ldw, elem_size(d.w_dtype), 1));
             ranges->push_back(matrix_range(d.G, d.rows, d.cols, ldg, elem_size(d.g_dtype), 0));

@@ -30,8 +30,14 @@ using namespace mo_host;
 
 namespace {
 
-constexpr int64_t kMaxSide = int64_t(1) << 23;   // tile indexes and 16-row load offsets fit 32 bits
+// Each side is also the side of a root, whose seven m_pad x m_pad fp32 buffers
+// take 7 * 4 * m_pad^2 bytes (120 GB at 65536) and whose upper tiles the
+// planner lists on the host.
+constexpr int64_t kMaxSide = int64_t(1) << 16;
 constexpr int32_t kMaxIters = 100;
+// Tiles of 256 x 256 over all roots and matrices of a bucket: bounds the work
+// lists and the host memory that builds them.
+constexpr int64_t kMaxTiles = int64_t(1) << 26;
 
 mo_status validate_hp(const mo_shampoo_hparams* hp) {
     if (!hp) return MO_ERR_INVALID_ARG;
@@ -50,6 +56,7 @@ Strides strides(const mo_shampoo_matrix& d) {
 mo_status validate(const mo_shampoo_matrix* mats, int32_t n, std::vector<Range>* ranges) {
     if (n < 0) return MO_ERR_INVALID_ARG;
     if (n > 0 && !mats) return MO_ERR_INVALID_ARG;
+    int64_t tiles = 0;
     for (int32_t i = 0; i < n; ++i) {
         const mo_shampoo_matrix& d = mats[i];
         if (d.rows < 0 || d.cols < 0) return MO_ERR_INVALID_ARG;
@@ -62,6 +69,9 @@ mo_status validate(const mo_shampoo_matrix* mats, int32_t n, std::vector<Range>*
         if (s.w < d.cols || s.g < d.cols || s.l < d.rows || s.r < d.cols || s.u < d.cols)
             return MO_ERR_INVALID_ARG;
         if (d.rows > kMaxSide || d.cols > kMaxSide) return MO_ERR_UNSUPPORTED;
+        const int64_t tr = (d.rows + 255) / 256, tc = (d.cols + 255) / 256;
+        tiles += tr * tr + tc * tc + tr * tc;
+        if (tiles > kMaxTiles) return MO_ERR_UNSUPPORTED;
         if (ranges) {
             ranges->push_back(matrix_range(d.W, d.rows, d.cols, s.w, elem_size(d.w_dtype), 1));
             ranges->push_back(matrix_range(d.G, d.rows, d.cols, s.g, elem_size(d.g_dtype), 0));

@@ -106,6 +106,7 @@ def test_null_arguments():
     (dict(ld_u=1, update_out=BASE + 50 * GiB), INVALID), (dict(ld_w=-1), INVALID),
     (dict(w_dtype=3), UNSUPPORTED), (dict(g_dtype=9), UNSUPPORTED),
     (dict(rows=(1 << 23) + 1, cols=1), UNSUPPORTED),
+    (dict(rows=1 << 23, cols=1 << 14), UNSUPPORTED),       # 2^37 elements
 ])
 def test_bad_descriptors(d, code):
     args = dict(rows=64, cols=96)
@@ -189,3 +190,16 @@ def test_profile_read_empty():
     assert lib.mo_profile_read(ms, cnt) == OK
     assert lib.mo_profile_read(None, cnt) == INVALID
     assert sum(cnt) == 0
+
+
+def test_planning_limits_fail_fast():
+    """Sizes whose work list would not fit host memory are refused before any
+    planning (the size query returns at once)."""
+    import time
+    t0 = time.perf_counter()
+    with pytest.raises(mo.MoError):
+        mo.workspace_bytes([desc(1 << 23, 1 << 23)], mo.hparams())
+    many = [desc(1 << 17, 1 << 17, k=k) for k in range(300)]  # 300 x 2^18 tiles > 2^26
+    with pytest.raises(mo.MoError):
+        mo.workspace_bytes(many, mo.hparams())
+    assert time.perf_counter() - t0 < 5

@@ -56,6 +56,7 @@ def test_null_arguments():
     (dict(ld_r=95), INVALID), (dict(ld_u=1, update_out=BASE + 150 * GiB), INVALID),
     (dict(ld_r=-1), INVALID), (dict(w_dtype=3), UNSUPPORTED), (dict(g_dtype=9), UNSUPPORTED),
     (dict(rows=(1 << 23) + 1, cols=1), UNSUPPORTED),
+    (dict(rows=1, cols=(1 << 16) + 1), UNSUPPORTED),        # a root side beyond 2^16
 ])
 def test_bad_descriptors(d, code):
     args = dict(rows=64, cols=96)
@@ -84,3 +85,16 @@ def test_workspace_size_and_check():
     assert bufs < need < bufs + (1 << 20)   # plus work list, partials, scales and slack
     assert step(d, ws_bytes=need - 1) == WS_SMALL
     assert step(d, ws=0, ws_bytes=need) == WS_SMALL
+
+
+def test_planning_limits_fail_fast():
+    """A 1 x 2^16 matrix (a 2^16-sided right root) still plans quickly; a
+    bucket whose roots exceed 2^26 tiles is refused before planning."""
+    import time
+    t0 = time.perf_counter()
+    need = mo.shampoo_workspace_bytes([desc(1, 1 << 16)], mo.shampoo_hparams())
+    assert need > 7 * 4 * (1 << 32)
+    many = [desc(1 << 16, 1 << 16, k=k) for k in range(400)]   # 400 x 3 x 2^16 tiles > 2^26
+    with pytest.raises(mo.MoError):
+        mo.shampoo_workspace_bytes(many, mo.shampoo_hparams())
+    assert time.perf_counter() - t0 < 30
