@@ -240,6 +240,14 @@ SHAMPOO_WORKLOADS = {
     "shampoo_decoder_layer_h2048": ShampooWorkload(
         key="shampoo_decoder_layer_h2048", seed=12, matrices=tuple(_decoder_layer(2048, 5632, 2048)),
         description="one decoder-layer owner bucket, hidden 2048, FFN 5632, fp32 weights and gradients"),
+    # One layer of the paper's model (§5.1: hidden 4096, intermediate 16384;
+    # 4 square attention matrices, MLP up and down), the shapes of its Shampoo
+    # run (§5.7); the up/down roots are 16384-sided.
+    "shampoo_paper_layer": ShampooWorkload(
+        key="shampoo_paper_layer", seed=13,
+        matrices=(MatrixSpec(4096, 4096, "q"), MatrixSpec(4096, 4096, "k"), MatrixSpec(4096, 4096, "v"),
+                  MatrixSpec(4096, 4096, "o"), MatrixSpec(16384, 4096, "up"), MatrixSpec(4096, 16384, "down")),
+        description="one layer of the paper's hidden-4096 / intermediate-16384 model, fp32"),
 }
 
 

@@ -193,3 +193,33 @@ def test_decoder_layer_full_size(gpu):
         d = rel(to_host(U) / f32(hp.lr), svd_route_update(G64, f32(hp.eps), hp.root_iters))
         print(spec.name, spec.rows, spec.cols, "delta rel", d)
         assert d <= TOL_U, spec
+
+
+def test_paper_layer_full_size(gpu):
+    """One layer of the paper's model (roots of side 4096 and 16384): sampled
+    statistics entries of every matrix, a finite update everywhere, and the
+    first 4096 x 4096 matrix's update against the SVD route."""
+    import torch
+    wl = wlmod.SHAMPOO_WORKLOADS["shampoo_paper_layer"]
+    hp = wl.hp
+    host = [wlmod.shampoo_inputs(wl, i) for i in range(len(wl.matrices))]
+    mats = [tuple(to_dev(x, "f32", gpu) for x in h) for h in host]
+    ups = [torch.empty(h[0].shape, dtype=torch.float32, device=gpu) for h in host]
+    mo.shampoo_owner_step(mats, update_out=ups, lr=hp.lr, weight_decay=hp.weight_decay, root_iters=hp.root_iters)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    for (W, G, L, R), (_, _, Ld, Rd), U, spec in zip(host, mats, ups, wl.matrices):
+        assert bool(torch.isfinite(U).all()), spec.name
+        G64 = G.astype(np.float64)
+        for S, n, M in ((Ld, G.shape[0], G64), (Rd, G.shape[1], G64.T)):
+            idx = rng.integers(0, n, size=(48, 2))
+            idx[32:, 1] = idx[32:, 0]
+            got = S[idx[:, 0], idx[:, 1]].cpu().numpy().astype(np.float64)
+            a, b = M[idx[:, 0]], M[idx[:, 1]]
+            diag = np.float32(hp.eps) * (idx[:, 0] == idx[:, 1])
+            want = np.einsum("ij,ij->i", a, b) + diag
+            scale = np.einsum("ij,ij->i", np.abs(a), np.abs(b)) + diag
+            assert np.all(np.abs(got - want) <= 4 * np.sqrt(M.shape[1]) * 2.0 ** -24 * scale), spec.name
+    d = rel(to_host(ups[0]) / f32(hp.lr), svd_route_update(host[0][1].astype(np.float64), f32(hp.eps), hp.root_iters))
+    print("q 4096 x 4096 delta rel", d)
+    assert d <= TOL_U
