@@ -155,3 +155,11 @@ def test_head_scale_invariance_bit_exact(gpu):
     _, b, ub = run_bucket(wl, gpu, mats=[(W.clone(), (G.float() * 4).to(G.dtype), M * 4)])
     assert torch.equal(a[0][0], b[0][0])
     assert torch.equal(ua[0], ub[0])
+
+
+def test_paper_owner_share_sampled(gpu):
+    """One rank's share of the paper's 16-layer timing model with the paper's
+    settings (K = 2, momentum 0.5, match_rms_adamw): the oracle on a 4096 x 4096
+    matrix and on both MLP matrices (16384 x 4096 tall, 4096 x 16384 wide)."""
+    wl = wlmod.get("paper_owner_share")
+    sampled_parity(wl, gpu, [0, 4, 5])
