@@ -111,7 +111,9 @@ __global__ __launch_bounds__(MOM_THREADS) void momentum_kernel(uint8_t* ws, floa
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int q = threadIdx.x + MOM_THREADS * i;
-        const int c = q & 63, rr = q >> 6;
+        // 8 consecutive threads write one whole 128-byte row of the transposed
+        // tile (LDS bank of element e: rr * 8 + c + e, distinct over a wave)
+        const int c = q >> 3, rr = q & 7;
         f32x8 o;
 #pragma unroll
         for (int e = 0; e < 8; ++e) o.v[e] = tile[rr * 8 + e][c];
