@@ -78,7 +78,9 @@ __global__ __launch_bounds__(SH_THREADS) void sh_layout_kernel(uint8_t* ws) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int q = threadIdx.x + SH_THREADS * i;
-        const int c = q & 63, rr = q >> 6;
+        // 8 consecutive threads write 256 contiguous bytes of one row of G^T
+        // (LDS bank of element e: rr * 8 + c + e, distinct over a wave)
+        const int c = q >> 3, rr = q & 7;
         f32x8 o;
 #pragma unroll
         for (int e = 0; e < 8; ++e) o.v[e] = tile[rr * 8 + e][c];
