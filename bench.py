@@ -26,6 +26,7 @@ METRIC = "Muon owner-step ms + Newton–Schulz TFLOP/s (% bf16 MFMA peak), 1 MI3
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3         # MI355X fp32 matrix
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+PEAK_F64_TFLOPS = 78.6          # MI355X fp64 (vector FMA)
 
 
 def parse():
@@ -42,9 +43,10 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the step, time the library's plain copy kernel over "
                          "MIB mebibytes (HBM ceiling; byte-counter calibration)")
-    ap.add_argument("--optimizer", default="muon", choices=["muon", "shampoo"],
+    ap.add_argument("--optimizer", default="muon", choices=["muon", "shampoo", "soap"],
                     help="shampoo: time the Shampoo owner step instead (workload "
-                         "shampoo_decoder_layer_h2048 unless --workload names another Shampoo one)")
+                         "shampoo_decoder_layer_h2048 unless --workload names another Shampoo one); "
+                         "soap: the SOAP owner step (workload soap_decoder_layer_h2048)")
     ap.add_argument("--adamw-sweep", action="store_true",
                     help="instead of the step, time adamw_tail_step over n = 2^24 .. 2^28 "
                          "fp32 elements (28 bytes moved per element) and print one JSON line per n")
@@ -301,6 +303,110 @@ def shampoo_main(args):
     print(json.dumps(out), flush=True)
 
 
+SOAP_METRIC = "SOAP owner-step ms (fp64 blocked-Jacobi eigensolver + fp32 products), 1 MI355X"
+
+
+def soap_cpu_baseline(wl):
+    """The fp64 oracle's SOAP step (numpy eigh for the eigenbases) on the
+    workload's smallest matrix, timed on the host."""
+    import numpy as np
+    from matrix_optimizers_amd import workloads as wlmod
+    from oracle import soap as osoap
+    try:
+        import threadpoolctl
+        cores = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    i = min(range(len(wl.matrices)), key=lambda k: wl.matrices[k].rows * wl.matrices[k].cols)
+    sp = wl.matrices[i]
+    hp = wl.hp
+    W = wlmod.normal(wl.seed, i, wlmod.ROLE_W, (sp.rows, sp.cols), wl.w_std, wl.w_dtype).astype(np.float64)
+    G = wlmod.normal(wl.seed, i, wlmod.ROLE_G, (sp.rows, sp.cols), wl.g_std, wl.g_dtype).astype(np.float64)
+    L = hp.stat_eps * np.eye(sp.rows)
+    R = hp.stat_eps * np.eye(sp.cols)
+    Z = np.zeros_like(W)
+    t0 = time.perf_counter()
+    osoap.soap_step(W, G, L, R, Z, Z, 1, hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay)
+    dt = time.perf_counter() - t0
+    # the same matrix's share of the GPU step, in the GPU's own work units
+    return {"value": round(dt * 1e3, 1), "unit": "ms per matrix step", "cores": int(cores), "kind": "oracle",
+            "sample": f"one {sp.rows}x{sp.cols} matrix of the bucket (two numpy fp64 eigh, six products), "
+                      f"{dt:.2f} s; the GPU line is the whole {len(wl.matrices)}-matrix bucket"}
+
+
+def soap_main(args):
+    import torch
+    import matrix_optimizers_amd as mo
+    from matrix_optimizers_amd import workloads as wlmod
+    key = args.workload if args.workload in wlmod.SOAP_WORKLOADS else "soap_decoder_layer_h2048"
+    wl = wlmod.SOAP_WORKLOADS[key]
+    hp = wl.hp
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] soap workload {wl.key}: {len(wl.matrices)} matrices", file=sys.stderr, flush=True)
+    mats = []
+    for i, sp in enumerate(wl.matrices):
+        W = wlmod.torch_normal(wl.seed, i, wlmod.ROLE_W, (sp.rows, sp.cols), wl.w_std, wl.w_dtype, dev)
+        G = wlmod.torch_normal(wl.seed, i, wlmod.ROLE_G, (sp.rows, sp.cols), wl.g_std, wl.g_dtype, dev)
+        L = torch.eye(sp.rows, device=dev) * hp.stat_eps
+        R = torch.eye(sp.cols, device=dev) * hp.stat_eps
+        M = torch.zeros((sp.rows, sp.cols), device=dev)
+        V = torch.zeros((sp.rows, sp.cols), device=dev)
+        mats.append((W, G, L, R, M, V))
+    step = mo.SoapOwnerStep(mats, lr=hp.lr, beta1=hp.beta1, beta2=hp.beta2, eps=hp.eps,
+                            weight_decay=hp.weight_decay, sweeps=hp.sweeps)
+    counter = {"t": 0}
+
+    def one():
+        counter["t"] += 1
+        step(counter["t"])
+    for _ in range(args.warmup):
+        one()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup {args.warmup} done; timing {args.steps} steps", file=sys.stderr, flush=True)
+    ms = timed_steps(one, args.steps)
+    print(f"[bench] {ms:.3f} ms/step", file=sys.stderr, flush=True)
+    prof = {}
+    if not args.no_phase_timing:
+        prof, _ = event_timed_steps(one, args.steps)
+    per_launch = {name: {"avg_ms": round(tot / cnt, 5), "launches": int(cnt), "ms_per_step": round(tot / args.steps, 5)}
+                  for name, (tot, cnt) in prof.items() if cnt}
+    jac = {"apply": 0.0, "solve": 0.0}
+    prod = 0.0
+    for sp in wl.matrices:
+        prod += wlmod.soap_product_flops(sp.rows, sp.cols)
+        for m in (sp.rows, sp.cols):
+            f = wlmod.soap_jacobi_flops(m, hp.sweeps)
+            jac["apply"] += f["apply"]
+            jac["solve"] += f["solve"]
+    out = {
+        "metric": SOAP_METRIC, "value": round(ms, 3), "unit": "ms/step", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f64+f32",
+        "data": "synthetic",
+        "config": {"workload": wl.key, "matrices": len(wl.matrices),
+                   "shapes": sorted({f"{s.rows}x{s.cols}" for s in wl.matrices}),
+                   "sweeps": hp.sweeps, "stat_eps": hp.stat_eps, "w_dtype": wl.w_dtype,
+                   "g_dtype": wl.g_dtype, "parallelism": "none (one owner's bucket)"},
+        "flops_per_step": {"jacobi_apply_f64": jac["apply"], "jacobi_solve_f64": jac["solve"],
+                           "products_f32": prod},
+        "phases": per_launch,
+    }
+    if "so_apply" in per_launch:
+        a = per_launch["so_apply"]
+        achieved = jac["apply"] / (a["ms_per_step"] * 1e-3) / 1e12
+        out["roofline"] = {"kernel": "so_jac_apply_kernel", "bound": "alu", "achieved": round(achieved, 3),
+                           "peak": PEAK_F64_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(achieved / PEAK_F64_TFLOPS, 4), "traffic": None,
+                           "algorithmic_per_launch": f"{jac['apply'] / (a['launches'] / args.steps):.4e} flop "
+                                                     f"(fp64, mean over {a['launches'] // args.steps} launches "
+                                                     f"per step)"}
+    if not args.no_cpu_baseline and not args.profile_only:
+        print("[bench] cpu_baseline (fp64 oracle on host)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = soap_cpu_baseline(wl)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -317,6 +423,8 @@ def main():
         return adamw_sweep(args)
     if args.optimizer == "shampoo":
         return shampoo_main(args)
+    if args.optimizer == "soap":
+        return soap_main(args)
     wl = wlmod.get(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -178,7 +178,13 @@ const char* mo_status_string(mo_status status);
 #define MO_PHASE_SH_ROOT    12  /* Shampoo: coupled Newton products */
 #define MO_PHASE_SH_LEFT    13  /* Shampoo: T = H_L G */
 #define MO_PHASE_SH_RIGHT   14  /* Shampoo: W <- decay W - lr T H_R */
-#define MO_PHASE_COUNT    15
+#define MO_PHASE_SO_PREP    15  /* SOAP: padded G, first moment M' */
+#define MO_PHASE_SO_STATS   16  /* SOAP: L' = L + G G^T, R' = R + G^T G */
+#define MO_PHASE_SO_SOLVE   17  /* SOAP: Jacobi pair problems of one round */
+#define MO_PHASE_SO_APPLY   18  /* SOAP: one round's rotations applied to A and E */
+#define MO_PHASE_SO_SORT    19  /* SOAP: E = I, eigenvalue sort, sorted fp32 eigenvectors */
+#define MO_PHASE_SO_ROTATE  20  /* SOAP: the six eigenbasis products, V', N and W written */
+#define MO_PHASE_COUNT    21
 
 /* Enable (1) or disable (0) per-launch timing on the calling thread.  While
  * enabled, every kernel launch is bracketed by HIP events on its own stream;
@@ -267,6 +273,76 @@ mo_status shampoo_workspace_bytes(const mo_shampoo_matrix* mats, int32_t n_mats,
 mo_status shampoo_owner_step(const mo_shampoo_matrix* mats, int32_t n_mats,
                              const mo_shampoo_hparams* hp, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/* ---- SOAP owner step -----------------------------------------------------
+ * [P §5.7]: next to Shampoo, the owner runs SOAP, which the paper describes as
+ * Adam in the Shampoo eigenbasis, with the same placement.  The pages print no
+ * formulas; this library follows the published SOAP algorithm (Vyas et al.,
+ * 2024), each choice it leaves open in its plainest form:
+ *   statistics  L' = L + G G^T, R' = R + G^T G (the caller starts them at
+ *               eps I and keeps them between steps)
+ *   eigenbasis  Q_L, Q_R: eigenvectors of L', R', recomputed every step, in
+ *               ascending order of their eigenvalues (the second moment is
+ *               indexed by that order; signs do not matter)
+ *   moments     M' = b1 M + (1 - b1) G in the weight's frame;
+ *               G~ = Q_L^T G Q_R, M~ = Q_L^T M' Q_R;
+ *               V' = b2 V + (1 - b2) G~^2 in the eigenbasis
+ *   update      N = (M~ / (1 - b1^t)) / (sqrt(V' / (1 - b2^t)) + eps);
+ *               W' = (1 - lr wd) W - lr Q_L N Q_R^T
+ * The eigenvectors come from a two-sided blocked Jacobi method in fp64
+ * (`sweeps` sweeps of all block pairs, rotations in Rutishauser's form); the
+ * statistics, moments and products are fp32.  Sides are at most 8192. */
+
+/* One whole matrix with its SOAP state.
+ *   W          rows x cols, w_dtype, row stride ld_w; updated in place
+ *   G          rows x cols, g_dtype, row stride ld_g; read only
+ *   L, R       rows x rows and cols x cols fp32 (strides ld_l, ld_r), symmetric;
+ *              updated in place (L', R')
+ *   M          rows x cols fp32 first moment (weight frame), stride ld_m; in place
+ *   V          rows x cols fp32 second moment (eigenbasis), stride ld_v; in place
+ *   update_out optional (NULL): rows x cols fp32, stride ld_u, receives
+ *              lr Q_L N Q_R^T
+ * rows == 0 or cols == 0 marks an empty shard (skipped; pointers may be NULL).
+ * Strides of 0 mean the natural ones. */
+typedef struct mo_soap_matrix {
+    void*       W;
+    const void* G;
+    float*      L;
+    float*      R;
+    float*      M;
+    float*      V;
+    float*      update_out;
+    int64_t     rows, cols;
+    int64_t     ld_w, ld_g, ld_l, ld_r, ld_m, ld_v, ld_u;
+    int32_t     w_dtype, g_dtype;
+} mo_soap_matrix;
+
+/* Adam hyperparameters, the step number t (>= 1) of the bias corrections, and
+ * the number of outer Jacobi sweeps (1 .. 100). */
+typedef struct mo_soap_hparams {
+    float   lr, beta1, beta2, eps, weight_decay;
+    int32_t step, sweeps;
+} mo_soap_hparams;
+
+/* Bytes of device workspace soap_owner_step needs: per matrix four fp32
+ * buffers of r_pad x c_pad; per side of size m three m_pad x m_pad buffers
+ * (two fp64, one fp32) and m_pad / 64 fp64 pair rotations of 64 x 64
+ * (x_pad = x rounded up to 64); plus the work list and 256 bytes of slack. */
+mo_status soap_workspace_bytes(const mo_soap_matrix* mats, int32_t n_mats,
+                               const mo_soap_hparams* hp, size_t* bytes);
+
+/* One SOAP step on every non-empty matrix of the bucket.  The eigensolver's
+ * launches are grouped over every statistics matrix of the bucket (two per
+ * round, sweeps x (m_pad / 32 - 1) rounds for the longest side); the rest is
+ * a few launches per matrix.  Workspace, stream and error conventions as
+ * muon_owner_step: MO_ERR_INVALID_ARG (null pointer with numel > 0, negative
+ * size, a stride below its row length, step < 1, sweeps outside 1 .. 100,
+ * non-finite lr, betas, eps or weight decay, betas outside [0, 1), eps < 0),
+ * MO_ERR_UNSUPPORTED (dtype not MO_F32/MO_BF16, a side longer than 8192),
+ * MO_ERR_WORKSPACE_TOO_SMALL, MO_ERR_ALIAS (a written tensor overlaps any
+ * tensor of the bucket or the workspace), MO_ERR_HIP. */
+mo_status soap_owner_step(const mo_soap_matrix* mats, int32_t n_mats, const mo_soap_hparams* hp,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---- owner planner (host only) --------------------------------------------
  * The step upstream of a bucket: which data-parallel rank owns each role

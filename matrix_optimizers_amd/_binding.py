@@ -28,7 +28,8 @@ DTYPES = {"f32": MO_F32, "float32": MO_F32, "bf16": MO_BF16, "bfloat16": MO_BF16
 LR_ADJUST = {"original": 0, "match_rms_adamw": 1, "none": 2}
 
 PHASES = ["momentum", "norm", "gram", "poly", "update", "apply", "adamw", "copy", "update_last",
-          "sh_layout", "sh_stats", "sh_rootprep", "sh_root", "sh_left", "sh_right"]
+          "sh_layout", "sh_stats", "sh_rootprep", "sh_root", "sh_left", "sh_right",
+          "so_prep", "so_stats", "so_solve", "so_apply", "so_sort", "so_rotate"]
 
 
 class MoError(RuntimeError):
@@ -70,12 +71,29 @@ class MoShampooHParams(ctypes.Structure):
                 ("root_iters", ctypes.c_int32)]
 
 
+class MoSoapMatrix(ctypes.Structure):
+    """mo_soap_matrix of include/mo.h."""
+    _fields_ = [("W", ctypes.c_void_p), ("G", ctypes.c_void_p), ("L", ctypes.c_void_p),
+                ("R", ctypes.c_void_p), ("M", ctypes.c_void_p), ("V", ctypes.c_void_p),
+                ("update_out", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("ld_w", ctypes.c_int64), ("ld_g", ctypes.c_int64), ("ld_l", ctypes.c_int64),
+                ("ld_r", ctypes.c_int64), ("ld_m", ctypes.c_int64), ("ld_v", ctypes.c_int64),
+                ("ld_u", ctypes.c_int64), ("w_dtype", ctypes.c_int32), ("g_dtype", ctypes.c_int32)]
+
+
+class MoSoapHParams(ctypes.Structure):
+    """mo_soap_hparams of include/mo.h."""
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float), ("step", ctypes.c_int32),
+                ("sweeps", ctypes.c_int32)]
+
+
 _lib = None
 
 EXPORTS = ["muon_workspace_bytes", "muon_build_worklist", "muon_owner_step", "adamw_tail_step",
            "mo_status_string", "mo_profile_enable", "mo_profile_read", "mo_device_copy",
            "mo_plan_owners", "mo_plan_score", "mo_plan_layout", "shampoo_workspace_bytes",
-           "shampoo_owner_step"]
+           "shampoo_owner_step", "soap_workspace_bytes", "soap_owner_step"]
 
 ROLE_MATRIX, ROLE_TAIL = 0, 1
 PLAN_POLICIES = {"role_greedy": 0, "scope_greedy": 1, "cost_aware": 2}
@@ -122,10 +140,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                             P(ctypes.c_size_t)]
     lib.shampoo_owner_step.argtypes = [P(MoShampooMatrix), ctypes.c_int32, P(MoShampooHParams),
                                        ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.soap_workspace_bytes.argtypes = [P(MoSoapMatrix), ctypes.c_int32, P(MoSoapHParams),
+                                         P(ctypes.c_size_t)]
+    lib.soap_owner_step.argtypes = [P(MoSoapMatrix), ctypes.c_int32, P(MoSoapHParams),
+                                    ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     for name in ("muon_workspace_bytes", "muon_build_worklist", "muon_owner_step",
                  "adamw_tail_step", "mo_profile_enable", "mo_profile_read", "mo_device_copy",
                  "mo_plan_owners", "mo_plan_score", "mo_plan_layout", "shampoo_workspace_bytes",
-                 "shampoo_owner_step"):
+                 "shampoo_owner_step", "soap_workspace_bytes", "soap_owner_step"):
         getattr(lib, name).restype = ctypes.c_int32
     _lib = lib
     return lib
@@ -415,6 +437,122 @@ def shampoo_owner_step(mats: Sequence[Tuple], *, update_out: Optional[Sequence] 
     _check(lib.shampoo_owner_step(arr, n, ctypes.byref(hp), ctypes.c_void_p(workspace.data_ptr()),
                                   workspace.numel(), ctypes.c_void_p(_stream_handle(stream))),
            "shampoo_owner_step")
+
+
+# ---------------------------------------------------------------------------
+# SOAP
+# ---------------------------------------------------------------------------
+
+def soap_hparams(lr: float = 1e-3, beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,
+                 weight_decay: float = 0.0, step: int = 1, sweeps: int = 10) -> MoSoapHParams:
+    return MoSoapHParams(lr=lr, beta1=beta1, beta2=beta2, eps=eps, weight_decay=weight_decay,
+                         step=int(step), sweeps=int(sweeps))
+
+
+def soap_descriptor(rows: int, cols: int, W: int = 0, G: int = 0, L: int = 0, R: int = 0, M: int = 0,
+                    V: int = 0, update_out: int = 0, w_dtype="f32", g_dtype="f32", **ld) -> MoSoapMatrix:
+    """A raw descriptor from integer addresses (host-side checks and tests); ld_* strides by name."""
+    code = lambda d: DTYPES[d] if isinstance(d, str) else int(d)
+    return MoSoapMatrix(W=W or None, G=G or None, L=L or None, R=R or None, M=M or None, V=V or None,
+                        update_out=update_out or None, rows=rows, cols=cols, w_dtype=code(w_dtype),
+                        g_dtype=code(g_dtype), **ld)
+
+
+def soap_tensor_descriptor(W, G, L, R, M, V, update_out=None) -> MoSoapMatrix:
+    torch = _torch()
+    if W.shape != G.shape or M.shape != W.shape or V.shape != W.shape:
+        raise ValueError("W, G, M and V must have one shape")
+    rows, cols = W.shape
+    if tuple(L.shape) != (rows, rows) or tuple(R.shape) != (cols, cols):
+        raise ValueError("L must be rows x rows and R cols x cols")
+    for t in (L, R, M, V):
+        if t.dtype != torch.float32:
+            raise TypeError("statistics and moments are float32")
+    dev = W.device
+    for t in (G, L, R, M, V) + ((update_out,) if update_out is not None else ()):
+        if t.device != dev:
+            raise ValueError("W, G, L, R, M, V, update_out must be on one device")
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a HIP device")
+    if update_out is not None and (update_out.shape != W.shape or update_out.dtype != torch.float32):
+        raise ValueError("update_out must be float32 and shaped like W")
+    ptr = lambda t: t.data_ptr() or None
+    return MoSoapMatrix(W=ptr(W), G=ptr(G), L=ptr(L), R=ptr(R), M=ptr(M), V=ptr(V),
+                        update_out=(update_out.data_ptr() if update_out is not None else None),
+                        rows=rows, cols=cols, ld_w=_row_stride(W), ld_g=_row_stride(G),
+                        ld_l=_row_stride(L), ld_r=_row_stride(R), ld_m=_row_stride(M),
+                        ld_v=_row_stride(V),
+                        ld_u=_row_stride(update_out) if update_out is not None else 0,
+                        w_dtype=_dtype_code(W), g_dtype=_dtype_code(G))
+
+
+def _so_array(descs: Sequence[MoSoapMatrix]):
+    n = len(descs)
+    arr = (MoSoapMatrix * max(n, 1))()
+    for i, d in enumerate(descs):
+        arr[i] = d
+    return arr, n
+
+
+def soap_workspace_bytes(descs: Sequence[MoSoapMatrix], hp: MoSoapHParams) -> int:
+    lib = load_library()
+    arr, n = _so_array(descs)
+    out = ctypes.c_size_t(0)
+    _check(lib.soap_workspace_bytes(arr, n, ctypes.byref(hp), ctypes.byref(out)), "soap_workspace_bytes")
+    return int(out.value)
+
+
+class SoapOwnerStep:
+    """Reusable SOAP step over a fixed bucket of (W, G, L, R, M, V) tensors:
+    descriptors and workspace are prepared once; ``__call__(step)`` launches
+    one step (W, L, R, M, V updated in place) on the current (or given) stream."""
+
+    def __init__(self, mats: Sequence[Tuple], update_out: Optional[Sequence] = None, **hp_kwargs):
+        torch = _torch()
+        self.lib = load_library()
+        self.hp_kwargs = dict(hp_kwargs)
+        self.hp = soap_hparams(**hp_kwargs)
+        ups = list(update_out) if update_out is not None else [None] * len(mats)
+        self.descs = [soap_tensor_descriptor(*mat, u) for mat, u in zip(mats, ups)]
+        self.arr, self.n = _so_array(self.descs)
+        self.bytes = soap_workspace_bytes(self.descs, self.hp)
+        dev = mats[0][0].device if mats else torch.device("cuda")
+        self.workspace = torch.empty(self.bytes, dtype=torch.uint8, device=dev)
+        self._keep = (mats, update_out)
+
+    def __call__(self, step: Optional[int] = None, stream=None) -> None:
+        if step is not None:
+            self.hp.step = int(step)
+        _check(self.lib.soap_owner_step(self.arr, self.n, ctypes.byref(self.hp),
+                                        ctypes.c_void_p(self.workspace.data_ptr()),
+                                        self.workspace.numel(),
+                                        ctypes.c_void_p(_stream_handle(stream))),
+               "soap_owner_step")
+
+
+def soap_owner_step(mats: Sequence[Tuple], *, update_out: Optional[Sequence] = None,
+                    workspace=None, stream=None, **hp_kwargs) -> None:
+    """One SOAP step over a bucket of (W, G, L, R, M, V) tensors, in place.
+
+    hp_kwargs: lr, beta1, beta2, eps, weight_decay, step (t of the bias
+    corrections), sweeps (outer Jacobi sweeps).  L and R are the float32
+    statistics (started by the caller at eps I), M the first moment in the
+    weight's frame and V the second moment in the eigenbasis (float32, zeros
+    at the start).
+    """
+    torch = _torch()
+    lib = load_library()
+    hp = soap_hparams(**hp_kwargs)
+    ups = list(update_out) if update_out is not None else [None] * len(mats)
+    descs = [soap_tensor_descriptor(*mat, u) for mat, u in zip(mats, ups)]
+    arr, n = _so_array(descs)
+    need = soap_workspace_bytes(descs, hp)
+    if workspace is None:
+        dev = mats[0][0].device if mats else torch.device("cuda")
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check(lib.soap_owner_step(arr, n, ctypes.byref(hp), ctypes.c_void_p(workspace.data_ptr()),
+                               workspace.numel(), ctypes.c_void_p(_stream_handle(stream))),
+           "soap_owner_step")
 
 
 def adamw_tail_step(p, g, m, v, step: int, *, lr: float = 1e-3, beta1: float = 0.9,

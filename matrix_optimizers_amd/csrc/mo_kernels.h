@@ -28,3 +28,15 @@ struct mo_sh_header;
 hipError_t mo_launch_sh_layout(const mo_sh_header& h, uint8_t* ws, hipStream_t s);
 hipError_t mo_launch_sh_rootprep(const mo_sh_header& h, uint8_t* ws, hipStream_t s);
 hipError_t mo_launch_sh_gemm(const mo_sh_header& h, uint8_t* ws, int list, int k, hipStream_t s);
+
+// SOAP step (soap_kernels.hip); `ws` holds the SOAP work list.
+struct mo_so_header;
+struct mo_so_mat;
+struct mo_so_eig;
+hipError_t mo_launch_so_prep(const mo_so_mat& mt, uint8_t* ws, uint32_t mi, hipStream_t s);
+hipError_t mo_launch_so_gemm(const mo_so_mat& mt, uint8_t* ws, uint32_t mi, int kind, hipStream_t s);
+hipError_t mo_launch_so_eig_init(const mo_so_eig& eg, uint8_t* ws, uint32_t ei, hipStream_t s);
+hipError_t mo_launch_so_solve(const mo_so_header& h, uint8_t* ws, uint32_t k, hipStream_t s);
+hipError_t mo_launch_so_apply(const mo_so_header& h, uint8_t* ws, uint32_t k, hipStream_t s);
+hipError_t mo_launch_so_sort(const mo_so_header& h, uint8_t* ws, hipStream_t s);
+hipError_t mo_launch_so_gather(const mo_so_eig& eg, uint8_t* ws, uint32_t ei, hipStream_t s);

@@ -1,0 +1,552 @@
+// gfx950 kernels of the owner-side SOAP step.
+//
+// [P] = "MatrixFSDP: communication-free matrix optimizers under ZeRO-3 parameter
+// sharding", §5.7: the owner runs SOAP, Adam in the Shampoo eigenbasis, on the
+// whole matrices it owns, with no collective.  Per matrix (the readings are
+// stated with the C entry point):
+//   L' = L + G G^T,  R' = R + G^T G                      fp32 statistics
+//   Q_L, Q_R = eigenvectors of L', R', ascending          fp64 blocked Jacobi
+//   M' = b1 M + (1 - b1) G
+//   G~ = Q_L^T G Q_R,  M~ = Q_L^T M' Q_R                  fp32 products
+//   V' = b2 V + (1 - b2) G~^2
+//   N = (M~ / (1 - b1^t)) / (sqrt(V' / (1 - b2^t)) + eps)
+//   W' = (1 - lr wd) W - lr Q_L N Q_R^T
+//
+// Eigensolver.  Two-sided blocked Jacobi (the cyclic Jacobi method of Jacobi
+// 1846 applied to blocks, with the round-robin ("circle") ordering of the
+// parallel Jacobi literature): the padded side is cut into 2P blocks of 32;
+// each round pairs all blocks, one workgroup diagonalises each 64 x 64 pair
+// problem in LDS by scalar cyclic Jacobi sweeps, and a second launch applies
+// the P pair rotations to A (both sides) and to the accumulated eigenvectors E.
+// Every rotation is applied in Rutishauser's form (the new value is the old
+// one plus a correction proportional to sin), and the pair rotations are kept
+// as V - I, so rounding scales with the correction, not with the matrix.  The
+// arithmetic is fp64: an fp32 version of the same scheme builds up a backward
+// error of a few hundred units over its rounds, which the eigenvectors of
+// closely spaced eigenvalues turn into large angle errors.
+#include "device_common.h"
+#include "so_worklist.h"
+#include "mo_kernels.h"
+
+namespace {
+
+constexpr int SO_THREADS = 256;
+constexpr int GB = 64;                 // GEMM tile
+constexpr int GK = 16;                 // GEMM K chunk
+constexpr int PW = 2 * MO_SO_BLK;      // pair width (64)
+constexpr int INNER_SWEEPS = 3;        // scalar sweeps per pair problem
+
+MO_DEV const mo_so_header* so_header(const uint8_t* ws) {
+    return reinterpret_cast<const mo_so_header*>(ws);
+}
+MO_DEV const mo_so_mat* so_mats(const uint8_t* ws) {
+    return reinterpret_cast<const mo_so_mat*>(ws + so_header(ws)->mats_offset);
+}
+MO_DEV const mo_so_eig* so_eigs(const uint8_t* ws) {
+    return reinterpret_cast<const mo_so_eig*>(ws + so_header(ws)->eigs_offset);
+}
+
+// Round k (0 .. n - 2) of the circle ordering over n (even) indices: pair j
+// (0 .. n/2 - 1).  Index 0 stays put and the others turn one place per round,
+// so that every pair meets exactly once in n - 1 rounds.
+MO_DEV void circle_pair(int n, int k, int j, int& a, int& b) {
+    auto f = [&](int i) { return (i + k) % (n - 1) + 1; };
+    if (j == 0) {
+        a = 0;
+        b = f(0);
+    } else {
+        a = f(j);
+        b = f(n - 1 - j);
+    }
+}
+
+// ============================================================================
+// prep: padded G and M' = b1 M + (1 - b1) G (the caller's M updated)
+// ============================================================================
+__global__ __launch_bounds__(SO_THREADS) void so_prep_kernel(uint8_t* ws, uint32_t mi) {
+    const mo_so_mat& mt = so_mats(ws)[mi];
+    const int64_t idx = int64_t(blockIdx.x) * SO_THREADS + threadIdx.x;
+    const int64_t total = int64_t(mt.r_pad) * mt.c_pad;
+    if (idx >= total) return;
+    const int64_t i = idx / mt.c_pad, j = idx % mt.c_pad;
+    float g = 0.f, m = 0.f;
+    if (i < mt.rows && j < mt.cols) {
+        g = load_elem(reinterpret_cast<const void*>(mt.G), i * mt.ld_g + j, mt.flags & MO_SOF_G_BF16);
+        float* M = reinterpret_cast<float*>(mt.M);
+        m = mt.beta1 * M[i * mt.ld_m + j] + (1.0f - mt.beta1) * g;
+        M[i * mt.ld_m + j] = m;
+    }
+    reinterpret_cast<float*>(ws + mt.off_G)[idx] = g;
+    reinterpret_cast<float*>(ws + mt.off_M)[idx] = m;
+}
+
+// ============================================================================
+// fp32 products C = op(A) op(B) on 64 x 64 tiles, with the step's epilogues
+// ============================================================================
+//
+// Operand element (i, k) of A sits at A[i * a_i + k * a_k], (k, j) of B at
+// B[k * b_k + j * b_j]; one of each pair of strides is 1, and the loads run
+// along it.  Every dimension is a multiple of 64 (zero padding), so no bounds
+// are tested until the epilogue writes the caller's tensors.
+struct SoProd {
+    const float* A;
+    int64_t a_i, a_k;
+    const float* B;
+    int64_t b_k, b_j;
+    int K;
+};
+
+MO_DEV SoProd so_prod(uint8_t* ws, const mo_so_mat& mt, int kind) {
+    const mo_so_eig* eigs = so_eigs(ws);
+    auto F = [&](uint64_t off) { return reinterpret_cast<const float*>(ws + off); };
+    const int64_t rp = mt.r_pad, cp = mt.c_pad;
+    const float* EL = F(eigs[mt.eig_l].off_E32);
+    const float* ER = F(eigs[mt.eig_r].off_E32);
+    SoProd p;
+    switch (kind) {
+    case MO_SOK_STATS_L: p = {F(mt.off_G), cp, 1, F(mt.off_G), 1, cp, int(cp)}; break;
+    case MO_SOK_STATS_R: p = {F(mt.off_G), 1, cp, F(mt.off_G), cp, 1, int(rp)}; break;
+    case MO_SOK_LEFT_G:  p = {EL, rp, 1, F(mt.off_G), cp, 1, int(rp)}; break;
+    case MO_SOK_LEFT_M:  p = {EL, rp, 1, F(mt.off_M), cp, 1, int(rp)}; break;
+    case MO_SOK_RIGHT_G:
+    case MO_SOK_RIGHT_M: p = {F(mt.off_T), cp, 1, ER, 1, cp, int(cp)}; break;
+    case MO_SOK_BACK_L:  p = {EL, 1, rp, F(mt.off_N), cp, 1, int(rp)}; break;
+    default:             p = {F(mt.off_T), cp, 1, ER, cp, 1, int(cp)}; break;   // BACK_R
+    }
+    return p;
+}
+
+// The epilogue of one row of four results: row i, columns j .. j + 3.
+MO_DEV void so_epilogue(uint8_t* ws, const mo_so_mat& mt, int kind, int64_t i, int64_t j, const float* v) {
+    const int64_t rp = mt.r_pad, cp = mt.c_pad;
+    if (kind == MO_SOK_STATS_L || kind == MO_SOK_STATS_R) {
+        const mo_so_eig& eg = so_eigs(ws)[kind == MO_SOK_STATS_L ? mt.eig_l : mt.eig_r];
+        float* ext = reinterpret_cast<float*>(eg.ext);
+        double* A = reinterpret_cast<double*>(ws + eg.off_A);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float s = 0.f;
+            if (i < eg.m && j + e < eg.m) {
+                s = ext[i * eg.ld_ext + j + e] + v[e];
+                ext[i * eg.ld_ext + j + e] = s;
+            }
+            A[i * eg.m_pad + j + e] = double(s);
+        }
+        return;
+    }
+    if (kind == MO_SOK_RIGHT_G) {
+        if (i >= mt.rows) return;
+        float* V = reinterpret_cast<float*>(mt.V);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (j + e < mt.cols) {
+                float& x = V[i * mt.ld_v + j + e];
+                x = mt.beta2 * x + (1.0f - mt.beta2) * v[e] * v[e];
+            }
+        return;
+    }
+    if (kind == MO_SOK_RIGHT_M) {
+        const float* V = reinterpret_cast<const float*>(mt.V);
+        float* N = reinterpret_cast<float*>(ws + mt.off_N);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float n = 0.f;
+            if (i < mt.rows && j + e < mt.cols)
+                n = (v[e] * mt.ibc1) / (sqrtf(V[i * mt.ld_v + j + e] * mt.ibc2) + mt.eps);
+            N[i * cp + j + e] = n;
+        }
+        return;
+    }
+    if (kind == MO_SOK_BACK_R) {
+        if (i >= mt.rows) return;
+        const bool wbf = mt.flags & MO_SOF_W_BF16;
+        void* W = reinterpret_cast<void*>(mt.W);
+        float* U = reinterpret_cast<float*>(mt.U);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (j + e < mt.cols) {
+                const int64_t wi = i * mt.ld_w + j + e;
+                store_elem(W, wi, mt.decay * load_elem(W, wi, wbf) - mt.lr * v[e], wbf);
+                if (U) U[i * mt.ld_u + j + e] = mt.lr * v[e];
+            }
+        return;
+    }
+    // LEFT_G, LEFT_M, BACK_L: the padded scratch product
+    float* T = reinterpret_cast<float*>(ws + mt.off_T);
+    (void)rp;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) T[i * cp + j + e] = v[e];
+}
+
+__global__ __launch_bounds__(SO_THREADS) void so_gemm_kernel(uint8_t* ws, uint32_t mi, int kind) {
+    __shared__ __align__(16) float As[GK][GB + 4];
+    __shared__ __align__(16) float Bs[GK][GB + 4];
+    const mo_so_mat& mt = so_mats(ws)[mi];
+    const SoProd p = so_prod(ws, mt, kind);
+    const int t = threadIdx.x;
+    const int64_t i0 = int64_t(blockIdx.y) * GB, j0 = int64_t(blockIdx.x) * GB;
+    const int r0 = (t / 16) * 4, c0 = (t % 16) * 4;
+    float acc[4][4] = {};
+    for (int k0 = 0; k0 < p.K; k0 += GK) {
+        if (p.a_k == 1) {   // 4 consecutive k of one row i
+            const int i = t / 4, kk = (t % 4) * 4;
+            const f32x4 a = *reinterpret_cast<const f32x4*>(p.A + (i0 + i) * p.a_i + k0 + kk);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) As[kk + e][i] = a[e];
+        } else {            // 4 consecutive i of one k
+            const int kk = t / 16, i = (t % 16) * 4;
+            *reinterpret_cast<f32x4*>(&As[kk][i]) =
+                *reinterpret_cast<const f32x4*>(p.A + (k0 + kk) * p.a_k + i0 + i);
+        }
+        if (p.b_j == 1) {   // 4 consecutive j of one k
+            const int kk = t / 16, j = (t % 16) * 4;
+            *reinterpret_cast<f32x4*>(&Bs[kk][j]) =
+                *reinterpret_cast<const f32x4*>(p.B + (k0 + kk) * p.b_k + j0 + j);
+        } else {            // 4 consecutive k of one column j
+            const int j = t / 4, kk = (t % 4) * 4;
+            const f32x4 b = *reinterpret_cast<const f32x4*>(p.B + (j0 + j) * p.b_j + k0 + kk);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Bs[kk + e][j] = b[e];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < GK; ++kk) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(&As[kk][r0]);
+            const f32x4 b = *reinterpret_cast<const f32x4*>(&Bs[kk][c0]);
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+#pragma unroll
+                for (int y = 0; y < 4; ++y) acc[x][y] = fmaf(a[x], b[y], acc[x][y]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x) so_epilogue(ws, mt, kind, i0 + r0 + x, j0 + c0, acc[x]);
+}
+
+// ============================================================================
+// eigensolver
+// ============================================================================
+
+template <typename Rec>
+MO_DEV uint32_t find_rec(const Rec* recs, uint32_t n, uint32_t item, uint32_t Rec::*begin) {
+    uint32_t lo = 0, hi = n - 1;
+    while (lo < hi) {   // last record whose first item is <= item
+        const uint32_t mid = (lo + hi + 1) >> 1;
+        if (recs[mid].*begin <= item) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// Global index of local index l (0 .. 63) of pair (p, q) of 32-wide blocks.
+MO_DEV int64_t pair_index(int p, int q, int l) {
+    return l < MO_SO_BLK ? int64_t(p) * MO_SO_BLK + l : int64_t(q) * MO_SO_BLK + (l - MO_SO_BLK);
+}
+
+// E = identity on the true diagonal (padding stays zero), one thread per element.
+__global__ __launch_bounds__(SO_THREADS) void so_eig_init_kernel(uint8_t* ws, uint32_t ei) {
+    const mo_so_eig& eg = so_eigs(ws)[ei];
+    const int64_t idx = int64_t(blockIdx.x) * SO_THREADS + threadIdx.x;
+    if (idx >= int64_t(eg.m_pad) * eg.m_pad) return;
+    const int64_t i = idx / eg.m_pad, j = idx % eg.m_pad;
+    reinterpret_cast<double*>(ws + eg.off_E)[idx] = (i == j && i < eg.m) ? 1.0 : 0.0;
+}
+
+// Rotation that zeroes S[a][b] of the symmetric 2 x 2 problem (app, apq; apq, aqq):
+// t = tan, s = sin, tau = sin / (1 + cos) (Rutishauser's formulas).
+MO_DEV void jacobi_rotation(double app, double aqq, double apq, double& t, double& s, double& tau) {
+    if (apq == 0.0) {
+        t = s = tau = 0.0;
+        return;
+    }
+    const double theta = (aqq - app) / (2.0 * apq);
+    if (fabs(theta) > 1e150) {
+        t = 0.5 / theta;
+    } else {
+        t = (theta >= 0.0 ? 1.0 : -1.0) / (fabs(theta) + sqrt(theta * theta + 1.0));
+    }
+    const double c = 1.0 / sqrt(t * t + 1.0);
+    s = t * c;
+    tau = s / (1.0 + c);
+}
+
+// One workgroup per (decomposition, block pair) of round k: diagonalise the
+// 64 x 64 pair problem S = A[pair][pair] by INNER_SWEEPS scalar cyclic sweeps
+// and store its rotation as D = V - I (V^T S V ~ diagonal).
+__global__ __launch_bounds__(SO_THREADS) void so_jac_solve_kernel(uint8_t* ws, uint32_t k) {
+    __shared__ double S[PW][PW + 1];
+    __shared__ double D[PW][PW + 1];
+    __shared__ double rs[PW / 2], rtau[PW / 2], rt[PW / 2], rapq[PW / 2];
+    __shared__ int ra[PW / 2], rb[PW / 2];
+    const mo_so_header* h = so_header(ws);
+    const mo_so_eig* eigs = so_eigs(ws);
+    const mo_so_eig& eg = eigs[find_rec(eigs, h->n_eigs, blockIdx.x, &mo_so_eig::solve_begin)];
+    if (k >= eg.rounds) return;
+    const int j = int(blockIdx.x - eg.solve_begin);
+    const int nb = 2 * int(eg.P);
+    int bp, bq;
+    circle_pair(nb, int(k % uint32_t(nb - 1)), j, bp, bq);
+    const double* A = reinterpret_cast<const double*>(ws + eg.off_A);
+    const int t = threadIdx.x;
+    for (int q = t; q < PW * PW; q += SO_THREADS) {
+        const int r = q / PW, c = q % PW;
+        S[r][c] = A[pair_index(bp, bq, r) * eg.m_pad + pair_index(bp, bq, c)];
+        D[r][c] = 0.0;
+    }
+    __syncthreads();
+    for (int sweep = 0; sweep < INNER_SWEEPS; ++sweep) {
+        for (int step = 0; step < PW - 1; ++step) {
+            if (t < PW / 2) {
+                int a, b;
+                circle_pair(PW, step, t, a, b);
+                double tt, s, tau;
+                const double apq = S[a][b];
+                jacobi_rotation(S[a][a], S[b][b], apq, tt, s, tau);
+                ra[t] = a; rb[t] = b; rs[t] = s; rtau[t] = tau; rt[t] = tt; rapq[t] = apq;
+            }
+            __syncthreads();
+            // two-sided update of the 2 x 2 blocks (u, v), u <= v, mirrored
+            for (int q = t; q < (PW / 2) * (PW / 2); q += SO_THREADS) {
+                const int u = q / (PW / 2), v = q % (PW / 2);
+                if (u > v) continue;
+                const int au = ra[u], bu = rb[u];
+                if (u == v) {
+                    const double tt = rt[u], apq = rapq[u];
+                    S[au][au] -= tt * apq;
+                    S[bu][bu] += tt * apq;
+                    S[au][bu] = 0.0;
+                    S[bu][au] = 0.0;
+                    continue;
+                }
+                const int av = ra[v], bv = rb[v];
+                const double su = rs[u], tu = rtau[u], sv = rs[v], tv = rtau[v];
+                double x00 = S[au][av], x01 = S[au][bv], x10 = S[bu][av], x11 = S[bu][bv];
+                // rows: J_u^T
+                double y00 = x00 - su * (x10 + tu * x00), y10 = x10 + su * (x00 - tu * x10);
+                double y01 = x01 - su * (x11 + tu * x01), y11 = x11 + su * (x01 - tu * x11);
+                // columns: J_v
+                const double z00 = y00 - sv * (y01 + tv * y00), z01 = y01 + sv * (y00 - tv * y01);
+                const double z10 = y10 - sv * (y11 + tv * y10), z11 = y11 + sv * (y10 - tv * y11);
+                S[au][av] = z00; S[au][bv] = z01; S[bu][av] = z10; S[bu][bv] = z11;
+                S[av][au] = z00; S[bv][au] = z01; S[av][bu] = z10; S[bv][bu] = z11;
+            }
+            // D <- D J + (J - I): rows r, pairs u
+            for (int q = t; q < PW * (PW / 2); q += SO_THREADS) {
+                const int r = q / (PW / 2), u = q % (PW / 2);
+                const int a = ra[u], b = rb[u];
+                const double s = rs[u], tau = rtau[u];
+                const double da = D[r][a], db = D[r][b];
+                double na = da - s * (db + tau * da), nb2 = db + s * (da - tau * db);
+                if (r == a) { na -= s * tau; nb2 += s; }
+                if (r == b) { na -= s; nb2 -= s * tau; }
+                D[r][a] = na;
+                D[r][b] = nb2;
+            }
+            __syncthreads();
+        }
+    }
+    double* Dout = reinterpret_cast<double*>(ws + eg.off_D) + int64_t(j) * PW * PW;
+    for (int q = t; q < PW * PW; q += SO_THREADS) Dout[q] = D[q / PW][q % PW];
+}
+
+// One workgroup per 64 x 64 tile of round k: an upper tile (I, J) of pairs of
+// A, A' = V_I^T A V_J (mirrored below the diagonal), or a tile (I, columns
+// 64 c ..) of E, E' = V_I^T E.  With V = I + D: C = X + X D_J, A' = C + D_I^T C.
+__global__ __launch_bounds__(SO_THREADS) void so_jac_apply_kernel(uint8_t* ws, uint32_t k) {
+    __shared__ double X[PW][PW + 1];
+    __shared__ double C[PW][PW + 1];
+    __shared__ double DI[PW][PW + 1];
+    __shared__ double DJ[PW][PW + 1];
+    const mo_so_header* h = so_header(ws);
+    const mo_so_eig* eigs = so_eigs(ws);
+    const mo_so_eig& eg = eigs[find_rec(eigs, h->n_eigs, blockIdx.x, &mo_so_eig::apply_begin)];
+    if (k >= eg.rounds) return;
+    const int P = int(eg.P);
+    const int nb = 2 * P;
+    const int kr = int(k % uint32_t(nb - 1));
+    int item = int(blockIdx.x - eg.apply_begin);
+    const int n_upper = P * (P + 1) / 2;
+    const bool is_a = item < n_upper;
+    int I = 0, J = 0;
+    if (is_a) {
+        while (item >= P - I) { item -= P - I; ++I; }
+        J = I + item;
+    } else {
+        item -= n_upper;
+        I = item / P;
+        J = item % P;   // column chunk of E
+    }
+    int pI, qI, pJ = 0, qJ = 0;
+    circle_pair(nb, kr, I, pI, qI);
+    if (is_a) circle_pair(nb, kr, J, pJ, qJ);
+    const double* Dall = reinterpret_cast<const double*>(ws + eg.off_D);
+    double* M = reinterpret_cast<double*>(ws + (is_a ? eg.off_A : eg.off_E));
+    const int64_t ld = eg.m_pad;
+    const int t = threadIdx.x;
+    for (int q = t; q < PW * PW; q += SO_THREADS) {
+        const int r = q / PW, c = q % PW;
+        const int64_t col = is_a ? pair_index(pJ, qJ, c) : int64_t(J) * PW + c;
+        X[r][c] = M[pair_index(pI, qI, r) * ld + col];
+        DI[r][c] = Dall[int64_t(I) * PW * PW + q];
+        if (is_a) DJ[r][c] = Dall[int64_t(J) * PW * PW + q];
+    }
+    __syncthreads();
+    const int r0 = (t / 16) * 4, c0 = (t % 16) * 4;
+    if (is_a) {   // C = X + X D_J
+        double acc[4][4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+            for (int y = 0; y < 4; ++y) acc[x][y] = 0.0;
+        for (int kk = 0; kk < PW; ++kk) {
+            double a[4], b[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) a[x] = X[r0 + x][kk];
+#pragma unroll
+            for (int y = 0; y < 4; ++y) b[y] = DJ[kk][c0 + y];
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+#pragma unroll
+                for (int y = 0; y < 4; ++y) acc[x][y] = fma(a[x], b[y], acc[x][y]);
+        }
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+            for (int y = 0; y < 4; ++y) C[r0 + x][c0 + y] = X[r0 + x][c0 + y] + acc[x][y];
+    } else {
+        for (int q = t; q < PW * PW; q += SO_THREADS) C[q / PW][q % PW] = X[q / PW][q % PW];
+    }
+    __syncthreads();
+    // Y = C + D_I^T C
+    double acc[4][4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) acc[x][y] = 0.0;
+    for (int kk = 0; kk < PW; ++kk) {
+        double a[4], b[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) a[x] = DI[kk][r0 + x];
+#pragma unroll
+        for (int y = 0; y < 4; ++y) b[y] = C[kk][c0 + y];
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+            for (int y = 0; y < 4; ++y) acc[x][y] = fma(a[x], b[y], acc[x][y]);
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+        const int64_t gr = pair_index(pI, qI, r0 + x);
+#pragma unroll
+        for (int y = 0; y < 4; ++y) {
+            const double val = C[r0 + x][c0 + y] + acc[x][y];
+            const int64_t gc = is_a ? pair_index(pJ, qJ, c0 + y) : int64_t(J) * PW + c0 + y;
+            M[gr * ld + gc] = val;
+            if (is_a && I != J) M[gc * ld + gr] = val;
+        }
+    }
+}
+
+// One workgroup per decomposition: sort the eigenvalues diag(A) ascending
+// (bitonic, padding last) and keep the permutation.
+constexpr int SORT_THREADS = 1024;
+__global__ __launch_bounds__(SORT_THREADS) void so_eig_sort_kernel(uint8_t* ws) {
+    __shared__ double key[MO_SO_MAXSIDE];
+    __shared__ int val[MO_SO_MAXSIDE];
+    const mo_so_eig& eg = so_eigs(ws)[blockIdx.x];
+    const double* A = reinterpret_cast<const double*>(ws + eg.off_A);
+    int n2 = 1;
+    while (n2 < int(eg.m_pad)) n2 <<= 1;
+    for (int i = threadIdx.x; i < n2; i += SORT_THREADS) {
+        key[i] = i < int(eg.m) ? A[int64_t(i) * eg.m_pad + i] : __builtin_huge_val();
+        val[i] = i;
+    }
+    __syncthreads();
+    for (int size = 2; size <= n2; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int i = threadIdx.x; i < n2; i += SORT_THREADS) {
+                const int p = i ^ stride;
+                if (p > i) {
+                    const bool up = (i & size) == 0;
+                    // ties by index keep the order deterministic
+                    const bool gt = key[i] > key[p] || (key[i] == key[p] && val[i] > val[p]);
+                    if (gt == up) {
+                        const double tk = key[i]; key[i] = key[p]; key[p] = tk;
+                        const int tv = val[i]; val[i] = val[p]; val[p] = tv;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+    int* perm = reinterpret_cast<int*>(ws + eg.off_perm);
+    for (int i = threadIdx.x; i < int(eg.m_pad); i += SORT_THREADS) perm[i] = val[i];
+}
+
+// E32 row r = E row perm[r] (fp32) for r < m, zero below.
+__global__ __launch_bounds__(SO_THREADS) void so_eig_gather_kernel(uint8_t* ws, uint32_t ei) {
+    const mo_so_eig& eg = so_eigs(ws)[ei];
+    const int64_t idx = int64_t(blockIdx.x) * SO_THREADS + threadIdx.x;
+    if (idx >= int64_t(eg.m_pad) * eg.m_pad) return;
+    const int64_t r = idx / eg.m_pad, c = idx % eg.m_pad;
+    const int* perm = reinterpret_cast<const int*>(ws + eg.off_perm);
+    const double* E = reinterpret_cast<const double*>(ws + eg.off_E);
+    // a non-finite eigenvalue has no order: its slot may hold a padding index
+    // (up to the sort's power of two), so the row read is bounded here
+    float v = 0.f;
+    if (r < eg.m) {
+        const int64_t pr = perm[r];
+        v = pr < eg.m_pad ? float(E[pr * eg.m_pad + c]) : __builtin_nanf("");
+    }
+    reinterpret_cast<float*>(ws + eg.off_E32)[idx] = v;
+}
+
+}  // namespace
+
+// ============================================================================
+// launchers
+// ============================================================================
+
+hipError_t mo_launch_so_prep(const mo_so_mat& mt, uint8_t* ws, uint32_t mi, hipStream_t s) {
+    const int64_t total = int64_t(mt.r_pad) * mt.c_pad;
+    hipLaunchKernelGGL(so_prep_kernel, dim3(unsigned((total + SO_THREADS - 1) / SO_THREADS)), dim3(SO_THREADS),
+                       0, s, ws, mi);
+    return hipGetLastError();
+}
+
+hipError_t mo_launch_so_gemm(const mo_so_mat& mt, uint8_t* ws, uint32_t mi, int kind, hipStream_t s) {
+    uint32_t rows = mt.r_pad, cols = mt.c_pad;
+    if (kind == MO_SOK_STATS_L) cols = mt.r_pad;
+    if (kind == MO_SOK_STATS_R) rows = mt.c_pad;
+    hipLaunchKernelGGL(so_gemm_kernel, dim3(cols / GB, rows / GB), dim3(SO_THREADS), 0, s, ws, mi, kind);
+    return hipGetLastError();
+}
+
+hipError_t mo_launch_so_eig_init(const mo_so_eig& eg, uint8_t* ws, uint32_t ei, hipStream_t s) {
+    const int64_t total = int64_t(eg.m_pad) * eg.m_pad;
+    hipLaunchKernelGGL(so_eig_init_kernel, dim3(unsigned((total + SO_THREADS - 1) / SO_THREADS)),
+                       dim3(SO_THREADS), 0, s, ws, ei);
+    return hipGetLastError();
+}
+
+hipError_t mo_launch_so_solve(const mo_so_header& h, uint8_t* ws, uint32_t k, hipStream_t s) {
+    hipLaunchKernelGGL(so_jac_solve_kernel, dim3(h.n_solve_items), dim3(SO_THREADS), 0, s, ws, k);
+    return hipGetLastError();
+}
+
+hipError_t mo_launch_so_apply(const mo_so_header& h, uint8_t* ws, uint32_t k, hipStream_t s) {
+    hipLaunchKernelGGL(so_jac_apply_kernel, dim3(h.n_apply_items), dim3(SO_THREADS), 0, s, ws, k);
+    return hipGetLastError();
+}
+
+hipError_t mo_launch_so_sort(const mo_so_header& h, uint8_t* ws, hipStream_t s) {
+    hipLaunchKernelGGL(so_eig_sort_kernel, dim3(h.n_eigs), dim3(SORT_THREADS), 0, s, ws);
+    return hipGetLastError();
+}
+
+hipError_t mo_launch_so_gather(const mo_so_eig& eg, uint8_t* ws, uint32_t ei, hipStream_t s) {
+    const int64_t total = int64_t(eg.m_pad) * eg.m_pad;
+    hipLaunchKernelGGL(so_eig_gather_kernel, dim3(unsigned((total + SO_THREADS - 1) / SO_THREADS)),
+                       dim3(SO_THREADS), 0, s, ws, ei);
+    return hipGetLastError();
+}

@@ -276,6 +276,63 @@ def shampoo_flops_algorithmic(rows: int, cols: int, root_iters: int) -> dict:
     return out
 
 
+@dataclasses.dataclass(frozen=True)
+class SoapHP:
+    """SOAP settings.  The pages run SOAP on the owners (§5.7) without printing
+    its settings; the plain reading: Adam's defaults (lr 1e-3, betas 0.9 and
+    0.999, eps 1e-8), no weight decay, statistics started at eps I with
+    eps = 1e-6 (as the Shampoo workloads), ten outer Jacobi sweeps."""
+    lr: float = 1e-3
+    beta1: float = 0.9
+    beta2: float = 0.999
+    eps: float = 1e-8
+    weight_decay: float = 0.0
+    stat_eps: float = 1e-6
+    sweeps: int = 10
+
+
+@dataclasses.dataclass(frozen=True)
+class SoapWorkload:
+    key: str
+    seed: int
+    matrices: Tuple[MatrixSpec, ...]
+    w_dtype: str = F32
+    g_dtype: str = F32
+    hp: SoapHP = SoapHP()
+    w_std: float = 0.02
+    g_std: float = 1e-3
+    description: str = ""
+
+
+SOAP_WORKLOADS = {
+    "soap_decoder_layer_h2048": SoapWorkload(
+        key="soap_decoder_layer_h2048", seed=14, matrices=tuple(_decoder_layer(2048, 5632, 2048)),
+        description="one decoder-layer owner bucket, hidden 2048, FFN 5632, fp32 weights and gradients"),
+}
+
+
+def soap_jacobi_flops(m: int, sweeps: int) -> dict:
+    """Flops of the blocked Jacobi eigensolver on one side m as built: per round,
+    every upper 64 x 64 tile pair of A takes two 64^3 products (C = X + X D_J,
+    A' = C + D_I^T C) and every 64 x 64 tile of E one; the pair problems take
+    INNER (3) scalar sweeps of 63 steps over a 64 x 64 matrix, each step about
+    6 flops per element of S and of D (counted as 12 * 64^2 per step)."""
+    P = (m + 63) // 64
+    rounds = sweeps * (2 * P - 1)
+    t3 = 2.0 * 64 ** 3
+    apply = rounds * (P * (P + 1) / 2 * 2 * t3 + P * P * t3)
+    solve = rounds * P * 3 * 63 * 12.0 * 64 * 64
+    return {"apply": apply, "solve": solve, "rounds": rounds}
+
+
+def soap_product_flops(rows: int, cols: int) -> float:
+    """The two statistics products and the six eigenbasis products (fp32), as
+    computed on the padded sides."""
+    r = (rows + 63) // 64 * 64
+    c = (cols + 63) // 64 * 64
+    return 2.0 * r * r * c + 2.0 * c * c * r + 3 * (2.0 * r * r * c + 2.0 * r * c * c)
+
+
 # ----------------------------------------------------------------------------
 # value generation
 # ----------------------------------------------------------------------------

@@ -1,0 +1,213 @@
+"""SOAP owner step on the GPU (soap_owner_step through the C ABI) against the
+fp64 oracle (oracle/soap.py), on the same stored inputs.
+
+Tolerance.  The step is fp32 except for its eigensolver (fp64).  Its update
+depends on the eigenvectors of the fp32 statistics, and where two eigenvalues
+are closer than the fp32 rounding of L' or R' can separate, the fp32
+statistics alone move those eigenvectors: the error of an fp32 step has a
+floor set by the conditioning of each input, not by the implementation.  The
+test measures that floor on the same stored inputs with a plain fp32 model of
+the step whose eigenvectors are exact (numpy's fp64 eigh of the fp32
+statistics, rounded once), and requires the GPU update within
+max(1e-4, 4 x floor) relative Frobenius of the oracle's; on most draws the
+floor is 2e-6 .. 2e-5, so the bar is the 1e-4 of the fp32 Muon path.  The
+statistics and the first moment are plain fp32 sums (1e-6); the warm second
+moment is dominated by b2 V (1e-6), the first one is (1 - b2) G~^2 (twice the
+update's bar).
+
+Workload: warm states (statistics summed over ten earlier gradients, M and V
+drawn as state, t = 10), where the step is well posed in fp32 (every shape
+keeps both statistics of full rank: a repeated eigenvalue with non-zero
+moments in its eigenspace would make the update depend on the basis chosen
+inside it); and a first
+step from zero moments with an Adam eps of 1e-3 (with a small eps the first
+step is a sign function of the rotated gradient, whose fp32 rounding of
+exactly-zero entries no fp32 implementation reproduces).
+"""
+import numpy as np
+import pytest
+
+from oracle import soap as osoap
+
+pytestmark = pytest.mark.gpu
+
+F32 = np.float32
+
+
+def rel(a, b):
+    return float(np.linalg.norm(np.asarray(a, np.float64) - b) / np.linalg.norm(b))
+
+
+def seeded(seed, *key):
+    return np.random.default_rng(np.random.SeedSequence([seed, *key]))
+
+
+def warm_state(seed, r, c, history=10):
+    """Stored (fp32-rounded) inputs of one warm matrix, as fp64 arrays."""
+    rng = seeded(seed, r, c)
+    q = lambda x: np.asarray(x, F32).astype(np.float64)
+    W = q(rng.normal(0, 0.02, (r, c)))
+    G = q(rng.normal(0, 1e-3, (r, c)))
+    L = 1e-6 * np.eye(r)
+    R = 1e-6 * np.eye(c)
+    for _ in range(history):
+        Gp = rng.normal(0, 1e-3, (r, c))
+        L += Gp @ Gp.T
+        R += Gp.T @ Gp
+    M = q(rng.normal(0, 1e-3, (r, c)))
+    V = q(rng.normal(0, 1e-3, (r, c)) ** 2)
+    return dict(W=W, G=G, L=q(L), R=q(R), M=M, V=V)
+
+
+def first_state(seed, r, c, eps_stat=1e-6):
+    rng = seeded(seed, r, c, 1)
+    q = lambda x: np.asarray(x, F32).astype(np.float64)
+    return dict(W=q(rng.normal(0, 0.02, (r, c))), G=q(rng.normal(0, 1e-3, (r, c))),
+                L=q(eps_stat * np.eye(r)), R=q(eps_stat * np.eye(c)), M=np.zeros((r, c)), V=np.zeros((r, c)))
+
+
+def fp32_floor(st, step, hp):
+    """Relative error of an fp32 step whose eigenvectors are exact (rounded once)."""
+    G = st["G"].astype(F32)
+    L1 = st["L"].astype(F32) + G @ G.T
+    R1 = st["R"].astype(F32) + G.T @ G
+    EL = np.linalg.eigh(L1.astype(np.float64))[1].T.astype(F32)
+    ER = np.linalg.eigh(R1.astype(np.float64))[1].T.astype(F32)
+    b1, b2 = F32(hp["beta1"]), F32(hp["beta2"])
+    M1 = b1 * st["M"].astype(F32) + (F32(1) - b1) * G
+    Gr = EL @ G @ ER.T
+    Mr = EL @ M1 @ ER.T
+    V1 = b2 * st["V"].astype(F32) + (F32(1) - b2) * Gr * Gr
+    N = (Mr / F32(1 - hp["beta1"] ** step)) / (np.sqrt(V1 / F32(1 - hp["beta2"] ** step)) + F32(hp["eps"]))
+    return F32(hp["lr"]) * (EL.T @ N @ ER)
+
+
+HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+
+
+def run_gpu(states, step, hp, w_dtype="f32", g_dtype="f32", sweeps=10):
+    import torch
+    import matrix_optimizers_amd as mo
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16}
+    dev = torch.device("cuda:0")
+    mats, ups = [], []
+    for st in states:
+        t = lambda x, d=torch.float32: torch.tensor(np.asarray(x, F32), device=dev).to(d).contiguous()
+        mats.append((t(st["W"], dt[w_dtype]), t(st["G"], dt[g_dtype]), t(st["L"]), t(st["R"]), t(st["M"]),
+                     t(st["V"])))
+        ups.append(torch.empty(st["W"].shape, dtype=torch.float32, device=dev))
+    mo.soap_owner_step(mats, update_out=ups, step=step, sweeps=sweeps, **hp)
+    torch.cuda.synchronize()
+    to = lambda x: x.float().cpu().numpy().astype(np.float64)
+    return [dict(W=to(m[0]), L=to(m[2]), R=to(m[3]), M=to(m[4]), V=to(m[5]), U=to(u)) for m, u in zip(mats, ups)]
+
+
+def check(st, out, step, hp, label):
+    W1, L1, R1, M1, V1, D = osoap.soap_step(st["W"], st["G"], st["L"], st["R"], st["M"], st["V"], step,
+                                            hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"])
+    floor = rel(fp32_floor(st, step, hp), D)
+    tol = max(1e-4, 4 * floor)
+    err = rel(out["U"], D)
+    print(f"{label}: update {err:.2e} (fp32 floor {floor:.2e}, tol {tol:.2e}); "
+          f"L {rel(out['L'], L1):.1e} R {rel(out['R'], R1):.1e} M {rel(out['M'], M1):.1e} "
+          f"V {rel(out['V'], V1):.1e}", flush=True)
+    assert np.all(np.isfinite(out["U"]))
+    assert err <= tol
+    assert rel(out["L"], L1) <= 1e-6 and rel(out["R"], R1) <= 1e-6
+    assert rel(out["M"], M1) <= 1e-6
+    # V' = b2 V + (1 - b2) G~^2: near b2 V's rounding when V is warm; from V = 0
+    # it carries twice the relative error of the rotated gradient, which is of
+    # the update's kind
+    assert rel(out["V"], V1) <= max(1e-6, 2 * tol)
+    # W' = (1 - lr wd) W - update, in fp32
+    decay = F32(1 - hp["lr"] * hp["weight_decay"])
+    Wexp = (decay * st["W"].astype(F32) - out["U"].astype(F32)).astype(np.float64)
+    assert np.max(np.abs(out["W"] - Wexp)) <= 4 * np.finfo(F32).eps * np.max(np.abs(Wexp))
+
+
+@pytest.mark.parametrize("shape", [(96, 160), (200, 136), (64, 64), (2, 16), (33, 5)])
+def test_warm_step(gpu, shape):
+    st = warm_state(11, *shape)
+    out = run_gpu([st], 10, HP)[0]
+    check(st, out, 10, HP, f"warm {shape}")
+
+
+def test_mixed_bucket_with_empty_shard(gpu):
+    """One launch sequence over several shapes; each matrix's result is the one
+    it gets alone (rows = 0 marks a skipped shard)."""
+    import torch
+    import matrix_optimizers_amd as mo
+    shapes = [(128, 192), (70, 130), (256, 64)]
+    states = [warm_state(21, *s) for s in shapes]
+    outs = run_gpu(states, 10, HP)
+    for s, st, out in zip(shapes, states, outs):
+        check(st, out, 10, HP, f"bucket {s}")
+    alone = run_gpu([states[1]], 10, HP)[0]
+    assert np.array_equal(alone["U"], outs[1]["U"])
+    # an empty shard in the descriptor list changes nothing
+    dev = torch.device("cuda:0")
+    e = torch.empty((0, 5), device=dev)
+    mo.soap_owner_step([(e, e, torch.empty((0, 0), device=dev), torch.empty((5, 5), device=dev), e, e)],
+                       step=1, **HP)
+    torch.cuda.synchronize()
+
+
+def test_first_step_large_eps(gpu):
+    hp = dict(HP, eps=1e-3)
+    st = first_state(31, 120, 200)
+    out = run_gpu([st], 1, hp)[0]
+    check(st, out, 1, hp, "first step (eps 1e-3)")
+
+
+def test_bf16_weight_and_gradient(gpu):
+    st = warm_state(41, 96, 160)
+    q = lambda x: np.asarray(x, np.float64)
+    import torch
+    bf = lambda a: torch.tensor(np.asarray(a, F32)).to(torch.bfloat16).float().numpy().astype(np.float64)
+    st = dict(st, W=bf(st["W"]), G=bf(st["G"]))
+    out = run_gpu([st], 10, HP, w_dtype="bf16", g_dtype="bf16")[0]
+    W1, L1, R1, M1, V1, D = osoap.soap_step(st["W"], st["G"], st["L"], st["R"], st["M"], st["V"], 10,
+                                            HP["lr"], HP["beta1"], HP["beta2"], HP["eps"], HP["weight_decay"])
+    floor = rel(fp32_floor(st, 10, HP), D)
+    assert rel(out["U"], D) <= max(1e-4, 4 * floor)
+    # W' is rounded once into bf16: within half a bf16 unit of decay W - update
+    Wexp = (1 - HP["lr"] * HP["weight_decay"]) * st["W"] - out["U"]
+    assert np.all(np.abs(out["W"] - Wexp) <= 2.0 ** -8 * np.abs(Wexp) + 1e-30)
+    assert q(out["M"]).shape == st["M"].shape
+
+
+def test_two_steps_carry_state(gpu):
+    """The state written by one call is the input of the next."""
+    import torch
+    import matrix_optimizers_amd as mo
+    st = warm_state(51, 80, 144)
+    rng = seeded(51, 2)
+    G2 = np.asarray(rng.normal(0, 1e-3, st["G"].shape), F32).astype(np.float64)
+    dev = torch.device("cuda:0")
+    t = lambda x: torch.tensor(np.asarray(x, F32), device=dev).contiguous()
+    W, G, L, R, M, V = (t(st[k]) for k in ("W", "G", "L", "R", "M", "V"))
+    U = torch.empty_like(W)
+    step = mo.SoapOwnerStep([(W, G, L, R, M, V)], update_out=[U], sweeps=10, **HP)
+    step(10)
+    G.copy_(t(G2))
+    step(11)
+    torch.cuda.synchronize()
+    o1 = osoap.soap_step(st["W"], st["G"], st["L"], st["R"], st["M"], st["V"], 10, HP["lr"], HP["beta1"],
+                         HP["beta2"], HP["eps"], HP["weight_decay"])
+    o2 = osoap.soap_step(o1[0], G2, o1[1], o1[2], o1[3], o1[4], 11, HP["lr"], HP["beta1"], HP["beta2"],
+                         HP["eps"], HP["weight_decay"])
+    err = rel(U.cpu().numpy(), o2[5])
+    st2 = dict(W=o1[0], G=G2, L=o1[1], R=o1[2], M=o1[3], V=o1[4])
+    floor = rel(fp32_floor(st2, 11, HP), o2[5])
+    print(f"two steps: update {err:.2e} (fp32 floor of the second step {floor:.2e})", flush=True)
+    # the second step also carries the first step's fp32 state
+    assert err <= max(2e-4, 8 * floor)
+    assert rel(L.cpu().numpy(), o2[1]) <= 1e-6
+
+
+def test_deterministic(gpu):
+    st = warm_state(61, 100, 100)
+    a = run_gpu([st], 10, HP)[0]
+    b = run_gpu([st], 10, HP)[0]
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
