@@ -181,10 +181,11 @@ const char* mo_status_string(mo_status status);
 #define MO_PHASE_SO_PREP    15  /* SOAP: padded G, first moment M' */
 #define MO_PHASE_SO_STATS   16  /* SOAP: L' = L + G G^T, R' = R + G^T G */
 #define MO_PHASE_SO_SOLVE   17  /* SOAP: Jacobi pair problems of one round */
-#define MO_PHASE_SO_APPLY   18  /* SOAP: one round's rotations applied to A and E */
+#define MO_PHASE_SO_APPLY   18  /* SOAP: one round's rotations applied to A (both sides) */
 #define MO_PHASE_SO_SORT    19  /* SOAP: E = I, eigenvalue sort, sorted fp32 eigenvectors */
 #define MO_PHASE_SO_ROTATE  20  /* SOAP: the six eigenbasis products, V', N and W written */
-#define MO_PHASE_COUNT    21
+#define MO_PHASE_SO_ETILE   21  /* SOAP: one round's rotations applied to the eigenvectors E */
+#define MO_PHASE_COUNT    22
 
 /* Enable (1) or disable (0) per-launch timing on the calling thread.  While
  * enabled, every kernel launch is bracketed by HIP events on its own stream;
@@ -290,7 +291,9 @@ mo_status shampoo_owner_step(const mo_shampoo_matrix* mats, int32_t n_mats,
  *   update      N = (M~ / (1 - b1^t)) / (sqrt(V' / (1 - b2^t)) + eps);
  *               W' = (1 - lr wd) W - lr Q_L N Q_R^T
  * The eigenvectors come from a two-sided blocked Jacobi method in fp64
- * (`sweeps` sweeps of all block pairs, rotations in Rutishauser's form); the
+ * (`sweeps` sweeps of all block pairs, rotations in Rutishauser's form; a
+ * rotation whose off-diagonal entry is below fp64's resolution of its two
+ * diagonal entries, |a_pq| <= 2^-52 sqrt(|a_pp a_qq|), is skipped); the
  * statistics, moments and products are fp32.  Sides are at most 8192. */
 
 /* One whole matrix with its SOAP state.
@@ -332,8 +335,9 @@ mo_status soap_workspace_bytes(const mo_soap_matrix* mats, int32_t n_mats,
                                const mo_soap_hparams* hp, size_t* bytes);
 
 /* One SOAP step on every non-empty matrix of the bucket.  The eigensolver's
- * launches are grouped over every statistics matrix of the bucket (two per
- * round, sweeps x (m_pad / 32 - 1) rounds for the longest side); the rest is
+ * launches are grouped over every statistics matrix of the bucket (three per
+ * round, sweeps x (m_pad / 32 - 1) rounds for the longest side; a pair
+ * left unrotated in a round costs its tiles nothing); the rest is
  * a few launches per matrix.  Workspace, stream and error conventions as
  * muon_owner_step: MO_ERR_INVALID_ARG (null pointer with numel > 0, negative
  * size, a stride below its row length, step < 1, sweeps outside 1 .. 100,

@@ -29,7 +29,7 @@ LR_ADJUST = {"original": 0, "match_rms_adamw": 1, "none": 2}
 
 PHASES = ["momentum", "norm", "gram", "poly", "update", "apply", "adamw", "copy", "update_last",
           "sh_layout", "sh_stats", "sh_rootprep", "sh_root", "sh_left", "sh_right",
-          "so_prep", "so_stats", "so_solve", "so_apply", "so_sort", "so_rotate"]
+          "so_prep", "so_stats", "so_solve", "so_apply", "so_sort", "so_rotate", "so_etile"]
 
 
 class MoError(RuntimeError):
@@ -444,7 +444,7 @@ def shampoo_owner_step(mats: Sequence[Tuple], *, update_out: Optional[Sequence] 
 # ---------------------------------------------------------------------------
 
 def soap_hparams(lr: float = 1e-3, beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,
-                 weight_decay: float = 0.0, step: int = 1, sweeps: int = 10) -> MoSoapHParams:
+                 weight_decay: float = 0.0, step: int = 1, sweeps: int = 14) -> MoSoapHParams:
     return MoSoapHParams(lr=lr, beta1=beta1, beta2=beta2, eps=eps, weight_decay=weight_decay,
                          step=int(step), sweeps=int(sweeps))
 

@@ -35,10 +35,11 @@ struct mo_so_header {
     uint32_t magic, version;
     uint32_t n_mats, n_eigs;
     uint32_t sweeps, max_rounds;          // outer Jacobi sweeps; rounds of the longest eigendecomposition
-    uint32_t n_solve_items, n_apply_items;
+    uint32_t n_solve_items, n_apply_items; // pair problems; upper 64 x 64 tiles of A
     uint64_t mats_offset, eigs_offset;    // bytes from list start
     uint64_t wl_bytes, ws_bytes;
-    uint32_t reserved[4];
+    uint32_t n_etile_items;               // 64 x 64 tiles of E
+    uint32_t reserved[3];
 };
 
 struct mo_so_mat {
@@ -55,17 +56,19 @@ struct mo_so_mat {
 // m_pad = 64 P: A (fp64, m_pad x m_pad) is rotated toward diagonal form, E
 // (fp64) accumulates the rotations (rows are eigenvectors), D holds the P
 // pair rotations of the current round (fp64, 64 x 64 each, as V - I), E32 the
-// eigenvectors sorted by ascending eigenvalue (fp32), perm the sort.
+// eigenvectors sorted by ascending eigenvalue (fp32), perm the sort, flag
+// one word per pair: whether its rotation of the current round is not the
+// identity.
 struct mo_so_eig {
-    uint64_t off_A, off_E, off_D, off_E32, off_perm;
+    uint64_t off_A, off_E, off_D, off_E32, off_perm, off_flag;
     uint64_t ext;                         // caller statistics (L or R), m x m fp32, row stride ld_ext
     int64_t  ld_ext;
     uint32_t m, m_pad, P, mat;
     uint32_t rounds;                      // sweeps x (2P - 1)
     uint32_t solve_begin, apply_begin;    // first item of this decomposition in each grouped launch
-    uint32_t reserved;
+    uint32_t etile_begin;
 };
 
 static_assert(sizeof(mo_so_header) == 80, "header layout");
 static_assert(sizeof(mo_so_mat) == 176, "matrix record layout");
-static_assert(sizeof(mo_so_eig) == 88, "eig record layout");
+static_assert(sizeof(mo_so_eig) == 96, "eig record layout");

@@ -9,7 +9,8 @@
 //   stats       per matrix: L' = L + G G^T, R' = R + G^T G (+ fp64 copies)
 //   E = I       per statistics matrix
 //   rounds      grouped over all statistics matrices: pair problems, then
-//               their rotations applied to A and E (two launches per round)
+//               their rotations applied to A and to E (three launches per
+//               round)
 //   sort        eigenvalues ascending, sorted fp32 eigenvectors
 //   products    per matrix: Q_L^T G, x Q_R (V'), Q_L^T M', x Q_R (N), Q_L N,
 //               x Q_R^T (W)
@@ -93,7 +94,7 @@ void build_plan(const mo_soap_matrix* mats, int32_t n, const mo_soap_hparams* hp
     std::vector<mo_so_eig>& eigs = plan->eigs;
     recs.clear();
     eigs.clear();
-    uint32_t solve_items = 0, apply_items = 0, max_rounds = 0;
+    uint32_t solve_items = 0, apply_items = 0, etile_items = 0, max_rounds = 0;
     auto add_eig = [&](uint32_t m, uint32_t mat, const float* ext, int64_t ld_ext) {
         mo_so_eig e;
         std::memset(&e, 0, sizeof(e));
@@ -106,8 +107,10 @@ void build_plan(const mo_soap_matrix* mats, int32_t n, const mo_soap_hparams* hp
         e.rounds = uint32_t(hp->sweeps) * (2 * e.P - 1);
         e.solve_begin = solve_items;
         e.apply_begin = apply_items;
+        e.etile_begin = etile_items;
         solve_items += e.P;
-        apply_items += e.P * (e.P + 1) / 2 + e.P * e.P;
+        apply_items += e.P * (e.P + 1) / 2;
+        etile_items += e.P * e.P;
         max_rounds = std::max(max_rounds, e.rounds);
         eigs.push_back(e);
         return uint32_t(eigs.size() - 1);
@@ -159,6 +162,7 @@ void build_plan(const mo_soap_matrix* mats, int32_t n, const mo_soap_hparams* hp
     h.max_rounds = max_rounds;
     h.n_solve_items = solve_items;
     h.n_apply_items = apply_items;
+    h.n_etile_items = etile_items;
     uint64_t off = align_up(sizeof(mo_so_header), MO_WS_ALIGN);
     h.mats_offset = off;
     off = align_up(off + uint64_t(nm) * sizeof(mo_so_mat), MO_WS_ALIGN);
@@ -180,6 +184,7 @@ void build_plan(const mo_soap_matrix* mats, int32_t n, const mo_soap_hparams* hp
         e.off_D = take(uint64_t(e.P) * 64 * 64 * 8);
         e.off_E32 = take(mm * 4);
         e.off_perm = take(uint64_t(e.m_pad) * 4);
+        e.off_flag = take(uint64_t(e.P) * 4);
     }
     h.ws_bytes = off;
     plan->header = h;
@@ -239,6 +244,7 @@ mo_status soap_owner_step(const mo_soap_matrix* mats, int32_t n, const mo_soap_h
     for (uint32_t k = 0; k < h.max_rounds; ++k) {
         if (!ok(MO_PHASE_SO_SOLVE, [&] { return mo_launch_so_solve(h, ws, k, s); })) return MO_ERR_HIP;
         if (!ok(MO_PHASE_SO_APPLY, [&] { return mo_launch_so_apply(h, ws, k, s); })) return MO_ERR_HIP;
+        if (!ok(MO_PHASE_SO_ETILE, [&] { return mo_launch_so_etile(h, ws, k, s); })) return MO_ERR_HIP;
     }
     if (!ok(MO_PHASE_SO_SORT, [&] { return mo_launch_so_sort(h, ws, s); })) return MO_ERR_HIP;
     for (uint32_t e = 0; e < h.n_eigs; ++e)

@@ -253,11 +253,15 @@ __global__ __launch_bounds__(SO_THREADS) void so_eig_init_kernel(uint8_t* ws, ui
 }
 
 // Rotation that zeroes S[a][b] of the symmetric 2 x 2 problem (app, apq; apq, aqq):
-// t = tan, s = sin, tau = sin / (1 + cos) (Rutishauser's formulas).
-MO_DEV void jacobi_rotation(double app, double aqq, double apq, double& t, double& s, double& tau) {
-    if (apq == 0.0) {
+// t = tan, s = sin, tau = sin / (1 + cos) (Rutishauser's formulas).  An
+// off-diagonal entry below fp64's resolution of the two diagonal entries,
+// |apq| <= 2^-52 sqrt(|app aqq|), is left as it is (no rotation): zeroing it
+// would change the matrix by less than its own rounding.  Returns whether it
+// rotates.
+MO_DEV bool jacobi_rotation(double app, double aqq, double apq, double& t, double& s, double& tau) {
+    if (fabs(apq) <= 0x1p-52 * sqrt(fabs(app * aqq))) {
         t = s = tau = 0.0;
-        return;
+        return false;
     }
     const double theta = (aqq - app) / (2.0 * apq);
     if (fabs(theta) > 1e150) {
@@ -268,16 +272,19 @@ MO_DEV void jacobi_rotation(double app, double aqq, double apq, double& t, doubl
     const double c = 1.0 / sqrt(t * t + 1.0);
     s = t * c;
     tau = s / (1.0 + c);
+    return true;
 }
 
 // One workgroup per (decomposition, block pair) of round k: diagonalise the
-// 64 x 64 pair problem S = A[pair][pair] by INNER_SWEEPS scalar cyclic sweeps
-// and store its rotation as D = V - I (V^T S V ~ diagonal).
+// 64 x 64 pair problem S = A[pair][pair] by at most INNER_SWEEPS scalar cyclic
+// sweeps (it stops after a sweep without a rotation) and store its rotation as
+// D = V - I (V^T S V ~ diagonal), and whether it rotated at all.
 __global__ __launch_bounds__(SO_THREADS) void so_jac_solve_kernel(uint8_t* ws, uint32_t k) {
     __shared__ double S[PW][PW + 1];
     __shared__ double D[PW][PW + 1];
     __shared__ double rs[PW / 2], rtau[PW / 2], rt[PW / 2], rapq[PW / 2];
     __shared__ int ra[PW / 2], rb[PW / 2];
+    __shared__ int rotated[2];   // per sweep parity: a rotation happened
     const mo_so_header* h = so_header(ws);
     const mo_so_eig* eigs = so_eigs(ws);
     const mo_so_eig& eg = eigs[find_rec(eigs, h->n_eigs, blockIdx.x, &mo_so_eig::solve_begin)];
@@ -293,17 +300,33 @@ __global__ __launch_bounds__(SO_THREADS) void so_jac_solve_kernel(uint8_t* ws, u
         S[r][c] = A[pair_index(bp, bq, r) * eg.m_pad + pair_index(bp, bq, c)];
         D[r][c] = 0.0;
     }
+    if (t == 0) rotated[0] = rotated[1] = 0;
     __syncthreads();
-    for (int sweep = 0; sweep < INNER_SWEEPS; ++sweep) {
+    // Already diagonal to fp64 resolution (every off-diagonal entry below the
+    // rotation threshold): no sweep would rotate, D stays zero.  The test uses
+    // flag 1, which sweep 0 first clears at its step 1, after every thread has
+    // passed step 0's barrier and so has read it here.
+    for (int q = t; q < PW * PW; q += SO_THREADS) {
+        const int r = q / PW, c = q % PW;
+        if (r != c && fabs(S[r][c]) > 0x1p-52 * sqrt(fabs(S[r][r] * S[c][c]))) rotated[1] = 1;
+    }
+    __syncthreads();
+    const int n_sweeps = rotated[1] ? INNER_SWEEPS : 0;
+    bool any = false;
+    for (int sweep = 0; sweep < n_sweeps; ++sweep) {
         for (int step = 0; step < PW - 1; ++step) {
             if (t < PW / 2) {
                 int a, b;
                 circle_pair(PW, step, t, a, b);
                 double tt, s, tau;
                 const double apq = S[a][b];
-                jacobi_rotation(S[a][a], S[b][b], apq, tt, s, tau);
+                if (jacobi_rotation(S[a][a], S[b][b], apq, tt, s, tau)) rotated[sweep & 1] = 1;
                 ra[t] = a; rb[t] = b; rs[t] = s; rtau[t] = tau; rt[t] = tt; rapq[t] = apq;
             }
+            // Clear the other parity's flag for the next sweep.  Every thread
+            // read it (the stop test of the previous sweep) before the barrier
+            // of this sweep's step 0, so the clear waits for step 1.
+            if (t == 0 && step == 1) rotated[(sweep + 1) & 1] = 0;
             __syncthreads();
             // two-sided update of the 2 x 2 blocks (u, v), u <= v, mirrored
             for (int q = t; q < (PW / 2) * (PW / 2); q += SO_THREADS) {
@@ -311,6 +334,7 @@ __global__ __launch_bounds__(SO_THREADS) void so_jac_solve_kernel(uint8_t* ws, u
                 if (u > v) continue;
                 const int au = ra[u], bu = rb[u];
                 if (u == v) {
+                    if (rs[u] == 0.0) continue;   // not rotated: S[a][b] stays
                     const double tt = rt[u], apq = rapq[u];
                     S[au][au] -= tt * apq;
                     S[bu][bu] += tt * apq;
@@ -344,14 +368,45 @@ __global__ __launch_bounds__(SO_THREADS) void so_jac_solve_kernel(uint8_t* ws, u
             }
             __syncthreads();
         }
+        if (!rotated[sweep & 1]) break;   // uniform: read after the barrier
+        any = true;
     }
     double* Dout = reinterpret_cast<double*>(ws + eg.off_D) + int64_t(j) * PW * PW;
     for (int q = t; q < PW * PW; q += SO_THREADS) Dout[q] = D[q / PW][q % PW];
+    if (t == 0) reinterpret_cast<uint32_t*>(ws + eg.off_flag)[j] = any ? 1u : 0u;
 }
 
-// One workgroup per 64 x 64 tile of round k: an upper tile (I, J) of pairs of
-// A, A' = V_I^T A V_J (mirrored below the diagonal), or a tile (I, columns
-// 64 c ..) of E, E' = V_I^T E.  With V = I + D: C = X + X D_J, A' = C + D_I^T C.
+// Loads the 64 x 64 pair rotation D_I of round k into LDS.
+MO_DEV void load_d(double (*Dl)[PW + 1], const double* Dall, int I) {
+    for (int q = threadIdx.x; q < PW * PW; q += SO_THREADS) Dl[q / PW][q % PW] = Dall[int64_t(I) * PW * PW + q];
+}
+
+// acc[x][y] = sum_k L(r0 + x, k) * Rm[k][c0 + y] over the 64-wide k, with
+// L(r, k) = Lm[r][k] (trans = false) or Lm[k][r] (trans = true).
+template <bool TRANS>
+MO_DEV void tile_product(const double (*Lm)[PW + 1], const double (*Rm)[PW + 1], int r0, int c0,
+                         double (&acc)[4][4]) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) acc[x][y] = 0.0;
+    for (int kk = 0; kk < PW; ++kk) {
+        double a[4], b[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) a[x] = TRANS ? Lm[kk][r0 + x] : Lm[r0 + x][kk];
+#pragma unroll
+        for (int y = 0; y < 4; ++y) b[y] = Rm[kk][c0 + y];
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+            for (int y = 0; y < 4; ++y) acc[x][y] = fma(a[x], b[y], acc[x][y]);
+    }
+}
+
+// One workgroup per upper 64 x 64 tile (I, J) of pairs of A in round k:
+// A' = V_I^T A V_J, mirrored below the diagonal.  With V = I + D:
+// C = X + X D_J, A' = C + D_I^T C.  A tile whose two pairs were not rotated is
+// left untouched (the products would add exact zeros).
 __global__ __launch_bounds__(SO_THREADS) void so_jac_apply_kernel(uint8_t* ws, uint32_t k) {
     __shared__ double X[PW][PW + 1];
     __shared__ double C[PW][PW + 1];
@@ -365,85 +420,83 @@ __global__ __launch_bounds__(SO_THREADS) void so_jac_apply_kernel(uint8_t* ws, u
     const int nb = 2 * P;
     const int kr = int(k % uint32_t(nb - 1));
     int item = int(blockIdx.x - eg.apply_begin);
-    const int n_upper = P * (P + 1) / 2;
-    const bool is_a = item < n_upper;
-    int I = 0, J = 0;
-    if (is_a) {
-        while (item >= P - I) { item -= P - I; ++I; }
-        J = I + item;
-    } else {
-        item -= n_upper;
-        I = item / P;
-        J = item % P;   // column chunk of E
-    }
-    int pI, qI, pJ = 0, qJ = 0;
+    int I = 0;
+    while (item >= P - I) { item -= P - I; ++I; }
+    const int J = I + item;
+    const uint32_t* flag = reinterpret_cast<const uint32_t*>(ws + eg.off_flag);
+    if (!flag[I] && !flag[J]) return;
+    int pI, qI, pJ, qJ;
     circle_pair(nb, kr, I, pI, qI);
-    if (is_a) circle_pair(nb, kr, J, pJ, qJ);
+    circle_pair(nb, kr, J, pJ, qJ);
     const double* Dall = reinterpret_cast<const double*>(ws + eg.off_D);
-    double* M = reinterpret_cast<double*>(ws + (is_a ? eg.off_A : eg.off_E));
+    double* M = reinterpret_cast<double*>(ws + eg.off_A);
     const int64_t ld = eg.m_pad;
     const int t = threadIdx.x;
     for (int q = t; q < PW * PW; q += SO_THREADS) {
         const int r = q / PW, c = q % PW;
-        const int64_t col = is_a ? pair_index(pJ, qJ, c) : int64_t(J) * PW + c;
-        X[r][c] = M[pair_index(pI, qI, r) * ld + col];
-        DI[r][c] = Dall[int64_t(I) * PW * PW + q];
-        if (is_a) DJ[r][c] = Dall[int64_t(J) * PW * PW + q];
+        X[r][c] = M[pair_index(pI, qI, r) * ld + pair_index(pJ, qJ, c)];
     }
+    load_d(DI, Dall, I);
+    load_d(DJ, Dall, J);
     __syncthreads();
     const int r0 = (t / 16) * 4, c0 = (t % 16) * 4;
-    if (is_a) {   // C = X + X D_J
-        double acc[4][4];
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-#pragma unroll
-            for (int y = 0; y < 4; ++y) acc[x][y] = 0.0;
-        for (int kk = 0; kk < PW; ++kk) {
-            double a[4], b[4];
-#pragma unroll
-            for (int x = 0; x < 4; ++x) a[x] = X[r0 + x][kk];
-#pragma unroll
-            for (int y = 0; y < 4; ++y) b[y] = DJ[kk][c0 + y];
-#pragma unroll
-            for (int x = 0; x < 4; ++x)
-#pragma unroll
-                for (int y = 0; y < 4; ++y) acc[x][y] = fma(a[x], b[y], acc[x][y]);
-        }
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-#pragma unroll
-            for (int y = 0; y < 4; ++y) C[r0 + x][c0 + y] = X[r0 + x][c0 + y] + acc[x][y];
-    } else {
-        for (int q = t; q < PW * PW; q += SO_THREADS) C[q / PW][q % PW] = X[q / PW][q % PW];
-    }
-    __syncthreads();
-    // Y = C + D_I^T C
     double acc[4][4];
+    tile_product<false>(X, DJ, r0, c0, acc);   // X D_J
 #pragma unroll
     for (int x = 0; x < 4; ++x)
 #pragma unroll
-        for (int y = 0; y < 4; ++y) acc[x][y] = 0.0;
-    for (int kk = 0; kk < PW; ++kk) {
-        double a[4], b[4];
-#pragma unroll
-        for (int x = 0; x < 4; ++x) a[x] = DI[kk][r0 + x];
-#pragma unroll
-        for (int y = 0; y < 4; ++y) b[y] = C[kk][c0 + y];
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-#pragma unroll
-            for (int y = 0; y < 4; ++y) acc[x][y] = fma(a[x], b[y], acc[x][y]);
-    }
+        for (int y = 0; y < 4; ++y) C[r0 + x][c0 + y] = X[r0 + x][c0 + y] + acc[x][y];
+    __syncthreads();
+    tile_product<true>(DI, C, r0, c0, acc);    // D_I^T C
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
         const int64_t gr = pair_index(pI, qI, r0 + x);
 #pragma unroll
         for (int y = 0; y < 4; ++y) {
             const double val = C[r0 + x][c0 + y] + acc[x][y];
-            const int64_t gc = is_a ? pair_index(pJ, qJ, c0 + y) : int64_t(J) * PW + c0 + y;
+            const int64_t gc = pair_index(pJ, qJ, c0 + y);
             M[gr * ld + gc] = val;
-            if (is_a && I != J) M[gc * ld + gr] = val;
+            if (I != J) M[gc * ld + gr] = val;
         }
+    }
+}
+
+// One workgroup per 64 x 64 tile (pair I, columns 64 c ..) of the accumulated
+// eigenvectors E in round k: E' = V_I^T E = X + D_I^T X.  Half the LDS of the
+// A kernel, so two workgroups share a CU.  Unrotated pairs are skipped.
+__global__ __launch_bounds__(SO_THREADS) void so_jac_etile_kernel(uint8_t* ws, uint32_t k) {
+    __shared__ double X[PW][PW + 1];
+    __shared__ double DI[PW][PW + 1];
+    const mo_so_header* h = so_header(ws);
+    const mo_so_eig* eigs = so_eigs(ws);
+    const mo_so_eig& eg = eigs[find_rec(eigs, h->n_eigs, blockIdx.x, &mo_so_eig::etile_begin)];
+    if (k >= eg.rounds) return;
+    const int P = int(eg.P);
+    const int nb = 2 * P;
+    const int kr = int(k % uint32_t(nb - 1));
+    const int item = int(blockIdx.x - eg.etile_begin);
+    const int I = item / P, cc = item % P;
+    if (!reinterpret_cast<const uint32_t*>(ws + eg.off_flag)[I]) return;
+    int pI, qI;
+    circle_pair(nb, kr, I, pI, qI);
+    const double* Dall = reinterpret_cast<const double*>(ws + eg.off_D);
+    double* E = reinterpret_cast<double*>(ws + eg.off_E);
+    const int64_t ld = eg.m_pad;
+    const int t = threadIdx.x;
+    for (int q = t; q < PW * PW; q += SO_THREADS) {
+        const int r = q / PW, c = q % PW;
+        X[r][c] = E[pair_index(pI, qI, r) * ld + int64_t(cc) * PW + c];
+    }
+    load_d(DI, Dall, I);
+    __syncthreads();
+    const int r0 = (t / 16) * 4, c0 = (t % 16) * 4;
+    double acc[4][4];
+    tile_product<true>(DI, X, r0, c0, acc);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+        const int64_t gr = pair_index(pI, qI, r0 + x);
+#pragma unroll
+        for (int y = 0; y < 4; ++y) E[gr * ld + int64_t(cc) * PW + c0 + y] = X[r0 + x][c0 + y] + acc[x][y];
     }
 }
 
@@ -536,6 +589,11 @@ hipError_t mo_launch_so_solve(const mo_so_header& h, uint8_t* ws, uint32_t k, hi
 
 hipError_t mo_launch_so_apply(const mo_so_header& h, uint8_t* ws, uint32_t k, hipStream_t s) {
     hipLaunchKernelGGL(so_jac_apply_kernel, dim3(h.n_apply_items), dim3(SO_THREADS), 0, s, ws, k);
+    return hipGetLastError();
+}
+
+hipError_t mo_launch_so_etile(const mo_so_header& h, uint8_t* ws, uint32_t k, hipStream_t s) {
+    hipLaunchKernelGGL(so_jac_etile_kernel, dim3(h.n_etile_items), dim3(SO_THREADS), 0, s, ws, k);
     return hipGetLastError();
 }
 

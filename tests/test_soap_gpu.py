@@ -85,7 +85,7 @@ def fp32_floor(st, step, hp):
 HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
 
 
-def run_gpu(states, step, hp, w_dtype="f32", g_dtype="f32", sweeps=10):
+def run_gpu(states, step, hp, w_dtype="f32", g_dtype="f32", sweeps=14):
     import torch
     import matrix_optimizers_amd as mo
     dt = {"f32": torch.float32, "bf16": torch.bfloat16}
@@ -187,7 +187,7 @@ def test_two_steps_carry_state(gpu):
     t = lambda x: torch.tensor(np.asarray(x, F32), device=dev).contiguous()
     W, G, L, R, M, V = (t(st[k]) for k in ("W", "G", "L", "R", "M", "V"))
     U = torch.empty_like(W)
-    step = mo.SoapOwnerStep([(W, G, L, R, M, V)], update_out=[U], sweeps=10, **HP)
+    step = mo.SoapOwnerStep([(W, G, L, R, M, V)], update_out=[U], sweeps=14, **HP)
     step(10)
     G.copy_(t(G2))
     step(11)
@@ -211,3 +211,62 @@ def test_deterministic(gpu):
     b = run_gpu([st], 10, HP)[0]
     for k in a:
         assert np.array_equal(a[k], b[k]), k
+
+
+def test_decoder_layer_full_size(gpu):
+    """The decoder-layer bucket (hidden 2048, FFN 5632) in one call at the
+    default 14 sweeps, from a warm state drawn on the device with torch: the
+    2048 x 2048 matrix against the oracle at its fp32 floor, sampled rows of the
+    5632-sided statistics in fp64, every output finite, and the eigensolver
+    converged (16 sweeps change no update by more than 1e-5 relative)."""
+    import torch
+    import matrix_optimizers_amd as mo
+    from matrix_optimizers_amd import workloads as wlmod
+    wl = wlmod.SOAP_WORKLOADS["soap_decoder_layer_h2048"]
+    dev = torch.device("cuda:0")
+    base = []
+    for i, sp in enumerate(wl.matrices):
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(7000 + i)
+        rnd = lambda std: torch.randn((sp.rows, sp.cols), device=dev, generator=gen) * std
+        W, G = rnd(0.02), rnd(1e-3)
+        L = torch.eye(sp.rows, device=dev) * wl.hp.stat_eps
+        R = torch.eye(sp.cols, device=dev) * wl.hp.stat_eps
+        for _ in range(10):
+            Gp = rnd(1e-3)
+            L += Gp @ Gp.T
+            R += Gp.T @ Gp
+        base.append((W, G, L, R, rnd(1e-3), rnd(1e-3) ** 2))
+    torch.cuda.synchronize()
+    host = [tuple(t.double().cpu().numpy() for t in m) for m in base]
+
+    def run(sweeps):
+        mats = [tuple(t.clone() for t in m) for m in base]
+        ups = [torch.empty_like(m[0]) for m in mats]
+        mo.soap_owner_step(mats, update_out=ups, step=10, sweeps=sweeps, lr=1e-3, beta1=0.9, beta2=0.999,
+                           eps=1e-8, weight_decay=0.01)
+        torch.cuda.synchronize()
+        return mats, ups
+
+    mats, ups = run(14)
+    _, ups16 = run(16)
+    for i, (u, u16) in enumerate(zip(ups, ups16)):
+        assert torch.isfinite(u).all() and torch.isfinite(mats[i][0]).all(), i
+        d = float((u - u16).norm() / u16.norm())
+        print(f"matrix {i} {tuple(u.shape)}: 14 vs 16 sweeps {d:.1e}", flush=True)
+        assert d <= 1e-5, i
+    # matrix 0 (2048 x 2048) against the oracle
+    W, G, L, R, M, V = host[0]
+    st = dict(W=W, G=G, L=L, R=R, M=M, V=V)
+    out = {k: mats[0][j].double().cpu().numpy() for j, k in enumerate(("W", "G", "L", "R", "M", "V"))}
+    out["U"] = ups[0].double().cpu().numpy()
+    check(st, out, 10, dict(HP, weight_decay=0.01), "decoder 2048x2048")
+    # sampled statistics rows of every 5632-sided matrix, in fp64
+    rng = np.random.default_rng(5)
+    for i, (W, G, L, R, M, V) in enumerate(host):
+        rows = rng.choice(G.shape[0], 4, replace=False)
+        Lr = L[rows] + G[rows] @ G.T
+        assert rel(mats[i][2][rows].double().cpu().numpy(), Lr) <= 1e-6, i
+        cols = rng.choice(G.shape[1], 4, replace=False)
+        Rc = R[cols] + G[:, cols].T @ G
+        assert rel(mats[i][3][cols].double().cpu().numpy(), Rc) <= 1e-6, i
