@@ -291,9 +291,10 @@ mo_status shampoo_owner_step(const mo_shampoo_matrix* mats, int32_t n_mats,
  *   update      N = (M~ / (1 - b1^t)) / (sqrt(V' / (1 - b2^t)) + eps);
  *               W' = (1 - lr wd) W - lr Q_L N Q_R^T
  * The eigenvectors come from a two-sided blocked Jacobi method in fp64
- * (`sweeps` sweeps of all block pairs, rotations in Rutishauser's form; a
- * rotation whose off-diagonal entry is below fp64's resolution of its two
- * diagonal entries, |a_pq| <= 2^-52 sqrt(|a_pp a_qq|), is skipped); the
+ * (`sweeps` sweeps of all block pairs, rotations in Rutishauser's form; an
+ * off-diagonal entry at or below 2^-48 ||L'||_F (or ||R'||_F) is left
+ * unrotated, which moves an eigenvector by at most that over its eigenvalue
+ * gap); the
  * statistics, moments and products are fp32.  Sides are at most 8192. */
 
 /* One whole matrix with its SOAP state.

@@ -58,9 +58,10 @@ struct mo_so_mat {
 // pair rotations of the current round (fp64, 64 x 64 each, as V - I), E32 the
 // eigenvectors sorted by ascending eigenvalue (fp32), perm the sort, flag
 // one word per pair: whether its rotation of the current round is not the
-// identity.
+// identity; norm the per-row sums of squares of A and, after them, the
+// rotation threshold 2^-48 ||A||_F (fp64).
 struct mo_so_eig {
-    uint64_t off_A, off_E, off_D, off_E32, off_perm, off_flag;
+    uint64_t off_A, off_E, off_D, off_E32, off_perm, off_flag, off_norm;
     uint64_t ext;                         // caller statistics (L or R), m x m fp32, row stride ld_ext
     int64_t  ld_ext;
     uint32_t m, m_pad, P, mat;
@@ -71,4 +72,4 @@ struct mo_so_eig {
 
 static_assert(sizeof(mo_so_header) == 80, "header layout");
 static_assert(sizeof(mo_so_mat) == 176, "matrix record layout");
-static_assert(sizeof(mo_so_eig) == 96, "eig record layout");
+static_assert(sizeof(mo_so_eig) == 104, "eig record layout");

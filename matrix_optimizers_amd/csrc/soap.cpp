@@ -7,7 +7,7 @@
 // stated with the entry points in mo.h.  Per bucket, stream-ordered:
 //   prep        per matrix: padded G, M' = b1 M + (1 - b1) G
 //   stats       per matrix: L' = L + G G^T, R' = R + G^T G (+ fp64 copies)
-//   E = I       per statistics matrix
+//   E = I       per statistics matrix, and its rotation threshold 2^-48 ||A||_F
 //   rounds      grouped over all statistics matrices: pair problems, then
 //               their rotations applied to A and to E (three launches per
 //               round)
@@ -185,6 +185,7 @@ void build_plan(const mo_soap_matrix* mats, int32_t n, const mo_soap_hparams* hp
         e.off_E32 = take(mm * 4);
         e.off_perm = take(uint64_t(e.m_pad) * 4);
         e.off_flag = take(uint64_t(e.P) * 4);
+        e.off_norm = take(uint64_t(e.m_pad + 1) * 8);
     }
     h.ws_bytes = off;
     plan->header = h;
@@ -239,8 +240,10 @@ mo_status soap_owner_step(const mo_soap_matrix* mats, int32_t n, const mo_soap_h
         if (!ok(MO_PHASE_SO_STATS, [&] { return mo_launch_so_gemm(mt, ws, i, MO_SOK_STATS_R, s); }))
             return MO_ERR_HIP;
     }
-    for (uint32_t e = 0; e < h.n_eigs; ++e)
+    for (uint32_t e = 0; e < h.n_eigs; ++e) {
         if (!ok(MO_PHASE_SO_SORT, [&] { return mo_launch_so_eig_init(plan.eigs[e], ws, e, s); })) return MO_ERR_HIP;
+        if (!ok(MO_PHASE_SO_SORT, [&] { return mo_launch_so_norm(plan.eigs[e], ws, e, s); })) return MO_ERR_HIP;
+    }
     for (uint32_t k = 0; k < h.max_rounds; ++k) {
         if (!ok(MO_PHASE_SO_SOLVE, [&] { return mo_launch_so_solve(h, ws, k, s); })) return MO_ERR_HIP;
         if (!ok(MO_PHASE_SO_APPLY, [&] { return mo_launch_so_apply(h, ws, k, s); })) return MO_ERR_HIP;

@@ -252,14 +252,49 @@ __global__ __launch_bounds__(SO_THREADS) void so_eig_init_kernel(uint8_t* ws, ui
     reinterpret_cast<double*>(ws + eg.off_E)[idx] = (i == j && i < eg.m) ? 1.0 : 0.0;
 }
 
+// Per row of A (one workgroup each), its sum of squares; then, in the row
+// order, ||A||_F and the rotation threshold thr = 2^-48 ||A||_F.  The rotations
+// leave ||A||_F unchanged, and after convergence the off-diagonal entries sit
+// at fp64 rounding of the whole matrix, a few units of 2^-53 ||A||; below thr
+// an entry is left as it is.  Leaving it moves an eigenvector by at most
+// thr / gap, far below what the fp32 statistics fix.
+__global__ __launch_bounds__(SO_THREADS) void so_norm_rows_kernel(uint8_t* ws, uint32_t ei) {
+    __shared__ double red[SO_THREADS];
+    const mo_so_eig& eg = so_eigs(ws)[ei];
+    const double* A = reinterpret_cast<const double*>(ws + eg.off_A) + int64_t(blockIdx.x) * eg.m_pad;
+    double s = 0.0;
+    for (uint32_t c = threadIdx.x; c < eg.m_pad; c += SO_THREADS) s += A[c] * A[c];
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int w = SO_THREADS / 2; w > 0; w >>= 1) {
+        if (int(threadIdx.x) < w) red[threadIdx.x] += red[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) reinterpret_cast<double*>(ws + eg.off_norm)[blockIdx.x] = red[0];
+}
+
+__global__ __launch_bounds__(SO_THREADS) void so_norm_final_kernel(uint8_t* ws, uint32_t ei) {
+    __shared__ double red[SO_THREADS];
+    const mo_so_eig& eg = so_eigs(ws)[ei];
+    double* nrm = reinterpret_cast<double*>(ws + eg.off_norm);
+    double s = 0.0;
+    for (uint32_t r = threadIdx.x; r < eg.m_pad; r += SO_THREADS) s += nrm[r];
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int w = SO_THREADS / 2; w > 0; w >>= 1) {
+        if (int(threadIdx.x) < w) red[threadIdx.x] += red[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) nrm[eg.m_pad] = 0x1p-48 * sqrt(red[0]);
+}
+
 // Rotation that zeroes S[a][b] of the symmetric 2 x 2 problem (app, apq; apq, aqq):
 // t = tan, s = sin, tau = sin / (1 + cos) (Rutishauser's formulas).  An
-// off-diagonal entry below fp64's resolution of the two diagonal entries,
-// |apq| <= 2^-52 sqrt(|app aqq|), is left as it is (no rotation): zeroing it
-// would change the matrix by less than its own rounding.  Returns whether it
-// rotates.
-MO_DEV bool jacobi_rotation(double app, double aqq, double apq, double& t, double& s, double& tau) {
-    if (fabs(apq) <= 0x1p-52 * sqrt(fabs(app * aqq))) {
+// off-diagonal entry at or below the threshold is left as it is (no
+// rotation).  Returns whether it rotates.
+MO_DEV bool jacobi_rotation(double app, double aqq, double apq, double thr, double& t, double& s,
+                            double& tau) {
+    if (fabs(apq) <= thr) {
         t = s = tau = 0.0;
         return false;
     }
@@ -302,13 +337,14 @@ __global__ __launch_bounds__(SO_THREADS) void so_jac_solve_kernel(uint8_t* ws, u
     }
     if (t == 0) rotated[0] = rotated[1] = 0;
     __syncthreads();
-    // Already diagonal to fp64 resolution (every off-diagonal entry below the
-    // rotation threshold): no sweep would rotate, D stays zero.  The test uses
+    // Already diagonal to the rotation threshold (every off-diagonal entry at or
+    // below it): no sweep would rotate, D stays zero.  The test uses
     // flag 1, which sweep 0 first clears at its step 1, after every thread has
     // passed step 0's barrier and so has read it here.
+    const double thr = reinterpret_cast<const double*>(ws + eg.off_norm)[eg.m_pad];
     for (int q = t; q < PW * PW; q += SO_THREADS) {
         const int r = q / PW, c = q % PW;
-        if (r != c && fabs(S[r][c]) > 0x1p-52 * sqrt(fabs(S[r][r] * S[c][c]))) rotated[1] = 1;
+        if (r != c && fabs(S[r][c]) > thr) rotated[1] = 1;
     }
     __syncthreads();
     const int n_sweeps = rotated[1] ? INNER_SWEEPS : 0;
@@ -320,7 +356,7 @@ __global__ __launch_bounds__(SO_THREADS) void so_jac_solve_kernel(uint8_t* ws, u
                 circle_pair(PW, step, t, a, b);
                 double tt, s, tau;
                 const double apq = S[a][b];
-                if (jacobi_rotation(S[a][a], S[b][b], apq, tt, s, tau)) rotated[sweep & 1] = 1;
+                if (jacobi_rotation(S[a][a], S[b][b], apq, thr, tt, s, tau)) rotated[sweep & 1] = 1;
                 ra[t] = a; rb[t] = b; rs[t] = s; rtau[t] = tau; rt[t] = tt; rapq[t] = apq;
             }
             // Clear the other parity's flag for the next sweep.  Every thread
@@ -579,6 +615,14 @@ hipError_t mo_launch_so_eig_init(const mo_so_eig& eg, uint8_t* ws, uint32_t ei, 
     const int64_t total = int64_t(eg.m_pad) * eg.m_pad;
     hipLaunchKernelGGL(so_eig_init_kernel, dim3(unsigned((total + SO_THREADS - 1) / SO_THREADS)),
                        dim3(SO_THREADS), 0, s, ws, ei);
+    return hipGetLastError();
+}
+
+hipError_t mo_launch_so_norm(const mo_so_eig& eg, uint8_t* ws, uint32_t ei, hipStream_t s) {
+    hipLaunchKernelGGL(so_norm_rows_kernel, dim3(eg.m_pad), dim3(SO_THREADS), 0, s, ws, ei);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(so_norm_final_kernel, dim3(1), dim3(SO_THREADS), 0, s, ws, ei);
     return hipGetLastError();
 }
 

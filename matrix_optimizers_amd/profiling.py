@@ -42,7 +42,13 @@ def sources_sha256() -> str:
 
 
 SH_KERNELS = (("sh_gemm_f32", "sh_gemm"), ("sh_layout_kernel", "sh_layout"), ("sh_sumsq_kernel", "sh_sumsq"),
-              ("sh_norm_kernel", "sh_norm"), ("sh_init_kernel", "sh_init"))
+              ("sh_norm_kernel", "sh_norm"), ("sh_init_kernel", "sh_init"),
+              # SOAP step
+              ("so_jac_apply_kernel", "so_apply"), ("so_jac_etile_kernel", "so_etile"),
+              ("so_jac_solve_kernel", "so_solve"), ("so_gemm_kernel", "so_gemm"), ("so_prep_kernel", "so_prep"),
+              ("so_eig_init_kernel", "so_eig_init"), ("so_norm_rows_kernel", "so_norm_rows"),
+              ("so_norm_final_kernel", "so_norm_final"), ("so_eig_sort_kernel", "so_sort"),
+              ("so_eig_gather_kernel", "so_gather"))
 
 
 def short_name(kernel: str) -> Optional[str]:
@@ -157,6 +163,22 @@ def summarize(trace_dir, counter_dir, copy_dirs, out_md, command, workload, copi
     return out_md
 
 
+def trace_summary(trace_dir, out_md, command, workload, note=""):
+    """Per-phase launches and durations from a kernel trace alone (no byte
+    counters)."""
+    stats = kernel_stats(trace_dir)
+    lines = [f"# rocprofv3 summary: {workload}", "", "Commands (run from the repository root on one MI355X):", "",
+             "```", command, "```", ""]
+    if note:
+        lines += [note, ""]
+    lines += ["| phase | launches | avg (us) | total (ms) |", "|---|---|---|---|"]
+    for name, d in sorted(stats.items(), key=lambda kv: -kv[1]["total_ns"]):
+        lines.append(f"| {name} | {d['calls']} | {d['avg_ns'] / 1e3:.2f} | {d['total_ns'] / 1e6:.3f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return out_md
+
+
 def read_traffic(profiles_dir: str, workload: str, phase: str) -> Optional[dict]:
     """HBM bytes per launch of `phase` measured on the current kernel sources,
     or None if no summary matches them."""
@@ -236,7 +258,17 @@ def _main():
     c.add_argument("pass_dirs", nargs="+")
     c.add_argument("--command", required=True)
     c.add_argument("--workload", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("trace_dir")
+    t.add_argument("out_md")
+    t.add_argument("--command", required=True)
+    t.add_argument("--workload", required=True)
+    t.add_argument("--note", default="")
     a = ap.parse_args()
+    if a.cmd == "trace":
+        trace_summary(a.trace_dir, a.out_md, a.command, a.workload, a.note)
+        print("wrote", a.out_md)
+        return
     if a.cmd == "counters":
         counters_summary(a.pass_dirs, a.trace_dir, a.out_md, a.command, a.workload)
         print("wrote", a.out_md)
