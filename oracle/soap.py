@@ -1,8 +1,7 @@
 """Plain fp64 SOAP owner step.
 
-TEST INFRASTRUCTURE ONLY: imported by tests/ (and, once the library has the
-step, by __graft_entry__.smoke() and bench.py's CPU baseline), never by the
-library or its binding.
+TEST INFRASTRUCTURE ONLY: imported by tests/, __graft_entry__.smoke() and
+bench.py's CPU baseline, never by the library or its binding.
 
 "MatrixFSDP: communication-free matrix optimizers under ZeRO-3 parameter
 sharding", §5.7: next to Shampoo, the paper runs SOAP on the owners, which it
@@ -19,10 +18,12 @@ that algorithm leaves to its implementation taken in its plainest form:
   N~ = (M~ / (1 - b1^t)) / (sqrt(V' / (1 - b2^t)) + eps)
   W' = (1 - lr wd) W - lr Q_L N~ Q_R^T       decoupled decay
 
-The update does not depend on the sign or the order of the eigenvectors; it
-does depend on the basis chosen inside a repeated eigenvalue wherever the
-rotated moments are non-zero there (one step from eps I keeps them zero in the
-eps-eigenspace, since G has no component there).
+The update does not depend on the sign of the eigenvectors.  Once V is
+non-zero it depends on their order (V is indexed by it): the eigenbasis is
+taken in ascending eigenvalue order, numpy's eigh order.  It also depends on
+the basis chosen inside a repeated eigenvalue wherever the rotated moments are
+non-zero there (one step from eps I keeps them zero in the eps-eigenspace,
+since G has no component there).
 """
 from __future__ import annotations
 
