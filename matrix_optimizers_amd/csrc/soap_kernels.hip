@@ -412,26 +412,40 @@ __global__ __launch_bounds__(SO_THREADS) void so_jac_solve_kernel(uint8_t* ws, u
     if (t == 0) reinterpret_cast<uint32_t*>(ws + eg.off_flag)[j] = any ? 1u : 0u;
 }
 
-// Loads the 64 x 64 pair rotation D_I of round k into LDS.
-MO_DEV void load_d(double (*Dl)[PW + 1], const double* Dall, int I) {
-    for (int q = threadIdx.x; q < PW * PW; q += SO_THREADS) Dl[q / PW][q % PW] = Dall[int64_t(I) * PW * PW + q];
+// Loads the 64 x 64 pair rotation D_I of round k into LDS (16-byte accesses).
+MO_DEV void load_d(double (*Dl)[PW], const double* Dall, int I) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(Dall + int64_t(I) * PW * PW);
+    f32x4* dst = reinterpret_cast<f32x4*>(&Dl[0][0]);
+    for (int q = threadIdx.x; q < PW * PW / 2; q += SO_THREADS) dst[q] = src[q];
 }
 
+typedef double f64x2 __attribute__((ext_vector_type(2)));
+
 // acc[x][y] = sum_k L(r0 + x, k) * Rm[k][c0 + y] over the 64-wide k, with
-// L(r, k) = Lm[r][k] (trans = false) or Lm[k][r] (trans = true).
-template <bool TRANS>
-MO_DEV void tile_product(const double (*Lm)[PW + 1], const double (*Rm)[PW + 1], int r0, int c0,
-                         double (&acc)[4][4]) {
+// L(r, k) = Lm[r][k] (LP = PW + 1: a row-padded array read down a column) or
+// Lm[k][r] (LP = PW: read along a row, like Rm).  Reads along a row take two
+// doubles per 16-byte LDS access; the loop is unrolled so that several k
+// steps' reads are in flight.
+template <int LP>
+MO_DEV void tile_product(const double (*Lm)[LP], const double (*Rm)[PW], int r0, int c0, double (&acc)[4][4]) {
 #pragma unroll
     for (int x = 0; x < 4; ++x)
 #pragma unroll
         for (int y = 0; y < 4; ++y) acc[x][y] = 0.0;
+#pragma unroll 8
     for (int kk = 0; kk < PW; ++kk) {
         double a[4], b[4];
+        if constexpr (LP == PW) {
+            const f64x2 a0 = *reinterpret_cast<const f64x2*>(&Lm[kk][r0]);
+            const f64x2 a1 = *reinterpret_cast<const f64x2*>(&Lm[kk][r0 + 2]);
+            a[0] = a0[0]; a[1] = a0[1]; a[2] = a1[0]; a[3] = a1[1];
+        } else {
 #pragma unroll
-        for (int x = 0; x < 4; ++x) a[x] = TRANS ? Lm[kk][r0 + x] : Lm[r0 + x][kk];
-#pragma unroll
-        for (int y = 0; y < 4; ++y) b[y] = Rm[kk][c0 + y];
+            for (int x = 0; x < 4; ++x) a[x] = Lm[r0 + x][kk];
+        }
+        const f64x2 b0 = *reinterpret_cast<const f64x2*>(&Rm[kk][c0]);
+        const f64x2 b1 = *reinterpret_cast<const f64x2*>(&Rm[kk][c0 + 2]);
+        b[0] = b0[0]; b[1] = b0[1]; b[2] = b1[0]; b[3] = b1[1];
 #pragma unroll
         for (int x = 0; x < 4; ++x)
 #pragma unroll
@@ -444,10 +458,10 @@ MO_DEV void tile_product(const double (*Lm)[PW + 1], const double (*Rm)[PW + 1],
 // C = X + X D_J, A' = C + D_I^T C.  A tile whose two pairs were not rotated is
 // left untouched (the products would add exact zeros).
 __global__ __launch_bounds__(SO_THREADS) void so_jac_apply_kernel(uint8_t* ws, uint32_t k) {
-    __shared__ double X[PW][PW + 1];
-    __shared__ double C[PW][PW + 1];
-    __shared__ double DI[PW][PW + 1];
-    __shared__ double DJ[PW][PW + 1];
+    __shared__ double X[PW][PW + 1];          // read down columns: padded
+    __shared__ __align__(16) double C[PW][PW];
+    __shared__ __align__(16) double DI[PW][PW];
+    __shared__ __align__(16) double DJ[PW][PW];
     const mo_so_header* h = so_header(ws);
     const mo_so_eig* eigs = so_eigs(ws);
     const mo_so_eig& eg = eigs[find_rec(eigs, h->n_eigs, blockIdx.x, &mo_so_eig::apply_begin)];
@@ -477,13 +491,13 @@ __global__ __launch_bounds__(SO_THREADS) void so_jac_apply_kernel(uint8_t* ws, u
     __syncthreads();
     const int r0 = (t / 16) * 4, c0 = (t % 16) * 4;
     double acc[4][4];
-    tile_product<false>(X, DJ, r0, c0, acc);   // X D_J
+    tile_product<PW + 1>(X, DJ, r0, c0, acc);   // X D_J
 #pragma unroll
     for (int x = 0; x < 4; ++x)
 #pragma unroll
         for (int y = 0; y < 4; ++y) C[r0 + x][c0 + y] = X[r0 + x][c0 + y] + acc[x][y];
     __syncthreads();
-    tile_product<true>(DI, C, r0, c0, acc);    // D_I^T C
+    tile_product<PW>(DI, C, r0, c0, acc);       // D_I^T C
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
         const int64_t gr = pair_index(pI, qI, r0 + x);
@@ -501,8 +515,8 @@ __global__ __launch_bounds__(SO_THREADS) void so_jac_apply_kernel(uint8_t* ws, u
 // eigenvectors E in round k: E' = V_I^T E = X + D_I^T X.  Half the LDS of the
 // A kernel, so two workgroups share a CU.  Unrotated pairs are skipped.
 __global__ __launch_bounds__(SO_THREADS) void so_jac_etile_kernel(uint8_t* ws, uint32_t k) {
-    __shared__ double X[PW][PW + 1];
-    __shared__ double DI[PW][PW + 1];
+    __shared__ __align__(16) double X[PW][PW];
+    __shared__ __align__(16) double DI[PW][PW];
     const mo_so_header* h = so_header(ws);
     const mo_so_eig* eigs = so_eigs(ws);
     const mo_so_eig& eg = eigs[find_rec(eigs, h->n_eigs, blockIdx.x, &mo_so_eig::etile_begin)];
@@ -527,7 +541,7 @@ __global__ __launch_bounds__(SO_THREADS) void so_jac_etile_kernel(uint8_t* ws, u
     __syncthreads();
     const int r0 = (t / 16) * 4, c0 = (t % 16) * 4;
     double acc[4][4];
-    tile_product<true>(DI, X, r0, c0, acc);
+    tile_product<PW>(DI, X, r0, c0, acc);
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
         const int64_t gr = pair_index(pI, qI, r0 + x);
