@@ -34,7 +34,7 @@ constexpr int SO_THREADS = 256;
 constexpr int GB = 64;                 // GEMM tile
 constexpr int GK = 16;                 // GEMM K chunk
 constexpr int PW = 2 * MO_SO_BLK;      // pair width (64)
-constexpr int INNER_SWEEPS = 2;        // scalar sweeps per pair problem
+constexpr int INNER_SWEEPS = 1;        // scalar sweeps per pair problem
 
 MO_DEV const mo_so_header* so_header(const uint8_t* ws) {
     return reinterpret_cast<const mo_so_header*>(ws);
