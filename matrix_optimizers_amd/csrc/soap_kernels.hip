@@ -419,44 +419,50 @@ MO_DEV void load_d(double (*Dl)[PW], const double* Dall, int I) {
     for (int q = threadIdx.x; q < PW * PW / 2; q += SO_THREADS) dst[q] = src[q];
 }
 
-typedef double f64x2 __attribute__((ext_vector_type(2)));
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 
-// acc[x][y] = sum_k L(r0 + x, k) * Rm[k][c0 + y] over the 64-wide k, with
-// L(r, k) = Lm[r][k] (LP = PW + 1: a row-padded array read down a column) or
-// Lm[k][r] (LP = PW: read along a row, like Rm).  Reads along a row take two
-// doubles per 16-byte LDS access; the loop is unrolled so that several k
-// steps' reads are in flight.
-template <int LP>
-MO_DEV void tile_product(const double (*Lm)[LP], const double (*Rm)[PW], int r0, int c0, double (&acc)[4][4]) {
+// acc = L R for one 64 x 64 tile on fp64 MFMA (v_mfma_f64_16x16x4_f64), over
+// the 64-wide k: L(r, k) = Lm[r * ldl + k], or Lm[k * ldl + r] when LT; R(k, c)
+// = Rm[k * ldr + c].  Wave w owns rows 32 (w / 2) .. + 31 and columns
+// 32 (w % 2) .. + 31 as 2 x 2 blocks of 16 x 16.  Per instruction, lane l
+// supplies A(l % 16, l / 16) and B(l / 16, l % 16) of the 16 x 4 and 4 x 16
+// operands and holds results (l / 16 + 4 v, l % 16) in its registers v = 0..3
+// (the layout read off the instruction with one-hot operands).
+template <bool LT>
+MO_DEV void mfma_tile(const double* Lm, int ldl, const double* Rm, int ldr, f64x4 (&acc)[2][2]) {
+    const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int r0 = 32 * (w >> 1) + (l & 15), c0 = 32 * (w & 1) + (l & 15);
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+    for (int x = 0; x < 2; ++x)
 #pragma unroll
-        for (int y = 0; y < 4; ++y) acc[x][y] = 0.0;
-#pragma unroll 8
-    for (int kk = 0; kk < PW; ++kk) {
-        double a[4], b[4];
-        if constexpr (LP == PW) {
-            const f64x2 a0 = *reinterpret_cast<const f64x2*>(&Lm[kk][r0]);
-            const f64x2 a1 = *reinterpret_cast<const f64x2*>(&Lm[kk][r0 + 2]);
-            a[0] = a0[0]; a[1] = a0[1]; a[2] = a1[0]; a[3] = a1[1];
-        } else {
+        for (int y = 0; y < 2; ++y) acc[x][y] = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+    for (int k0 = 0; k0 < PW; k0 += 4) {
+        const int kq = k0 + (l >> 4);
+        double a[2], b[2];
 #pragma unroll
-            for (int x = 0; x < 4; ++x) a[x] = Lm[r0 + x][kk];
+        for (int x = 0; x < 2; ++x) {
+            const int r = r0 + 16 * x;
+            a[x] = LT ? Lm[kq * ldl + r] : Lm[r * ldl + kq];
         }
-        const f64x2 b0 = *reinterpret_cast<const f64x2*>(&Rm[kk][c0]);
-        const f64x2 b1 = *reinterpret_cast<const f64x2*>(&Rm[kk][c0 + 2]);
-        b[0] = b0[0]; b[1] = b0[1]; b[2] = b1[0]; b[3] = b1[1];
 #pragma unroll
-        for (int x = 0; x < 4; ++x)
+        for (int y = 0; y < 2; ++y) b[y] = Rm[kq * ldr + c0 + 16 * y];
 #pragma unroll
-            for (int y = 0; y < 4; ++y) acc[x][y] = fma(a[x], b[y], acc[x][y]);
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int y = 0; y < 2; ++y) acc[x][y] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[x], b[y], acc[x][y], 0, 0, 0);
     }
 }
+
+// Tile row and column of result register v of block (x, y) in this lane.
+MO_DEV int mfma_row(int x, int v) { return 32 * (threadIdx.x >> 7) + 16 * x + ((threadIdx.x & 63) >> 4) + 4 * v; }
+MO_DEV int mfma_col(int y) { return 32 * ((threadIdx.x >> 6) & 1) + 16 * y + (threadIdx.x & 15); }
 
 // One workgroup per upper 64 x 64 tile (I, J) of pairs of A in round k:
 // A' = V_I^T A V_J, mirrored below the diagonal.  With V = I + D:
 // C = X + X D_J, A' = C + D_I^T C.  A tile whose two pairs were not rotated is
-// left untouched (the products would add exact zeros).
+// left untouched (the products would add exact zeros).  The result is staged
+// in LDS so that the tile and its mirror are both written by rows.
 __global__ __launch_bounds__(SO_THREADS) void so_jac_apply_kernel(uint8_t* ws, uint32_t k) {
     __shared__ double X[PW][PW + 1];          // read down columns: padded
     __shared__ __align__(16) double C[PW][PW];
@@ -489,24 +495,38 @@ __global__ __launch_bounds__(SO_THREADS) void so_jac_apply_kernel(uint8_t* ws, u
     load_d(DI, Dall, I);
     load_d(DJ, Dall, J);
     __syncthreads();
-    const int r0 = (t / 16) * 4, c0 = (t % 16) * 4;
-    double acc[4][4];
-    tile_product<PW + 1>(X, DJ, r0, c0, acc);   // X D_J
+    f64x4 acc[2][2];
+    mfma_tile<false>(&X[0][0], PW + 1, &DJ[0][0], PW, acc);   // X D_J
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+    for (int x = 0; x < 2; ++x)
 #pragma unroll
-        for (int y = 0; y < 4; ++y) C[r0 + x][c0 + y] = X[r0 + x][c0 + y] + acc[x][y];
+        for (int y = 0; y < 2; ++y)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int r = mfma_row(x, v), c = mfma_col(y);
+                C[r][c] = X[r][c] + acc[x][y][v];
+            }
     __syncthreads();
-    tile_product<PW>(DI, C, r0, c0, acc);       // D_I^T C
+    mfma_tile<true>(&DI[0][0], PW, &C[0][0], PW, acc);         // D_I^T C
+    // X is no longer read: stage the result there
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-        const int64_t gr = pair_index(pI, qI, r0 + x);
+    for (int x = 0; x < 2; ++x)
 #pragma unroll
-        for (int y = 0; y < 4; ++y) {
-            const double val = C[r0 + x][c0 + y] + acc[x][y];
-            const int64_t gc = pair_index(pJ, qJ, c0 + y);
-            M[gr * ld + gc] = val;
-            if (I != J) M[gc * ld + gr] = val;
+        for (int y = 0; y < 2; ++y)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int r = mfma_row(x, v), c = mfma_col(y);
+                X[r][c] = C[r][c] + acc[x][y][v];
+            }
+    __syncthreads();
+    for (int q = t; q < PW * PW; q += SO_THREADS) {
+        const int r = q / PW, c = q % PW;
+        M[pair_index(pI, qI, r) * ld + pair_index(pJ, qJ, c)] = X[r][c];
+    }
+    if (I != J) {
+        for (int q = t; q < PW * PW; q += SO_THREADS) {
+            const int c = q / PW, r = q % PW;
+            M[pair_index(pJ, qJ, c) * ld + pair_index(pI, qI, r)] = X[r][c];
         }
     }
 }
@@ -539,15 +559,17 @@ __global__ __launch_bounds__(SO_THREADS) void so_jac_etile_kernel(uint8_t* ws, u
     }
     load_d(DI, Dall, I);
     __syncthreads();
-    const int r0 = (t / 16) * 4, c0 = (t % 16) * 4;
-    double acc[4][4];
-    tile_product<PW>(DI, X, r0, c0, acc);
+    f64x4 acc[2][2];
+    mfma_tile<true>(&DI[0][0], PW, &X[0][0], PW, acc);
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-        const int64_t gr = pair_index(pI, qI, r0 + x);
+    for (int x = 0; x < 2; ++x)
 #pragma unroll
-        for (int y = 0; y < 4; ++y) E[gr * ld + int64_t(cc) * PW + c0 + y] = X[r0 + x][c0 + y] + acc[x][y];
-    }
+        for (int y = 0; y < 2; ++y)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int r = mfma_row(x, v), c = mfma_col(y);
+                E[pair_index(pI, qI, r) * ld + int64_t(cc) * PW + c] = X[r][c] + acc[x][y][v];
+            }
 }
 
 // One workgroup per decomposition: sort the eigenvalues diag(A) ascending
