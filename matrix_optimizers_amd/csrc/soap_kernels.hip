@@ -419,6 +419,7 @@ MO_DEV void load_d(double (*Dl)[PW], const double* Dall, int I) {
     for (int q = threadIdx.x; q < PW * PW / 2; q += SO_THREADS) dst[q] = src[q];
 }
 
+typedef double f64x2 __attribute__((ext_vector_type(2)));
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 // acc = L R for one 64 x 64 tile on fp64 MFMA (v_mfma_f64_16x16x4_f64), over
@@ -488,9 +489,12 @@ __global__ __launch_bounds__(SO_THREADS) void so_jac_apply_kernel(uint8_t* ws, u
     double* M = reinterpret_cast<double*>(ws + eg.off_A);
     const int64_t ld = eg.m_pad;
     const int t = threadIdx.x;
-    for (int q = t; q < PW * PW; q += SO_THREADS) {
-        const int r = q / PW, c = q % PW;
-        X[r][c] = M[pair_index(pI, qI, r) * ld + pair_index(pJ, qJ, c)];
+    // 16-byte loads: two doubles of one row (a row of a tile is two 256-byte runs)
+    for (int q = t; q < PW * PW / 2; q += SO_THREADS) {
+        const int r = q / (PW / 2), c = 2 * (q % (PW / 2));
+        const f64x2 v = *reinterpret_cast<const f64x2*>(M + pair_index(pI, qI, r) * ld + pair_index(pJ, qJ, c));
+        X[r][c] = v[0];
+        X[r][c + 1] = v[1];
     }
     load_d(DI, Dall, I);
     load_d(DJ, Dall, J);
@@ -519,9 +523,9 @@ __global__ __launch_bounds__(SO_THREADS) void so_jac_apply_kernel(uint8_t* ws, u
                 X[r][c] = C[r][c] + acc[x][y][v];
             }
     __syncthreads();
-    for (int q = t; q < PW * PW; q += SO_THREADS) {
-        const int r = q / PW, c = q % PW;
-        M[pair_index(pI, qI, r) * ld + pair_index(pJ, qJ, c)] = X[r][c];
+    for (int q = t; q < PW * PW / 2; q += SO_THREADS) {
+        const int r = q / (PW / 2), c = 2 * (q % (PW / 2));
+        *reinterpret_cast<f64x2*>(M + pair_index(pI, qI, r) * ld + pair_index(pJ, qJ, c)) = f64x2{X[r][c], X[r][c + 1]};
     }
     if (I != J) {
         for (int q = t; q < PW * PW; q += SO_THREADS) {
@@ -553,23 +557,36 @@ __global__ __launch_bounds__(SO_THREADS) void so_jac_etile_kernel(uint8_t* ws, u
     double* E = reinterpret_cast<double*>(ws + eg.off_E);
     const int64_t ld = eg.m_pad;
     const int t = threadIdx.x;
-    for (int q = t; q < PW * PW; q += SO_THREADS) {
-        const int r = q / PW, c = q % PW;
-        X[r][c] = E[pair_index(pI, qI, r) * ld + int64_t(cc) * PW + c];
+    for (int q = t; q < PW * PW / 2; q += SO_THREADS) {
+        const int r = q / (PW / 2), c = 2 * (q % (PW / 2));
+        *reinterpret_cast<f64x2*>(&X[r][c]) =
+            *reinterpret_cast<const f64x2*>(E + pair_index(pI, qI, r) * ld + int64_t(cc) * PW + c);
     }
     load_d(DI, Dall, I);
     __syncthreads();
     f64x4 acc[2][2];
     mfma_tile<true>(&DI[0][0], PW, &X[0][0], PW, acc);
+    // every wave has read X before the result replaces it
+    double y_own[2][2][4];
 #pragma unroll
     for (int x = 0; x < 2; ++x)
 #pragma unroll
         for (int y = 0; y < 2; ++y)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int r = mfma_row(x, v), c = mfma_col(y);
-                E[pair_index(pI, qI, r) * ld + int64_t(cc) * PW + c] = X[r][c] + acc[x][y][v];
-            }
+            for (int v = 0; v < 4; ++v) y_own[x][y][v] = X[mfma_row(x, v)][mfma_col(y)] + acc[x][y][v];
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) X[mfma_row(x, v)][mfma_col(y)] = y_own[x][y][v];
+    __syncthreads();
+    for (int q = t; q < PW * PW / 2; q += SO_THREADS) {
+        const int r = q / (PW / 2), c = 2 * (q % (PW / 2));
+        *reinterpret_cast<f64x2*>(E + pair_index(pI, qI, r) * ld + int64_t(cc) * PW + c) =
+            *reinterpret_cast<const f64x2*>(&X[r][c]);
+    }
 }
 
 // One workgroup per decomposition: sort the eigenvalues diag(A) ascending
