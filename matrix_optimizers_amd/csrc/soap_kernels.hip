@@ -30,6 +30,9 @@
 
 namespace {
 
+typedef double f64x2 __attribute__((ext_vector_type(2)));
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
 constexpr int SO_THREADS = 256;
 constexpr int GB = 64;                 // GEMM tile
 constexpr int GK = 16;                 // GEMM K chunk
@@ -330,10 +333,13 @@ __global__ __launch_bounds__(SO_THREADS) void so_jac_solve_kernel(uint8_t* ws, u
     circle_pair(nb, int(k % uint32_t(nb - 1)), j, bp, bq);
     const double* A = reinterpret_cast<const double*>(ws + eg.off_A);
     const int t = threadIdx.x;
-    for (int q = t; q < PW * PW; q += SO_THREADS) {
-        const int r = q / PW, c = q % PW;
-        S[r][c] = A[pair_index(bp, bq, r) * eg.m_pad + pair_index(bp, bq, c)];
+    for (int q = t; q < PW * PW / 2; q += SO_THREADS) {
+        const int r = q / (PW / 2), c = 2 * (q % (PW / 2));
+        const f64x2 v = *reinterpret_cast<const f64x2*>(A + pair_index(bp, bq, r) * eg.m_pad + pair_index(bp, bq, c));
+        S[r][c] = v[0];
+        S[r][c + 1] = v[1];
         D[r][c] = 0.0;
+        D[r][c + 1] = 0.0;
     }
     if (t == 0) rotated[0] = rotated[1] = 0;
     __syncthreads();
@@ -408,7 +414,10 @@ __global__ __launch_bounds__(SO_THREADS) void so_jac_solve_kernel(uint8_t* ws, u
         any = true;
     }
     double* Dout = reinterpret_cast<double*>(ws + eg.off_D) + int64_t(j) * PW * PW;
-    for (int q = t; q < PW * PW; q += SO_THREADS) Dout[q] = D[q / PW][q % PW];
+    for (int q = t; q < PW * PW / 2; q += SO_THREADS) {
+        const int r = q / (PW / 2), c = 2 * (q % (PW / 2));
+        *reinterpret_cast<f64x2*>(Dout + r * PW + c) = f64x2{D[r][c], D[r][c + 1]};
+    }
     if (t == 0) reinterpret_cast<uint32_t*>(ws + eg.off_flag)[j] = any ? 1u : 0u;
 }
 
@@ -419,8 +428,6 @@ MO_DEV void load_d(double (*Dl)[PW], const double* Dall, int I) {
     for (int q = threadIdx.x; q < PW * PW / 2; q += SO_THREADS) dst[q] = src[q];
 }
 
-typedef double f64x2 __attribute__((ext_vector_type(2)));
-typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 // acc = L R for one 64 x 64 tile on fp64 MFMA (v_mfma_f64_16x16x4_f64), over
 // the 64-wide k: L(r, k) = Lm[r * ldl + k], or Lm[k * ldl + r] when LT; R(k, c)
@@ -528,9 +535,10 @@ __global__ __launch_bounds__(SO_THREADS) void so_jac_apply_kernel(uint8_t* ws, u
         *reinterpret_cast<f64x2*>(M + pair_index(pI, qI, r) * ld + pair_index(pJ, qJ, c)) = f64x2{X[r][c], X[r][c + 1]};
     }
     if (I != J) {
-        for (int q = t; q < PW * PW; q += SO_THREADS) {
-            const int c = q / PW, r = q % PW;
-            M[pair_index(pJ, qJ, c) * ld + pair_index(pI, qI, r)] = X[r][c];
+        for (int q = t; q < PW * PW / 2; q += SO_THREADS) {
+            const int c = q / (PW / 2), r = 2 * (q % (PW / 2));
+            *reinterpret_cast<f64x2*>(M + pair_index(pJ, qJ, c) * ld + pair_index(pI, qI, r)) =
+                f64x2{X[r][c], X[r + 1][c]};
         }
     }
 }
