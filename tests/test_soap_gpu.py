@@ -270,3 +270,37 @@ def test_decoder_layer_full_size(gpu):
         cols = rng.choice(G.shape[1], 4, replace=False)
         Rc = R[cols] + G[:, cols].T @ G
         assert rel(mats[i][3][cols].double().cpu().numpy(), Rc) <= 1e-6, i
+
+
+def test_strided_views_and_mixed_dtypes(gpu):
+    """Every tensor as a view into a wider buffer (row stride above its column
+    count), bf16 W with fp32 G: the same update as the contiguous call."""
+    import torch
+    import matrix_optimizers_amd as mo
+    st = warm_state(71, 72, 104)
+    dev = torch.device("cuda:0")
+    r, c = st["W"].shape
+
+    def view(x, extra, dtype=torch.float32):
+        rows, cols = x.shape
+        big = torch.full((rows, cols + extra), float("nan"), device=dev, dtype=dtype)
+        big[:, :cols] = torch.tensor(np.asarray(x, F32), device=dev).to(dtype)
+        return big[:, :cols]
+
+    W = view(st["W"], 24, torch.bfloat16)
+    G = view(st["G"], 8)
+    L, R = view(st["L"], 16), view(st["R"], 40)
+    M, V = view(st["M"], 4), view(st["V"], 12)
+    U = view(np.zeros((r, c)), 36)
+    mo.soap_owner_step([(W, G, L, R, M, V)], update_out=[U], step=10, **HP)
+    torch.cuda.synchronize()
+    ref = run_gpu([st], 10, HP, w_dtype="bf16")[0]
+    assert np.array_equal(U.cpu().numpy(), ref["U"].astype(F32))
+    assert np.array_equal(M.cpu().numpy(), ref["M"].astype(F32))
+    assert np.array_equal(V.cpu().numpy(), ref["V"].astype(F32))
+    assert np.array_equal(L.cpu().numpy(), ref["L"].astype(F32))
+    assert np.array_equal(W.float().cpu().numpy(), ref["W"].astype(F32))
+    # the padding columns of every buffer are untouched
+    for t in (W, G, L, R, M, V, U):
+        base = t.as_strided((t.shape[0], t.stride(0)), (t.stride(0), 1))
+        assert torch.isnan(base[:, t.shape[1]:].float()).all()
