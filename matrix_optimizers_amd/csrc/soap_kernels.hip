@@ -469,13 +469,15 @@ MO_DEV int mfma_col(int y) { return 32 * ((threadIdx.x >> 6) & 1) + 16 * y + (th
 // One workgroup per upper 64 x 64 tile (I, J) of pairs of A in round k:
 // A' = V_I^T A V_J, mirrored below the diagonal.  With V = I + D:
 // C = X + X D_J, A' = C + D_I^T C.  A tile whose two pairs were not rotated is
-// left untouched (the products would add exact zeros).  The result is staged
-// in LDS so that the tile and its mirror are both written by rows.
+// left untouched (the products would add exact zeros).
+// Two 32 KB buffers in LDS, so two workgroups share a CU: T0 holds X^T (loaded
+// from the mirror tile, rows of pair J: A is kept exactly symmetric off the
+// diagonal tiles, and on them the two orientations differ by rounding only),
+// then C; T1 holds D_J, then D_I, then the result, which is written by rows
+// both to the tile and to its mirror.
 __global__ __launch_bounds__(SO_THREADS) void so_jac_apply_kernel(uint8_t* ws, uint32_t k) {
-    __shared__ double X[PW][PW + 1];          // read down columns: padded
-    __shared__ __align__(16) double C[PW][PW];
-    __shared__ __align__(16) double DI[PW][PW];
-    __shared__ __align__(16) double DJ[PW][PW];
+    __shared__ __align__(16) double T0[PW][PW];
+    __shared__ __align__(16) double T1[PW][PW];
     const mo_so_header* h = so_header(ws);
     const mo_so_eig* eigs = so_eigs(ws);
     const mo_so_eig& eg = eigs[find_rec(eigs, h->n_eigs, blockIdx.x, &mo_so_eig::apply_begin)];
@@ -496,49 +498,57 @@ __global__ __launch_bounds__(SO_THREADS) void so_jac_apply_kernel(uint8_t* ws, u
     double* M = reinterpret_cast<double*>(ws + eg.off_A);
     const int64_t ld = eg.m_pad;
     const int t = threadIdx.x;
-    // 16-byte loads: two doubles of one row (a row of a tile is two 256-byte runs)
+    // X^T[c][r] = A[J row c][I column r]
     for (int q = t; q < PW * PW / 2; q += SO_THREADS) {
-        const int r = q / (PW / 2), c = 2 * (q % (PW / 2));
-        const f64x2 v = *reinterpret_cast<const f64x2*>(M + pair_index(pI, qI, r) * ld + pair_index(pJ, qJ, c));
-        X[r][c] = v[0];
-        X[r][c + 1] = v[1];
+        const int c = q / (PW / 2), r = 2 * (q % (PW / 2));
+        *reinterpret_cast<f64x2*>(&T0[c][r]) =
+            *reinterpret_cast<const f64x2*>(M + pair_index(pJ, qJ, c) * ld + pair_index(pI, qI, r));
     }
-    load_d(DI, Dall, I);
-    load_d(DJ, Dall, J);
+    load_d(T1, Dall, J);
     __syncthreads();
     f64x4 acc[2][2];
-    mfma_tile<false>(&X[0][0], PW + 1, &DJ[0][0], PW, acc);   // X D_J
+    mfma_tile<true>(&T0[0][0], PW, &T1[0][0], PW, acc);     // X D_J, X read through X^T
+    double own[2][2][4];
 #pragma unroll
     for (int x = 0; x < 2; ++x)
 #pragma unroll
         for (int y = 0; y < 2; ++y)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int r = mfma_row(x, v), c = mfma_col(y);
-                C[r][c] = X[r][c] + acc[x][y][v];
-            }
+            for (int v = 0; v < 4; ++v) own[x][y][v] = T0[mfma_col(y)][mfma_row(x, v)] + acc[x][y][v];
+    __syncthreads();                                          // T0 and T1 fully read
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) T0[mfma_row(x, v)][mfma_col(y)] = own[x][y][v];   // C
+    load_d(T1, Dall, I);
     __syncthreads();
-    mfma_tile<true>(&DI[0][0], PW, &C[0][0], PW, acc);         // D_I^T C
-    // X is no longer read: stage the result there
+    mfma_tile<true>(&T1[0][0], PW, &T0[0][0], PW, acc);     // D_I^T C
 #pragma unroll
     for (int x = 0; x < 2; ++x)
 #pragma unroll
         for (int y = 0; y < 2; ++y)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int r = mfma_row(x, v), c = mfma_col(y);
-                X[r][c] = C[r][c] + acc[x][y][v];
-            }
+            for (int v = 0; v < 4; ++v) own[x][y][v] = T0[mfma_row(x, v)][mfma_col(y)] + acc[x][y][v];
+    __syncthreads();                                          // T1 (D_I) fully read
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) T1[mfma_row(x, v)][mfma_col(y)] = own[x][y][v];
     __syncthreads();
     for (int q = t; q < PW * PW / 2; q += SO_THREADS) {
         const int r = q / (PW / 2), c = 2 * (q % (PW / 2));
-        *reinterpret_cast<f64x2*>(M + pair_index(pI, qI, r) * ld + pair_index(pJ, qJ, c)) = f64x2{X[r][c], X[r][c + 1]};
+        *reinterpret_cast<f64x2*>(M + pair_index(pI, qI, r) * ld + pair_index(pJ, qJ, c)) =
+            *reinterpret_cast<const f64x2*>(&T1[r][c]);
     }
     if (I != J) {
         for (int q = t; q < PW * PW / 2; q += SO_THREADS) {
             const int c = q / (PW / 2), r = 2 * (q % (PW / 2));
             *reinterpret_cast<f64x2*>(M + pair_index(pJ, qJ, c) * ld + pair_index(pI, qI, r)) =
-                f64x2{X[r][c], X[r + 1][c]};
+                f64x2{T1[r][c], T1[r + 1][c]};
         }
     }
 }
