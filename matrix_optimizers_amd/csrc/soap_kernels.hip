@@ -554,10 +554,13 @@ __global__ __launch_bounds__(SO_THREADS) void so_jac_apply_kernel(uint8_t* ws, u
 }
 
 // One workgroup per 64 x 64 tile (pair I, columns 64 c ..) of the accumulated
-// eigenvectors E in round k: E' = V_I^T E = X + D_I^T X.  Half the LDS of the
-// A kernel, so two workgroups share a CU.  Unrotated pairs are skipped.
+// eigenvectors E in round k: E' = V_I^T E = X + D_I^T X.  Only D_I sits in LDS
+// (32 KB, so several workgroups share a CU); the MFMA B operand and the old
+// values come straight from E (each element is read by the two waves that
+// share its columns, the second read mostly from L2), and the results are
+// written from registers, 16 lanes to 128 contiguous bytes.  Unrotated pairs
+// are skipped.
 __global__ __launch_bounds__(SO_THREADS) void so_jac_etile_kernel(uint8_t* ws, uint32_t k) {
-    __shared__ __align__(16) double X[PW][PW];
     __shared__ __align__(16) double DI[PW][PW];
     const mo_so_header* h = so_header(ws);
     const mo_so_eig* eigs = so_eigs(ws);
@@ -574,37 +577,48 @@ __global__ __launch_bounds__(SO_THREADS) void so_jac_etile_kernel(uint8_t* ws, u
     const double* Dall = reinterpret_cast<const double*>(ws + eg.off_D);
     double* E = reinterpret_cast<double*>(ws + eg.off_E);
     const int64_t ld = eg.m_pad;
-    const int t = threadIdx.x;
-    for (int q = t; q < PW * PW / 2; q += SO_THREADS) {
-        const int r = q / (PW / 2), c = 2 * (q % (PW / 2));
-        *reinterpret_cast<f64x2*>(&X[r][c]) =
-            *reinterpret_cast<const f64x2*>(E + pair_index(pI, qI, r) * ld + int64_t(cc) * PW + c);
-    }
+    double* Ecol = E + int64_t(cc) * PW;      // row g of the tile: Ecol[g * ld + c]
     load_d(DI, Dall, I);
+    // the old values of this lane's outputs
+    double own[2][2][4];
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) own[x][y][v] = Ecol[pair_index(pI, qI, mfma_row(x, v)) * ld + mfma_col(y)];
     __syncthreads();
+    // acc = D_I^T X with X(k, c) = E[pair row k][64 cc + c]
+    const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int r0 = 32 * (w >> 1) + (l & 15), c0 = 32 * (w & 1) + (l & 15);
     f64x4 acc[2][2];
-    mfma_tile<true>(&DI[0][0], PW, &X[0][0], PW, acc);
-    // every wave has read X before the result replaces it
-    double y_own[2][2][4];
 #pragma unroll
     for (int x = 0; x < 2; ++x)
 #pragma unroll
-        for (int y = 0; y < 2; ++y)
+        for (int y = 0; y < 2; ++y) acc[x][y] = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+    for (int k0 = 0; k0 < PW; k0 += 4) {
+        const int kq = k0 + (l >> 4);
+        const double* xrow = Ecol + pair_index(pI, qI, kq) * ld;
+        double a[2], b[2];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) y_own[x][y][v] = X[mfma_row(x, v)][mfma_col(y)] + acc[x][y][v];
-    __syncthreads();
+        for (int x = 0; x < 2; ++x) a[x] = DI[kq][r0 + 16 * x];
 #pragma unroll
-    for (int x = 0; x < 2; ++x)
+        for (int y = 0; y < 2; ++y) b[y] = xrow[c0 + 16 * y];
 #pragma unroll
-        for (int y = 0; y < 2; ++y)
+        for (int x = 0; x < 2; ++x)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) X[mfma_row(x, v)][mfma_col(y)] = y_own[x][y][v];
-    __syncthreads();
-    for (int q = t; q < PW * PW / 2; q += SO_THREADS) {
-        const int r = q / (PW / 2), c = 2 * (q % (PW / 2));
-        *reinterpret_cast<f64x2*>(E + pair_index(pI, qI, r) * ld + int64_t(cc) * PW + c) =
-            *reinterpret_cast<const f64x2*>(&X[r][c]);
+            for (int y = 0; y < 2; ++y) acc[x][y] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[x], b[y], acc[x][y], 0, 0, 0);
     }
+    // every wave has read every row it needs before any row is replaced
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                Ecol[pair_index(pI, qI, mfma_row(x, v)) * ld + mfma_col(y)] = own[x][y][v] + acc[x][y][v];
 }
 
 // One workgroup per decomposition: sort the eigenvalues diag(A) ascending
