@@ -470,14 +470,14 @@ MO_DEV int mfma_col(int y) { return 32 * ((threadIdx.x >> 6) & 1) + 16 * y + (th
 // A' = V_I^T A V_J, mirrored below the diagonal.  With V = I + D:
 // C = X + X D_J, A' = C + D_I^T C.  A tile whose two pairs were not rotated is
 // left untouched (the products would add exact zeros).
-// Two 32 KB buffers in LDS, so two workgroups share a CU: T0 holds X^T (loaded
-// from the mirror tile, rows of pair J: A is kept exactly symmetric off the
-// diagonal tiles, and on them the two orientations differ by rounding only),
-// then C; T1 holds D_J, then D_I, then the result, which is written by rows
-// both to the tile and to its mirror.
+// Only C sits in LDS (32 KB, so several workgroups share a CU).  The operands
+// of both products come straight from memory: X through its mirror (rows of
+// pair J, X^T[c][r] = A[J row c][I column r]; A is kept exactly symmetric off
+// the diagonal tiles, and on them the two orientations differ by rounding
+// only), D_J and D_I from the round's rotations (L2).  The result replaces C
+// in LDS and is written by rows, to the tile and to its mirror.
 __global__ __launch_bounds__(SO_THREADS) void so_jac_apply_kernel(uint8_t* ws, uint32_t k) {
-    __shared__ __align__(16) double T0[PW][PW];
-    __shared__ __align__(16) double T1[PW][PW];
+    __shared__ __align__(16) double C[PW][PW];
     const mo_so_header* h = so_header(ws);
     const mo_so_eig* eigs = so_eigs(ws);
     const mo_so_eig& eg = eigs[find_rec(eigs, h->n_eigs, blockIdx.x, &mo_so_eig::apply_begin)];
@@ -495,60 +495,92 @@ __global__ __launch_bounds__(SO_THREADS) void so_jac_apply_kernel(uint8_t* ws, u
     circle_pair(nb, kr, I, pI, qI);
     circle_pair(nb, kr, J, pJ, qJ);
     const double* Dall = reinterpret_cast<const double*>(ws + eg.off_D);
+    const double* DI = Dall + int64_t(I) * PW * PW;
+    const double* DJ = Dall + int64_t(J) * PW * PW;
     double* M = reinterpret_cast<double*>(ws + eg.off_A);
     const int64_t ld = eg.m_pad;
     const int t = threadIdx.x;
-    // X^T[c][r] = A[J row c][I column r]
-    for (int q = t; q < PW * PW / 2; q += SO_THREADS) {
-        const int c = q / (PW / 2), r = 2 * (q % (PW / 2));
-        *reinterpret_cast<f64x2*>(&T0[c][r]) =
-            *reinterpret_cast<const f64x2*>(M + pair_index(pJ, qJ, c) * ld + pair_index(pI, qI, r));
-    }
-    load_d(T1, Dall, J);
-    __syncthreads();
-    f64x4 acc[2][2];
-    mfma_tile<true>(&T0[0][0], PW, &T1[0][0], PW, acc);     // X D_J, X read through X^T
+    const int l = t & 63, w = t >> 6;
+    const int r0 = 32 * (w >> 1) + (l & 15), c0 = 32 * (w & 1) + (l & 15);
+    // I-pair column offsets of this lane's two A-operand rows
+    int64_t colI[2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) colI[x] = pair_index(pI, qI, r0 + 16 * x);
     double own[2][2][4];
 #pragma unroll
     for (int x = 0; x < 2; ++x)
 #pragma unroll
         for (int y = 0; y < 2; ++y)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) own[x][y][v] = T0[mfma_col(y)][mfma_row(x, v)] + acc[x][y][v];
-    __syncthreads();                                          // T0 and T1 fully read
+            for (int v = 0; v < 4; ++v)
+                own[x][y][v] = M[pair_index(pJ, qJ, mfma_col(y)) * ld + pair_index(pI, qI, mfma_row(x, v))];
+    f64x4 acc[2][2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) acc[x][y] = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+    for (int k0 = 0; k0 < PW; k0 += 4) {   // X D_J
+        const int kq = k0 + (l >> 4);
+        const double* xrow = M + pair_index(pJ, qJ, kq) * ld;   // X^T row kq
+        double a[2], b[2];
+#pragma unroll
+        for (int x = 0; x < 2; ++x) a[x] = xrow[colI[x]];
+#pragma unroll
+        for (int y = 0; y < 2; ++y) b[y] = DJ[kq * PW + c0 + 16 * y];
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int y = 0; y < 2; ++y) acc[x][y] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[x], b[y], acc[x][y], 0, 0, 0);
+    }
 #pragma unroll
     for (int x = 0; x < 2; ++x)
 #pragma unroll
         for (int y = 0; y < 2; ++y)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) T0[mfma_row(x, v)][mfma_col(y)] = own[x][y][v];   // C
-    load_d(T1, Dall, I);
+            for (int v = 0; v < 4; ++v) C[mfma_row(x, v)][mfma_col(y)] = own[x][y][v] + acc[x][y][v];
     __syncthreads();
-    mfma_tile<true>(&T1[0][0], PW, &T0[0][0], PW, acc);     // D_I^T C
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) acc[x][y] = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+    for (int k0 = 0; k0 < PW; k0 += 4) {   // D_I^T C
+        const int kq = k0 + (l >> 4);
+        double a[2], b[2];
+#pragma unroll
+        for (int x = 0; x < 2; ++x) a[x] = DI[kq * PW + r0 + 16 * x];
+#pragma unroll
+        for (int y = 0; y < 2; ++y) b[y] = C[kq][c0 + 16 * y];
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int y = 0; y < 2; ++y) acc[x][y] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[x], b[y], acc[x][y], 0, 0, 0);
+    }
 #pragma unroll
     for (int x = 0; x < 2; ++x)
 #pragma unroll
         for (int y = 0; y < 2; ++y)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) own[x][y][v] = T0[mfma_row(x, v)][mfma_col(y)] + acc[x][y][v];
-    __syncthreads();                                          // T1 (D_I) fully read
+            for (int v = 0; v < 4; ++v) own[x][y][v] = C[mfma_row(x, v)][mfma_col(y)] + acc[x][y][v];
+    __syncthreads();                          // C fully read: the result replaces it
 #pragma unroll
     for (int x = 0; x < 2; ++x)
 #pragma unroll
         for (int y = 0; y < 2; ++y)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) T1[mfma_row(x, v)][mfma_col(y)] = own[x][y][v];
+            for (int v = 0; v < 4; ++v) C[mfma_row(x, v)][mfma_col(y)] = own[x][y][v];
     __syncthreads();
     for (int q = t; q < PW * PW / 2; q += SO_THREADS) {
         const int r = q / (PW / 2), c = 2 * (q % (PW / 2));
         *reinterpret_cast<f64x2*>(M + pair_index(pI, qI, r) * ld + pair_index(pJ, qJ, c)) =
-            *reinterpret_cast<const f64x2*>(&T1[r][c]);
+            *reinterpret_cast<const f64x2*>(&C[r][c]);
     }
     if (I != J) {
         for (int q = t; q < PW * PW / 2; q += SO_THREADS) {
             const int c = q / (PW / 2), r = 2 * (q % (PW / 2));
             *reinterpret_cast<f64x2*>(M + pair_index(pJ, qJ, c) * ld + pair_index(pI, qI, r)) =
-                f64x2{T1[r][c], T1[r + 1][c]};
+                f64x2{C[r][c], C[r + 1][c]};
         }
     }
 }
