@@ -216,7 +216,8 @@ def test_deterministic(gpu):
 def test_decoder_layer_full_size(gpu):
     """The decoder-layer bucket (hidden 2048, FFN 5632) in one call at the
     default 14 sweeps, from a warm state drawn on the device with torch: the
-    2048 x 2048 matrix against the oracle at its fp32 floor, sampled rows of the
+    2048 x 2048 and one 5632 x 2048 matrix against the oracle at their fp32
+    floors, sampled rows of the
     5632-sided statistics in fp64, every output finite, and the eigensolver
     converged (16 sweeps change no update by more than 1e-5 relative)."""
     import torch
@@ -261,6 +262,12 @@ def test_decoder_layer_full_size(gpu):
     out = {k: mats[0][j].double().cpu().numpy() for j, k in enumerate(("W", "G", "L", "R", "M", "V"))}
     out["U"] = ups[0].double().cpu().numpy()
     check(st, out, 10, dict(HP, weight_decay=0.01), "decoder 2048x2048")
+    # matrix 4 (5632 x 2048: a 5632-sided L) against the oracle
+    W, G, L, R, M, V = host[4]
+    st = dict(W=W, G=G, L=L, R=R, M=M, V=V)
+    out = {k: mats[4][j].double().cpu().numpy() for j, k in enumerate(("W", "G", "L", "R", "M", "V"))}
+    out["U"] = ups[4].double().cpu().numpy()
+    check(st, out, 10, dict(HP, weight_decay=0.01), "decoder 5632x2048")
     # sampled statistics rows of every 5632-sided matrix, in fp64
     rng = np.random.default_rng(5)
     for i, (W, G, L, R, M, V) in enumerate(host):
