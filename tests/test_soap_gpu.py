@@ -311,3 +311,22 @@ def test_strided_views_and_mixed_dtypes(gpu):
     for t in (W, G, L, R, M, V, U):
         base = t.as_strided((t.shape[0], t.stride(0)), (t.stride(0), 1))
         assert torch.isnan(base[:, t.shape[1]:].float()).all()
+
+
+def test_zero_state_and_gradient(gpu):
+    """G = L = R = M = V = 0: no rotation happens (the threshold is zero and so
+    is every entry), the update is exactly zero and W' = (1 - lr wd) W."""
+    import torch
+    import matrix_optimizers_amd as mo
+    dev = torch.device("cuda:0")
+    r, c = 70, 130
+    W = torch.randn((r, c), device=dev) * 0.02
+    W0 = W.clone()
+    z = lambda *s: torch.zeros(s, device=dev)
+    U = torch.full((r, c), float("nan"), device=dev)
+    hp = dict(HP, weight_decay=0.1)
+    mo.soap_owner_step([(W, z(r, c), z(r, r), z(c, c), z(r, c), z(r, c))], update_out=[U], step=1, **hp)
+    torch.cuda.synchronize()
+    assert torch.equal(U, torch.zeros_like(U))
+    decay = np.float32(1 - hp["lr"] * hp["weight_decay"])
+    assert torch.equal(W, W0 * float(decay))
