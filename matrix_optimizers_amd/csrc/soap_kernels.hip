@@ -370,43 +370,71 @@ __global__ __launch_bounds__(SO_THREADS) void so_jac_solve_kernel(uint8_t* ws, u
             // of this sweep's step 0, so the clear waits for step 1.
             if (t == 0 && step == 1) rotated[(sweep + 1) & 1] = 0;
             __syncthreads();
-            // two-sided update of the 2 x 2 blocks (u, v), u <= v, mirrored
-            for (int q = t; q < (PW / 2) * (PW / 2); q += SO_THREADS) {
-                const int u = q / (PW / 2), v = q % (PW / 2);
-                if (u > v) continue;
-                const int au = ra[u], bu = rb[u];
-                if (u == v) {
-                    if (rs[u] == 0.0) continue;   // not rotated: S[a][b] stays
-                    const double tt = rt[u], apq = rapq[u];
-                    S[au][au] -= tt * apq;
-                    S[bu][bu] += tt * apq;
-                    S[au][bu] = 0.0;
-                    S[bu][au] = 0.0;
-                    continue;
+            // Two-sided update of the off-diagonal 2 x 2 blocks, each unordered
+            // pair {u, v} once, mirrored: slot b (0 .. 511) is u = b / 16 with
+            // v = u + 1 + b % 16 (mod 32); the pairs 16 apart come up twice and
+            // run from the lower u only.  Each thread takes two slots, with all
+            // loads issued before the arithmetic.
+            {
+                int au[2], bu[2], av[2], bv[2];
+                bool on[2];
+                double x[2][4];
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int bidx = t + SO_THREADS * i;
+                    const int u = bidx >> 4, dv = bidx & 15, v = (u + 1 + dv) & 31;
+                    on[i] = dv != 15 || u < 16;
+                    au[i] = ra[u]; bu[i] = rb[u]; av[i] = ra[v]; bv[i] = rb[v];
+                    x[i][0] = S[au[i]][av[i]]; x[i][1] = S[au[i]][bv[i]];
+                    x[i][2] = S[bu[i]][av[i]]; x[i][3] = S[bu[i]][bv[i]];
                 }
-                const int av = ra[v], bv = rb[v];
-                const double su = rs[u], tu = rtau[u], sv = rs[v], tv = rtau[v];
-                double x00 = S[au][av], x01 = S[au][bv], x10 = S[bu][av], x11 = S[bu][bv];
-                // rows: J_u^T
-                double y00 = x00 - su * (x10 + tu * x00), y10 = x10 + su * (x00 - tu * x10);
-                double y01 = x01 - su * (x11 + tu * x01), y11 = x11 + su * (x01 - tu * x11);
-                // columns: J_v
-                const double z00 = y00 - sv * (y01 + tv * y00), z01 = y01 + sv * (y00 - tv * y01);
-                const double z10 = y10 - sv * (y11 + tv * y10), z11 = y11 + sv * (y10 - tv * y11);
-                S[au][av] = z00; S[au][bv] = z01; S[bu][av] = z10; S[bu][bv] = z11;
-                S[av][au] = z00; S[bv][au] = z01; S[av][bu] = z10; S[bv][bu] = z11;
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int bidx = t + SO_THREADS * i;
+                    const int u = bidx >> 4, v = (u + 1 + (bidx & 15)) & 31;
+                    const double su = rs[u], tu = rtau[u], sv = rs[v], tv = rtau[v];
+                    const double x00 = x[i][0], x01 = x[i][1], x10 = x[i][2], x11 = x[i][3];
+                    // rows: J_u^T
+                    const double y00 = x00 - su * (x10 + tu * x00), y10 = x10 + su * (x00 - tu * x10);
+                    const double y01 = x01 - su * (x11 + tu * x01), y11 = x11 + su * (x01 - tu * x11);
+                    // columns: J_v
+                    const double z00 = y00 - sv * (y01 + tv * y00), z01 = y01 + sv * (y00 - tv * y01);
+                    const double z10 = y10 - sv * (y11 + tv * y10), z11 = y11 + sv * (y10 - tv * y11);
+                    if (on[i]) {
+                        S[au[i]][av[i]] = z00; S[au[i]][bv[i]] = z01; S[bu[i]][av[i]] = z10; S[bu[i]][bv[i]] = z11;
+                        S[av[i]][au[i]] = z00; S[bv[i]][au[i]] = z01; S[av[i]][bu[i]] = z10; S[bv[i]][bu[i]] = z11;
+                    }
+                }
+                // the diagonal blocks: the rotated 2 x 2 problem itself
+                if (t < PW / 2 && rs[t] != 0.0) {   // not rotated: S[a][b] stays
+                    const int a2 = ra[t], b2 = rb[t];
+                    const double tt = rt[t], apq = rapq[t];
+                    S[a2][a2] -= tt * apq;
+                    S[b2][b2] += tt * apq;
+                    S[a2][b2] = 0.0;
+                    S[b2][a2] = 0.0;
+                }
             }
-            // D <- D J + (J - I): rows r, pairs u
-            for (int q = t; q < PW * (PW / 2); q += SO_THREADS) {
-                const int r = q / (PW / 2), u = q % (PW / 2);
-                const int a = ra[u], b = rb[u];
-                const double s = rs[u], tau = rtau[u];
-                const double da = D[r][a], db = D[r][b];
-                double na = da - s * (db + tau * da), nb2 = db + s * (da - tau * db);
-                if (r == a) { na -= s * tau; nb2 += s; }
-                if (r == b) { na -= s; nb2 -= s * tau; }
-                D[r][a] = na;
-                D[r][b] = nb2;
+            // D <- D J + (J - I): thread t takes pair u = t % 32 in rows t / 32 + 8 i
+            {
+                const int u = t & 31, a2 = ra[u], b2 = rb[u];
+                const double s2 = rs[u], tau = rtau[u];
+                double da[8], db[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int r = (t >> 5) + 8 * i;
+                    da[i] = D[r][a2];
+                    db[i] = D[r][b2];
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int r = (t >> 5) + 8 * i;
+                    double na = da[i] - s2 * (db[i] + tau * da[i]), nb2 = db[i] + s2 * (da[i] - tau * db[i]);
+                    if (r == a2) { na -= s2 * tau; nb2 += s2; }
+                    if (r == b2) { na -= s2; nb2 -= s2 * tau; }
+                    D[r][a2] = na;
+                    D[r][b2] = nb2;
+                }
             }
             __syncthreads();
         }
