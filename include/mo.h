@@ -181,10 +181,10 @@ const char* mo_status_string(mo_status status);
 #define MO_PHASE_SO_PREP    15  /* SOAP: padded G, first moment M' */
 #define MO_PHASE_SO_STATS   16  /* SOAP: L' = L + G G^T, R' = R + G^T G */
 #define MO_PHASE_SO_SOLVE   17  /* SOAP: Jacobi pair problems of one round */
-#define MO_PHASE_SO_APPLY   18  /* SOAP: one round's rotations applied to A (both sides) */
+#define MO_PHASE_SO_APPLY   18  /* SOAP: one round's rotations applied to A (both sides) and E */
 #define MO_PHASE_SO_SORT    19  /* SOAP: E = I, eigenvalue sort, sorted fp32 eigenvectors */
 #define MO_PHASE_SO_ROTATE  20  /* SOAP: the six eigenbasis products, V', N and W written */
-#define MO_PHASE_SO_ETILE   21  /* SOAP: one round's rotations applied to the eigenvectors E */
+#define MO_PHASE_SO_ETILE   21  /* SOAP: unused (the E tiles share the MO_PHASE_SO_APPLY launch) */
 #define MO_PHASE_COUNT    22
 
 /* Enable (1) or disable (0) per-launch timing on the calling thread.  While
@@ -336,7 +336,7 @@ mo_status soap_workspace_bytes(const mo_soap_matrix* mats, int32_t n_mats,
                                const mo_soap_hparams* hp, size_t* bytes);
 
 /* One SOAP step on every non-empty matrix of the bucket.  The eigensolver's
- * launches are grouped over every statistics matrix of the bucket (three per
+ * launches are grouped over every statistics matrix of the bucket (two per
  * round, sweeps x (m_pad / 32 - 1) rounds for the longest side; a pair
  * left unrotated in a round costs its tiles nothing); the rest is
  * a few launches per matrix.  Workspace, stream and error conventions as

@@ -9,8 +9,7 @@
 //   stats       per matrix: L' = L + G G^T, R' = R + G^T G (+ fp64 copies)
 //   E = I       per statistics matrix, and its rotation threshold 2^-48 ||A||_F
 //   rounds      grouped over all statistics matrices: pair problems, then
-//               their rotations applied to A and to E (three launches per
-//               round)
+//               their rotations applied to A and to E (two launches per round)
 //   sort        eigenvalues ascending, sorted fp32 eigenvectors
 //   products    per matrix: Q_L^T G, x Q_R (V'), Q_L^T M', x Q_R (N), Q_L N,
 //               x Q_R^T (W)
@@ -246,8 +245,7 @@ mo_status soap_owner_step(const mo_soap_matrix* mats, int32_t n, const mo_soap_h
     }
     for (uint32_t k = 0; k < h.max_rounds; ++k) {
         if (!ok(MO_PHASE_SO_SOLVE, [&] { return mo_launch_so_solve(h, ws, k, s); })) return MO_ERR_HIP;
-        if (!ok(MO_PHASE_SO_APPLY, [&] { return mo_launch_so_apply(h, ws, k, s); })) return MO_ERR_HIP;
-        if (!ok(MO_PHASE_SO_ETILE, [&] { return mo_launch_so_etile(h, ws, k, s); })) return MO_ERR_HIP;
+        if (!ok(MO_PHASE_SO_APPLY, [&] { return mo_launch_so_rotate(h, ws, k, s); })) return MO_ERR_HIP;
     }
     if (!ok(MO_PHASE_SO_SORT, [&] { return mo_launch_so_sort(h, ws, s); })) return MO_ERR_HIP;
     for (uint32_t e = 0; e < h.n_eigs; ++e)

@@ -504,16 +504,15 @@ MO_DEV int mfma_col(int y) { return 32 * ((threadIdx.x >> 6) & 1) + 16 * y + (th
 // the diagonal tiles, and on them the two orientations differ by rounding
 // only), D_J and D_I from the round's rotations (L2).  The result replaces C
 // in LDS and is written by rows, to the tile and to its mirror.
-__global__ __launch_bounds__(SO_THREADS) void so_jac_apply_kernel(uint8_t* ws, uint32_t k) {
-    __shared__ __align__(16) double C[PW][PW];
+MO_DEV void apply_a_tile(uint8_t* ws, uint32_t k, uint32_t blk, double (*C)[PW]) {
     const mo_so_header* h = so_header(ws);
     const mo_so_eig* eigs = so_eigs(ws);
-    const mo_so_eig& eg = eigs[find_rec(eigs, h->n_eigs, blockIdx.x, &mo_so_eig::apply_begin)];
+    const mo_so_eig& eg = eigs[find_rec(eigs, h->n_eigs, blk, &mo_so_eig::apply_begin)];
     if (k >= eg.rounds) return;
     const int P = int(eg.P);
     const int nb = 2 * P;
     const int kr = int(k % uint32_t(nb - 1));
-    int item = int(blockIdx.x - eg.apply_begin);
+    int item = int(blk - eg.apply_begin);
     int I = 0;
     while (item >= P - I) { item -= P - I; ++I; }
     const int J = I + item;
@@ -620,16 +619,15 @@ __global__ __launch_bounds__(SO_THREADS) void so_jac_apply_kernel(uint8_t* ws, u
 // share its columns, the second read mostly from L2), and the results are
 // written from registers, 16 lanes to 128 contiguous bytes.  Unrotated pairs
 // are skipped.
-__global__ __launch_bounds__(SO_THREADS) void so_jac_etile_kernel(uint8_t* ws, uint32_t k) {
-    __shared__ __align__(16) double DI[PW][PW];
+MO_DEV void apply_e_tile(uint8_t* ws, uint32_t k, uint32_t blk, double (*DI)[PW]) {
     const mo_so_header* h = so_header(ws);
     const mo_so_eig* eigs = so_eigs(ws);
-    const mo_so_eig& eg = eigs[find_rec(eigs, h->n_eigs, blockIdx.x, &mo_so_eig::etile_begin)];
+    const mo_so_eig& eg = eigs[find_rec(eigs, h->n_eigs, blk, &mo_so_eig::etile_begin)];
     if (k >= eg.rounds) return;
     const int P = int(eg.P);
     const int nb = 2 * P;
     const int kr = int(k % uint32_t(nb - 1));
-    const int item = int(blockIdx.x - eg.etile_begin);
+    const int item = int(blk - eg.etile_begin);
     const int I = item / P, cc = item % P;
     if (!reinterpret_cast<const uint32_t*>(ws + eg.off_flag)[I]) return;
     int pI, qI;
@@ -679,6 +677,16 @@ __global__ __launch_bounds__(SO_THREADS) void so_jac_etile_kernel(uint8_t* ws, u
 #pragma unroll
             for (int v = 0; v < 4; ++v)
                 Ecol[pair_index(pI, qI, mfma_row(x, v)) * ld + mfma_col(y)] = own[x][y][v] + acc[x][y][v];
+}
+
+// All rotations of round k in one launch: workgroups 0 .. n_apply_items - 1
+// take the upper tiles of A (the heavier items, dispatched first), the rest
+// the tiles of E.  Both keep one 64 x 64 fp64 tile in LDS.
+__global__ __launch_bounds__(SO_THREADS) void so_jac_rotate_kernel(uint8_t* ws, uint32_t k) {
+    __shared__ __align__(16) double buf[PW][PW];
+    const uint32_t na = so_header(ws)->n_apply_items;
+    if (blockIdx.x < na) apply_a_tile(ws, k, blockIdx.x, buf);
+    else apply_e_tile(ws, k, blockIdx.x - na, buf);
 }
 
 // One workgroup per decomposition: sort the eigenvalues diag(A) ascending
@@ -776,13 +784,9 @@ hipError_t mo_launch_so_solve(const mo_so_header& h, uint8_t* ws, uint32_t k, hi
     return hipGetLastError();
 }
 
-hipError_t mo_launch_so_apply(const mo_so_header& h, uint8_t* ws, uint32_t k, hipStream_t s) {
-    hipLaunchKernelGGL(so_jac_apply_kernel, dim3(h.n_apply_items), dim3(SO_THREADS), 0, s, ws, k);
-    return hipGetLastError();
-}
-
-hipError_t mo_launch_so_etile(const mo_so_header& h, uint8_t* ws, uint32_t k, hipStream_t s) {
-    hipLaunchKernelGGL(so_jac_etile_kernel, dim3(h.n_etile_items), dim3(SO_THREADS), 0, s, ws, k);
+hipError_t mo_launch_so_rotate(const mo_so_header& h, uint8_t* ws, uint32_t k, hipStream_t s) {
+    hipLaunchKernelGGL(so_jac_rotate_kernel, dim3(h.n_apply_items + h.n_etile_items), dim3(SO_THREADS), 0, s,
+                       ws, k);
     return hipGetLastError();
 }
 

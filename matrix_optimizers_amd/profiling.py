@@ -44,7 +44,7 @@ def sources_sha256() -> str:
 SH_KERNELS = (("sh_gemm_f32", "sh_gemm"), ("sh_layout_kernel", "sh_layout"), ("sh_sumsq_kernel", "sh_sumsq"),
               ("sh_norm_kernel", "sh_norm"), ("sh_init_kernel", "sh_init"),
               # SOAP step
-              ("so_jac_apply_kernel", "so_apply"), ("so_jac_etile_kernel", "so_etile"),
+              ("so_jac_rotate_kernel", "so_rotate_tiles"),
               ("so_jac_solve_kernel", "so_solve"), ("so_gemm_kernel", "so_gemm"), ("so_prep_kernel", "so_prep"),
               ("so_eig_init_kernel", "so_eig_init"), ("so_norm_rows_kernel", "so_norm_rows"),
               ("so_norm_final_kernel", "so_norm_final"), ("so_eig_sort_kernel", "so_sort"),
