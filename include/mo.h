@@ -343,7 +343,8 @@ mo_status soap_workspace_bytes(const mo_soap_matrix* mats, int32_t n_mats,
  * muon_owner_step: MO_ERR_INVALID_ARG (null pointer with numel > 0, negative
  * size, a stride below its row length, step < 1, sweeps outside 1 .. 100,
  * non-finite lr, betas, eps or weight decay, betas outside [0, 1), eps < 0),
- * MO_ERR_UNSUPPORTED (dtype not MO_F32/MO_BF16, a side longer than 8192),
+ * MO_ERR_UNSUPPORTED (dtype not MO_F32/MO_BF16, a side longer than 8192, more
+ * than 2^30 rotation tiles of 64 x 64 over the bucket's sides),
  * MO_ERR_WORKSPACE_TOO_SMALL, MO_ERR_ALIAS (a written tensor overlaps any
  * tensor of the bucket or the workspace), MO_ERR_HIP. */
 mo_status soap_owner_step(const mo_soap_matrix* mats, int32_t n_mats, const mo_soap_hparams* hp,

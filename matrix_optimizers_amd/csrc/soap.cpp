@@ -29,6 +29,9 @@ using namespace mo_host;
 namespace {
 
 constexpr int32_t kMaxSweeps = 100;
+// 64 x 64 work items of one grouped rotation launch (upper A tiles plus E tiles
+// over every side of the bucket): bounds the 32-bit item counts and the grid.
+constexpr int64_t kMaxItems = int64_t(1) << 30;
 
 mo_status validate_hp(const mo_soap_hparams* hp) {
     if (!hp) return MO_ERR_INVALID_ARG;
@@ -52,6 +55,7 @@ Strides strides(const mo_soap_matrix& d) {
 mo_status validate(const mo_soap_matrix* mats, int32_t n, std::vector<Range>* ranges) {
     if (n < 0) return MO_ERR_INVALID_ARG;
     if (n > 0 && !mats) return MO_ERR_INVALID_ARG;
+    int64_t items = 0;
     for (int32_t i = 0; i < n; ++i) {
         const mo_soap_matrix& d = mats[i];
         if (d.rows < 0 || d.cols < 0) return MO_ERR_INVALID_ARG;
@@ -66,6 +70,11 @@ mo_status validate(const mo_soap_matrix* mats, int32_t n, std::vector<Range>* ra
             s.u < d.cols)
             return MO_ERR_INVALID_ARG;
         if (d.rows > MO_SO_MAXSIDE || d.cols > MO_SO_MAXSIDE) return MO_ERR_UNSUPPORTED;
+        for (int64_t m : {d.rows, d.cols}) {
+            const int64_t P = (m + MO_SO_PAD - 1) / MO_SO_PAD;
+            items += P * (P + 1) / 2 + P * P;
+        }
+        if (items > kMaxItems) return MO_ERR_UNSUPPORTED;
         if (ranges) {
             ranges->push_back(matrix_range(d.W, d.rows, d.cols, s.w, elem_size(d.w_dtype), 1));
             ranges->push_back(matrix_range(d.G, d.rows, d.cols, s.g, elem_size(d.g_dtype), 0));

@@ -85,3 +85,13 @@ def test_aliasing_is_rejected():
     assert step([a, desc(k=1, W=a.G)]) == ALIAS          # a written W over another's G
     assert step([desc(V=BASE + 2 * GiB + 8)]) == ALIAS  # V inside L
     assert step([desc()], ws=BASE + 4 * GiB) == ALIAS    # workspace over M
+
+
+def test_rotation_item_limit_fails_fast():
+    """A bucket whose rotation tiles would overflow the 32-bit item counts is
+    refused on the host (2^30 tiles of 64 x 64; an 8192-sided matrix has
+    2 x (128 x 129 / 2 + 128^2) = 49280)."""
+    many = [desc(8192, 8192, k=k) for k in range(21790)]
+    assert mo.soap_workspace_bytes(many[:100], mo.soap_hparams()) > 0
+    with pytest.raises(mo.MoError):
+        mo.soap_workspace_bytes(many, mo.soap_hparams())
