@@ -426,12 +426,21 @@ def soap_main(args):
         if cnt:
             flops = f2["apply"] + f2["etile"]
             ach = flops / (tot * 1e-3) / 1e12
+            # HBM bytes per launch from the committed rocprofv3 summary (a mean over
+            # the whole step's launches), only if taken on the current sources
+            from matrix_optimizers_amd import profiling
+            tr = profiling.read_traffic(os.path.join(ROOT, "profiles"), wl.key, "so_rotate_tiles")
             out["roofline"] = {
                 "kernel": "so_jac_rotate_kernel", "bound": "alu", "achieved": round(ach, 3),
                 "peak": PEAK_F64_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_F64_TFLOPS, 4),
-                "traffic": None,
+                "traffic": None if tr is None else round(tr["read_bytes"] + tr["write_bytes"]),
                 "algorithmic_per_launch": f"{flops / cnt:.4e} flop (fp64, mean over the {cnt} launches of a "
                                           f"two-sweep pass, avg {tot / cnt:.3f} ms)"}
+            if tr is not None:
+                out["roofline"]["traffic_detail"] = {
+                    "read_bytes": round(tr["read_bytes"]), "write_bytes": round(tr["write_bytes"]),
+                    "profile": tr["source"], "profile_avg_ms": round(tr["avg_ns"] / 1e6, 5),
+                    "note": "mean over the launches of a whole step, converged late sweeps included"}
     if not args.no_cpu_baseline and not args.profile_only:
         print("[bench] cpu_baseline (fp64 oracle on host)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = soap_cpu_baseline(wl)

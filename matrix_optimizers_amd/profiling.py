@@ -30,7 +30,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # (host_common.*) do not.
 KERNEL_SOURCES = ["csrc/ns_kernels.hip", "csrc/tail_kernels.hip", "csrc/device_common.h",
                   "csrc/mo_worklist.h", "csrc/host.cpp", "csrc/gemm_core.h", "csrc/tile_dispatch.h",
-                  "csrc/shampoo_kernels.hip", "csrc/sh_worklist.h", "csrc/shampoo.cpp"]
+                  "csrc/shampoo_kernels.hip", "csrc/sh_worklist.h", "csrc/shampoo.cpp",
+                  "csrc/soap_kernels.hip", "csrc/so_worklist.h", "csrc/soap.cpp"]
 
 
 def sources_sha256() -> str:
@@ -131,7 +132,7 @@ def copy_factor(copy_dir: str, counter: str, copied_bytes: int) -> float:
     return copied_bytes / m
 
 
-def summarize(trace_dir, counter_dir, copy_dirs, out_md, command, workload, copied_mib=1024):
+def summarize(trace_dir, counter_dir, copy_dirs, out_md, command, workload, copied_mib=1024, note=""):
     stats = kernel_stats(trace_dir)
     copied = copied_mib << 20
     fetch = counter_means(os.path.join(counter_dir, "FETCH_SIZE"), "FETCH_SIZE")
@@ -141,7 +142,7 @@ def summarize(trace_dir, counter_dir, copy_dirs, out_md, command, workload, copi
     lines = [f"# rocprofv3 summary: {workload}", "",
              "Commands (run from the repository root on one MI355X):", "",
              "```", command, "```", "",
-             f"Kernel sources SHA-256: `{sources_sha256()}`", "",
+             f"Kernel sources SHA-256: `{sources_sha256()}`", ""] + ([note, ""] if note else []) + [
              f"Byte-counter calibration with the library's copy kernel ({copied_mib} MiB read + written): "
              f"FETCH_SIZE x {ff:.4g} B, WRITE_SIZE x {wf:.4g} B.", "",
              "| phase | launches | avg (us) | total (ms) | HBM read / launch (MB) | HBM write / launch (MB) |",
@@ -252,6 +253,7 @@ def _main():
     s.add_argument("--command", required=True)
     s.add_argument("--workload", required=True)
     s.add_argument("--copy-mib", type=int, default=1024)
+    s.add_argument("--note", default="")
     c = sub.add_parser("counters")
     c.add_argument("trace_dir")
     c.add_argument("out_md")
@@ -276,7 +278,7 @@ def _main():
     summarize(a.trace_dir, a.counter_dir,
               {"FETCH_SIZE": os.path.join(a.copy_dir, "copy_FETCH_SIZE"),
                "WRITE_SIZE": os.path.join(a.copy_dir, "copy_WRITE_SIZE")},
-              a.out_md, a.command, a.workload, a.copy_mib)
+              a.out_md, a.command, a.workload, a.copy_mib, a.note)
     print("wrote", a.out_md)
 
 
