@@ -637,24 +637,22 @@ MO_DEV void apply_e_tile(uint8_t* ws, uint32_t k, uint32_t blk, double (*DI)[PW]
     const int64_t ld = eg.m_pad;
     double* Ecol = E + int64_t(cc) * PW;      // row g of the tile: Ecol[g * ld + c]
     load_d(DI, Dall, I);
-    // the old values of this lane's outputs
+    __syncthreads();
+    // acc = D_I^T X with X(k, c) = E[pair row k][64 cc + c].  The old value of
+    // this lane's output (row 32 h + 16 x + l / 16 + 4 v, column c0 + 16 y),
+    // h = w / 2, is the B operand it loads at k-step 32 h + 16 x + 4 v: it is
+    // kept from there instead of being read again (the loop is unrolled, so
+    // the register it goes to is fixed; only the wave's h is tested).
+    const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int hw = w >> 1;
+    const int r0 = 32 * hw + (l & 15), c0 = 32 * (w & 1) + (l & 15);
+    f64x4 acc[2][2];
     double own[2][2][4];
 #pragma unroll
     for (int x = 0; x < 2; ++x)
 #pragma unroll
-        for (int y = 0; y < 2; ++y)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) own[x][y][v] = Ecol[pair_index(pI, qI, mfma_row(x, v)) * ld + mfma_col(y)];
-    __syncthreads();
-    // acc = D_I^T X with X(k, c) = E[pair row k][64 cc + c]
-    const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int r0 = 32 * (w >> 1) + (l & 15), c0 = 32 * (w & 1) + (l & 15);
-    f64x4 acc[2][2];
-#pragma unroll
-    for (int x = 0; x < 2; ++x)
-#pragma unroll
         for (int y = 0; y < 2; ++y) acc[x][y] = f64x4{0.0, 0.0, 0.0, 0.0};
-#pragma unroll 4
+#pragma unroll
     for (int k0 = 0; k0 < PW; k0 += 4) {
         const int kq = k0 + (l >> 4);
         const double* xrow = Ecol + pair_index(pI, qI, kq) * ld;
@@ -663,6 +661,10 @@ MO_DEV void apply_e_tile(uint8_t* ws, uint32_t k, uint32_t blk, double (*DI)[PW]
         for (int x = 0; x < 2; ++x) a[x] = DI[kq][r0 + 16 * x];
 #pragma unroll
         for (int y = 0; y < 2; ++y) b[y] = xrow[c0 + 16 * y];
+        if (hw == (k0 >> 5)) {
+#pragma unroll
+            for (int y = 0; y < 2; ++y) own[(k0 >> 4) & 1][y][(k0 >> 2) & 3] = b[y];
+        }
 #pragma unroll
         for (int x = 0; x < 2; ++x)
 #pragma unroll
