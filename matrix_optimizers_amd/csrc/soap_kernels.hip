@@ -498,13 +498,13 @@ MO_DEV int mfma_col(int y) { return 32 * ((threadIdx.x >> 6) & 1) + 16 * y + (th
 // A' = V_I^T A V_J, mirrored below the diagonal.  With V = I + D:
 // C = X + X D_J, A' = C + D_I^T C.  A tile whose two pairs were not rotated is
 // left untouched (the products would add exact zeros).
-// Only C sits in LDS (32 KB, so several workgroups share a CU).  The operands
-// of both products come straight from memory: X through its mirror (rows of
-// pair J, X^T[c][r] = A[J row c][I column r]; A is kept exactly symmetric off
-// the diagonal tiles, and on them the two orientations differ by rounding
-// only), D_J and D_I from the round's rotations (L2).  The result replaces C
-// in LDS and is written by rows, to the tile and to its mirror.
-MO_DEV void apply_a_tile(uint8_t* ws, uint32_t k, uint32_t blk, double (*C)[PW]) {
+// One 64 x 65 fp64 buffer in LDS (33 KB, so several workgroups share a CU)
+// holds X^T, then C, then the result.  X is read once, through its mirror
+// (rows of pair J, X^T[c][r] = A[J row c][I column r]; A is kept exactly
+// symmetric off the diagonal tiles, and on them the two orientations differ
+// by rounding only); D_J and D_I come straight from the round's rotations
+// (L2).  The result is written by rows, to the tile and to its mirror.
+MO_DEV void apply_a_tile(uint8_t* ws, uint32_t k, uint32_t blk, double (*C)[PW + 1]) {
     const mo_so_header* h = so_header(ws);
     const mo_so_eig* eigs = so_eigs(ws);
     const mo_so_eig& eg = eigs[find_rec(eigs, h->n_eigs, blk, &mo_so_eig::apply_begin)];
@@ -529,30 +529,26 @@ MO_DEV void apply_a_tile(uint8_t* ws, uint32_t k, uint32_t blk, double (*C)[PW])
     const int t = threadIdx.x;
     const int l = t & 63, w = t >> 6;
     const int r0 = 32 * (w >> 1) + (l & 15), c0 = 32 * (w & 1) + (l & 15);
-    // I-pair column offsets of this lane's two A-operand rows
-    int64_t colI[2];
-#pragma unroll
-    for (int x = 0; x < 2; ++x) colI[x] = pair_index(pI, qI, r0 + 16 * x);
-    double own[2][2][4];
-#pragma unroll
-    for (int x = 0; x < 2; ++x)
-#pragma unroll
-        for (int y = 0; y < 2; ++y)
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-                own[x][y][v] = M[pair_index(pJ, qJ, mfma_col(y)) * ld + pair_index(pI, qI, mfma_row(x, v))];
+    // X^T (rows of pair J, columns of pair I) staged in the buffer, one read of
+    // A per element; the buffer then takes C
+    for (int q = t; q < PW * PW / 2; q += SO_THREADS) {
+        const int c = q / (PW / 2), r = 2 * (q % (PW / 2));
+        const f64x2 v = *reinterpret_cast<const f64x2*>(M + pair_index(pJ, qJ, c) * ld + pair_index(pI, qI, r));
+        C[c][r] = v[0];
+        C[c][r + 1] = v[1];
+    }
+    __syncthreads();
     f64x4 acc[2][2];
 #pragma unroll
     for (int x = 0; x < 2; ++x)
 #pragma unroll
         for (int y = 0; y < 2; ++y) acc[x][y] = f64x4{0.0, 0.0, 0.0, 0.0};
-#pragma unroll 4
+#pragma unroll
     for (int k0 = 0; k0 < PW; k0 += 4) {   // X D_J
         const int kq = k0 + (l >> 4);
-        const double* xrow = M + pair_index(pJ, qJ, kq) * ld;   // X^T row kq
         double a[2], b[2];
 #pragma unroll
-        for (int x = 0; x < 2; ++x) a[x] = xrow[colI[x]];
+        for (int x = 0; x < 2; ++x) a[x] = C[kq][r0 + 16 * x];   // X[r][kq] = X^T[kq][r]
 #pragma unroll
         for (int y = 0; y < 2; ++y) b[y] = DJ[kq * PW + c0 + 16 * y];
 #pragma unroll
@@ -560,18 +556,26 @@ MO_DEV void apply_a_tile(uint8_t* ws, uint32_t k, uint32_t blk, double (*C)[PW])
 #pragma unroll
             for (int y = 0; y < 2; ++y) acc[x][y] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[x], b[y], acc[x][y], 0, 0, 0);
     }
+    double own[2][2][4];
 #pragma unroll
     for (int x = 0; x < 2; ++x)
 #pragma unroll
         for (int y = 0; y < 2; ++y)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) C[mfma_row(x, v)][mfma_col(y)] = own[x][y][v] + acc[x][y][v];
+            for (int v = 0; v < 4; ++v) own[x][y][v] = C[mfma_col(y)][mfma_row(x, v)] + acc[x][y][v];
+    __syncthreads();                          // X^T fully read: C replaces it
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) C[mfma_row(x, v)][mfma_col(y)] = own[x][y][v];
     __syncthreads();
 #pragma unroll
     for (int x = 0; x < 2; ++x)
 #pragma unroll
         for (int y = 0; y < 2; ++y) acc[x][y] = f64x4{0.0, 0.0, 0.0, 0.0};
-#pragma unroll 4
+#pragma unroll
     for (int k0 = 0; k0 < PW; k0 += 4) {   // D_I^T C
         const int kq = k0 + (l >> 4);
         double a[2], b[2];
@@ -601,7 +605,7 @@ MO_DEV void apply_a_tile(uint8_t* ws, uint32_t k, uint32_t blk, double (*C)[PW])
     for (int q = t; q < PW * PW / 2; q += SO_THREADS) {
         const int r = q / (PW / 2), c = 2 * (q % (PW / 2));
         *reinterpret_cast<f64x2*>(M + pair_index(pI, qI, r) * ld + pair_index(pJ, qJ, c)) =
-            *reinterpret_cast<const f64x2*>(&C[r][c]);
+            f64x2{C[r][c], C[r][c + 1]};
     }
     if (I != J) {
         for (int q = t; q < PW * PW / 2; q += SO_THREADS) {
@@ -685,10 +689,10 @@ MO_DEV void apply_e_tile(uint8_t* ws, uint32_t k, uint32_t blk, double (*DI)[PW]
 // take the upper tiles of A (the heavier items, dispatched first), the rest
 // the tiles of E.  Both keep one 64 x 64 fp64 tile in LDS.
 __global__ __launch_bounds__(SO_THREADS) void so_jac_rotate_kernel(uint8_t* ws, uint32_t k) {
-    __shared__ __align__(16) double buf[PW][PW];
+    __shared__ __align__(16) double buf[PW * (PW + 1)];
     const uint32_t na = so_header(ws)->n_apply_items;
-    if (blockIdx.x < na) apply_a_tile(ws, k, blockIdx.x, buf);
-    else apply_e_tile(ws, k, blockIdx.x - na, buf);
+    if (blockIdx.x < na) apply_a_tile(ws, k, blockIdx.x, reinterpret_cast<double (*)[PW + 1]>(buf));
+    else apply_e_tile(ws, k, blockIdx.x - na, reinterpret_cast<double (*)[PW]>(buf));
 }
 
 // One workgroup per decomposition: sort the eigenvalues diag(A) ascending
