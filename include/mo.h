@@ -295,7 +295,7 @@ mo_status shampoo_owner_step(const mo_shampoo_matrix* mats, int32_t n_mats,
  * off-diagonal entry at or below 2^-48 ||L'||_F (or ||R'||_F) is left
  * unrotated, which moves an eigenvector by at most that over its eigenvalue
  * gap); the
- * statistics, moments and products are fp32.  Sides are at most 8192. */
+ * statistics, moments and products are fp32.  Sides are at most 16384. */
 
 /* One whole matrix with its SOAP state.
  *   W          rows x cols, w_dtype, row stride ld_w; updated in place
@@ -343,7 +343,7 @@ mo_status soap_workspace_bytes(const mo_soap_matrix* mats, int32_t n_mats,
  * muon_owner_step: MO_ERR_INVALID_ARG (null pointer with numel > 0, negative
  * size, a stride below its row length, step < 1, sweeps outside 1 .. 100,
  * non-finite lr, betas, eps or weight decay, betas outside [0, 1), eps < 0),
- * MO_ERR_UNSUPPORTED (dtype not MO_F32/MO_BF16, a side longer than 8192, more
+ * MO_ERR_UNSUPPORTED (dtype not MO_F32/MO_BF16, a side longer than 16384, more
  * than 2^30 rotation tiles of 64 x 64 over the bucket's sides),
  * MO_ERR_WORKSPACE_TOO_SMALL, MO_ERR_ALIAS (a written tensor overlaps any
  * tensor of the bucket or the workspace), MO_ERR_HIP. */

@@ -39,5 +39,5 @@ hipError_t mo_launch_so_eig_init(const mo_so_eig& eg, uint8_t* ws, uint32_t ei, 
 hipError_t mo_launch_so_norm(const mo_so_eig& eg, uint8_t* ws, uint32_t ei, hipStream_t s);
 hipError_t mo_launch_so_solve(const mo_so_header& h, uint8_t* ws, uint32_t k, hipStream_t s);
 hipError_t mo_launch_so_rotate(const mo_so_header& h, uint8_t* ws, uint32_t k, hipStream_t s);
-hipError_t mo_launch_so_sort(const mo_so_header& h, uint8_t* ws, hipStream_t s);
+hipError_t mo_launch_so_rank(const mo_so_eig& eg, uint8_t* ws, uint32_t ei, hipStream_t s);
 hipError_t mo_launch_so_gather(const mo_so_eig& eg, uint8_t* ws, uint32_t ei, hipStream_t s);

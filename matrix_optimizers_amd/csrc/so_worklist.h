@@ -14,7 +14,7 @@
 
 #define MO_SO_PAD    64   // padding of every side (the eigensolver's pair of 32-wide blocks)
 #define MO_SO_BLK    32   // Jacobi block width
-#define MO_SO_MAXSIDE 8192  // the eigenvalue sort runs in one workgroup's LDS
+#define MO_SO_MAXSIDE 16384  // the paper's MLP side; each side holds 5 m_pad^2 fp64-equivalents of workspace
 
 // fp32 products of the step (C = op(A) op(B), 64 x 64 tiles)
 #define MO_SOK_STATS_L 0   // L' = L + G G^T: caller L and the fp64 copy the eigensolver works on

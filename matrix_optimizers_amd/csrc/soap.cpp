@@ -256,9 +256,10 @@ mo_status soap_owner_step(const mo_soap_matrix* mats, int32_t n, const mo_soap_h
         if (!ok(MO_PHASE_SO_SOLVE, [&] { return mo_launch_so_solve(h, ws, k, s); })) return MO_ERR_HIP;
         if (!ok(MO_PHASE_SO_APPLY, [&] { return mo_launch_so_rotate(h, ws, k, s); })) return MO_ERR_HIP;
     }
-    if (!ok(MO_PHASE_SO_SORT, [&] { return mo_launch_so_sort(h, ws, s); })) return MO_ERR_HIP;
-    for (uint32_t e = 0; e < h.n_eigs; ++e)
+    for (uint32_t e = 0; e < h.n_eigs; ++e) {
+        if (!ok(MO_PHASE_SO_SORT, [&] { return mo_launch_so_rank(plan.eigs[e], ws, e, s); })) return MO_ERR_HIP;
         if (!ok(MO_PHASE_SO_SORT, [&] { return mo_launch_so_gather(plan.eigs[e], ws, e, s); })) return MO_ERR_HIP;
+    }
     static const int kProducts[] = {MO_SOK_LEFT_G, MO_SOK_RIGHT_G, MO_SOK_LEFT_M,
                                     MO_SOK_RIGHT_M, MO_SOK_BACK_L,  MO_SOK_BACK_R};
     for (uint32_t i = 0; i < h.n_mats; ++i)

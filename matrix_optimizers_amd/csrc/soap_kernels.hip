@@ -189,7 +189,10 @@ __global__ __launch_bounds__(SO_THREADS) void so_gemm_kernel(uint8_t* ws, uint32
     const int t = threadIdx.x;
     const int64_t i0 = int64_t(blockIdx.y) * GB, j0 = int64_t(blockIdx.x) * GB;
     const int r0 = (t / 16) * 4, c0 = (t % 16) * 4;
-    float acc[4][4] = {};
+    // fp64 accumulation: K runs up to the long side (16384), where a sequential
+    // fp32 sum drops the small terms that follow a large partial sum, always
+    // the same way; each result is rounded to fp32 once
+    double acc[4][4] = {};
     for (int k0 = 0; k0 < p.K; k0 += GK) {
         if (p.a_k == 1) {   // 4 consecutive k of one row i
             const int i = t / 4, kk = (t % 4) * 4;
@@ -219,12 +222,15 @@ __global__ __launch_bounds__(SO_THREADS) void so_gemm_kernel(uint8_t* ws, uint32
 #pragma unroll
             for (int x = 0; x < 4; ++x)
 #pragma unroll
-                for (int y = 0; y < 4; ++y) acc[x][y] = fmaf(a[x], b[y], acc[x][y]);
+                for (int y = 0; y < 4; ++y) acc[x][y] = fma(double(a[x]), double(b[y]), acc[x][y]);
         }
         __syncthreads();
     }
 #pragma unroll
-    for (int x = 0; x < 4; ++x) so_epilogue(ws, mt, kind, i0 + r0 + x, j0 + c0, acc[x]);
+    for (int x = 0; x < 4; ++x) {
+        const float v[4] = {float(acc[x][0]), float(acc[x][1]), float(acc[x][2]), float(acc[x][3])};
+        so_epilogue(ws, mt, kind, i0 + r0 + x, j0 + c0, v);
+    }
 }
 
 // ============================================================================
@@ -695,40 +701,44 @@ __global__ __launch_bounds__(SO_THREADS) void so_jac_rotate_kernel(uint8_t* ws, 
     else apply_e_tile(ws, k, blockIdx.x - na, reinterpret_cast<double (*)[PW]>(buf));
 }
 
-// One workgroup per decomposition: sort the eigenvalues diag(A) ascending
-// (bitonic, padding last) and keep the permutation.
-constexpr int SORT_THREADS = 1024;
-__global__ __launch_bounds__(SORT_THREADS) void so_eig_sort_kernel(uint8_t* ws) {
-    __shared__ double key[MO_SO_MAXSIDE];
-    __shared__ int val[MO_SO_MAXSIDE];
-    const mo_so_eig& eg = so_eigs(ws)[blockIdx.x];
-    const double* A = reinterpret_cast<const double*>(ws + eg.off_A);
-    int n2 = 1;
-    while (n2 < int(eg.m_pad)) n2 <<= 1;
-    for (int i = threadIdx.x; i < n2; i += SORT_THREADS) {
-        key[i] = i < int(eg.m) ? A[int64_t(i) * eg.m_pad + i] : __builtin_huge_val();
-        val[i] = i;
+// The eigenvalues in ascending order, as a permutation: lam[i] = A[i][i] for
+// i < m, +inf for padding (and for a NaN, which has no order), then the rank
+// of each, counting the smaller keys and, among equal keys, the lower
+// indices.  The keys and indices give a total order, so the ranks are a
+// permutation of 0 .. m_pad - 1 for any input.  lam reuses the row sums of
+// squares of the norm launch, whose threshold (entry m_pad) stays.
+__global__ __launch_bounds__(SO_THREADS) void so_eig_diag_kernel(uint8_t* ws, uint32_t ei) {
+    const mo_so_eig& eg = so_eigs(ws)[ei];
+    const int64_t i = int64_t(blockIdx.x) * SO_THREADS + threadIdx.x;
+    if (i >= eg.m_pad) return;
+    double v = __builtin_huge_val();
+    if (i < eg.m) {
+        const double d = reinterpret_cast<const double*>(ws + eg.off_A)[i * eg.m_pad + i];
+        if (d == d) v = d;
     }
-    __syncthreads();
-    for (int size = 2; size <= n2; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = threadIdx.x; i < n2; i += SORT_THREADS) {
-                const int p = i ^ stride;
-                if (p > i) {
-                    const bool up = (i & size) == 0;
-                    // ties by index keep the order deterministic
-                    const bool gt = key[i] > key[p] || (key[i] == key[p] && val[i] > val[p]);
-                    if (gt == up) {
-                        const double tk = key[i]; key[i] = key[p]; key[p] = tk;
-                        const int tv = val[i]; val[i] = val[p]; val[p] = tv;
-                    }
-                }
-            }
-            __syncthreads();
+    reinterpret_cast<double*>(ws + eg.off_norm)[i] = v;
+}
+
+constexpr int RANK_CHUNK = 1024;
+__global__ __launch_bounds__(SO_THREADS) void so_eig_rank_kernel(uint8_t* ws, uint32_t ei) {
+    __shared__ double chunk[RANK_CHUNK];
+    const mo_so_eig& eg = so_eigs(ws)[ei];
+    const double* lam = reinterpret_cast<const double*>(ws + eg.off_norm);
+    const int n = int(eg.m_pad);
+    const int i = int(blockIdx.x) * SO_THREADS + int(threadIdx.x);
+    const double key = i < n ? lam[i] : 0.0;
+    int rank = 0;
+    for (int c0 = 0; c0 < n; c0 += RANK_CHUNK) {
+        const int len = min(RANK_CHUNK, n - c0);
+        __syncthreads();
+        for (int q = threadIdx.x; q < len; q += SO_THREADS) chunk[q] = lam[c0 + q];
+        __syncthreads();
+        for (int q = 0; q < len; ++q) {
+            const double v = chunk[q];
+            rank += (v < key) || (v == key && c0 + q < i);
         }
     }
-    int* perm = reinterpret_cast<int*>(ws + eg.off_perm);
-    for (int i = threadIdx.x; i < int(eg.m_pad); i += SORT_THREADS) perm[i] = val[i];
+    if (i < n) reinterpret_cast<int*>(ws + eg.off_perm)[rank] = i;
 }
 
 // E32 row r = E row perm[r] (fp32) for r < m, zero below.
@@ -739,12 +749,12 @@ __global__ __launch_bounds__(SO_THREADS) void so_eig_gather_kernel(uint8_t* ws, 
     const int64_t r = idx / eg.m_pad, c = idx % eg.m_pad;
     const int* perm = reinterpret_cast<const int*>(ws + eg.off_perm);
     const double* E = reinterpret_cast<const double*>(ws + eg.off_E);
-    // a non-finite eigenvalue has no order: its slot may hold a padding index
-    // (up to the sort's power of two), so the row read is bounded here
+    // the permutation is total (see the rank kernel); the row read is bounded
+    // all the same
     float v = 0.f;
     if (r < eg.m) {
         const int64_t pr = perm[r];
-        v = pr < eg.m_pad ? float(E[pr * eg.m_pad + c]) : __builtin_nanf("");
+        v = (pr >= 0 && pr < eg.m_pad) ? float(E[pr * eg.m_pad + c]) : __builtin_nanf("");
     }
     reinterpret_cast<float*>(ws + eg.off_E32)[idx] = v;
 }
@@ -796,8 +806,12 @@ hipError_t mo_launch_so_rotate(const mo_so_header& h, uint8_t* ws, uint32_t k, h
     return hipGetLastError();
 }
 
-hipError_t mo_launch_so_sort(const mo_so_header& h, uint8_t* ws, hipStream_t s) {
-    hipLaunchKernelGGL(so_eig_sort_kernel, dim3(h.n_eigs), dim3(SORT_THREADS), 0, s, ws);
+hipError_t mo_launch_so_rank(const mo_so_eig& eg, uint8_t* ws, uint32_t ei, hipStream_t s) {
+    const unsigned blocks = (eg.m_pad + SO_THREADS - 1) / SO_THREADS;
+    hipLaunchKernelGGL(so_eig_diag_kernel, dim3(blocks), dim3(SO_THREADS), 0, s, ws, ei);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(so_eig_rank_kernel, dim3(blocks), dim3(SO_THREADS), 0, s, ws, ei);
     return hipGetLastError();
 }
 

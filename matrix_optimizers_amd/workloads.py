@@ -309,6 +309,13 @@ SOAP_WORKLOADS = {
     "soap_decoder_layer_h2048": SoapWorkload(
         key="soap_decoder_layer_h2048", seed=14, matrices=tuple(_decoder_layer(2048, 5632, 2048)),
         description="one decoder-layer owner bucket, hidden 2048, FFN 5632, fp32 weights and gradients"),
+    # One layer of the paper's model (hidden 4096, intermediate 16384), as in
+    # the Shampoo workload of the same name: two 16384-sided statistics.
+    "soap_paper_layer": SoapWorkload(
+        key="soap_paper_layer", seed=15,
+        matrices=(MatrixSpec(4096, 4096, "q"), MatrixSpec(4096, 4096, "k"), MatrixSpec(4096, 4096, "v"),
+                  MatrixSpec(4096, 4096, "o"), MatrixSpec(16384, 4096, "up"), MatrixSpec(4096, 16384, "down")),
+        description="one layer of the paper's hidden-4096 / intermediate-16384 model, fp32"),
 }
 
 

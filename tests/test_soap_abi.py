@@ -58,7 +58,7 @@ def test_null_arguments():
     (dict(ld_r=95), INVALID), (dict(ld_m=95), INVALID), (dict(ld_v=10), INVALID),
     (dict(ld_u=1, update_out=BASE + 250 * GiB), INVALID), (dict(ld_m=-1), INVALID),
     (dict(w_dtype=3), UNSUPPORTED), (dict(g_dtype=9), UNSUPPORTED),
-    (dict(rows=8193, cols=1), UNSUPPORTED), (dict(rows=1, cols=8193), UNSUPPORTED),
+    (dict(rows=16385, cols=1), UNSUPPORTED), (dict(rows=1, cols=16385), UNSUPPORTED),
 ])
 def test_bad_descriptors(d, code):
     rows, cols = d.pop("rows", 64), d.pop("cols", 96)

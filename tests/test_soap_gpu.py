@@ -1,7 +1,8 @@
 """SOAP owner step on the GPU (soap_owner_step through the C ABI) against the
 fp64 oracle (oracle/soap.py), on the same stored inputs.
 
-Tolerance.  The step is fp32 except for its eigensolver (fp64).  Its update
+Tolerance.  The step stores fp32 and accumulates its products in fp64; its
+eigensolver is fp64.  Its update
 depends on the eigenvectors of the fp32 statistics, and where two eigenvalues
 are closer than the fp32 rounding of L' or R' can separate, the fp32
 statistics alone move those eigenvectors: the error of an fp32 step has a
@@ -330,3 +331,28 @@ def test_zero_state_and_gradient(gpu):
     assert torch.equal(U, torch.zeros_like(U))
     decay = np.float32(1 - hp["lr"] * hp["weight_decay"])
     assert torch.equal(W, W0 * float(decay))
+
+
+def test_side_beyond_8192_first_step_closed_form(gpu):
+    """A 9000-sided statistic (9000 x 64 matrix, m_pad 9024, 141 block pairs):
+    one step from eps I and zero moments.  With G = U S W^T (thin SVD), the
+    eigenbases are U (plus the eps-eigenspace, where G, M' and V' vanish) and
+    W, so G~ is S in those bases and the update is lr U diag(s / (s + eps)) W^T
+    (t = 1: the bias corrections cancel b1 and b2), the oracle's step in closed
+    form (it matches the oracle to 6e-13 at 900 x 64).  The first step divides
+    the rotated gradient's small entries by eps, so it amplifies the fp32
+    rounding of the statistics by 1 / eps; Adam's eps is 1e-2 here (the
+    singular values are about 0.09).  The bar is the fp32 floor of this input:
+    the fp32 model of the step with exact eigenvectors (fp32_floor) measures
+    1.04e-3 against the closed form; the GPU, which accumulates its products in
+    fp64, must stay within it."""
+    r, c = 9000, 64
+    st = first_state(81, r, c)
+    hp = dict(HP, eps=1e-2, weight_decay=0.0)
+    out = run_gpu([st], 1, hp)[0]
+    U, sv, Wt = np.linalg.svd(st["G"], full_matrices=False)
+    D = hp["lr"] * (U * (sv / (sv + hp["eps"]))) @ Wt
+    err = rel(out["U"], D)
+    print(f"9000 x 64 first step: update {err:.2e} against the closed form", flush=True)
+    assert np.all(np.isfinite(out["U"]))
+    assert err <= 1e-3
