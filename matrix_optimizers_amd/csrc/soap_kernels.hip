@@ -34,6 +34,7 @@ typedef double f64x2 __attribute__((ext_vector_type(2)));
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 constexpr int SO_THREADS = 256;
+constexpr int SV_THREADS = 512;        // the pair solve: one slot of 2 x 2 blocks per thread
 constexpr int GB = 64;                 // GEMM tile
 constexpr int GK = 16;                 // GEMM K chunk
 constexpr int PW = 2 * MO_SO_BLK;      // pair width (64)
@@ -323,7 +324,7 @@ MO_DEV bool jacobi_rotation(double app, double aqq, double apq, double thr, doub
 // 64 x 64 pair problem S = A[pair][pair] by at most INNER_SWEEPS scalar cyclic
 // sweeps (it stops after a sweep without a rotation) and store its rotation as
 // D = V - I (V^T S V ~ diagonal), and whether it rotated at all.
-__global__ __launch_bounds__(SO_THREADS) void so_jac_solve_kernel(uint8_t* ws, uint32_t k) {
+__global__ __launch_bounds__(SV_THREADS) void so_jac_solve_kernel(uint8_t* ws, uint32_t k) {
     __shared__ double S[PW][PW + 1];
     __shared__ double D[PW][PW + 1];
     __shared__ double rs[PW / 2], rtau[PW / 2], rt[PW / 2], rapq[PW / 2];
@@ -339,7 +340,7 @@ __global__ __launch_bounds__(SO_THREADS) void so_jac_solve_kernel(uint8_t* ws, u
     circle_pair(nb, int(k % uint32_t(nb - 1)), j, bp, bq);
     const double* A = reinterpret_cast<const double*>(ws + eg.off_A);
     const int t = threadIdx.x;
-    for (int q = t; q < PW * PW / 2; q += SO_THREADS) {
+    for (int q = t; q < PW * PW / 2; q += SV_THREADS) {
         const int r = q / (PW / 2), c = 2 * (q % (PW / 2));
         const f64x2 v = *reinterpret_cast<const f64x2*>(A + pair_index(bp, bq, r) * eg.m_pad + pair_index(bp, bq, c));
         S[r][c] = v[0];
@@ -354,7 +355,7 @@ __global__ __launch_bounds__(SO_THREADS) void so_jac_solve_kernel(uint8_t* ws, u
     // flag 1, which sweep 0 first clears at its step 1, after every thread has
     // passed step 0's barrier and so has read it here.
     const double thr = reinterpret_cast<const double*>(ws + eg.off_norm)[eg.m_pad];
-    for (int q = t; q < PW * PW; q += SO_THREADS) {
+    for (int q = t; q < PW * PW; q += SV_THREADS) {
         const int r = q / PW, c = q % PW;
         if (r != c && fabs(S[r][c]) > thr) rotated[1] = 1;
     }
@@ -377,39 +378,24 @@ __global__ __launch_bounds__(SO_THREADS) void so_jac_solve_kernel(uint8_t* ws, u
             if (t == 0 && step == 1) rotated[(sweep + 1) & 1] = 0;
             __syncthreads();
             // Two-sided update of the off-diagonal 2 x 2 blocks, each unordered
-            // pair {u, v} once, mirrored: slot b (0 .. 511) is u = b / 16 with
-            // v = u + 1 + b % 16 (mod 32); the pairs 16 apart come up twice and
-            // run from the lower u only.  Each thread takes two slots, with all
-            // loads issued before the arithmetic.
+            // pair {u, v} once, mirrored: slot t (0 .. 511) is u = t / 16 with
+            // v = u + 1 + t % 16 (mod 32); the pairs 16 apart come up twice and
+            // run from the lower u only.  Loads are issued before the arithmetic.
             {
-                int au[2], bu[2], av[2], bv[2];
-                bool on[2];
-                double x[2][4];
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const int bidx = t + SO_THREADS * i;
-                    const int u = bidx >> 4, dv = bidx & 15, v = (u + 1 + dv) & 31;
-                    on[i] = dv != 15 || u < 16;
-                    au[i] = ra[u]; bu[i] = rb[u]; av[i] = ra[v]; bv[i] = rb[v];
-                    x[i][0] = S[au[i]][av[i]]; x[i][1] = S[au[i]][bv[i]];
-                    x[i][2] = S[bu[i]][av[i]]; x[i][3] = S[bu[i]][bv[i]];
-                }
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const int bidx = t + SO_THREADS * i;
-                    const int u = bidx >> 4, v = (u + 1 + (bidx & 15)) & 31;
-                    const double su = rs[u], tu = rtau[u], sv = rs[v], tv = rtau[v];
-                    const double x00 = x[i][0], x01 = x[i][1], x10 = x[i][2], x11 = x[i][3];
-                    // rows: J_u^T
-                    const double y00 = x00 - su * (x10 + tu * x00), y10 = x10 + su * (x00 - tu * x10);
-                    const double y01 = x01 - su * (x11 + tu * x01), y11 = x11 + su * (x01 - tu * x11);
-                    // columns: J_v
-                    const double z00 = y00 - sv * (y01 + tv * y00), z01 = y01 + sv * (y00 - tv * y01);
-                    const double z10 = y10 - sv * (y11 + tv * y10), z11 = y11 + sv * (y10 - tv * y11);
-                    if (on[i]) {
-                        S[au[i]][av[i]] = z00; S[au[i]][bv[i]] = z01; S[bu[i]][av[i]] = z10; S[bu[i]][bv[i]] = z11;
-                        S[av[i]][au[i]] = z00; S[bv[i]][au[i]] = z01; S[av[i]][bu[i]] = z10; S[bv[i]][bu[i]] = z11;
-                    }
+                const int u = t >> 4, dv = t & 15, v = (u + 1 + dv) & 31;
+                const bool on = dv != 15 || u < 16;
+                const int au = ra[u], bu = rb[u], av = ra[v], bv = rb[v];
+                const double x00 = S[au][av], x01 = S[au][bv], x10 = S[bu][av], x11 = S[bu][bv];
+                const double su = rs[u], tu = rtau[u], sv = rs[v], tv = rtau[v];
+                // rows: J_u^T
+                const double y00 = x00 - su * (x10 + tu * x00), y10 = x10 + su * (x00 - tu * x10);
+                const double y01 = x01 - su * (x11 + tu * x01), y11 = x11 + su * (x01 - tu * x11);
+                // columns: J_v
+                const double z00 = y00 - sv * (y01 + tv * y00), z01 = y01 + sv * (y00 - tv * y01);
+                const double z10 = y10 - sv * (y11 + tv * y10), z11 = y11 + sv * (y10 - tv * y11);
+                if (on) {
+                    S[au][av] = z00; S[au][bv] = z01; S[bu][av] = z10; S[bu][bv] = z11;
+                    S[av][au] = z00; S[bv][au] = z01; S[av][bu] = z10; S[bv][bu] = z11;
                 }
                 // the diagonal blocks: the rotated 2 x 2 problem itself
                 if (t < PW / 2 && rs[t] != 0.0) {   // not rotated: S[a][b] stays
@@ -421,20 +407,21 @@ __global__ __launch_bounds__(SO_THREADS) void so_jac_solve_kernel(uint8_t* ws, u
                     S[b2][a2] = 0.0;
                 }
             }
-            // D <- D J + (J - I): thread t takes pair u = t % 32 in rows t / 32 + 8 i
+            // D <- D J + (J - I): thread t takes pair u = t % 32 in rows t / 32 + 16 i
             {
                 const int u = t & 31, a2 = ra[u], b2 = rb[u];
                 const double s2 = rs[u], tau = rtau[u];
-                double da[8], db[8];
+                constexpr int NR = PW * (PW / 2) / SV_THREADS;
+                double da[NR], db[NR];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int r = (t >> 5) + 8 * i;
+                for (int i = 0; i < NR; ++i) {
+                    const int r = (t >> 5) + (SV_THREADS / 32) * i;
                     da[i] = D[r][a2];
                     db[i] = D[r][b2];
                 }
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int r = (t >> 5) + 8 * i;
+                for (int i = 0; i < NR; ++i) {
+                    const int r = (t >> 5) + (SV_THREADS / 32) * i;
                     double na = da[i] - s2 * (db[i] + tau * da[i]), nb2 = db[i] + s2 * (da[i] - tau * db[i]);
                     if (r == a2) { na -= s2 * tau; nb2 += s2; }
                     if (r == b2) { na -= s2; nb2 -= s2 * tau; }
@@ -448,7 +435,7 @@ __global__ __launch_bounds__(SO_THREADS) void so_jac_solve_kernel(uint8_t* ws, u
         any = true;
     }
     double* Dout = reinterpret_cast<double*>(ws + eg.off_D) + int64_t(j) * PW * PW;
-    for (int q = t; q < PW * PW / 2; q += SO_THREADS) {
+    for (int q = t; q < PW * PW / 2; q += SV_THREADS) {
         const int r = q / (PW / 2), c = 2 * (q % (PW / 2));
         *reinterpret_cast<f64x2*>(Dout + r * PW + c) = f64x2{D[r][c], D[r][c + 1]};
     }
@@ -796,7 +783,7 @@ hipError_t mo_launch_so_norm(const mo_so_eig& eg, uint8_t* ws, uint32_t ei, hipS
 }
 
 hipError_t mo_launch_so_solve(const mo_so_header& h, uint8_t* ws, uint32_t k, hipStream_t s) {
-    hipLaunchKernelGGL(so_jac_solve_kernel, dim3(h.n_solve_items), dim3(SO_THREADS), 0, s, ws, k);
+    hipLaunchKernelGGL(so_jac_solve_kernel, dim3(h.n_solve_items), dim3(SV_THREADS), 0, s, ws, k);
     return hipGetLastError();
 }
 
