@@ -145,7 +145,7 @@ def algorithmic_flops(spec_rows, spec_cols, steps):
 
 
 CPU_BUDGET_S = 20.0          # oracle work per bench run
-ORACLE_TFLOPS_GUESS = 0.5    # fp64 numpy on a GPU machine's host, for sizing the sample only
+ORACLE_TFLOPS_GUESS = 0.5    # fp64 numpy on the measuring machine's host, for sizing the sample only
 
 
 def cpu_baseline(wl, args):
