@@ -117,3 +117,29 @@ def test_statistics_and_decay():
     np.testing.assert_array_equal(L1, [[6.0, 2.0], [2.0, 3.0]])
     np.testing.assert_array_equal(R1, [[2.0, 2.0, 0.0], [2.0, 6.0, -1.0], [0.0, -1.0, 2.0]])
     np.testing.assert_allclose(W1, 0.95 * W - D, rtol=0, atol=1e-15)
+
+
+def test_eigenvector_order_matters_once_v_is_warm(monkeypatch):
+    """The second moment V is indexed by the eigenbasis, so with a warm V the
+    update depends on the eigenvectors' order (the reading fixes ascending
+    eigenvalue order, numpy's eigh), while their signs still do not matter:
+    reversing the order changes the update, flipping signs does not."""
+    rng = np.random.default_rng(9)
+    m, n = 5, 7
+    G = rng.standard_normal((m, n))
+    L = 0.1 * np.eye(m) + (lambda A: A @ A.T)(rng.standard_normal((m, 2 * m)))
+    R = 0.1 * np.eye(n) + (lambda A: A @ A.T)(rng.standard_normal((n, 2 * n)))
+    M = rng.standard_normal((m, n))
+    V = rng.standard_normal((m, n)) ** 2
+    ref = osoap.soap_step(np.zeros((m, n)), G, L, R, M, V, 5, 1.0, eps=1e-3)[5]
+    plain = osoap.eigenbasis
+
+    def signs(S):
+        Q = plain(S)
+        return Q * np.where(np.arange(Q.shape[1]) % 2 == 0, -1.0, 1.0)
+    monkeypatch.setattr(osoap, "eigenbasis", signs)
+    flipped = osoap.soap_step(np.zeros((m, n)), G, L, R, M, V, 5, 1.0, eps=1e-3)[5]
+    np.testing.assert_allclose(flipped, ref, rtol=0, atol=1e-12)
+    monkeypatch.setattr(osoap, "eigenbasis", lambda S: plain(S)[:, ::-1])
+    reordered = osoap.soap_step(np.zeros((m, n)), G, L, R, M, V, 5, 1.0, eps=1e-3)[5]
+    assert np.linalg.norm(reordered - ref) > 1e-2 * np.linalg.norm(ref)
