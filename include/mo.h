@@ -183,9 +183,8 @@ const char* mo_status_string(mo_status status);
 #define MO_PHASE_SO_SOLVE   17  /* SOAP: Jacobi pair problems of one round */
 #define MO_PHASE_SO_APPLY   18  /* SOAP: one round's rotations applied to A (both sides) and E */
 #define MO_PHASE_SO_SORT    19  /* SOAP: E = I, eigenvalue sort, sorted fp32 eigenvectors */
-#define MO_PHASE_SO_ROTATE  20  /* SOAP: the six eigenbasis products, V', N and W written */
-#define MO_PHASE_SO_ETILE   21  /* SOAP: unused (the E tiles share the MO_PHASE_SO_APPLY launch) */
-#define MO_PHASE_COUNT    22
+#define MO_PHASE_SO_PRODUCTS 20 /* SOAP: the six eigenbasis products, V', N and W written */
+#define MO_PHASE_COUNT    21
 
 /* Enable (1) or disable (0) per-launch timing on the calling thread.  While
  * enabled, every kernel launch is bracketed by HIP events on its own stream;

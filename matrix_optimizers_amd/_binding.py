@@ -29,7 +29,7 @@ LR_ADJUST = {"original": 0, "match_rms_adamw": 1, "none": 2}
 
 PHASES = ["momentum", "norm", "gram", "poly", "update", "apply", "adamw", "copy", "update_last",
           "sh_layout", "sh_stats", "sh_rootprep", "sh_root", "sh_left", "sh_right",
-          "so_prep", "so_stats", "so_solve", "so_apply", "so_sort", "so_rotate", "so_etile"]
+          "so_prep", "so_stats", "so_solve", "so_apply", "so_sort", "so_products"]
 
 
 class MoError(RuntimeError):

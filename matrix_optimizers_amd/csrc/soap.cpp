@@ -264,7 +264,7 @@ mo_status soap_owner_step(const mo_soap_matrix* mats, int32_t n, const mo_soap_h
                                     MO_SOK_RIGHT_M, MO_SOK_BACK_L,  MO_SOK_BACK_R};
     for (uint32_t i = 0; i < h.n_mats; ++i)
         for (int kind : kProducts)
-            if (!ok(MO_PHASE_SO_ROTATE, [&] { return mo_launch_so_gemm(plan.mats[i], ws, i, kind, s); }))
+            if (!ok(MO_PHASE_SO_PRODUCTS, [&] { return mo_launch_so_gemm(plan.mats[i], ws, i, kind, s); }))
                 return MO_ERR_HIP;
     return MO_OK;
 }
