@@ -280,6 +280,23 @@ def _stream_handle(stream) -> Optional[int]:
     return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _workspace_for(nbytes: int, mats, stream):
+    """A uint8 workspace tensor allocated on the stream the step launches on.
+
+    The caching allocator ties a block to the stream current at allocation and
+    hands it out again, once freed, in that stream's order; a workspace made on
+    another stream than the launch stream could be reused by later work there
+    while the step's kernels still read it."""
+    torch = _torch()
+    dev = mats[0][0].device if mats else torch.device("cuda")
+    if stream is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    if not isinstance(stream, torch.cuda.Stream):
+        stream = torch.cuda.ExternalStream(_stream_handle(stream), device=dev)
+    with torch.cuda.stream(stream):
+        return torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+
 def muon_owner_step(mats: Sequence[Tuple], *, update_out: Optional[Sequence] = None,
                     workspace=None, stream=None, **hp_kwargs) -> None:
     """One Muon step over a bucket of (W, G, M) tensors, in place.
@@ -287,9 +304,10 @@ def muon_owner_step(mats: Sequence[Tuple], *, update_out: Optional[Sequence] = N
     hp_kwargs: lr, weight_decay, momentum, nesterov, ns_steps, ns_coefficients,
     eps, adjust_lr_fn ("original" | "match_rms_adamw" | "none"), ns_dtype
     ("bf16" | "f32").  workspace: an optional uint8 device tensor of at least
-    workspace_bytes(); one is allocated when omitted.
+    workspace_bytes(); one is allocated on the launch stream when omitted.  A
+    caller's workspace must not be freed or reused by other work until the
+    step has finished on ``stream``.
     """
-    torch = _torch()
     lib = load_library()
     hp = hparams(**hp_kwargs)
     ups = list(update_out) if update_out is not None else [None] * len(mats)
@@ -299,8 +317,7 @@ def muon_owner_step(mats: Sequence[Tuple], *, update_out: Optional[Sequence] = N
     _check(lib.muon_workspace_bytes(arr, n, ctypes.byref(hp), ctypes.byref(need)),
            "muon_workspace_bytes")
     if workspace is None:
-        dev = mats[0][0].device if mats else torch.device("cuda")
-        workspace = torch.empty(int(need.value), dtype=torch.uint8, device=dev)
+        workspace = _workspace_for(int(need.value), mats, stream)
     _check(lib.muon_owner_step(arr, n, ctypes.byref(hp), ctypes.c_void_p(workspace.data_ptr()),
                                workspace.numel(), ctypes.c_void_p(_stream_handle(stream))),
            "muon_owner_step")
@@ -424,7 +441,6 @@ def shampoo_owner_step(mats: Sequence[Tuple], *, update_out: Optional[Sequence] 
     hp_kwargs: lr, weight_decay, root_iters.  L and R are the float32
     statistics (rows x rows, cols x cols), started by the caller at eps I.
     """
-    torch = _torch()
     lib = load_library()
     hp = shampoo_hparams(**hp_kwargs)
     ups = list(update_out) if update_out is not None else [None] * len(mats)
@@ -432,8 +448,7 @@ def shampoo_owner_step(mats: Sequence[Tuple], *, update_out: Optional[Sequence] 
     arr, n = _sh_array(descs)
     need = shampoo_workspace_bytes(descs, hp)
     if workspace is None:
-        dev = mats[0][0].device if mats else torch.device("cuda")
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        workspace = _workspace_for(need, mats, stream)
     _check(lib.shampoo_owner_step(arr, n, ctypes.byref(hp), ctypes.c_void_p(workspace.data_ptr()),
                                   workspace.numel(), ctypes.c_void_p(_stream_handle(stream))),
            "shampoo_owner_step")
@@ -540,7 +555,6 @@ def soap_owner_step(mats: Sequence[Tuple], *, update_out: Optional[Sequence] = N
     weight's frame and V the second moment in the eigenbasis (float32, zeros
     at the start).
     """
-    torch = _torch()
     lib = load_library()
     hp = soap_hparams(**hp_kwargs)
     ups = list(update_out) if update_out is not None else [None] * len(mats)
@@ -548,8 +562,7 @@ def soap_owner_step(mats: Sequence[Tuple], *, update_out: Optional[Sequence] = N
     arr, n = _so_array(descs)
     need = soap_workspace_bytes(descs, hp)
     if workspace is None:
-        dev = mats[0][0].device if mats else torch.device("cuda")
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        workspace = _workspace_for(need, mats, stream)
     _check(lib.soap_owner_step(arr, n, ctypes.byref(hp), ctypes.c_void_p(workspace.data_ptr()),
                                workspace.numel(), ctypes.c_void_p(_stream_handle(stream))),
            "soap_owner_step")
