@@ -325,7 +325,9 @@ def muon_owner_step(mats: Sequence[Tuple], *, update_out: Optional[Sequence] = N
 
 class MuonOwnerStep:
     """Reusable step over a fixed bucket: descriptors and workspace are prepared
-    once; ``__call__`` launches the step on the current (or given) stream."""
+    once; ``__call__`` launches the step on the current (or given) stream.
+    Every call uses the one workspace: calls on different streams must not
+    overlap in time."""
 
     def __init__(self, mats: Sequence[Tuple], update_out: Optional[Sequence] = None,
                  **hp_kwargs):
@@ -412,7 +414,9 @@ def shampoo_workspace_bytes(descs: Sequence[MoShampooMatrix], hp: MoShampooHPara
 class ShampooOwnerStep:
     """Reusable Shampoo step over a fixed bucket of (W, G, L, R) tensors:
     descriptors and workspace are prepared once; ``__call__`` launches the step
-    (W, L, R updated in place) on the current (or given) stream."""
+    (W, L, R updated in place) on the current (or given) stream.  Every call
+    uses the one workspace: calls on different streams must not overlap in
+    time."""
 
     def __init__(self, mats: Sequence[Tuple], update_out: Optional[Sequence] = None, **hp_kwargs):
         torch = _torch()
@@ -520,7 +524,9 @@ def soap_workspace_bytes(descs: Sequence[MoSoapMatrix], hp: MoSoapHParams) -> in
 class SoapOwnerStep:
     """Reusable SOAP step over a fixed bucket of (W, G, L, R, M, V) tensors:
     descriptors and workspace are prepared once; ``__call__(step)`` launches
-    one step (W, L, R, M, V updated in place) on the current (or given) stream."""
+    one step (W, L, R, M, V updated in place) on the current (or given)
+    stream.  Every call uses the one workspace: calls on different streams
+    must not overlap in time."""
 
     def __init__(self, mats: Sequence[Tuple], update_out: Optional[Sequence] = None, **hp_kwargs):
         torch = _torch()
