@@ -450,8 +450,8 @@ def soap_main(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: the owner step issues no collectives and this "
-              f"build measures one owner's share (--gpus {args.gpus} requested)", file=sys.stderr)
+        print(f"bench.py runs on one GPU only: the owner step issues no collectives, and the "
+              f"benchmark measures one owner's share (--gpus {args.gpus} requested)", file=sys.stderr)
         sys.exit(2)
     import torch
     import matrix_optimizers_amd as mo
