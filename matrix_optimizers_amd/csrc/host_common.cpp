@@ -3,11 +3,14 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <vector>
 
 #include "../../include/mo.h"
 #include "host_common.h"
+#include "timing_ring.h"
 
 namespace mo_host {
 
@@ -79,32 +82,65 @@ hipError_t upload(const void* src, size_t bytes, void* dst, hipStream_t s) {
 }
 
 // ---- optional per-launch timing --------------------------------------------------
-struct Timed { int phase; hipEvent_t a, b; };
+// The pending event pairs of the calling thread, bounded (timing_ring.h).
+struct HipEventOps {
+    using Event = hipEvent_t;
+    int create(Event* ev) { return int(hipEventCreate(ev)); }
+    void destroy(Event ev) { (void)hipEventDestroy(ev); }
+    int elapsed_ms(Event a, Event b, float* ms) {
+        hipError_t e = hipEventSynchronize(b);
+        if (e == hipSuccess) e = hipEventElapsedTime(ms, a, b);
+        return int(e);
+    }
+};
+using Ring = TimingRing<HipEventOps, MO_PHASE_COUNT>;
+
+namespace {
 thread_local bool g_prof_on = false;
-thread_local std::vector<Timed> g_prof;
+// Allocated on first use and never freed: destroying events from a thread-exit
+// destructor could run after the HIP runtime has shut down.
+thread_local Ring* g_ring = nullptr;
+
+Ring& ring() {
+    if (!g_ring) g_ring = new Ring(HipEventOps(), kTimingCap);
+    return *g_ring;
+}
+}  // namespace
 
 bool profiling_on() { return g_prof_on; }
-void profile_push(int phase, hipEvent_t a, hipEvent_t b) { g_prof.push_back(Timed{phase, a, b}); }
-
-// free timing events of the calling thread, all created on g_pool_dev
-thread_local std::vector<hipEvent_t> g_pool;
-thread_local int g_pool_dev = -1;
 
 hipError_t profile_event(hipEvent_t* ev) {
     int dev = 0;
     hipError_t e;
     if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
-    if (dev != g_pool_dev) {
-        for (hipEvent_t x : g_pool) (void)hipEventDestroy(x);
-        g_pool.clear();
-        g_pool_dev = dev;
+    Ring& r = ring();
+    if (dev != r.device()) {
+        // pairs recorded on the previous device go into the sums first
+        r.flush_pending();
+        r.reset_device(dev);
     }
-    if (!g_pool.empty()) {
-        *ev = g_pool.back();
-        g_pool.pop_back();
-        return hipSuccess;
-    }
-    return hipEventCreate(ev);
+    return hipError_t(r.take(ev));
+}
+
+void profile_giveback(hipEvent_t ev) { ring().give_back(ev); }
+
+void profile_push(int phase, hipEvent_t a, hipEvent_t b) { ring().push(phase, a, b); }
+
+bool debug_sync_on() {
+    static const bool on = [] {
+        const char* v = std::getenv("MO_DEBUG_SYNC");
+        return v && v[0] && std::strcmp(v, "0") != 0;
+    }();
+    return on;
+}
+
+hipError_t debug_sync_check(int phase, hipStream_t s, hipError_t launch_status) {
+    hipError_t e = launch_status;
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e != hipSuccess)
+        std::fprintf(stderr, "libmo: phase %d failed: %s\n", phase, hipGetErrorString(e));
+    return e;
 }
 
 }  // namespace mo_host
@@ -120,27 +156,7 @@ mo_status mo_profile_enable(int32_t enable) {
 
 mo_status mo_profile_read(double* ms, int64_t* launches) {
     if (!ms || !launches) return MO_ERR_INVALID_ARG;
-    mo_status st = MO_OK;
-    for (Timed& t : g_prof) {
-        float f = 0.f;
-        if (hipEventSynchronize(t.b) != hipSuccess || hipEventElapsedTime(&f, t.a, t.b) != hipSuccess)
-            st = MO_ERR_HIP;
-        else if (t.phase >= 0 && t.phase < MO_PHASE_COUNT) {
-            ms[t.phase] += double(f);
-            launches[t.phase] += 1;
-        }
-        // back to the pool (events of another device than the pool's are destroyed)
-        int dev = -1;
-        if (hipGetDevice(&dev) == hipSuccess && dev == g_pool_dev) {
-            g_pool.push_back(t.a);
-            g_pool.push_back(t.b);
-        } else {
-            (void)hipEventDestroy(t.a);
-            (void)hipEventDestroy(t.b);
-        }
-    }
-    g_prof.clear();
-    return st;
+    return ring().read(ms, launches) == 0 ? MO_OK : MO_ERR_HIP;
 }
 
 }  // extern "C"
