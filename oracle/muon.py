@@ -51,7 +51,7 @@ def frobenius_norm(X: np.ndarray) -> float:
 
 
 def newton_schulz(X: np.ndarray, a: float, b: float, c: float, steps: int,
-                  eps: float) -> np.ndarray:
+                  eps: float, on_step=None) -> np.ndarray:
     """Frobenius normalisation, then `steps` quintic Newton-Schulz iterations.
 
     [P §2]: the orthogonalisation's steps are built from products X X^T, which
@@ -63,15 +63,19 @@ def newton_schulz(X: np.ndarray, a: float, b: float, c: float, steps: int,
     Pins: SVD brute force (U p^K(S/||X||) V^T), rank-1 and scaled-identity
     closed forms, the cubic (1.5, -0.5) variant converging to the polar factor,
     orthogonal / scale / transpose equivariance.
+    on_step: optional callable(k) run after iteration k (progress reporting
+    for large inputs; it does not touch the arithmetic).
     """
     X = np.array(X, dtype=np.float64, copy=True)
     if X.size == 0:
         return X
     X = X / max(frobenius_norm(X), eps)
-    for _ in range(int(steps)):
+    for k in range(int(steps)):
         A = X @ X.T
         B = b * A + c * (A @ A)
         X = a * X + B @ X
+        if on_step is not None:
+            on_step(k + 1)
     return X
 
 
@@ -87,16 +91,16 @@ def lr_multiplier(rows: int, cols: int, lr_adjust: str) -> float:
     raise ValueError(f"unknown lr_adjust {lr_adjust!r}")
 
 
-def orthogonalize(U: np.ndarray, hp) -> np.ndarray:
+def orthogonalize(U: np.ndarray, hp, on_step=None) -> np.ndarray:
     """Newton-Schulz in the short-side frame, returned in U's own frame."""
     rows, cols = U.shape
     transposed = rows > cols
     X = U.T if transposed else U
-    O = newton_schulz(X, hp.ns_a, hp.ns_b, hp.ns_c, hp.ns_steps, hp.eps)
+    O = newton_schulz(X, hp.ns_a, hp.ns_b, hp.ns_c, hp.ns_steps, hp.eps, on_step)
     return O.T if transposed else O
 
 
-def muon_step(W: np.ndarray, G: np.ndarray, M: np.ndarray, hp):
+def muon_step(W: np.ndarray, G: np.ndarray, M: np.ndarray, hp, on_step=None):
     """One owner-side Muon step on one whole matrix.
 
     [P §3]: the owner holds the full reduced gradient, applies the Newton-Schulz
@@ -106,13 +110,14 @@ def muon_step(W: np.ndarray, G: np.ndarray, M: np.ndarray, hp):
     Returns (W', M', delta) with delta = lr_eff * O, so W' = (1-lr*wd)*W - delta.
     Pins: zero-gradient closed form W' = (1-lr*wd) W; torch.optim.Muon witness
     (bf16 Newton-Schulz, so only to 3e-2); the pins of newton_schulz.
+    on_step: passed to newton_schulz (progress only).
     """
     W = np.asarray(W, np.float64)
     rows, cols = W.shape
     if rows == 0 or cols == 0:
         return W.copy(), np.asarray(M, np.float64).copy(), np.zeros_like(W)
     M_new, U = momentum(G, M, hp.momentum, hp.nesterov)
-    O = orthogonalize(U, hp)
+    O = orthogonalize(U, hp, on_step)
     lr_eff = hp.lr * lr_multiplier(rows, cols, hp.lr_adjust)
     delta = lr_eff * O
     W_new = (1.0 - hp.lr * hp.weight_decay) * W - delta

@@ -119,12 +119,13 @@ def run_gpu(cases: Sequence[Case], hp: wlmod.MuonHP, device, with_update: bool =
             for (W, G, M), U in zip(mats, ups)]
 
 
-def check_case(c: Case, got, hp: wlmod.MuonHP, tol: Optional[float] = None) -> dict:
-    """Compare one GPU result with the oracle; returns the measured errors."""
+def check_case(c: Case, got, hp: wlmod.MuonHP, tol: Optional[float] = None, on_step=None) -> dict:
+    """Compare one GPU result with the oracle; returns the measured errors.
+    on_step: progress callback of the oracle's Newton-Schulz loop."""
     W1, M1, D1 = got
     hpo = hp_f32(hp)
     Wo, Mo, Do = omuon.muon_step(c.W.astype(np.float64), c.G.astype(np.float64),
-                                 c.M.astype(np.float64), hpo)
+                                 c.M.astype(np.float64), hpo, on_step=on_step)
     tol = TOL[hp.ns_dtype] if tol is None else tol
     out = {}
     if c.W.size == 0:

@@ -1,16 +1,22 @@
 """Full-size workloads, in the launch configuration bench.py times (one call over
-the whole bucket), checked against the fp64 oracle on sampled matrices and, for
-matrices too large for the oracle, by properties that hold at any size.
+the whole bucket), checked against the fp64 oracle matrix by matrix.
 
 Sampled parity: every matrix of a bucket is an independent output, so the
-oracle recomputes a sample of whole matrices from the same stored inputs.
-Properties (large matrices): momentum is elementwise, so sampled rows of M'
-are compared with the oracle's momentum; the orthogonalised update O of a
+oracle recomputes a sample of whole matrices from the same stored inputs.  The
+largest matrices (28672 x 8192 and the 128256 x 4096 output head of the large
+workload, the 14336-sided MLP matrices of the Llama-shaped share) are compared
+whole, element by element, at the same tolerances as the small cases; the
+oracle takes one to two minutes per matrix on the host and prints a line per
+Newton-Schulz iteration.
+
+Properties, kept as extra checks: momentum is elementwise, so sampled rows of
+M' are compared with the oracle's momentum; the orthogonalised update O of a
 Gaussian gradient has every singular value in the band the quintic maps
 [1e-3, 1] into after five steps ([0.4727, 1.2024]); O U^T is symmetric
 positive semidefinite (O = U_s p(S) V^T and U = U_s S V^T); a transposed twin
 of a matrix gets the transposed update; scaling G and M by 4 changes nothing.
 """
+import time
 import dataclasses
 
 import numpy as np
@@ -52,6 +58,24 @@ def sampled_parity(wl, device, sample):
         s = wl.matrices[k]
         print(f"{wl.key} #{k} {s.rows}x{s.cols}", check_case(c, got, wl.hp), flush=True)
     return before, after, ups
+
+
+def oracle_whole(wl, before, after, ups, k, capsys):
+    """The fp64 oracle on matrix k of the bucket, compared element by element;
+    progress goes straight to the terminal (one line per oracle iteration)."""
+    s = wl.matrices[k]
+    t0 = time.perf_counter()
+
+    def say(msg):
+        with capsys.disabled():
+            print(f"[{wl.key} #{k} {s.rows}x{s.cols}] {msg} ({time.perf_counter() - t0:.0f} s)", flush=True)
+
+    say("oracle start")
+    c = host_case(before, k, wl)
+    got = (to_host(after[k][0]), to_host(after[k][2]), to_host(ups[k]))
+    out = check_case(c, got, wl.hp, on_step=lambda it: say(f"oracle NS step {it}/{wl.hp.ns_steps}"))
+    say(f"errors {out}")
+    return out
 
 
 def test_batched_1024_sampled(gpu):
@@ -112,6 +136,29 @@ def test_llama8b_4layers_sampled_and_properties(gpu):
         assert e <= 1e-6
         assert 0.40 <= gmin and gmax <= 1.30
         assert asym <= 3e-2 and evr > -1e-2 and 0.2 <= frob <= 1.5
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("k", [4, 6])
+def test_llama8b_long_sides_oracle(gpu, capsys, k):
+    """w_gate (14336 x 4096, tall) and w_down (4096 x 14336, wide) of layer 0,
+    from one call over the whole 28-matrix bucket, against the fp64 oracle."""
+    wl = wlmod.get("llama8b_4layers")
+    before, after, ups = run_bucket(wl, gpu)
+    oracle_whole(wl, before, after, ups, k, capsys)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("k", [2, 0])
+def test_large_single_oracle(gpu, capsys, k):
+    """The 128256 x 4096 output head (k = 2) and the 28672 x 8192 MLP matrix
+    (k = 0), from one call over the whole large bucket, against the fp64
+    oracle: update within 3e-2, momentum within 1e-6, weights within one bf16
+    ulp of decay W - delta.  The 8192 x 28672 matrix is the 28672 x 8192
+    case's transpose in frame (checked by the transposed-twin test below)."""
+    wl = wlmod.get("large_single")
+    before, after, ups = run_bucket(wl, gpu)
+    oracle_whole(wl, before, after, ups, k, capsys)
 
 
 def test_large_single_properties(gpu):

@@ -246,3 +246,56 @@ def test_half_width_tiles_parity(gpu, ns):
     got = run_gpu(cases, hp, gpu)
     for k in (0, 5):
         print(ns, k, check_case(cases[k], got[k], hp))
+
+
+@pytest.mark.parametrize("ns", ["bf16", "f32"])
+def test_two_consecutive_steps_carry_state(gpu, ns):
+    """Two consecutive owner steps on one bucket, carrying W and M between them
+    ([P §3], [P §4.4]: the owner keeps its Muon state from step to step), against
+    two chained oracle steps.  Step 2's update and momentum are compared with
+    the oracle's own second step; the written weights with decay W1 - delta2 of
+    the GPU's own W1.  Then the second step is run again from a saved copy of
+    the state after step 1, on a fresh workspace: it must give the same bits
+    as the consecutive run (a saved and restored state is the same state)."""
+    import torch
+    import matrix_optimizers_amd as mo
+    from _parity import hp_f32, bf16_ulp
+    from oracle import muon as omuon
+    hp = dataclasses.replace(BF, ns_dtype=ns)
+    wd = "bf16" if ns == "bf16" else "f32"
+    shapes = [(192, 320), (320, 192), (256, 256)]
+    cases = [random_case(r, c, wd, wd, seed=40 + i) for i, (r, c) in enumerate(shapes)]
+    g2s = [random_case(r, c, wd, wd, seed=80 + i).G for i, (r, c) in enumerate(shapes)]
+    mats = [(to_dev(c.W, wd, gpu), to_dev(c.G, wd, gpu), to_dev(c.M, "f32", gpu)) for c in cases]
+    ups = [torch.empty(W.shape, dtype=torch.float32, device=gpu) for (W, _, _) in mats]
+    mo.muon_owner_step(mats, update_out=ups, **hp_kwargs(hp))
+    # step 2: new gradients, the state carried in place
+    mats2 = [(W, to_dev(g2, wd, gpu), M) for (W, _, M), g2 in zip(mats, g2s)]
+    saved = [(W.clone(), M.clone()) for (W, _, M) in mats2]
+    mo.muon_owner_step(mats2, update_out=ups, **hp_kwargs(hp))
+    torch.cuda.synchronize()
+    hpo = hp_f32(hp)
+    tol = 3e-2 if ns == "bf16" else 1e-4
+    for c, g2, (W2, _, M2), U2, (W1s, _) in zip(cases, g2s, mats2, ups, saved):
+        W1o, M1o, _ = omuon.muon_step(c.W, c.G, c.M, hpo)
+        _, M2o, D2o = omuon.muon_step(W1o, g2.astype(np.float64), M1o, hpo)
+        e_d, e_m = rel(to_host(U2), D2o), rel(to_host(M2), M2o)
+        decay = np.float32(1.0 - np.float64(np.float32(hp.lr)) * np.float64(np.float32(hp.weight_decay)))
+        want = (decay * to_host(W1s).astype(np.float32) - to_host(U2).astype(np.float32)).astype(np.float64)
+        got = to_host(W2)
+        if wd == "bf16":
+            w_err = float((np.abs(got - want) / (bf16_ulp(np.maximum(np.abs(got), np.abs(want)))
+                                                 + 4 * 2.0 ** -24 * np.abs(want) + 1e-30)).max())
+            assert w_err <= 1.0, w_err
+        else:
+            w_err = rel(got, want)
+            assert w_err <= 1e-6, w_err
+        print(c.W.shape, ns, f"step-2 delta {e_d:.2e} momentum {e_m:.2e} weights {w_err:.2e}")
+        assert e_d <= tol and e_m <= 1e-6
+    # the second step again, from the saved state, on a fresh workspace
+    mats3 = [(W1s.clone(), G2, M1s.clone()) for (W1s, M1s), (_, G2, _) in zip(saved, mats2)]
+    ups3 = [torch.empty_like(u) for u in ups]
+    mo.muon_owner_step(mats3, update_out=ups3, **hp_kwargs(hp))
+    torch.cuda.synchronize()
+    for (W2, _, M2), (W3, _, M3), u2, u3 in zip(mats2, mats3, ups, ups3):
+        assert torch.equal(W2, W3) and torch.equal(M2, M3) and torch.equal(u2, u3)

@@ -66,3 +66,29 @@ def test_soap_on_side_stream(gpu):
     mats = _inputs(torch, 3, [(96, 160), (64, 64)], lambda r, c, g: [eye(r), eye(c), zeros(r, c), zeros(r, c)])
     _run_both(torch, lambda m, s: mo.soap_owner_step([tuple(x) for x in m], stream=s, step=1, lr=1e-3,
                                                     eps=1e-3), mats)
+
+
+def test_reusable_step_dropped_after_side_stream_call(gpu):
+    """A reusable step (workspace allocated once, on the current stream) called
+    on a side stream and dropped at once, while the current stream allocates
+    and fills memory: the launch stream is recorded on the workspace block, so
+    the caching allocator keeps it until the side stream's work is done, and
+    the results equal the same step run on the current stream."""
+    import torch
+    mats = _inputs(torch, 4, [(512, 768), (768, 256)], lambda r, c, g: [torch.zeros((r, c), device="cuda")])
+    ref = _clone(mats)
+    mo.MuonOwnerStep([tuple(x) for x in ref], lr=0.02)()
+    torch.cuda.synchronize()
+    for as_handle in (False, True):
+        got = _clone(mats)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        step = mo.MuonOwnerStep([tuple(x) for x in got], lr=0.02)
+        step(side.cuda_stream if as_handle else side)
+        del step
+        churn = [torch.full((1 << 22,), float(k), device="cuda") for k in range(16)]
+        del churn
+        torch.cuda.synchronize()
+        for a, b in zip(got, ref):
+            for x, y in zip(a, b):
+                assert torch.equal(x, y)
