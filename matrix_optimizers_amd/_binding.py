@@ -93,7 +93,7 @@ _lib = None
 EXPORTS = ["muon_workspace_bytes", "muon_build_worklist", "muon_owner_step", "adamw_tail_step",
            "mo_status_string", "mo_profile_enable", "mo_profile_read", "mo_device_copy",
            "mo_plan_owners", "mo_plan_score", "mo_plan_layout", "shampoo_workspace_bytes",
-           "shampoo_owner_step", "soap_workspace_bytes", "soap_owner_step"]
+           "shampoo_owner_step", "soap_workspace_bytes", "soap_owner_step", "soap_converged"]
 
 ROLE_MATRIX, ROLE_TAIL = 0, 1
 PLAN_POLICIES = {"role_greedy": 0, "scope_greedy": 1, "cost_aware": 2}
@@ -144,10 +144,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                          P(ctypes.c_size_t)]
     lib.soap_owner_step.argtypes = [P(MoSoapMatrix), ctypes.c_int32, P(MoSoapHParams),
                                     ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.soap_converged.argtypes = [P(MoSoapMatrix), ctypes.c_int32, P(MoSoapHParams), ctypes.c_void_p,
+                                   ctypes.c_size_t, P(ctypes.c_int32), ctypes.c_void_p]
     for name in ("muon_workspace_bytes", "muon_build_worklist", "muon_owner_step",
                  "adamw_tail_step", "mo_profile_enable", "mo_profile_read", "mo_device_copy",
                  "mo_plan_owners", "mo_plan_score", "mo_plan_layout", "shampoo_workspace_bytes",
-                 "shampoo_owner_step", "soap_workspace_bytes", "soap_owner_step"):
+                 "shampoo_owner_step", "soap_workspace_bytes", "soap_owner_step", "soap_converged"):
         getattr(lib, name).restype = ctypes.c_int32
     _lib = lib
     return lib
@@ -297,6 +299,21 @@ def _workspace_for(nbytes: int, mats, stream):
         return torch.empty(nbytes, dtype=torch.uint8, device=dev)
 
 
+def _record_launch_stream(workspace, alloc_stream: int, stream) -> None:
+    """A reusable step's workspace was allocated on ``alloc_stream``; when a
+    call launches on another stream, that stream is recorded on the block, so
+    the caching allocator does not hand it out again (after the step object is
+    dropped) before the work queued there has finished."""
+    torch = _torch()
+    handle = _stream_handle(stream)
+    if handle == alloc_stream:
+        return
+    if isinstance(stream, torch.cuda.Stream):
+        workspace.record_stream(stream)
+    else:
+        workspace.record_stream(torch.cuda.ExternalStream(handle, device=workspace.device))
+
+
 def muon_owner_step(mats: Sequence[Tuple], *, update_out: Optional[Sequence] = None,
                     workspace=None, stream=None, **hp_kwargs) -> None:
     """One Muon step over a bucket of (W, G, M) tensors, in place.
@@ -340,9 +357,11 @@ class MuonOwnerStep:
         self.bytes = workspace_bytes(self.descs, self.hp)
         dev = mats[0][0].device if mats else torch.device("cuda")
         self.workspace = torch.empty(self.bytes, dtype=torch.uint8, device=dev)
+        self._alloc_stream = int(torch.cuda.current_stream(dev).cuda_stream)
         self._keep = (mats, update_out)
 
     def __call__(self, stream=None) -> None:
+        _record_launch_stream(self.workspace, self._alloc_stream, stream)
         _check(self.lib.muon_owner_step(self.arr, self.n, ctypes.byref(self.hp),
                                         ctypes.c_void_p(self.workspace.data_ptr()),
                                         self.workspace.numel(),
@@ -428,9 +447,11 @@ class ShampooOwnerStep:
         self.bytes = shampoo_workspace_bytes(self.descs, self.hp)
         dev = mats[0][0].device if mats else torch.device("cuda")
         self.workspace = torch.empty(self.bytes, dtype=torch.uint8, device=dev)
+        self._alloc_stream = int(torch.cuda.current_stream(dev).cuda_stream)
         self._keep = (mats, update_out)
 
     def __call__(self, stream=None) -> None:
+        _record_launch_stream(self.workspace, self._alloc_stream, stream)
         _check(self.lib.shampoo_owner_step(self.arr, self.n, ctypes.byref(self.hp),
                                            ctypes.c_void_p(self.workspace.data_ptr()),
                                            self.workspace.numel(),
@@ -539,16 +560,43 @@ class SoapOwnerStep:
         self.bytes = soap_workspace_bytes(self.descs, self.hp)
         dev = mats[0][0].device if mats else torch.device("cuda")
         self.workspace = torch.empty(self.bytes, dtype=torch.uint8, device=dev)
+        self._alloc_stream = int(torch.cuda.current_stream(dev).cuda_stream)
         self._keep = (mats, update_out)
 
     def __call__(self, step: Optional[int] = None, stream=None) -> None:
         if step is not None:
             self.hp.step = int(step)
+        _record_launch_stream(self.workspace, self._alloc_stream, stream)
         _check(self.lib.soap_owner_step(self.arr, self.n, ctypes.byref(self.hp),
                                         ctypes.c_void_p(self.workspace.data_ptr()),
                                         self.workspace.numel(),
                                         ctypes.c_void_p(_stream_handle(stream))),
                "soap_owner_step")
+
+    def rotating_pairs(self, stream=None) -> List[Tuple[int, int]]:
+        """(L', R') per matrix: pair slots that still rotated in the last
+        call's final Jacobi sweep (0 = converged); waits for that call."""
+        out = (ctypes.c_int32 * max(2 * self.n, 1))()
+        _check(self.lib.soap_converged(self.arr, self.n, ctypes.byref(self.hp),
+                                       ctypes.c_void_p(self.workspace.data_ptr()), self.workspace.numel(),
+                                       out, ctypes.c_void_p(_stream_handle(stream))),
+               "soap_converged")
+        return [(int(out[2 * i]), int(out[2 * i + 1])) for i in range(self.n)]
+
+
+def soap_converged(mats: Sequence[Tuple], workspace, *, stream=None, **hp_kwargs) -> List[Tuple[int, int]]:
+    """After soap_owner_step(mats, workspace=workspace, **hp_kwargs): per matrix,
+    (L', R') pair slots that still rotated in the final Jacobi sweep (0 =
+    converged).  Waits for the step on ``stream``."""
+    lib = load_library()
+    hp = soap_hparams(**hp_kwargs)
+    descs = [soap_tensor_descriptor(*mat) for mat in mats]
+    arr, n = _so_array(descs)
+    out = (ctypes.c_int32 * max(2 * n, 1))()
+    _check(lib.soap_converged(arr, n, ctypes.byref(hp), ctypes.c_void_p(workspace.data_ptr()),
+                              workspace.numel(), out, ctypes.c_void_p(_stream_handle(stream))),
+           "soap_converged")
+    return [(int(out[2 * i]), int(out[2 * i + 1])) for i in range(n)]
 
 
 def soap_owner_step(mats: Sequence[Tuple], *, update_out: Optional[Sequence] = None,

@@ -10,7 +10,7 @@
 #include <stdint.h>
 
 #define MO_SO_MAGIC   0x4F534F4Du  // "MOSO"
-#define MO_SO_VERSION 1u
+#define MO_SO_VERSION 2u
 
 #define MO_SO_PAD    64   // padding of every side (the eigensolver's pair of 32-wide blocks)
 #define MO_SO_BLK    32   // Jacobi block width
@@ -59,9 +59,12 @@ struct mo_so_mat {
 // eigenvectors sorted by ascending eigenvalue (fp32), perm the sort, flag
 // one word per pair: whether its rotation of the current round is not the
 // identity; norm the per-row sums of squares of A and, after them, the
-// rotation threshold 2^-48 ||A||_F (fp64).
+// rotation threshold 2^-48 ||A||_F (fp64); last one word per pair slot: set
+// when that slot's pair problem rotated in some round of the final sweep
+// (all zero: the final sweep rotated nothing, so A was diagonal to the
+// threshold, the convergence test of cyclic Jacobi).
 struct mo_so_eig {
-    uint64_t off_A, off_E, off_D, off_E32, off_perm, off_flag, off_norm;
+    uint64_t off_A, off_E, off_D, off_E32, off_perm, off_flag, off_norm, off_last;
     uint64_t ext;                         // caller statistics (L or R), m x m fp32, row stride ld_ext
     int64_t  ld_ext;
     uint32_t m, m_pad, P, mat;
@@ -72,4 +75,4 @@ struct mo_so_eig {
 
 static_assert(sizeof(mo_so_header) == 80, "header layout");
 static_assert(sizeof(mo_so_mat) == 176, "matrix record layout");
-static_assert(sizeof(mo_so_eig) == 104, "eig record layout");
+static_assert(sizeof(mo_so_eig) == 112, "eig record layout");

@@ -193,6 +193,7 @@ void build_plan(const mo_soap_matrix* mats, int32_t n, const mo_soap_hparams* hp
         e.off_E32 = take(mm * 4);
         e.off_perm = take(uint64_t(e.m_pad) * 4);
         e.off_flag = take(uint64_t(e.P) * 4);
+        e.off_last = take(uint64_t(e.P) * 4);
         e.off_norm = take(uint64_t(e.m_pad + 1) * 8);
     }
     h.ws_bytes = off;
@@ -266,6 +267,44 @@ mo_status soap_owner_step(const mo_soap_matrix* mats, int32_t n, const mo_soap_h
         for (int kind : kProducts)
             if (!ok(MO_PHASE_SO_PRODUCTS, [&] { return mo_launch_so_gemm(plan.mats[i], ws, i, kind, s); }))
                 return MO_ERR_HIP;
+    return MO_OK;
+}
+
+mo_status soap_converged(const mo_soap_matrix* mats, int32_t n, const mo_soap_hparams* hp,
+                         const void* workspace, size_t workspace_bytes, int32_t* rotating, void* stream) {
+    mo_status st = validate_hp(hp);
+    if (st != MO_OK) return st;
+    if ((st = validate(mats, n, nullptr)) != MO_OK) return st;
+    if (n > 0 && !rotating) return MO_ERR_INVALID_ARG;
+    for (int32_t i = 0; i < 2 * n; ++i) rotating[i] = 0;
+    SoPlan plan;
+    build_plan(mats, n, hp, &plan);
+    const mo_so_header& h = plan.header;
+    if (h.n_mats == 0) return MO_OK;
+    const size_t need = size_t(h.ws_bytes) + MO_WS_ALIGN;
+    if (!workspace || workspace_bytes < need) return MO_ERR_WORKSPACE_TOO_SMALL;
+    const uint8_t* ws = reinterpret_cast<const uint8_t*>(
+        align_up(reinterpret_cast<uintptr_t>(workspace), MO_WS_ALIGN));
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    // the flag words of every decomposition, copied after the step's work on s
+    std::vector<std::vector<uint32_t>> words(h.n_eigs);
+    for (uint32_t e = 0; e < h.n_eigs; ++e) {
+        words[e].assign(plan.eigs[e].P, 0u);
+        if (hipMemcpyAsync(words[e].data(), ws + plan.eigs[e].off_last, size_t(plan.eigs[e].P) * 4,
+                           hipMemcpyDeviceToHost, s) != hipSuccess)
+            return MO_ERR_HIP;
+    }
+    if (hipStreamSynchronize(s) != hipSuccess) return MO_ERR_HIP;
+    uint32_t live = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        if (mats[i].rows == 0 || mats[i].cols == 0) continue;
+        const mo_so_mat& mt = plan.mats[live++];
+        for (int side = 0; side < 2; ++side) {
+            int32_t c = 0;
+            for (uint32_t w : words[side ? mt.eig_r : mt.eig_l]) c += w ? 1 : 0;
+            rotating[2 * i + side] = c;
+        }
+    }
     return MO_OK;
 }
 

@@ -257,6 +257,7 @@ MO_DEV int64_t pair_index(int p, int q, int l) {
 __global__ __launch_bounds__(SO_THREADS) void so_eig_init_kernel(uint8_t* ws, uint32_t ei) {
     const mo_so_eig& eg = so_eigs(ws)[ei];
     const int64_t idx = int64_t(blockIdx.x) * SO_THREADS + threadIdx.x;
+    if (idx < int64_t(eg.P)) reinterpret_cast<uint32_t*>(ws + eg.off_last)[idx] = 0u;   // final-sweep flags
     if (idx >= int64_t(eg.m_pad) * eg.m_pad) return;
     const int64_t i = idx / eg.m_pad, j = idx % eg.m_pad;
     reinterpret_cast<double*>(ws + eg.off_E)[idx] = (i == j && i < eg.m) ? 1.0 : 0.0;
@@ -440,6 +441,9 @@ __global__ __launch_bounds__(SV_THREADS) void so_jac_solve_kernel(uint8_t* ws, u
         *reinterpret_cast<f64x2*>(Dout + r * PW + c) = f64x2{D[r][c], D[r][c + 1]};
     }
     if (t == 0) reinterpret_cast<uint32_t*>(ws + eg.off_flag)[j] = any ? 1u : 0u;
+    // rounds of the final sweep: mark this pair slot if its problem rotated
+    if (t == 0 && any && k + uint32_t(nb - 1) >= eg.rounds)
+        reinterpret_cast<uint32_t*>(ws + eg.off_last)[j] = 1u;
 }
 
 // Loads the 64 x 64 pair rotation D_I of round k into LDS (16-byte accesses).

@@ -70,9 +70,11 @@ def test_workspace_checks_and_size():
     hp = mo.soap_hparams()
     need = mo.soap_workspace_bytes(d, hp)
     # per matrix four fp32 r_pad x c_pad buffers; per side two fp64 and one fp32
-    # m_pad^2 buffer, m_pad / 64 fp64 pair rotations of 64 x 64 and the permutation
+    # m_pad^2 buffer, m_pad / 64 fp64 pair rotations of 64 x 64, the permutation
+    # and the final-sweep rotation flags (one word per pair slot, 256-aligned)
     mats = 4 * 128 * 128 * 4
-    side = lambda m: 2 * m * m * 8 + (m // 64) * 64 * 64 * 8 + m * m * 4 + max(m * 4, 256)
+    side = lambda m: (2 * m * m * 8 + (m // 64) * 64 * 64 * 8 + m * m * 4 + max(m * 4, 256)
+                      + max((m // 64) * 4, 256))
     assert need >= mats + 2 * side(128)
     assert need <= mats + 2 * side(128) + 4096
     assert step(d, ws_bytes=need - 1) == WS_SMALL
@@ -95,3 +97,25 @@ def test_rotation_item_limit_fails_fast():
     assert mo.soap_workspace_bytes(many[:100], mo.soap_hparams()) > 0
     with pytest.raises(mo.MoError):
         mo.soap_workspace_bytes(many, mo.soap_hparams())
+
+
+def converged(descs, hp=None, ws=BASE + 300 * GiB, ws_bytes=1 << 40, out=True):
+    lib = mo.load_library()
+    arr, cnt = B._so_array(descs)
+    hp = hp or mo.soap_hparams()
+    buf = (ctypes.c_int32 * max(2 * cnt, 1))(*([-7] * max(2 * cnt, 1)))
+    st = lib.soap_converged(arr, cnt, ctypes.byref(hp), ctypes.c_void_p(ws), ws_bytes,
+                            buf if out else None, None)
+    return st, list(buf)
+
+
+def test_converged_argument_checks_without_hip():
+    """The convergence query checks its arguments before touching the device:
+    bad hyperparameters, a missing output array, a small workspace; a bucket
+    of empty descriptors reports zeros."""
+    assert converged([desc()], hp=mo.soap_hparams(sweeps=0))[0] == INVALID
+    assert converged([desc()], out=False)[0] == INVALID
+    assert converged([desc()], ws_bytes=1024)[0] == WS_SMALL
+    assert converged([desc()], ws=0)[0] == WS_SMALL
+    st, buf = converged([desc(0, 10), desc(10, 0, k=1)], ws=0, ws_bytes=0)
+    assert st == OK and buf == [0, 0, 0, 0]

@@ -359,3 +359,31 @@ def test_long_side_first_step_closed_form(gpu, rows, bar):
     print(f"{r} x {c} first step: update {err:.2e} against the closed form", flush=True)
     assert np.all(np.isfinite(out["U"]))
     assert err <= bar
+
+
+def test_convergence_report(gpu):
+    """soap_converged after a step: a single sweep leaves a warm 256 x 384 pair
+    of statistics unconverged (pair problems still rotate in the final sweep),
+    the default sweep count converges it (a final sweep without rotations),
+    and the converged step passes the parity check."""
+    import torch
+    import matrix_optimizers_amd as mo
+    st = warm_state(91, 256, 384)
+    dev = torch.device("cuda:0")
+    res = {}
+    for sweeps in (1, 14):
+        t = lambda x: torch.tensor(np.asarray(x, F32), device=dev).contiguous()
+        mats = [(t(st["W"]), t(st["G"]), t(st["L"]), t(st["R"]), t(st["M"]), t(st["V"]))]
+        ups = [torch.empty(st["W"].shape, dtype=torch.float32, device=dev)]
+        step = mo.SoapOwnerStep(mats, update_out=ups, sweeps=sweeps, **HP)
+        step(10)
+        res[sweeps] = step.rotating_pairs()
+        torch.cuda.synchronize()
+        if sweeps == 14:
+            to = lambda x: x.float().cpu().numpy().astype(np.float64)
+            m = mats[0]
+            check(st, dict(W=to(m[0]), L=to(m[2]), R=to(m[3]), M=to(m[4]), V=to(m[5]), U=to(ups[0])), 10, HP,
+                  "converged 256x384")
+    print("rotating pair slots in the final sweep:", res, flush=True)
+    assert min(res[1][0]) > 0
+    assert res[14] == [(0, 0)]
