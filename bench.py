@@ -34,7 +34,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="decoder_layer_h2048")
+    ap.add_argument("--workload", default="large_single",
+                    help="Muon workload (default large_single: 28672x8192, 8192x28672 and a "
+                         "128256x4096 head, the largest configuration that fits one GPU)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-phase-timing", action="store_true",
                     help="skip the second, event-instrumented pass (no phases, no roofline object)")
@@ -126,15 +128,57 @@ def timed_steps(fn, steps):
     return (time.perf_counter() - t0) * 1e3 / steps
 
 
-def event_timed_steps(fn, steps):
+def event_timed_steps(fn, steps, per_step=None):
     """The same steps with every library launch bracketed by HIP events on its
-    stream; returns ({phase: (total ms, launches)}, wall ms per step)."""
+    stream; returns ({phase: (total ms, launches)}, wall ms per step).  With a
+    list `per_step`, it also receives each step's duration in ms from events
+    recorded on the current stream (the launch stream) between steps."""
+    import torch
     import matrix_optimizers_amd as mo
     mo.profile_read()               # drop anything recorded before
     mo.profile_enable(True)
-    ms = timed_steps(fn, steps)
+    if per_step is None:
+        ms = timed_steps(fn, steps)
+    else:
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        evs[0].record()
+        for k in range(steps):
+            fn()
+            evs[k + 1].record()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        per_step.extend(evs[k].elapsed_time(evs[k + 1]) for k in range(steps))
     mo.profile_enable(False)
     return mo.profile_read(), ms
+
+
+def machine_info():
+    """ROCm / HIP version, gfx target and the shader clock that rocm-smi reports
+    right after the timed region (best effort: None where a tool is missing)."""
+    import subprocess
+    import torch
+    info = {"hip": getattr(torch.version, "hip", None), "torch": torch.__version__}
+    try:
+        info["gfx"] = torch.cuda.get_device_properties(0).gcnArchName
+    except Exception:
+        info["gfx"] = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            info["rocm"] = f.read().strip()
+    except OSError:
+        info["rocm"] = None
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                             timeout=20).stdout
+        d = json.loads(out)
+        card = next(iter(d.values()))
+        info["sclk_after_run"] = card.get("sclk clock speed:")
+        info["mclk_after_run"] = card.get("mclk clock speed:")
+    except Exception:
+        info["sclk_after_run"] = None
+    return info
 
 
 def algorithmic_flops(spec_rows, spec_cols, steps):
@@ -143,6 +187,9 @@ def algorithmic_flops(spec_rows, spec_cols, steps):
     m, n = min(spec_rows, spec_cols), max(spec_rows, spec_cols)
     return {"gram": float(m) * m * n, "poly": float(m) ** 3, "update": 2.0 * m * m * n}
 
+
+# copies of X0 the momentum kernel writes beyond the one the step needs (its transpose)
+MOMENTUM_EXTRA_COPIES = 1
 
 CPU_BUDGET_S = 20.0          # oracle work per bench run
 ORACLE_TFLOPS_GUESS = 0.5    # fp64 numpy on the measuring machine's host, for sizing the sample only
@@ -194,12 +241,18 @@ def cpu_baseline(wl, args):
         oadamw.adamw_step(t.p, t.g, t.m, t.v, a.step, a.lr, a.beta1, a.beta2, a.eps, a.weight_decay)
     dt = time.perf_counter() - t0
     desc = ", ".join(f"{wl.matrices[i].rows}x{wl.matrices[i].cols}" for i in sample)
-    what = "one matrix of each distinct shape" if len(sample) == len(shapes) else "a bounded sample of matrices"
-    steps = "" if hp.ns_steps == wl.hp.ns_steps else f" with {hp.ns_steps} of {wl.hp.ns_steps} NS steps"
+    if len(sample) == len(shapes) and hp.ns_steps == wl.hp.ns_steps:
+        what = f"one whole matrix of each distinct shape ({desc}), full step"
+    else:
+        what = (f"{len(sample)} whole matrix{'es' if len(sample) > 1 else ''} of the bucket ({desc}): "
+                f"momentum, normalisation and {hp.ns_steps} of the {wl.hp.ns_steps} Newton-Schulz steps")
+    total = sum(wlmod.ns_flops_nominal(m.rows, m.cols, wl.hp.ns_steps) for m in wl.matrices)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{what} ({desc}){steps}"
+            "sample": what
                       + (f" + the {wl.tail_numel}-element AdamW tail" if wl.tail_numel else "")
-                      + f", fp64 numpy, {dt:.2f} s"}
+                      + f"; fp64 numpy, {dt:.2f} s; rate = nominal NS flops of what ran / time",
+            "projected_full_step_s": round(dt * total / flops, 1),
+            "projection_note": "the whole bucket at the sample's rate (a projection, not a measurement)"}
 
 
 SHAMPOO_METRIC = "Shampoo owner-step ms + fp32 TFLOP/s (algorithmic, % fp32 MFMA peak), 1 MI355X"
@@ -500,8 +553,9 @@ def main():
     ms = timed_steps(one_step, args.steps)
     print(f"[bench] {ms:.3f} ms/step", file=sys.stderr, flush=True)
     prof = None
+    per_step = []
     if not args.no_phase_timing:
-        prof, ms_events = event_timed_steps(one_step, args.steps)
+        prof, ms_events = event_timed_steps(one_step, args.steps, per_step)
         print(f"[bench] {ms_events:.3f} ms/step with per-launch events", file=sys.stderr, flush=True)
 
     nominal = sum(wlmod.ns_flops_nominal(s.rows, s.cols, hp.ns_steps) for s in wl.matrices)
@@ -524,6 +578,12 @@ def main():
     }
     if prof is not None:
         out["ms_per_step_with_launch_events"] = round(ms_events, 4)
+        srt = sorted(per_step)
+        out["step_ms_events"] = {"median": round(srt[len(srt) // 2] if len(srt) % 2 else
+                                                 0.5 * (srt[len(srt) // 2 - 1] + srt[len(srt) // 2]), 4),
+                                 "min": round(srt[0], 4), "max": round(srt[-1], 4),
+                                 "note": "per-step durations from events between steps, in the pass with "
+                                         "per-launch events"}
         per_launch = {}
         flops_launch = {"gram": 0.0, "poly": 0.0, "update": 0.0, "update_last": 0.0}
         for s in wl.matrices:
@@ -554,13 +614,22 @@ def main():
                     "read_bytes": round(tr["read_bytes"]), "write_bytes": round(tr["write_bytes"]),
                     "profile": tr["source"], "profile_avg_ms": round(tr["avg_ns"] / 1e6, 5)}
         if "momentum" in per_launch:
-            # momentum kernel: read G (w) + M (4), write M' (4) + U twice in the NS dtype
+            # momentum kernel, algorithmic bytes: read G (2 or 4) + M (4), write
+            # M' (4) + X0 once in the NS dtype (2 or 4): 12 B/elem for bf16 G and
+            # NS dtype.  The kernel also writes X0's transpose (moved bytes).
             es_g = 2 if wl.g_dtype == "bf16" else 4
             es_x = 2 if hp.ns_dtype == "bf16" else 4
-            nbytes = sum(s.rows * s.cols for s in wl.matrices) * (es_g + 8 + 2 * es_x)
-            gbs = nbytes / (per_launch["momentum"]["avg_ms"] * 1e-3) / 1e9
+            elems = sum(s.rows * s.cols for s in wl.matrices)
+            algo_b = elems * (es_g + 8 + es_x)
+            moved_b = elems * (es_g + 8 + es_x * (1 + MOMENTUM_EXTRA_COPIES))
+            t = per_launch["momentum"]["avg_ms"] * 1e-3
+            gbs = algo_b / t / 1e9
             out["momentum_kernel"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                                      "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}
+                                      "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                      "algorithmic_per_launch": f"{algo_b} B ({es_g + 8 + es_x} B/elem)",
+                                      "moved_GBps": round(moved_b / t / 1e9, 1),
+                                      "moved_per_launch": f"{moved_b} B"}
+    out["machine"] = machine_info()
     if not args.no_cpu_baseline and not args.profile_only:
         print("[bench] cpu_baseline (fp64 oracle on host)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, args)

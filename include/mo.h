@@ -104,7 +104,9 @@ mo_status muon_workspace_bytes(const mo_matrix* mats, int32_t n_mats,
  * If host_buf is NULL, *bytes_inout receives the size; otherwise *bytes_inout
  * must hold at least that size and the list is written to host_buf.  The byte
  * layout (little-endian, natural alignment, version 5):
- *   header   mo_wl_header (128 bytes)
+ *   header   mo_wl_header (128 bytes); its 14th word is the number of
+ *            wavefronts per workgroup of the GEMM kernels the list is built
+ *            for (4, or 8 for kernels without quarter-width tiles)
  *   matrices mo_wl_mat[n_live] (192 bytes each), one per non-empty descriptor,
  *            in descriptor order
  *   items    three dispatch lists of mo_wl_item (16 bytes: record index, tile
@@ -123,7 +125,8 @@ mo_status muon_workspace_bytes(const mo_matrix* mats, int32_t n_mats,
  * Then, where full tiles would leave CUs idle, tiles are split by columns: a
  * queue of n <= 32 tiles (32 CUs per XCD) has every tile split, a longer one
  * the n % 32 tiles of its last round, into S = 4 quarter-width (nb = 1) or
- * S = 2 half-width (nb = 2) tiles, the largest S with S x (tiles split) <= 32;
+ * S = 2 half-width (nb = 2) tiles, the largest S with S x (tiles split) <= 32
+ * (S = 4 only for 4-wavefront kernels);
  * the parts take the tile's place in the queue, in column order.  Entry 8 j + x
  * of a list is the j-th tile of queue x, or a pad entry (record index
  * 0xFFFFFFFF) where queue x is shorter. */
@@ -348,6 +351,22 @@ mo_status soap_workspace_bytes(const mo_soap_matrix* mats, int32_t n_mats,
  * tensor of the bucket or the workspace), MO_ERR_HIP. */
 mo_status soap_owner_step(const mo_soap_matrix* mats, int32_t n_mats, const mo_soap_hparams* hp,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Convergence of the last soap_owner_step's eigensolver.  Call it with the
+ * same bucket, hyperparameters and workspace as that step, on its stream,
+ * before the workspace is reused; it waits for the step.  Cyclic Jacobi has
+ * converged when a whole sweep rotates nothing: every off-diagonal entry is
+ * then at or below 2^-48 ||A||_F.  rotating[2 i] (L' of matrix i) and
+ * rotating[2 i + 1] (R') receive the number of pair slots (at most
+ * m_pad / 64) whose pair problem still rotated during the final sweep: 0
+ * means converged; otherwise the sweep count was too small for this input
+ * and the eigenvectors, hence the update, may be off by more than the fp32
+ * statistics fix.  Empty descriptors get 0.  rotating is host memory of 2 n
+ * int32.  Errors: as soap_workspace_bytes, MO_ERR_INVALID_ARG (rotating NULL
+ * with n > 0), MO_ERR_WORKSPACE_TOO_SMALL, MO_ERR_HIP. */
+mo_status soap_converged(const mo_soap_matrix* mats, int32_t n_mats, const mo_soap_hparams* hp,
+                         const void* workspace, size_t workspace_bytes, int32_t* rotating,
+                         void* stream);
 
 /* ---- owner planner (host only) --------------------------------------------
  * The step upstream of a bucket: which data-parallel rank owns each role

@@ -15,6 +15,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <vector>
@@ -90,6 +91,16 @@ struct Plan {
     mo_wl_header header;
 };
 
+// Wavefronts per GEMM workgroup: 4 (one per SIMD) unless MO_NS_WAVES=8 selects
+// the eight-wavefront kernels (read once per process).
+uint32_t gemm_waves() {
+    static const uint32_t w = [] {
+        const char* v = std::getenv("MO_NS_WAVES");
+        return (v && std::strcmp(v, "8") == 0) ? 8u : 4u;
+    }();
+    return w;
+}
+
 double lr_factor(int64_t rows, int64_t cols, int32_t adjust) {
     if (adjust == MO_LR_ORIGINAL) return std::sqrt(std::max(1.0, double(rows) / double(cols)));
     if (adjust == MO_LR_MATCH_RMS_ADAMW) return 0.2 * std::sqrt(double(std::max(rows, cols)));
@@ -158,12 +169,16 @@ void build_plan(const mo_matrix* mats, int32_t n, const mo_muon_hparams* hp, Pla
         return js;
     };
     // Dispatch lists: tiles to XCD queues (tile_dispatch.h).
+    // the 8-wave kernels run tiles of full and half width only
+    const uint32_t waves = gemm_waves(), max_split = waves == 8 ? 2 : 4;
     std::vector<mo_wl_item> gram, poly, upd;
-    mo_dispatch_tiles(jobs(order([&](const mo_wl_mat& r) { return upper(r) * r.n_pad; }), true, true), gram);
-    mo_dispatch_tiles(jobs(order([&](const mo_wl_mat& r) { return upper(r) * r.m_pad; }), true, false), poly);
+    mo_dispatch_tiles(jobs(order([&](const mo_wl_mat& r) { return upper(r) * r.n_pad; }), true, true), gram,
+                      max_split);
+    mo_dispatch_tiles(jobs(order([&](const mo_wl_mat& r) { return upper(r) * r.m_pad; }), true, false), poly,
+                      max_split);
     mo_dispatch_tiles(jobs(order([&](const mo_wl_mat& r) {
                                return uint64_t(r.m_pad / T) * (r.n_pad / T) * r.m_pad; }), false, false),
-                      upd);
+                      upd, max_split);
 
     mo_wl_header h;
     std::memset(&h, 0, sizeof(h));
@@ -180,6 +195,7 @@ void build_plan(const mo_matrix* mats, int32_t n, const mo_muon_hparams* hp, Pla
     h.n_poly_items = uint32_t(poly.size());
     h.n_upd_items = uint32_t(upd.size());
     h.max_partials = max_partials;
+    h.gemm_waves = waves;
     h.mats_offset = sizeof(mo_wl_header);
     h.gram_offset = align_up(h.mats_offset + uint64_t(nm) * sizeof(mo_wl_mat), MO_WS_ALIGN);
     h.poly_offset = align_up(h.gram_offset + gram.size() * sizeof(mo_wl_item), MO_WS_ALIGN);

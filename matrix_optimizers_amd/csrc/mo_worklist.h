@@ -37,7 +37,8 @@ struct mo_wl_header {
     uint32_t magic, version;
     uint32_t n_mats, ns_steps, ns_dtype, gemm_tile, mom_tile, elem_bytes;
     uint32_t n_mom_items, n_gram_items, n_poly_items, n_upd_items;
-    uint32_t max_partials, reserved0;
+    uint32_t max_partials;
+    uint32_t gemm_waves;    // wavefronts per workgroup of the GEMM kernels (4 or 8)
     uint64_t mats_offset, gram_offset, poly_offset, upd_offset;  // bytes from list start
     uint64_t wl_bytes;      // size of the list, a multiple of MO_WS_ALIGN
     uint64_t ws_bytes;      // workspace bytes from the aligned base (list included)

@@ -31,7 +31,8 @@ struct mo_gemm_job {
 // XCD would pass an even share of the total, and the list interleaves the 8
 // queues: entry 8 j + x is the j-th tile of XCD x, or a pad entry (record
 // index MO_WL_PAD) where that queue is shorter.
-inline void mo_dispatch_tiles(const std::vector<mo_gemm_job>& jobs, std::vector<mo_wl_item>& out) {
+inline void mo_dispatch_tiles(const std::vector<mo_gemm_job>& jobs, std::vector<mo_wl_item>& out,
+                              uint32_t max_split = 4) {
     constexpr uint32_t SB_R = 4, SB_C = 8, NXCD = 8, CU_PER_XCD = 32;
     struct Blk { std::vector<mo_wl_item> tiles; uint64_t klen; };
     std::vector<Blk> blocks;
@@ -84,7 +85,9 @@ inline void mo_dispatch_tiles(const std::vector<mo_gemm_job>& jobs, std::vector<
         if (n == 0) continue;
         const size_t first = n <= CU_PER_XCD ? 0 : n - n % CU_PER_XCD;
         const size_t r = n - first;
-        const uint32_t S = r == 0 ? 1 : 4 * r <= CU_PER_XCD ? 4 : 2 * r <= CU_PER_XCD ? 2 : 1;
+        const uint32_t S = r == 0 ? 1
+                         : (max_split >= 4 && 4 * r <= CU_PER_XCD) ? 4
+                         : (max_split >= 2 && 2 * r <= CU_PER_XCD) ? 2 : 1;
         if (S == 1) continue;
         std::vector<mo_wl_item> w(v.begin(), v.begin() + first);
         for (size_t k = first; k < n; ++k)

@@ -28,7 +28,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # What decides the kernels' memory traffic: the device code and the host code
 # that builds the work lists (tile order); the upload and timing helpers
 # (host_common.*) do not.
-KERNEL_SOURCES = ["csrc/ns_kernels.hip", "csrc/tail_kernels.hip", "csrc/device_common.h",
+KERNEL_SOURCES = ["csrc/ns_kernels.hip", "csrc/tail_kernels.hip", "csrc/device_common.h", "csrc/gemm_core8.h",
                   "csrc/mo_worklist.h", "csrc/host.cpp", "csrc/gemm_core.h", "csrc/tile_dispatch.h",
                   "csrc/shampoo_kernels.hip", "csrc/sh_worklist.h", "csrc/shampoo.cpp",
                   "csrc/soap_kernels.hip", "csrc/so_worklist.h", "csrc/soap.cpp"]

@@ -8,7 +8,7 @@ Python's ``struct`` so that the C++ builder can be checked byte for byte.
 Layout (little-endian, natural alignment, version 5):
   header (128 B): magic 'MOWL', version, n_mats, ns_steps, ns_dtype, gemm_tile,
       mom_tile, elem_bytes, n_mom_items, n_gram_items, n_poly_items,
-      n_upd_items, max_partials, 0, mats_offset, gram_offset, poly_offset,
+      n_upd_items, max_partials, gemm_waves, mats_offset, gram_offset, poly_offset,
       upd_offset, wl_bytes, ws_bytes (u64), ns_a, ns_b, ns_c, eps (f32), 2 x 0
   matrix record (192 B) per non-empty descriptor, descriptor order: W, G, M,
       update_out (u64), ld_w, ld_g, ld_m, ld_u (i64; 0 -> cols), off_X,
@@ -131,14 +131,16 @@ def build(descs: Sequence[dict], hp: dict) -> bytes:
                 i += take
         # Queues of at most 32 tiles (32 CUs per XCD) have every tile split,
         # longer ones the len % 32 tiles of the last round: into S = 4 quarter
-        # or S = 2 half-width tiles, the largest S with S * (tiles split) <= 32.
+        # or S = 2 half-width tiles, the largest S with S * (tiles split) <= 32
+        # that the kernels run (8-wavefront kernels: half width only).
         for x, q in enumerate(queues):
             n = len(q)
             if n == 0:
                 continue
             first = 0 if n <= 32 else n - n % 32
             r = n - first
-            S = 1 if r == 0 else 4 if 4 * r <= 32 else 2 if 2 * r <= 32 else 1
+            S = (1 if r == 0 else 4 if (max_split >= 4 and 4 * r <= 32)
+                 else 2 if (max_split >= 2 and 2 * r <= 32) else 1)
             if S > 1:
                 queues[x] = q[:first] + [(j, a, b * S + p, 4 // S) for (j, a, b, _) in q[first:]
                                          for p in range(S)]
@@ -146,6 +148,8 @@ def build(descs: Sequence[dict], hp: dict) -> bytes:
         return [queues[x][j] if j < len(queues[x]) else (PAD, 0, 0, 0)
                 for j in range(longest) for x in range(8)]
 
+    waves = hp.get("gemm_waves", 4)
+    max_split = 2 if waves == 8 else 4
     gram = dispatch(ordered(lambda r: upper(r) * r["n_pad"]), True, True)
     poly = dispatch(ordered(lambda r: upper(r) * r["m_pad"]), True, False)
     upd = dispatch(ordered(lambda r: (r["m_pad"] // T) * (r["n_pad"] // T) * r["m_pad"]), False, False)
@@ -168,7 +172,7 @@ def build(descs: Sequence[dict], hp: dict) -> bytes:
 
     out = bytearray(wl_bytes)
     struct.pack_into("<14I6Q4f2I", out, 0, MAGIC, 5, len(recs), hp["ns_steps"], hp["ns_dtype"],
-                     T, MT, es, mom, len(gram), len(poly), len(upd), max_partials, 0,
+                     T, MT, es, mom, len(gram), len(poly), len(upd), max_partials, waves,
                      mats_off, gram_off, poly_off, upd_off, wl_bytes, ws_bytes,
                      hp["ns_a"], hp["ns_b"], hp["ns_c"], hp["eps"], 0, 0)
     for k, r in enumerate(recs):
