@@ -149,6 +149,27 @@ mo_status muon_owner_step(const mo_matrix* mats, int32_t n_mats,
                           const mo_muon_hparams* hp, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * step as muon_owner_step, with the same kernels and bit-identical results,
+ * on a workspace that is a static array of the library instead of a caller
+ * buffer.  It calls no hipMalloc, hipFree or other allocating routine: the
+ * array (MO_NOALLOC_SCRATCH_BYTES = 512 MiB per device) is part of the
+ * library's code object, loaded on a device with the first call there and
+ * held until the process ends, and the work list is uploaded through kernel
+ * arguments (one small launch per 3.5 KB of list), not a staging buffer.
+ * Every call on a device shares that device's array: calls that may overlap
+ * in time on one device (other streams, other threads) race and must be
+ * serialised by the caller; stream-ordered calls on one stream are safe.
+ * Nothing in the array needs to start at zero (every region is written before
+ * it is read).  With mo_profile_enable on, the timing path creates its events
+ * on first use.  Errors as muon_owner_step, with MO_ERR_WORKSPACE_TOO_SMALL
+ * when the bucket's muon_workspace_bytes() exceeds MO_NOALLOC_SCRATCH_BYTES
+ * (nothing is launched then). */
+#define MO_NOALLOC_SCRATCH_BYTES ((size_t)512 << 20)
+mo_status muon_owner_step_noalloc(const mo_matrix* mats, int32_t n_mats,
+                                  const mo_muon_hparams* hp, void* stream);
+
 /* One AdamW step on a packed fp32 tail of n elements, in place ([P §3]: the
  * non-2D tensors stay on the AdamW path; [P §5.1] gives the hyperparameters):
  *   m' = b1 m + (1-b1) g;  v' = b2 v + (1-b2) g^2;

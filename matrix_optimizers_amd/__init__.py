@@ -22,7 +22,8 @@ from ._binding import (  # noqa: F401
     MoSoapHParams, MoSoapMatrix, SoapOwnerStep, soap_descriptor, soap_hparams, soap_owner_step,
     soap_converged, soap_tensor_descriptor, soap_workspace_bytes,
     PHASES, adamw_tail_step, build_worklist, descriptor, device_copy, hparams, load_library,
-    mo_status_string, muon_build_worklist, muon_owner_step, muon_workspace_bytes, plan_layout,
+    mo_status_string, muon_build_worklist, muon_owner_step, muon_owner_step_noalloc, muon_workspace_bytes,
+    NOALLOC_SCRATCH_BYTES, plan_layout,
     plan_owners, plan_score, profile_enable, profile_read, status_string, tensor_descriptor,
     workspace_bytes,
 )

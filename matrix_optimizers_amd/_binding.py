@@ -93,7 +93,8 @@ _lib = None
 EXPORTS = ["muon_workspace_bytes", "muon_build_worklist", "muon_owner_step", "adamw_tail_step",
            "mo_status_string", "mo_profile_enable", "mo_profile_read", "mo_device_copy",
            "mo_plan_owners", "mo_plan_score", "mo_plan_layout", "shampoo_workspace_bytes",
-           "shampoo_owner_step", "soap_workspace_bytes", "soap_owner_step", "soap_converged"]
+           "shampoo_owner_step", "soap_workspace_bytes", "soap_owner_step", "soap_converged",
+           "muon_owner_step_noalloc"]
 
 ROLE_MATRIX, ROLE_TAIL = 0, 1
 PLAN_POLICIES = {"role_greedy": 0, "scope_greedy": 1, "cost_aware": 2}
@@ -121,6 +122,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                         ctypes.c_void_p, P(ctypes.c_size_t)]
     lib.muon_owner_step.argtypes = [P(MoMatrix), ctypes.c_int32, P(MoMuonHParams),
                                     ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.muon_owner_step_noalloc.argtypes = [P(MoMatrix), ctypes.c_int32, P(MoMuonHParams), ctypes.c_void_p]
     lib.adamw_tail_step.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64, ctypes.c_int64] + \
         [ctypes.c_float] * 5 + [ctypes.c_void_p]
     lib.mo_status_string.argtypes = [ctypes.c_int32]
@@ -149,7 +151,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     for name in ("muon_workspace_bytes", "muon_build_worklist", "muon_owner_step",
                  "adamw_tail_step", "mo_profile_enable", "mo_profile_read", "mo_device_copy",
                  "mo_plan_owners", "mo_plan_score", "mo_plan_layout", "shampoo_workspace_bytes",
-                 "shampoo_owner_step", "soap_workspace_bytes", "soap_owner_step", "soap_converged"):
+                 "shampoo_owner_step", "soap_workspace_bytes", "soap_owner_step", "soap_converged",
+                 "muon_owner_step_noalloc"):
         getattr(lib, name).restype = ctypes.c_int32
     _lib = lib
     return lib
@@ -338,6 +341,24 @@ def muon_owner_step(mats: Sequence[Tuple], *, update_out: Optional[Sequence] = N
     _check(lib.muon_owner_step(arr, n, ctypes.byref(hp), ctypes.c_void_p(workspace.data_ptr()),
                                workspace.numel(), ctypes.c_void_p(_stream_handle(stream))),
            "muon_owner_step")
+
+
+NOALLOC_SCRATCH_BYTES = 512 << 20   # MO_NOALLOC_SCRATCH_BYTES of include/mo.h
+
+
+def muon_owner_step_noalloc(mats: Sequence[Tuple], *, update_out: Optional[Sequence] = None,
+                            stream=None, **hp_kwargs) -> None:
+    """muon_owner_step on the library's static per-device scratch array: no
+    workspace argument and no device allocation (for callers that cannot
+    allocate).  Buckets whose workspace exceeds NOALLOC_SCRATCH_BYTES are
+    refused; calls that overlap in time on one device race."""
+    lib = load_library()
+    hp = hparams(**hp_kwargs)
+    ups = list(update_out) if update_out is not None else [None] * len(mats)
+    descs = [tensor_descriptor(W, G, M, u) for (W, G, M), u in zip(mats, ups)]
+    arr, n = _array(descs)
+    _check(lib.muon_owner_step_noalloc(arr, n, ctypes.byref(hp), ctypes.c_void_p(_stream_handle(stream))),
+           "muon_owner_step_noalloc")
 
 
 class MuonOwnerStep:

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(HERE, "libmo.so")
 ARCH = "gfx950"
 
 SOURCES = ["host.cpp", "host_common.cpp", "planner.cpp", "shampoo.cpp", "soap.cpp", "ns_kernels.hip",
-           "shampoo_kernels.hip", "soap_kernels.hip", "tail_kernels.hip"]
+           "shampoo_kernels.hip", "soap_kernels.hip", "tail_kernels.hip", "static_scratch.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC,

@@ -235,6 +235,39 @@ void build_plan(const mo_matrix* mats, int32_t n, const mo_muon_hparams* hp, Pla
 
 }  // namespace
 
+namespace {
+
+// The launches of one step on the uploaded work list at ws.
+mo_status run_phases(const mo_wl_header& h, const mo_muon_hparams* hp, uint8_t* ws, hipStream_t s) {
+    const float beta = hp->momentum;
+    const int nest = hp->nesterov ? 1 : 0;
+    if (timed_launch(MO_PHASE_MOMENTUM, s, [&] { return mo_launch_momentum(h, ws, beta, nest, s); }) != hipSuccess)
+        return MO_ERR_HIP;
+    if (timed_launch(MO_PHASE_NORM, s, [&] { return mo_launch_norm(h, ws, s); }) != hipSuccess)
+        return MO_ERR_HIP;
+    const int K = hp->ns_steps;
+    if (K == 0) {
+        if (timed_launch(MO_PHASE_APPLY, s, [&] { return mo_launch_apply(h, ws, s); }) != hipSuccess)
+            return MO_ERR_HIP;
+        return MO_OK;
+    }
+    int xt = 0;   // which transposed buffer holds the current X^T
+    for (int k = 0; k < K; ++k) {
+        const int first = k == 0, last = k == K - 1;
+        if (timed_launch(MO_PHASE_GRAM, s, [&] { return mo_launch_gram(h, ws, first, xt, s); }) != hipSuccess)
+            return MO_ERR_HIP;
+        if (timed_launch(MO_PHASE_POLY, s, [&] { return mo_launch_poly(h, ws, s); }) != hipSuccess)
+            return MO_ERR_HIP;
+        if (timed_launch(last ? MO_PHASE_UPDATE_LAST : MO_PHASE_UPDATE, s,
+                         [&] { return mo_launch_update(h, ws, first, last, xt, s); }) != hipSuccess)
+            return MO_ERR_HIP;
+        xt ^= 1;
+    }
+    return MO_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* mo_status_string(mo_status st) {
@@ -300,32 +333,31 @@ mo_status muon_owner_step(const mo_matrix* mats, int32_t n, const mo_muon_hparam
     uint8_t* ws = reinterpret_cast<uint8_t*>(
         align_up(reinterpret_cast<uintptr_t>(workspace), MO_WS_ALIGN));
     if (upload(plan.bytes.data(), plan.bytes.size(), ws, s) != hipSuccess) return MO_ERR_HIP;
+    return run_phases(h, hp, ws, s);
+}
 
-    const float beta = hp->momentum;
-    const int nest = hp->nesterov ? 1 : 0;
-    if (timed_launch(MO_PHASE_MOMENTUM, s, [&] { return mo_launch_momentum(h, ws, beta, nest, s); }) != hipSuccess)
-        return MO_ERR_HIP;
-    if (timed_launch(MO_PHASE_NORM, s, [&] { return mo_launch_norm(h, ws, s); }) != hipSuccess)
-        return MO_ERR_HIP;
-    const int K = hp->ns_steps;
-    if (K == 0) {
-        if (timed_launch(MO_PHASE_APPLY, s, [&] { return mo_launch_apply(h, ws, s); }) != hipSuccess)
-            return MO_ERR_HIP;
-        return MO_OK;
-    }
-    int xt = 0;   // which transposed buffer holds the current X^T
-    for (int k = 0; k < K; ++k) {
-        const int first = k == 0, last = k == K - 1;
-        if (timed_launch(MO_PHASE_GRAM, s, [&] { return mo_launch_gram(h, ws, first, xt, s); }) != hipSuccess)
-            return MO_ERR_HIP;
-        if (timed_launch(MO_PHASE_POLY, s, [&] { return mo_launch_poly(h, ws, s); }) != hipSuccess)
-            return MO_ERR_HIP;
-        if (timed_launch(last ? MO_PHASE_UPDATE_LAST : MO_PHASE_UPDATE, s,
-                         [&] { return mo_launch_update(h, ws, first, last, xt, s); }) != hipSuccess)
-            return MO_ERR_HIP;
-        xt ^= 1;
-    }
-    return MO_OK;
+mo_status muon_owner_step_noalloc(const mo_matrix* mats, int32_t n, const mo_muon_hparams* hp,
+                                  void* stream) {
+    mo_status st = validate_hparams(hp);
+    if (st != MO_OK) return st;
+    std::vector<Range> ranges;
+    if ((st = validate_mats(mats, n, &ranges)) != MO_OK) return st;
+    if (n == 0) return MO_OK;
+    Plan plan;
+    build_plan(mats, n, hp, &plan);
+    const mo_wl_header& h = plan.header;
+    if (h.n_mats == 0) return MO_OK;
+    // the array is 256-byte aligned, so no alignment slack is needed
+    if (size_t(h.ws_bytes) > MO_NOALLOC_SCRATCH_BYTES) return MO_ERR_WORKSPACE_TOO_SMALL;
+    void* scratch = nullptr;
+    if (mo_static_scratch(&scratch) != hipSuccess) return MO_ERR_HIP;
+    ranges.push_back(Range{reinterpret_cast<uintptr_t>(scratch),
+                           reinterpret_cast<uintptr_t>(scratch) + MO_NOALLOC_SCRATCH_BYTES, 1});
+    if (ranges_conflict(ranges)) return MO_ERR_ALIAS;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    uint8_t* ws = reinterpret_cast<uint8_t*>(scratch);
+    if (mo_launch_wl_upload(ws, plan.bytes.data(), plan.bytes.size(), s) != hipSuccess) return MO_ERR_HIP;
+    return run_phases(h, hp, ws, s);
 }
 
 mo_status adamw_tail_step(float* p, const float* g, float* m, float* v, int64_t n, int64_t step,

@@ -6,6 +6,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/mo.h"
 #include "mo_worklist.h"
 
 // `ws` is the 256-byte-aligned workspace base; the work list sits at ws[0].
@@ -22,6 +23,12 @@ hipError_t mo_launch_adamw(float* p, const float* g, float* m, float* v, int64_t
                            float beta1, float beta2, float step_size, float inv_sqrt_bc2,
                            float eps, hipStream_t s);
 hipError_t mo_launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
+
+// Allocation-free Muon step (static_scratch.hip): this device's static scratch
+// array (MO_NOALLOC_SCRATCH_BYTES), and a work-list upload carried in kernel
+// arguments.
+hipError_t mo_static_scratch(void** ptr);
+hipError_t mo_launch_wl_upload(uint8_t* dst, const uint8_t* src, size_t bytes, hipStream_t s);
 
 // Shampoo step (shampoo_kernels.hip); `ws` holds the Shampoo work list.
 struct mo_sh_header;

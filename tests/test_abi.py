@@ -203,3 +203,21 @@ def test_planning_limits_fail_fast():
     with pytest.raises(mo.MoError):
         mo.workspace_bytes(many, mo.hparams())
     assert time.perf_counter() - t0 < 5
+
+
+def test_noalloc_entry_point_checks_without_hip():
+    """The allocation-free step validates like muon_owner_step and refuses a
+    bucket beyond its static array before touching the device."""
+    lib = mo.load_library()
+    hp = mo.hparams()
+    assert lib.muon_owner_step_noalloc(None, 0, ctypes.byref(hp), None) == OK
+    assert lib.muon_owner_step_noalloc(None, 1, ctypes.byref(hp), None) == INVALID
+    assert lib.muon_owner_step_noalloc(None, 0, None, None) == INVALID
+    base = 1 << 44
+    big = [mo.descriptor(8192, 8192, W=base, G=base + (1 << 34), M=base + (2 << 34))]
+    arr, n = B._array(big)
+    assert mo.workspace_bytes(big, hp) > mo.NOALLOC_SCRATCH_BYTES
+    assert lib.muon_owner_step_noalloc(arr, n, ctypes.byref(hp), None) == WS_SMALL
+    bad = [mo.descriptor(16, 16, W=base, G=0, M=base + (2 << 34))]
+    arr, n = B._array(bad)
+    assert lib.muon_owner_step_noalloc(arr, n, ctypes.byref(hp), None) == INVALID
