@@ -107,7 +107,7 @@ struct EpiPasses {
 //                            with CAP)
 //   passes(off_diag)         which passes run (EpiPasses)
 //   operand(oj, oi, o)       the mirrored pass's epilogue operand at (oj, oi..+7)
-//   combine(v, o)            final values of the mirrored pass
+//   combine(oj, oi, v, o)    final values of the mirrored pass at (oj, oi..+7)
 //   mirror(oj, oi, v)        write them at row oj, columns oi .. oi + 7
 //   tile_value(v)            final values in the tile pass when nothing is handed over
 //   tile(gi, gj, v)          write row gi, columns gj .. gj + 7
@@ -369,7 +369,7 @@ __device__ __forceinline__ void gemm_core(uint8_t* smem, const T* Pm, const T* Q
                 } else {
                     ep.operand(oj, oi, o);
                 }
-                ep.combine(v, o);
+                ep.combine(oj, oi, v, o);
                 if (write_b) ep.mirror(oj, oi, v);
                 if (hand_over) {
                     *s0 = f32x4{v.v[0], v.v[1], v.v[2], v.v[3]};

@@ -15,7 +15,6 @@
 
 #include <algorithm>
 #include <cmath>
-#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <vector>
@@ -91,15 +90,9 @@ struct Plan {
     mo_wl_header header;
 };
 
-// Wavefronts per GEMM workgroup: 4 (one per SIMD) unless MO_NS_WAVES=8 selects
-// the eight-wavefront kernels (read once per process).
-uint32_t gemm_waves() {
-    static const uint32_t w = [] {
-        const char* v = std::getenv("MO_NS_WAVES");
-        return (v && std::strcmp(v, "8") == 0) ? 8u : 4u;
-    }();
-    return w;
-}
+// Wavefronts per workgroup of the Newton-Schulz GEMM kernels (two per SIMD);
+// they run tiles of full and half width only.
+constexpr uint32_t kGemmWaves = 8, kMaxSplit = 2;
 
 double lr_factor(int64_t rows, int64_t cols, int32_t adjust) {
     if (adjust == MO_LR_ORIGINAL) return std::sqrt(std::max(1.0, double(rows) / double(cols)));
@@ -169,8 +162,7 @@ void build_plan(const mo_matrix* mats, int32_t n, const mo_muon_hparams* hp, Pla
         return js;
     };
     // Dispatch lists: tiles to XCD queues (tile_dispatch.h).
-    // the 8-wave kernels run tiles of full and half width only
-    const uint32_t waves = gemm_waves(), max_split = waves == 8 ? 2 : 4;
+    const uint32_t waves = kGemmWaves, max_split = kMaxSplit;
     std::vector<mo_wl_item> gram, poly, upd;
     mo_dispatch_tiles(jobs(order([&](const mo_wl_mat& r) { return upper(r) * r.n_pad; }), true, true), gram,
                       max_split);

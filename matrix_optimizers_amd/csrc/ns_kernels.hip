@@ -17,7 +17,6 @@
 //   Poly    A A = A A^T       P = A,  Q = A      (A symmetric; upper tiles)
 //   Update  B X = B (X^T)^T   P = B,  Q = X^T
 #include "device_common.h"
-#include "gemm_core.h"
 #include "gemm_core8.h"
 #include "mo_kernels.h"
 
@@ -186,61 +185,69 @@ enum { KIND_GRAM = 0, KIND_POLY = 1, KIND_UPDATE = 2 };
 // pass ("pass B": for a sub-tile column j, 8 consecutive rows) runs first and
 // forms the final values; the tile pass ("pass A": for a sub-tile row, 8
 // consecutive columns) writes them in the tile's own orientation.
-template <typename T, int KIND, bool LAST, bool CAPTURE = true>
+template <typename T, int KIND, bool LAST>
 struct Epi {
-    // bf16 Poly / Update take their epilogue operand (A[i][j] = A[j][i],
-    // X[i][j] = X^T[j][i]) from the Q stage in LDS (4-wave core only)
-    static constexpr bool CAP = CAPTURE && sizeof(T) == 2 && KIND != KIND_GRAM;
+    // Poly reads its epilogue operand A[i][j] = A[j][i] (small, in L2).  The
+    // Update has no operand: the a X term is folded into the Poly output,
+    // B' = a I + b A + c A^2, so the Update is the plain product X' = B' X
+    // (exactly a X + B X; with bf16 B' the emulated error against the fp64
+    // reference is no larger than with a X added in the fp32 epilogue).
+    static constexpr bool CAP = false;
     static constexpr bool KROT = false;
     const mo_wl_mat* mt;
     T *X, *Xt_cur, *Xt_nxt, *A, *B;
     float alpha, sx, na, nb, nc;
-    int64_t m_pad, n_pad;
+    int64_t m_pad, n_pad, m;
     bool trans;
 
     // Gram and Poly write the mirror of an off-diagonal tile; Update writes
     // X^T (or, last, W when the weight is the transposed frame).  The tile
     // pass writes everything except the last Update of a transposed weight.
-    // Gram scales in each pass; the other kinds form their values in the
-    // mirrored pass and hand them to the tile pass through the staging slice.
+    // Poly forms its values in the mirrored pass (it needs the operand) and
+    // hands them to the tile pass through the staging slice; Gram and Update
+    // scale in each pass (the same fp32 arithmetic, so the same values).  The
+    // last Update of a weight in the NS frame needs no mirrored pass at all.
     MO_DEV EpiPasses passes(bool off_diag) const {
         EpiPasses p;
-        p.run_b = KIND == KIND_GRAM ? off_diag : true;
+        p.run_b = KIND == KIND_GRAM ? off_diag : KIND == KIND_POLY ? true : (!LAST || trans);
         p.write_b = KIND == KIND_UPDATE ? (!LAST || trans) : off_diag;
         p.run_a = !(KIND == KIND_UPDATE && LAST && trans);
-        p.hand_over = KIND != KIND_GRAM && p.run_a;
+        p.hand_over = KIND == KIND_POLY && p.run_a;
         return p;
     }
 
-    // the epilogue operand when it is not captured (fp32)
+    // the Poly operand when it is not captured
     MO_DEV void operand(int64_t oj, int64_t oi, f32x8& o) const {
         if (KIND == KIND_POLY) load8(A + oj * m_pad + oi, o);            // A[i][j] = A[j][i]
-        else if (KIND == KIND_UPDATE) load8(Xt_cur + oj * m_pad + oi, o); // X[i][j] = X^T[j][i]
     }
 
     MO_DEV void tile_value(f32x8& v) const {
         if (KIND == KIND_GRAM) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) v.v[e] *= alpha;
-        }
-    }
-
-    // Final values from the product v and the epilogue operand o (A[i][j] for
-    // Poly, X[i][j] for Update; unused for Gram).
-    MO_DEV void combine(f32x8& v, const f32x8& o) const {
-        if (KIND == KIND_GRAM) {
+        } else if (KIND == KIND_UPDATE) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v.v[e] *= alpha;
-        } else if (KIND == KIND_POLY) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v.v[e] = quantize<T>(nc * v.v[e] + nb * o.v[e]);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v.v[e] = sx * (na * o.v[e] + v.v[e]);
+            for (int e = 0; e < 8; ++e) v.v[e] *= sx;
             if (!LAST) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) v.v[e] = quantize<T>(v.v[e]);
             }
+        }
+    }
+
+    // Final values of the mirrored pass at row oj, columns oi .. oi + 7 of the
+    // mirrored product, from the product v and (Poly) the operand o = A[i][j]:
+    // B' = c A A + b A, plus a on the matrix's diagonal (i = j < m; the
+    // padding stays zero).
+    MO_DEV void combine(int64_t oj, int64_t oi, f32x8& v, const f32x8& o) const {
+        if (KIND == KIND_POLY) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float d = (oi + e == oj && oj < m) ? na : 0.0f;
+                v.v[e] = quantize<T>(nc * v.v[e] + nb * o.v[e] + d);
+            }
+        } else {
+            tile_value(v);
         }
     }
 
@@ -299,14 +306,14 @@ struct Epi {
     }
 };
 
-// One Newton-Schulz tile: the phase's operands and epilogue around the shared
-// GEMM core.
+// One Newton-Schulz tile (width 256 or 128): the phase's operands and
+// epilogue around the 8-wavefront GEMM core (gemm_core8.h).
 //   Gram    A = X X^T         P = X,  Q = X      (upper tiles; mirrored)
 //   Poly    A A = A A^T       P = A,  Q = A      (A symmetric; upper tiles)
-//   Update  B X = B (X^T)^T   P = B,  Q = X^T
+//   Update  B' X = B' (X^T)^T P = B', Q = X^T
 template <typename T, int KIND, bool LAST, int NB>
 __device__ __forceinline__ void gemm_tile(uint8_t* smem, uint8_t* ws, const mo_wl_item& it, int first,
-                                          int xt_cur) {
+                                           int xt_cur) {
     const mo_wl_header* h = wl_header(ws);
     const mo_wl_mat& mt = wl_mats(ws)[it.mat];
     const int64_t m_pad = mt.m_pad, n_pad = mt.n_pad;
@@ -324,42 +331,7 @@ __device__ __forceinline__ void gemm_tile(uint8_t* smem, uint8_t* ws, const mo_w
         ep.alpha = (KIND == KIND_GRAM && first) ? scale[1] : 1.0f;
         ep.sx = (KIND == KIND_UPDATE && first) ? scale[0] : 1.0f;
         ep.na = h->ns_a; ep.nb = h->ns_b; ep.nc = h->ns_c;
-        ep.m_pad = m_pad; ep.n_pad = n_pad;
-        ep.trans = mt.flags & MO_WLF_TRANSPOSED;
-        const int64_t wes = (mt.flags & MO_WLF_W_BF16) ? 2 : 4;
-        ep.vec_w = ((mt.W | uint64_t(mt.ld_w * wes)) & 15) == 0;
-        ep.vec_u = ((mt.U | uint64_t(mt.ld_u * 4)) & 15) == 0;
-        return ep;
-    };
-    const int ti = int(it.ti), tj = int(it.tj);
-    if (KIND == KIND_GRAM) gemm_core<T, NB>(smem, X, X, n_pad, ti, tj, make_ep);
-    else if (KIND == KIND_POLY) gemm_core<T, NB>(smem, A, A, m_pad, ti, tj, make_ep);
-    else gemm_core<T, NB>(smem, B, Xt_cur, m_pad, ti, tj, make_ep);
-}
-
-// The same tile on the 8-wavefront core (gemm_core8.h): tile widths 256 and
-// 128, the epilogue operand read from memory.
-template <typename T, int KIND, bool LAST, int NB>
-__device__ __forceinline__ void gemm_tile8(uint8_t* smem, uint8_t* ws, const mo_wl_item& it, int first,
-                                           int xt_cur) {
-    const mo_wl_header* h = wl_header(ws);
-    const mo_wl_mat& mt = wl_mats(ws)[it.mat];
-    const int64_t m_pad = mt.m_pad, n_pad = mt.n_pad;
-    T* X = reinterpret_cast<T*>(ws + mt.off_X);
-    T* Xt_cur = reinterpret_cast<T*>(ws + (xt_cur ? mt.off_Xt1 : mt.off_Xt0));
-    T* Xt_nxt = reinterpret_cast<T*>(ws + (xt_cur ? mt.off_Xt0 : mt.off_Xt1));
-    T* A = reinterpret_cast<T*>(ws + mt.off_A);
-    T* B = reinterpret_cast<T*>(ws + mt.off_B);
-    const float* scale = reinterpret_cast<const float*>(ws + mt.off_scale);
-
-    auto make_ep = [&]() __attribute__((always_inline)) {
-        Epi<T, KIND, LAST, false> ep;
-        ep.mt = &mt;
-        ep.X = X; ep.Xt_cur = Xt_cur; ep.Xt_nxt = Xt_nxt; ep.A = A; ep.B = B;
-        ep.alpha = (KIND == KIND_GRAM && first) ? scale[1] : 1.0f;
-        ep.sx = (KIND == KIND_UPDATE && first) ? scale[0] : 1.0f;
-        ep.na = h->ns_a; ep.nb = h->ns_b; ep.nc = h->ns_c;
-        ep.m_pad = m_pad; ep.n_pad = n_pad;
+        ep.m_pad = m_pad; ep.n_pad = n_pad; ep.m = mt.m;
         ep.trans = mt.flags & MO_WLF_TRANSPOSED;
         const int64_t wes = (mt.flags & MO_WLF_W_BF16) ? 2 : 4;
         ep.vec_w = ((mt.W | uint64_t(mt.ld_w * wes)) & 15) == 0;
@@ -372,20 +344,6 @@ __device__ __forceinline__ void gemm_tile8(uint8_t* smem, uint8_t* ws, const mo_
     else gemm_core8<T, NB>(smem, B, Xt_cur, m_pad, ti, tj, make_ep);
 }
 
-template <typename T, int KIND, bool LAST>
-__device__ __forceinline__ void gemm_entry8(uint8_t* ws, int first, int xt_cur) {
-    __shared__ __align__(16) uint8_t smem[GEMM_LDS];
-    const mo_wl_header* h = wl_header(ws);
-    const uint64_t items_off = KIND == KIND_GRAM ? h->gram_offset
-                             : KIND == KIND_POLY ? h->poly_offset : h->upd_offset;
-    const mo_wl_item it = reinterpret_cast<const mo_wl_item*>(ws + items_off)[blockIdx.x];
-    if (it.mat == MO_WL_PAD) return;
-    if (it.nb == 4) gemm_tile8<T, KIND, LAST, 4>(smem, ws, it, first, xt_cur);
-    else gemm_tile8<T, KIND, LAST, 2>(smem, ws, it, first, xt_cur);
-}
-
-inline unsigned grid_for(uint32_t items) { return items; }   // dispatch lists are padded to 8
-
 // Entry b of the phase's dispatch list is workgroup b's tile; the tile width
 // (NB) is uniform per workgroup.
 template <typename T, int KIND, bool LAST>
@@ -397,13 +355,15 @@ __device__ __forceinline__ void gemm_entry(uint8_t* ws, int first, int xt_cur) {
     const mo_wl_item it = reinterpret_cast<const mo_wl_item*>(ws + items_off)[blockIdx.x];
     if (it.mat == MO_WL_PAD) return;
     if (it.nb == 4) gemm_tile<T, KIND, LAST, 4>(smem, ws, it, first, xt_cur);
-    else if (it.nb == 2) gemm_tile<T, KIND, LAST, 2>(smem, ws, it, first, xt_cur);
-    else gemm_tile<T, KIND, LAST, 1>(smem, ws, it, first, xt_cur);
+    else gemm_tile<T, KIND, LAST, 2>(smem, ws, it, first, xt_cur);
 }
 
-// One plainly named kernel per (phase, NS dtype), so profiles name them unambiguously.
+inline unsigned grid_for(uint32_t items) { return items; }   // dispatch lists are padded to 8
+
+// One plainly named kernel per (phase, NS dtype), so profiles name them
+// unambiguously; 512 threads, two wavefronts per SIMD.
 #define MO_GEMM_KERNEL(name, T, KIND, LAST)                                               \
-    __global__ __launch_bounds__(G_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))    \
+    __global__ __launch_bounds__(G8_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))   \
     void name(uint8_t* ws, int first, int xt_cur) { gemm_entry<T, KIND, LAST>(ws, first, xt_cur); }
 MO_GEMM_KERNEL(gram_bf16, bf16_t, KIND_GRAM, false)
 MO_GEMM_KERNEL(gram_f32, float, KIND_GRAM, false)
@@ -414,19 +374,6 @@ MO_GEMM_KERNEL(update_f32, float, KIND_UPDATE, false)
 MO_GEMM_KERNEL(update_last_bf16, bf16_t, KIND_UPDATE, true)
 MO_GEMM_KERNEL(update_last_f32, float, KIND_UPDATE, true)
 #undef MO_GEMM_KERNEL
-
-#define MO_GEMM8_KERNEL(name, T, KIND, LAST)                                              \
-    __global__ __launch_bounds__(G8_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))   \
-    void name(uint8_t* ws, int first, int xt_cur) { gemm_entry8<T, KIND, LAST>(ws, first, xt_cur); }
-MO_GEMM8_KERNEL(gram8_bf16, bf16_t, KIND_GRAM, false)
-MO_GEMM8_KERNEL(gram8_f32, float, KIND_GRAM, false)
-MO_GEMM8_KERNEL(poly8_bf16, bf16_t, KIND_POLY, false)
-MO_GEMM8_KERNEL(poly8_f32, float, KIND_POLY, false)
-MO_GEMM8_KERNEL(update8_bf16, bf16_t, KIND_UPDATE, false)
-MO_GEMM8_KERNEL(update8_f32, float, KIND_UPDATE, false)
-MO_GEMM8_KERNEL(update_last8_bf16, bf16_t, KIND_UPDATE, true)
-MO_GEMM8_KERNEL(update_last8_f32, float, KIND_UPDATE, true)
-#undef MO_GEMM8_KERNEL
 
 }  // namespace
 
@@ -462,24 +409,22 @@ hipError_t mo_launch_apply(const mo_wl_header& h, uint8_t* ws, hipStream_t s) {
 typedef void (*gemm_fn)(uint8_t*, int, int);
 
 static hipError_t launch_gemm(const mo_wl_header& h, uint32_t items, gemm_fn bf, gemm_fn f32,
-                              gemm_fn bf8, gemm_fn f328, uint8_t* ws, int first, int xt_cur, hipStream_t s) {
+                              uint8_t* ws, int first, int xt_cur, hipStream_t s) {
     if (items == 0) return hipSuccess;
-    const bool w8 = h.gemm_waves == 8;
-    const gemm_fn fn = h.ns_dtype == MO_BF16 ? (w8 ? bf8 : bf) : (w8 ? f328 : f32);
-    hipLaunchKernelGGL(fn, dim3(grid_for(items)), dim3(w8 ? G8_THREADS : G_THREADS), 0, s, ws, first, xt_cur);
+    if (h.gemm_waves != G8_THREADS / 64) return hipErrorInvalidValue;   // list built for other kernels
+    hipLaunchKernelGGL((h.ns_dtype == MO_BF16 ? bf : f32), dim3(grid_for(items)), dim3(G8_THREADS), 0, s,
+                       ws, first, xt_cur);
     return hipGetLastError();
 }
 
 hipError_t mo_launch_gram(const mo_wl_header& h, uint8_t* ws, int first, int xt_cur, hipStream_t s) {
-    return launch_gemm(h, h.n_gram_items, gram_bf16, gram_f32, gram8_bf16, gram8_f32, ws, first, xt_cur, s);
+    return launch_gemm(h, h.n_gram_items, gram_bf16, gram_f32, ws, first, xt_cur, s);
 }
 hipError_t mo_launch_poly(const mo_wl_header& h, uint8_t* ws, hipStream_t s) {
-    return launch_gemm(h, h.n_poly_items, poly_bf16, poly_f32, poly8_bf16, poly8_f32, ws, 0, 0, s);
+    return launch_gemm(h, h.n_poly_items, poly_bf16, poly_f32, ws, 0, 0, s);
 }
 hipError_t mo_launch_update(const mo_wl_header& h, uint8_t* ws, int first, int last, int xt_cur,
                             hipStream_t s) {
-    return last ? launch_gemm(h, h.n_upd_items, update_last_bf16, update_last_f32, update_last8_bf16,
-                              update_last8_f32, ws, first, xt_cur, s)
-                : launch_gemm(h, h.n_upd_items, update_bf16, update_f32, update8_bf16, update8_f32, ws,
-                              first, xt_cur, s);
+    return last ? launch_gemm(h, h.n_upd_items, update_last_bf16, update_last_f32, ws, first, xt_cur, s)
+                : launch_gemm(h, h.n_upd_items, update_bf16, update_f32, ws, first, xt_cur, s);
 }

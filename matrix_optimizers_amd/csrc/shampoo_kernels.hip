@@ -219,7 +219,7 @@ struct ShEpi {
         }
     }
 
-    MO_DEV void combine(f32x8& v, const f32x8& o) const {
+    MO_DEV void combine(int64_t, int64_t, f32x8& v, const f32x8& o) const {
         if (kind == MO_SHK_STATS) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) v.v[e] += o.v[e];

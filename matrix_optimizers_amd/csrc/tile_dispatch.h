@@ -77,9 +77,10 @@ inline void mo_dispatch_tiles(const std::vector<mo_gemm_job>& jobs, std::vector<
     // Narrow tiles where full ones would leave an XCD's CUs idle: a queue of
     // n <= 32 tiles (one partial round) has every tile split, and a longer
     // queue the n % 32 tiles of its last round, into S = 4 quarter-width
-    // or S = 2 half-width tiles, the largest S that still fits the 32 CUs
-    // (none if even halves do not).  Split tiles keep their place in the
-    // queue, the S parts in column order.
+    // or S = 2 half-width tiles, the largest S up to max_split (the widths
+    // the launch's kernels run) that still fits the 32 CUs (none if even
+    // halves do not).  Split tiles keep their place in the queue, the S parts
+    // in column order.
     for (auto& v : q) {
         const size_t n = v.size();
         if (n == 0) continue;

@@ -130,9 +130,9 @@ def build(descs: Sequence[dict], hp: dict) -> bytes:
                 load[x] += klen * take
                 i += take
         # Queues of at most 32 tiles (32 CUs per XCD) have every tile split,
-        # longer ones the len % 32 tiles of the last round: into S = 4 quarter
-        # or S = 2 half-width tiles, the largest S with S * (tiles split) <= 32
-        # that the kernels run (8-wavefront kernels: half width only).
+        # longer ones the len % 32 tiles of the last round: into S = 2
+        # half-width tiles when 2 * (tiles split) <= 32 (S = 4 quarter widths
+        # only for lists built for 4-wavefront kernels, max_split 4).
         for x, q in enumerate(queues):
             n = len(q)
             if n == 0:
@@ -148,7 +148,7 @@ def build(descs: Sequence[dict], hp: dict) -> bytes:
         return [queues[x][j] if j < len(queues[x]) else (PAD, 0, 0, 0)
                 for j in range(longest) for x in range(8)]
 
-    waves = hp.get("gemm_waves", 4)
+    waves = hp.get("gemm_waves", 8)
     max_split = 2 if waves == 8 else 4
     gram = dispatch(ordered(lambda r: upper(r) * r["n_pad"]), True, True)
     poly = dispatch(ordered(lambda r: upper(r) * r["m_pad"]), True, False)

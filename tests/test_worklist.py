@@ -99,22 +99,23 @@ def test_dispatch_lists_cover_every_tile_once(key):
 
 
 def test_underfilled_launch_uses_narrow_tiles():
-    """A bucket with few tiles per XCD queue splits them (quarter width when the
-    parts still fit the XCD's 32 CUs).  In the decoder-layer bucket the Update
-    queues (98 tiles each) split only the 2 tiles of their last round, the Poly
-    queues (31-32 tiles) none, and the Gram queues that the K-length balance
-    left short (the long-K tiles) split all of theirs."""
+    """A bucket with few tiles per XCD queue splits them into half-width tiles
+    when the halves still fit the XCD's 32 CUs (the 8-wavefront kernels have
+    no quarter width).  In the decoder-layer bucket the Update queues (98
+    tiles each) split only the 2 tiles of their last round, the Poly queues
+    (31-32 tiles) none, and the Gram queues that the K-length balance left
+    short (the long-K tiles) split theirs."""
     descs, hp = CASES["ragged_not_tile_multiple"]
     _, lists = _parse(c_build(descs, hp)[0])
     for items in lists:
-        assert {nb for m, _, _, nb in items if m != 0xFFFFFFFF} == {1}
+        assert {nb for m, _, _, nb in items if m != 0xFFFFFFFF} == {2}
     descs, hp = CASES["decoder_layer_h2048"]
     _, lists = _parse(c_build(descs, hp)[0])
     upd = [nb for m, _, _, nb in lists[2] if m != 0xFFFFFFFF]
-    assert upd.count(4) == 768 and upd.count(1) == 64 and len(upd) == 832
+    assert upd.count(4) == 768 and upd.count(2) == 32 and len(upd) == 800
     assert {nb for m, _, _, nb in lists[1] if m != 0xFFFFFFFF} == {4}
     gram = [(m, nb) for m, _, _, nb in lists[0] if m != 0xFFFFFFFF]
-    assert {nb for _, nb in gram} == {1, 2, 4}
+    assert {nb for _, nb in gram} == {2, 4}
 
 
 # ---- record-level pins, derived from the step's definition (not from the twin) ----
