@@ -49,6 +49,9 @@ def parse():
                     help="shampoo: time the Shampoo owner step instead (workload "
                          "shampoo_decoder_layer_h2048 unless --workload names another Shampoo one); "
                          "soap: the SOAP owner step (workload soap_decoder_layer_h2048)")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the Muon step (the allocation-free entry point) once in a HIP graph and "
+                         "time its replays (for launch-bound buckets); no per-phase timing")
     ap.add_argument("--adamw-sweep", action="store_true",
                     help="instead of the step, time adamw_tail_step over n = 2^24 .. 2^28 "
                          "fp32 elements (28 bytes moved per element) and print one JSON line per n")
@@ -533,8 +536,30 @@ def main():
     a = wl.adamw
     t_count = [a.step]
 
+    muon = step
+    if args.graph:
+        # The allocation-free entry point uploads its work list through kernel
+        # arguments, so the whole step is capturable; each replay is one step
+        # on the same tensors.  The first call (outside the capture) loads the
+        # code objects and takes the static array's address.
+        kw = dict(lr=hp.lr, weight_decay=hp.weight_decay, momentum=hp.momentum, nesterov=hp.nesterov,
+                  ns_steps=hp.ns_steps, ns_coefficients=(hp.ns_a, hp.ns_b, hp.ns_c), eps=hp.eps,
+                  adjust_lr_fn=hp.lr_adjust, ns_dtype=hp.ns_dtype)
+        need = mo.workspace_bytes([mo.tensor_descriptor(*m) for m in mats], mo.hparams(**kw))
+        if need > mo.NOALLOC_SCRATCH_BYTES:
+            print(f"bench.py --graph: workload {wl.key} needs {need >> 20} MiB of workspace, more than "
+                  f"the allocation-free step's {mo.NOALLOC_SCRATCH_BYTES >> 20} MiB", file=sys.stderr)
+            sys.exit(2)
+        mo.muon_owner_step_noalloc(mats, **kw)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            mo.muon_owner_step_noalloc(mats, **kw)
+        muon = graph.replay
+        args.no_phase_timing = True
+
     def one_step():
-        step()
+        muon()
         if tail is not None:
             mo.adamw_tail_step(*tail, t_count[0], lr=a.lr, beta1=a.beta1, beta2=a.beta2,
                                eps=a.eps, weight_decay=a.weight_decay)
@@ -571,7 +596,8 @@ def main():
                    "shapes": sorted({f"{s.rows}x{s.cols}" for s in wl.matrices}),
                    "tail_elems": wl.tail_numel, "ns_steps": hp.ns_steps,
                    "w_dtype": wl.w_dtype, "g_dtype": wl.g_dtype, "momentum_dtype": "f32",
-                   "parallelism": "none (one owner's bucket)"},
+                   "parallelism": "none (one owner's bucket)",
+                   "launch": "HIP graph replay of muon_owner_step_noalloc" if args.graph else "eager launches"},
         "ns_tflops_nominal": round(tflops, 3),
         "ns_tflops_algorithmic": round(algo / (ms * 1e-3) / 1e12, 3),
         "pct_peak_nominal": round(100.0 * tflops / peak, 2),

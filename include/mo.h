@@ -106,11 +106,11 @@ mo_status muon_workspace_bytes(const mo_matrix* mats, int32_t n_mats,
  * layout (little-endian, natural alignment, version 5):
  *   header   mo_wl_header (128 bytes); its 14th word is the number of
  *            wavefronts per workgroup of the GEMM kernels the list is built
- *            for (8)
+ *            for (8 with a bf16 ns_dtype, 4 with fp32)
  *   matrices mo_wl_mat[n_live] (192 bytes each), one per non-empty descriptor,
  *            in descriptor order
  *   items    three dispatch lists of mo_wl_item (16 bytes: record index, tile
- *            row ti, tile column tj, width nb in {4, 2}; the tile covers
+ *            row ti, tile column tj, width nb in {4, 2, 1}; the tile covers
  *            rows 256 ti .. +256 and columns 64 nb tj .. +64 nb): Gram, Poly,
  *            Update, each starting on a 256-byte boundary; entry b is the tile
  *            run by workgroup b
@@ -124,8 +124,9 @@ mo_status muon_workspace_bytes(const mo_matrix* mats, int32_t n_mats,
  * reach the share (at least one) and the rest goes on to the next queue.
  * Then, where full tiles would leave CUs idle, tiles are split by columns: a
  * queue of n <= 32 tiles (32 CUs per XCD) has every tile split, a longer one
- * the n % 32 tiles of its last round, into S = 2 half-width (nb = 2) tiles
- * when 2 x (tiles split) <= 32;
+ * the n % 32 tiles of its last round, into S = 4 quarter-width (nb = 1, fp32
+ * lists only) or S = 2 half-width (nb = 2) tiles, the largest S with
+ * S x (tiles split) <= 32;
  * the parts take the tile's place in the queue, in column order.  Entry 8 j + x
  * of a list is the j-th tile of queue x, or a pad entry (record index
  * 0xFFFFFFFF) where queue x is shorter. */

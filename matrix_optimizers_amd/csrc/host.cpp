@@ -90,9 +90,10 @@ struct Plan {
     mo_wl_header header;
 };
 
-// Wavefronts per workgroup of the Newton-Schulz GEMM kernels (two per SIMD);
-// they run tiles of full and half width only.
-constexpr uint32_t kGemmWaves = 8, kMaxSplit = 2;
+// Wavefronts per workgroup of the Newton-Schulz GEMM kernels: bf16 products
+// run on 8 (two per SIMD; tiles of full and half width), fp32 ones on 4 (one
+// per SIMD; full, half and quarter width).
+uint32_t gemm_waves(int32_t ns_dtype) { return ns_dtype == MO_BF16 ? 8u : 4u; }
 
 double lr_factor(int64_t rows, int64_t cols, int32_t adjust) {
     if (adjust == MO_LR_ORIGINAL) return std::sqrt(std::max(1.0, double(rows) / double(cols)));
@@ -162,7 +163,7 @@ void build_plan(const mo_matrix* mats, int32_t n, const mo_muon_hparams* hp, Pla
         return js;
     };
     // Dispatch lists: tiles to XCD queues (tile_dispatch.h).
-    const uint32_t waves = kGemmWaves, max_split = kMaxSplit;
+    const uint32_t waves = gemm_waves(hp->ns_dtype), max_split = waves == 8 ? 2 : 4;
     std::vector<mo_wl_item> gram, poly, upd;
     mo_dispatch_tiles(jobs(order([&](const mo_wl_mat& r) { return upper(r) * r.n_pad; }), true, true), gram,
                       max_split);

@@ -17,6 +17,7 @@
 //   Poly    A A = A A^T       P = A,  Q = A      (A symmetric; upper tiles)
 //   Update  B X = B (X^T)^T   P = B,  Q = X^T
 #include "device_common.h"
+#include "gemm_core.h"
 #include "gemm_core8.h"
 #include "mo_kernels.h"
 
@@ -311,9 +312,9 @@ struct Epi {
 //   Gram    A = X X^T         P = X,  Q = X      (upper tiles; mirrored)
 //   Poly    A A = A A^T       P = A,  Q = A      (A symmetric; upper tiles)
 //   Update  B' X = B' (X^T)^T P = B', Q = X^T
-template <typename T, int KIND, bool LAST, int NB>
+template <typename T, int KIND, bool LAST, int NB, bool EIGHT>
 __device__ __forceinline__ void gemm_tile(uint8_t* smem, uint8_t* ws, const mo_wl_item& it, int first,
-                                           int xt_cur) {
+                                          int xt_cur) {
     const mo_wl_header* h = wl_header(ws);
     const mo_wl_mat& mt = wl_mats(ws)[it.mat];
     const int64_t m_pad = mt.m_pad, n_pad = mt.n_pad;
@@ -339,13 +340,26 @@ __device__ __forceinline__ void gemm_tile(uint8_t* smem, uint8_t* ws, const mo_w
         return ep;
     };
     const int ti = int(it.ti), tj = int(it.tj);
-    if (KIND == KIND_GRAM) gemm_core8<T, NB>(smem, X, X, n_pad, ti, tj, make_ep);
-    else if (KIND == KIND_POLY) gemm_core8<T, NB>(smem, A, A, m_pad, ti, tj, make_ep);
-    else gemm_core8<T, NB>(smem, B, Xt_cur, m_pad, ti, tj, make_ep);
+    const T* P = KIND == KIND_GRAM ? X : KIND == KIND_POLY ? A : B;
+    const T* Q = KIND == KIND_GRAM ? X : KIND == KIND_POLY ? A : Xt_cur;
+    const int64_t ld = KIND == KIND_GRAM ? n_pad : m_pad;
+    if constexpr (EIGHT) gemm_core8<T, NB>(smem, P, Q, ld, ti, tj, make_ep);
+    else gemm_core<T, NB>(smem, P, Q, ld, ti, tj, make_ep);
 }
 
 // Entry b of the phase's dispatch list is workgroup b's tile; the tile width
-// (NB) is uniform per workgroup.
+// (NB) is uniform per workgroup.  bf16 products run on the 8-wavefront core
+// (widths 256 and 128); fp32 ones, whose buckets are small and whose fp32
+// MFMAs run at a sixteenth of the bf16 rate, on the 4-wavefront core, which
+// also has the quarter width (64) and so spreads a small product over more
+// CUs.
+template <typename T, int KIND, bool LAST, int NB>
+__device__ __forceinline__ void gemm_tile_any(uint8_t* smem, uint8_t* ws, const mo_wl_item& it, int first,
+                                              int xt_cur) {
+    if constexpr (sizeof(T) == 2) gemm_tile<T, KIND, LAST, NB, true>(smem, ws, it, first, xt_cur);
+    else gemm_tile<T, KIND, LAST, NB, false>(smem, ws, it, first, xt_cur);
+}
+
 template <typename T, int KIND, bool LAST>
 __device__ __forceinline__ void gemm_entry(uint8_t* ws, int first, int xt_cur) {
     __shared__ __align__(16) uint8_t smem[GEMM_LDS];
@@ -354,26 +368,32 @@ __device__ __forceinline__ void gemm_entry(uint8_t* ws, int first, int xt_cur) {
                              : KIND == KIND_POLY ? h->poly_offset : h->upd_offset;
     const mo_wl_item it = reinterpret_cast<const mo_wl_item*>(ws + items_off)[blockIdx.x];
     if (it.mat == MO_WL_PAD) return;
-    if (it.nb == 4) gemm_tile<T, KIND, LAST, 4>(smem, ws, it, first, xt_cur);
-    else gemm_tile<T, KIND, LAST, 2>(smem, ws, it, first, xt_cur);
+    if (it.nb == 4) gemm_tile_any<T, KIND, LAST, 4>(smem, ws, it, first, xt_cur);
+    else if (it.nb == 2) gemm_tile_any<T, KIND, LAST, 2>(smem, ws, it, first, xt_cur);
+    else if constexpr (sizeof(T) == 4) gemm_tile_any<T, KIND, LAST, 1>(smem, ws, it, first, xt_cur);
 }
 
 inline unsigned grid_for(uint32_t items) { return items; }   // dispatch lists are padded to 8
 
 // One plainly named kernel per (phase, NS dtype), so profiles name them
-// unambiguously; 512 threads, two wavefronts per SIMD.
-#define MO_GEMM_KERNEL(name, T, KIND, LAST)                                               \
+// unambiguously: bf16 on 512 threads (two wavefronts per SIMD), fp32 on 256
+// (one per SIMD, all 512 registers per lane).
+#define MO_GEMM_KERNEL8(name, T, KIND, LAST)                                              \
     __global__ __launch_bounds__(G8_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))   \
     void name(uint8_t* ws, int first, int xt_cur) { gemm_entry<T, KIND, LAST>(ws, first, xt_cur); }
-MO_GEMM_KERNEL(gram_bf16, bf16_t, KIND_GRAM, false)
-MO_GEMM_KERNEL(gram_f32, float, KIND_GRAM, false)
-MO_GEMM_KERNEL(poly_bf16, bf16_t, KIND_POLY, false)
-MO_GEMM_KERNEL(poly_f32, float, KIND_POLY, false)
-MO_GEMM_KERNEL(update_bf16, bf16_t, KIND_UPDATE, false)
-MO_GEMM_KERNEL(update_f32, float, KIND_UPDATE, false)
-MO_GEMM_KERNEL(update_last_bf16, bf16_t, KIND_UPDATE, true)
-MO_GEMM_KERNEL(update_last_f32, float, KIND_UPDATE, true)
-#undef MO_GEMM_KERNEL
+#define MO_GEMM_KERNEL4(name, T, KIND, LAST)                                              \
+    __global__ __launch_bounds__(G_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))    \
+    void name(uint8_t* ws, int first, int xt_cur) { gemm_entry<T, KIND, LAST>(ws, first, xt_cur); }
+MO_GEMM_KERNEL8(gram_bf16, bf16_t, KIND_GRAM, false)
+MO_GEMM_KERNEL4(gram_f32, float, KIND_GRAM, false)
+MO_GEMM_KERNEL8(poly_bf16, bf16_t, KIND_POLY, false)
+MO_GEMM_KERNEL4(poly_f32, float, KIND_POLY, false)
+MO_GEMM_KERNEL8(update_bf16, bf16_t, KIND_UPDATE, false)
+MO_GEMM_KERNEL4(update_f32, float, KIND_UPDATE, false)
+MO_GEMM_KERNEL8(update_last_bf16, bf16_t, KIND_UPDATE, true)
+MO_GEMM_KERNEL4(update_last_f32, float, KIND_UPDATE, true)
+#undef MO_GEMM_KERNEL8
+#undef MO_GEMM_KERNEL4
 
 }  // namespace
 
@@ -411,9 +431,10 @@ typedef void (*gemm_fn)(uint8_t*, int, int);
 static hipError_t launch_gemm(const mo_wl_header& h, uint32_t items, gemm_fn bf, gemm_fn f32,
                               uint8_t* ws, int first, int xt_cur, hipStream_t s) {
     if (items == 0) return hipSuccess;
-    if (h.gemm_waves != G8_THREADS / 64) return hipErrorInvalidValue;   // list built for other kernels
-    hipLaunchKernelGGL((h.ns_dtype == MO_BF16 ? bf : f32), dim3(grid_for(items)), dim3(G8_THREADS), 0, s,
-                       ws, first, xt_cur);
+    const bool bf16 = h.ns_dtype == MO_BF16;
+    const uint32_t threads = bf16 ? G8_THREADS : G_THREADS;
+    if (h.gemm_waves != threads / 64) return hipErrorInvalidValue;   // list built for other kernels
+    hipLaunchKernelGGL((bf16 ? bf : f32), dim3(grid_for(items)), dim3(threads), 0, s, ws, first, xt_cur);
     return hipGetLastError();
 }
 

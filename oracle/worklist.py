@@ -148,7 +148,7 @@ def build(descs: Sequence[dict], hp: dict) -> bytes:
         return [queues[x][j] if j < len(queues[x]) else (PAD, 0, 0, 0)
                 for j in range(longest) for x in range(8)]
 
-    waves = hp.get("gemm_waves", 8)
+    waves = 8 if hp["ns_dtype"] == 1 else 4   # bf16 lists: 8-wavefront kernels
     max_split = 2 if waves == 8 else 4
     gram = dispatch(ordered(lambda r: upper(r) * r["n_pad"]), True, True)
     poly = dispatch(ordered(lambda r: upper(r) * r["m_pad"]), True, False)

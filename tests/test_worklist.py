@@ -99,16 +99,18 @@ def test_dispatch_lists_cover_every_tile_once(key):
 
 
 def test_underfilled_launch_uses_narrow_tiles():
-    """A bucket with few tiles per XCD queue splits them into half-width tiles
-    when the halves still fit the XCD's 32 CUs (the 8-wavefront kernels have
-    no quarter width).  In the decoder-layer bucket the Update queues (98
-    tiles each) split only the 2 tiles of their last round, the Poly queues
-    (31-32 tiles) none, and the Gram queues that the K-length balance left
-    short (the long-K tiles) split theirs."""
+    """A bucket with few tiles per XCD queue splits them, into quarter widths
+    when the parts still fit the XCD's 32 CUs and the list is built for the
+    fp32 (4-wavefront) kernels, into half widths for the bf16 (8-wavefront)
+    kernels, which have no quarter width.  The ragged case runs fp32.  In the
+    bf16 decoder-layer bucket the Update queues (98 tiles each) split only the
+    2 tiles of their last round, the Poly queues (31-32 tiles) none, and the
+    Gram queues that the K-length balance left short (the long-K tiles) split
+    theirs."""
     descs, hp = CASES["ragged_not_tile_multiple"]
     _, lists = _parse(c_build(descs, hp)[0])
     for items in lists:
-        assert {nb for m, _, _, nb in items if m != 0xFFFFFFFF} == {2}
+        assert {nb for m, _, _, nb in items if m != 0xFFFFFFFF} == {1}
     descs, hp = CASES["decoder_layer_h2048"]
     _, lists = _parse(c_build(descs, hp)[0])
     upd = [nb for m, _, _, nb in lists[2] if m != 0xFFFFFFFF]
