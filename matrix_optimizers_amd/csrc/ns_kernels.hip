@@ -34,6 +34,34 @@ namespace {
 
 constexpr int MOM_THREADS = 256;
 
+// Streaming (non-temporal) 16-byte loads: G and M are read once per step.
+// Stores stay ordinary: the transposed tile is written in 16-byte pieces of
+// 128-byte rows, which L2 merges before they reach HBM (non-temporal stores
+// measured 10-14 % slower).
+MO_DEV u32x4 ld_nt(const void* p) { return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)); }
+MO_DEV void st_nt(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
+MO_DEV void unpack_bf16x8(const u32x4& raw, f32x8& o) {
+    const bf16x8 b = __builtin_bit_cast(bf16x8, raw);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o.v[e] = (float)b[e];
+}
+MO_DEV void unpack_f32x8(const u32x4& a, const u32x4& b, f32x8& o) {
+    const f32x4 fa = __builtin_bit_cast(f32x4, a), fb = __builtin_bit_cast(f32x4, b);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { o.v[e] = fa[e]; o.v[4 + e] = fb[e]; }
+}
+template <typename T> MO_DEV void st8_nt(T* p, const f32x8& v);
+template <> MO_DEV void st8_nt<bf16_t>(bf16_t* p, const f32x8& v) {
+    bf16x8 b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) b[e] = (bf16_t)v.v[e];
+    st_nt(p, __builtin_bit_cast(u32x4, b));
+}
+template <> MO_DEV void st8_nt<float>(float* p, const f32x8& v) {
+    st_nt(p, __builtin_bit_cast(u32x4, f32x4{v.v[0], v.v[1], v.v[2], v.v[3]}));
+    st_nt(p + 4, __builtin_bit_cast(u32x4, f32x4{v.v[4], v.v[5], v.v[6], v.v[7]}));
+}
+
 template <typename XT>
 __global__ __launch_bounds__(MOM_THREADS) void momentum_kernel(uint8_t* ws, float beta,
                                                                int nesterov) {
@@ -65,48 +93,61 @@ __global__ __launch_bounds__(MOM_THREADS) void momentum_kernel(uint8_t* ws, floa
     const bool mvec = ((mt.M | uint64_t(mt.ld_m * 4)) & 15) == 0;
     const float omb = 1.0f - beta;
 
+    // Thread q of the tile owns row q / 8, columns 8 (q % 8) .. + 7, for q =
+    // thread and thread + 256.  Whole 8-column chunks of 16-byte-aligned
+    // rows go through streaming vector loads, all issued before any store;
+    // the matrix's edge goes element by element (zeros outside it).
+    f32x8 g[2], mm[2];
+    bool fast[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int q = threadIdx.x + MOM_THREADS * i;
+        const int64_t row = R0 + (q >> 3), col0 = C0 + (q & 7) * 8;
+        fast[i] = row < rows && col0 + 8 <= cols && gvec && mvec;
+        if (fast[i]) {
+            const float* mp = M + row * mt.ld_m + col0;
+            const u32x4 m0 = ld_nt(mp), m1 = ld_nt(mp + 4);
+            if (gbf) {
+                unpack_bf16x8(ld_nt(reinterpret_cast<const bf16_t*>(G) + row * mt.ld_g + col0), g[i]);
+            } else {
+                const float* gp = reinterpret_cast<const float*>(G) + row * mt.ld_g + col0;
+                unpack_f32x8(ld_nt(gp), ld_nt(gp + 4), g[i]);
+            }
+            unpack_f32x8(m0, m1, mm[i]);
+        } else {
+            const bool inrow = row < rows;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const bool in = inrow && col0 + e < cols;
+                g[i].v[e] = in ? load_elem(G, row * mt.ld_g + col0 + e, gbf) : 0.f;
+                mm[i].v[e] = in ? M[row * mt.ld_m + col0 + e] : 0.f;
+            }
+        }
+    }
     float sq = 0.f;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int q = threadIdx.x + MOM_THREADS * i;
         const int r = q >> 3, cc = q & 7;
         const int64_t row = R0 + r, col0 = C0 + cc * 8;
-        f32x8 g, mm, u;
-        const bool inrow = row < rows;
-        const bool full = inrow && col0 + 8 <= cols;
-        if (full && gvec) {
-            if (gbf) load8(reinterpret_cast<const bf16_t*>(G) + row * mt.ld_g + col0, g);
-            else load8(reinterpret_cast<const float*>(G) + row * mt.ld_g + col0, g);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                g.v[e] = (inrow && col0 + e < cols) ? load_elem(G, row * mt.ld_g + col0 + e, gbf) : 0.f;
-        }
-        if (full && mvec) {
-            load8(M + row * mt.ld_m + col0, mm);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                mm.v[e] = (inrow && col0 + e < cols) ? M[row * mt.ld_m + col0 + e] : 0.f;
-        }
-        f32x8 mn;
+        f32x8 mn, u;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float mnew = beta * mm.v[e] + omb * g.v[e];
-            const float uu = nesterov ? omb * g.v[e] + beta * mnew : mnew;
+            const float mnew = beta * mm[i].v[e] + omb * g[i].v[e];
+            const float uu = nesterov ? omb * g[i].v[e] + beta * mnew : mnew;
             mn.v[e] = mnew;
             u.v[e] = quantize<XT>(uu);          // zero outside the matrix
             sq += u.v[e] * u.v[e];
             tile[r][cc * 8 + e] = u.v[e];
         }
-        if (full && mvec) {
-            store8(M + row * mt.ld_m + col0, mn);
+        if (fast[i]) {
+            st8_nt<float>(M + row * mt.ld_m + col0, mn);
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                if (inrow && col0 + e < cols) M[row * mt.ld_m + col0 + e] = mn.v[e];
+                if (row < rows && col0 + e < cols) M[row * mt.ld_m + col0 + e] = mn.v[e];
         }
-        store8(direct + row * ld_direct + col0, u);
+        st8_nt<XT>(direct + row * ld_direct + col0, u);
     }
     __syncthreads();
 #pragma unroll
@@ -118,7 +159,7 @@ __global__ __launch_bounds__(MOM_THREADS) void momentum_kernel(uint8_t* ws, floa
         f32x8 o;
 #pragma unroll
         for (int e = 0; e < 8; ++e) o.v[e] = tile[rr * 8 + e][c];
-        store8(transp + (C0 + c) * ld_transp + R0 + rr * 8, o);
+        st8_nt<XT>(transp + (C0 + c) * ld_transp + R0 + rr * 8, o);
     }
     const float tot = block_sum<MOM_THREADS>(sq, red);
     if (threadIdx.x == 0) reinterpret_cast<float*>(ws + mt.off_partials)[t] = tot;
