@@ -639,6 +639,14 @@ def main():
                 out["roofline"]["traffic_detail"] = {
                     "read_bytes": round(tr["read_bytes"]), "write_bytes": round(tr["write_bytes"]),
                     "profile": tr["source"], "profile_avg_ms": round(tr["avg_ns"] / 1e6, 5)}
+            # executed utilisation from the committed counter summary (same sources):
+            # the matrix cores' busy share at the clock the part actually ran
+            ex = profiling.read_executed(os.path.join(ROOT, "profiles"), wl.key, f"{dom}[{hp.ns_dtype}]")
+            if ex is not None:
+                out["roofline"]["executed"] = {
+                    "mfma_busy_per_simd_cycle": ex["mfma_busy"], "shader_clock_ghz": ex["clock_ghz"],
+                    "peak_at_that_clock_TFLOPs": round(peak * ex["clock_ghz"] / 2.4, 1),
+                    "profile": ex["source"]}
         if "momentum" in per_launch:
             # momentum kernel, algorithmic bytes: read G (2 or 4) + M (4), write
             # M' (4) + X0 once in the NS dtype (2 or 4): 12 B/elem for bf16 G and

@@ -225,6 +225,7 @@ def counters_summary(pass_dirs, trace_dir, out_md, command, workload, flops_per_
              f"SQ_VALU_MFMA_BUSY_CYCLES is summed over the {SIMDS} SIMDs.", "",
              "| phase | avg (us) | MFMA instr | MFMA busy / SIMD-cycle | clock (GHz) | L2 hit | mean L1->L2 read latency (cycles) |",
              "|---|---|---|---|---|---|---|"]
+    machine = []
     for name in sorted(mean, key=lambda k: -stats.get(k, {}).get("total_ns", 0.0)):
         c = mean[name]
         if "SQ_INSTS_MFMA" not in c or c["SQ_INSTS_MFMA"] == 0:
@@ -237,9 +238,26 @@ def counters_summary(pass_dirs, trace_dir, out_md, command, workload, flops_per_
         lat = c.get("TCP_TCC_READ_REQ_LATENCY_sum", 0.0) / max(c.get("TCP_TCC_READ_REQ_sum", 0.0), 1.0)
         lines.append(f"| {name} | {avg_ns / 1e3 if avg_ns else float('nan'):.1f} | {c['SQ_INSTS_MFMA']:.4g} | "
                      f"{busy:.3f} | {clock:.2f} | {hit:.3f} | {lat:.0f} |")
+        machine.append(f"executed {workload} {name} {busy:.4f} {clock:.3f} {sources_sha256()}")
+    lines += ["", "Machine-readable (bench.py reads these lines: phase, MFMA busy share, clock in GHz):", ""]
+    lines += machine
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
     return out_md
+
+
+def read_executed(profiles_dir: str, workload: str, phase: str) -> Optional[dict]:
+    """MFMA-busy share and shader clock of one phase from a committed counter
+    summary, if it was taken on the current kernel sources."""
+    path = os.path.join(profiles_dir, f"counters_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    cur = sources_sha256()
+    for line in open(path):
+        f = line.split()
+        if len(f) == 6 and f[0] == "executed" and f[1] == workload and f[2] == phase and f[5] == cur:
+            return {"mfma_busy": float(f[3]), "clock_ghz": float(f[4]), "source": os.path.basename(path)}
+    return None
 
 
 def _main():
