@@ -334,6 +334,15 @@ def soap_jacobi_flops(m: int, sweeps: int) -> dict:
     return {"apply": apply, "etile": etile, "solve": solve, "rounds": rounds}
 
 
+def soap_jacobi_bytes(m: int, sweeps: int) -> dict:
+    """Algorithmic HBM bytes of the rotation launches on one side m: every round
+    reads and writes A (fp64, m_pad x m_pad) and E (the same), 32 m_pad^2 bytes
+    (the pair rotations D, 64 x 64 each, are small and L2-resident)."""
+    P = (m + 63) // 64
+    rounds = sweeps * (2 * P - 1)
+    return {"per_round": 32.0 * (64 * P) ** 2, "rounds": rounds}
+
+
 def soap_product_flops(rows: int, cols: int) -> float:
     """The two statistics products and the six eigenbasis products (fp32), as
     computed on the padded sides."""
