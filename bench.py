@@ -478,9 +478,9 @@ def soap_main(args):
                 f2["apply"] += f["apply"]
                 f2["etile"] += f["etile"]
         # One launch per round applies the rotations to the A tiles and the E
-        # tiles.  It is bound by memory traffic: every round reads and writes A
-        # and E in full (32 m_pad^2 bytes per decomposition still rotating), so
-        # its roofline is HBM; the fp64 rate is reported beside.
+        # tiles.  Every round reads and writes the upper blocks of A (fp64) and
+        # all of E (fp32), about 16 m_pad^2 bytes per decomposition still
+        # rotating; the roofline is HBM, and the fp64 rate is reported beside.
         tot, cnt = p2.get("so_apply", (0.0, 0))
         if cnt:
             flops = f2["apply"] + f2["etile"]
@@ -498,7 +498,7 @@ def soap_main(args):
                 "kernel": "so_jac_rotate_kernel", "bound": "hbm", "achieved": round(gbs, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                 "traffic": None if tr is None else round(tr["read_bytes"] + tr["write_bytes"]),
-                "algorithmic_per_launch": f"{nbytes / cnt:.4e} B (A and E read and written once per round, "
+                "algorithmic_per_launch": f"{nbytes / cnt:.4e} B (upper blocks of A in fp64 and E in fp32, read and written once per round, "
                                           f"mean over the {cnt} launches of a two-sweep pass, avg {tot / cnt:.3f} ms)",
                 "fp64_TFLOPs": round(flops / (tot * 1e-3) / 1e12, 3),
                 "fp64_frac": round(flops / (tot * 1e-3) / 1e12 / PEAK_F64_TFLOPS, 4)}

@@ -10,7 +10,8 @@
 #include <stdint.h>
 
 #define MO_SO_MAGIC   0x4F534F4Du  // "MOSO"
-#define MO_SO_VERSION 2u
+#define MO_SO_VERSION 3u
+#define MO_SO_ECOLS 4u     // 64-column tiles of E per rotation work item (one D_I load each)
 
 #define MO_SO_PAD    64   // padding of every side (the eigensolver's pair of 32-wide blocks)
 #define MO_SO_BLK    32   // Jacobi block width
@@ -53,8 +54,10 @@ struct mo_so_mat {
 };
 
 // One eigendecomposition (of L' or R' of matrix `mat`), side m padded to
-// m_pad = 64 P: A (fp64, m_pad x m_pad) is rotated toward diagonal form, E
-// (fp64) accumulates the rotations (rows are eigenvectors), D holds the P
+// m_pad = 64 P: A (fp64, m_pad x m_pad) is rotated toward diagonal form (the
+// statistics launch writes it whole; the rounds keep only its upper 32 x 32
+// blocks, a lower block being the transpose of its mirror), E (fp32 between
+// rounds) accumulates the rotations (rows are eigenvectors), D holds the P
 // pair rotations of the current round (fp64, 64 x 64 each, as V - I), E32 the
 // eigenvectors sorted by ascending eigenvalue (fp32), perm the sort, flag
 // one word per pair: whether its rotation of the current round is not the

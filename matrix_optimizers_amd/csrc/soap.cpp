@@ -118,7 +118,7 @@ void build_plan(const mo_soap_matrix* mats, int32_t n, const mo_soap_hparams* hp
         e.etile_begin = etile_items;
         solve_items += e.P;
         apply_items += e.P * (e.P + 1) / 2;
-        etile_items += e.P * e.P;
+        etile_items += e.P * ((e.P + MO_SO_ECOLS - 1) / MO_SO_ECOLS);
         max_rounds = std::max(max_rounds, e.rounds);
         eigs.push_back(e);
         return uint32_t(eigs.size() - 1);
@@ -188,7 +188,7 @@ void build_plan(const mo_soap_matrix* mats, int32_t n, const mo_soap_hparams* hp
     for (mo_so_eig& e : eigs) {
         const uint64_t mm = uint64_t(e.m_pad) * e.m_pad;
         e.off_A = take(mm * 8);
-        e.off_E = take(mm * 8);
+        e.off_E = take(mm * 4);
         e.off_D = take(uint64_t(e.P) * 64 * 64 * 8);
         e.off_E32 = take(mm * 4);
         e.off_perm = take(uint64_t(e.m_pad) * 4);

@@ -260,7 +260,7 @@ __global__ __launch_bounds__(SO_THREADS) void so_eig_init_kernel(uint8_t* ws, ui
     if (idx < int64_t(eg.P)) reinterpret_cast<uint32_t*>(ws + eg.off_last)[idx] = 0u;   // final-sweep flags
     if (idx >= int64_t(eg.m_pad) * eg.m_pad) return;
     const int64_t i = idx / eg.m_pad, j = idx % eg.m_pad;
-    reinterpret_cast<double*>(ws + eg.off_E)[idx] = (i == j && i < eg.m) ? 1.0 : 0.0;
+    reinterpret_cast<float*>(ws + eg.off_E)[idx] = (i == j && i < eg.m) ? 1.f : 0.f;
 }
 
 // Per row of A (one workgroup each), its sum of squares; then, in the row
@@ -340,15 +340,29 @@ __global__ __launch_bounds__(SV_THREADS) void so_jac_solve_kernel(uint8_t* ws, u
     int bp, bq;
     circle_pair(nb, int(k % uint32_t(nb - 1)), j, bp, bq);
     const double* A = reinterpret_cast<const double*>(ws + eg.off_A);
+    const int64_t ld = eg.m_pad;
     const int t = threadIdx.x;
-    for (int q = t; q < PW * PW / 2; q += SV_THREADS) {
-        const int r = q / (PW / 2), c = 2 * (q % (PW / 2));
-        const f64x2 v = *reinterpret_cast<const f64x2*>(A + pair_index(bp, bq, r) * eg.m_pad + pair_index(bp, bq, c));
-        S[r][c] = v[0];
-        S[r][c + 1] = v[1];
-        D[r][c] = 0.0;
-        D[r][c + 1] = 0.0;
+    // the four 32 x 32 blocks of the pair problem, each from where A keeps it
+    // (upper blocks only: a lower block is the transpose of its mirror)
+    for (int b = 0; b < 4; ++b) {
+        const int ho = MO_SO_BLK * (b >> 1), vo = MO_SO_BLK * (b & 1);
+        const int x = (b >> 1) ? bq : bp, y = (b & 1) ? bq : bp;
+        const bool direct = x <= y;
+        const double* src = direct ? A + int64_t(x) * MO_SO_BLK * ld + int64_t(y) * MO_SO_BLK
+                                   : A + int64_t(y) * MO_SO_BLK * ld + int64_t(x) * MO_SO_BLK;
+        for (int q = t; q < MO_SO_BLK * MO_SO_BLK / 2; q += SV_THREADS) {
+            const int i = q / (MO_SO_BLK / 2), j = 2 * (q % (MO_SO_BLK / 2));
+            const f64x2 v = *reinterpret_cast<const f64x2*>(src + i * ld + j);
+            if (direct) {
+                S[ho + i][vo + j] = v[0];
+                S[ho + i][vo + j + 1] = v[1];
+            } else {
+                S[ho + j][vo + i] = v[0];
+                S[ho + j + 1][vo + i] = v[1];
+            }
+        }
     }
+    for (int q = t; q < PW * PW; q += SV_THREADS) D[q / PW][q % PW] = 0.0;
     if (t == 0) rotated[0] = rotated[1] = 0;
     __syncthreads();
     // Already diagonal to the rotation threshold (every off-diagonal entry at or
@@ -492,15 +506,14 @@ MO_DEV int mfma_row(int x, int v) { return 32 * (threadIdx.x >> 7) + 16 * x + ((
 MO_DEV int mfma_col(int y) { return 32 * ((threadIdx.x >> 6) & 1) + 16 * y + (threadIdx.x & 15); }
 
 // One workgroup per upper 64 x 64 tile (I, J) of pairs of A in round k:
-// A' = V_I^T A V_J, mirrored below the diagonal.  With V = I + D:
-// C = X + X D_J, A' = C + D_I^T C.  A tile whose two pairs were not rotated is
-// left untouched (the products would add exact zeros).
-// One 64 x 65 fp64 buffer in LDS (33 KB, so several workgroups share a CU)
-// holds X^T, then C, then the result.  X is read once, through its mirror
-// (rows of pair J, X^T[c][r] = A[J row c][I column r]; A is kept exactly
-// symmetric off the diagonal tiles, and on them the two orientations differ
-// by rounding only); D_J and D_I come straight from the round's rotations
-// (L2).  The result is written by rows, to the tile and to its mirror.
+// A' = V_I^T A V_J.  With V = I + D: C = X + X D_J, A' = C + D_I^T C.  A tile
+// whose two pairs were not rotated is left untouched (the products would add
+// exact zeros).  A is symmetric, and the rounds keep only its upper 32 x 32
+// blocks (x <= y; a lower block is the transpose of its mirror), so each
+// block of the tile is read once and written once, in whichever orientation
+// A keeps it.  One 64 x 65 fp64 buffer in LDS (33 KB, so several workgroups
+// share a CU) holds X^T, then C, then the result; D_J and D_I come straight
+// from the round's rotations (L2).
 MO_DEV void apply_a_tile(uint8_t* ws, uint32_t k, uint32_t blk, double (*C)[PW + 1]) {
     const mo_so_header* h = so_header(ws);
     const mo_so_eig* eigs = so_eigs(ws);
@@ -526,13 +539,28 @@ MO_DEV void apply_a_tile(uint8_t* ws, uint32_t k, uint32_t blk, double (*C)[PW +
     const int t = threadIdx.x;
     const int l = t & 63, w = t >> 6;
     const int r0 = 32 * (w >> 1) + (l & 15), c0 = 32 * (w & 1) + (l & 15);
-    // X^T (rows of pair J, columns of pair I) staged in the buffer, one read of
-    // A per element; the buffer then takes C
-    for (int q = t; q < PW * PW / 2; q += SO_THREADS) {
-        const int c = q / (PW / 2), r = 2 * (q % (PW / 2));
-        const f64x2 v = *reinterpret_cast<const f64x2*>(M + pair_index(pJ, qJ, c) * ld + pair_index(pI, qI, r));
-        C[c][r] = v[0];
-        C[c][r + 1] = v[1];
+    // X^T (rows of pair J, columns of pair I) staged in the buffer, block by
+    // block of 32 x 32: block (x, y) of X is kept by A as itself when x < y,
+    // which is transposed into the buffer, and as the rows of its transpose
+    // (y, x) otherwise (on a diagonal tile, the diagonal blocks as stored).
+    // The buffer then takes C.
+    for (int b = 0; b < 4; ++b) {
+        const int ro = MO_SO_BLK * (b >> 1), co = MO_SO_BLK * (b & 1);
+        const int x = (b >> 1) ? qI : pI, y = (b & 1) ? qJ : pJ;
+        const bool trans = x < y;
+        const double* src = trans ? M + int64_t(x) * MO_SO_BLK * ld + int64_t(y) * MO_SO_BLK
+                                  : M + int64_t(y) * MO_SO_BLK * ld + int64_t(x) * MO_SO_BLK;
+        for (int q = t; q < MO_SO_BLK * MO_SO_BLK / 2; q += SO_THREADS) {
+            const int i = q / (MO_SO_BLK / 2), j = 2 * (q % (MO_SO_BLK / 2));
+            const f64x2 v = *reinterpret_cast<const f64x2*>(src + i * ld + j);
+            if (trans) {
+                C[co + j][ro + i] = v[0];
+                C[co + j + 1][ro + i] = v[1];
+            } else {
+                C[co + i][ro + j] = v[0];
+                C[co + i][ro + j + 1] = v[1];
+            }
+        }
     }
     __syncthreads();
     f64x4 acc[2][2];
@@ -599,27 +627,40 @@ MO_DEV void apply_a_tile(uint8_t* ws, uint32_t k, uint32_t blk, double (*C)[PW +
 #pragma unroll
             for (int v = 0; v < 4; ++v) C[mfma_row(x, v)][mfma_col(y)] = own[x][y][v];
     __syncthreads();
-    for (int q = t; q < PW * PW / 2; q += SO_THREADS) {
-        const int r = q / (PW / 2), c = 2 * (q % (PW / 2));
-        *reinterpret_cast<f64x2*>(M + pair_index(pI, qI, r) * ld + pair_index(pJ, qJ, c)) =
-            f64x2{C[r][c], C[r][c + 1]};
-    }
-    if (I != J) {
-        for (int q = t; q < PW * PW / 2; q += SO_THREADS) {
-            const int c = q / (PW / 2), r = 2 * (q % (PW / 2));
-            *reinterpret_cast<f64x2*>(M + pair_index(pJ, qJ, c) * ld + pair_index(pI, qI, r)) =
-                f64x2{C[r][c], C[r + 1][c]};
+    // each block of the result goes to where A keeps it: an upper block by
+    // rows, a lower one as its transpose; on a diagonal tile the lower one of
+    // the two off-diagonal blocks is the mirror of the other and is not written
+    for (int b = 0; b < 4; ++b) {
+        const int ro = MO_SO_BLK * (b >> 1), co = MO_SO_BLK * (b & 1);
+        const int x = (b >> 1) ? qI : pI, y = (b & 1) ? qJ : pJ;
+        if (x <= y) {
+            double* dst = M + int64_t(x) * MO_SO_BLK * ld + int64_t(y) * MO_SO_BLK;
+            for (int q = t; q < MO_SO_BLK * MO_SO_BLK / 2; q += SO_THREADS) {
+                const int i = q / (MO_SO_BLK / 2), j = 2 * (q % (MO_SO_BLK / 2));
+                *reinterpret_cast<f64x2*>(dst + i * ld + j) = f64x2{C[ro + i][co + j], C[ro + i][co + j + 1]};
+            }
+        } else if (I != J) {
+            double* dst = M + int64_t(y) * MO_SO_BLK * ld + int64_t(x) * MO_SO_BLK;
+            for (int q = t; q < MO_SO_BLK * MO_SO_BLK / 2; q += SO_THREADS) {
+                const int i = q / (MO_SO_BLK / 2), j = 2 * (q % (MO_SO_BLK / 2));
+                *reinterpret_cast<f64x2*>(dst + i * ld + j) = f64x2{C[ro + j][co + i], C[ro + j + 1][co + i]};
+            }
         }
     }
 }
 
-// One workgroup per 64 x 64 tile (pair I, columns 64 c ..) of the accumulated
-// eigenvectors E in round k: E' = V_I^T E = X + D_I^T X.  Only D_I sits in LDS
-// (32 KB, so several workgroups share a CU); the MFMA B operand and the old
-// values come straight from E (each element is read by the two waves that
-// share its columns, the second read mostly from L2), and the results are
-// written from registers, 16 lanes to 128 contiguous bytes.  Unrotated pairs
-// are skipped.
+// One workgroup per pair I and MO_SO_ECOLS consecutive 64-column tiles of the
+// accumulated eigenvectors E in round k: E' = V_I^T E = X + D_I^T X.  E is
+// kept in fp32 between rounds and each round's product is taken in fp64 and
+// rounded once: the rounding moves an eigenvector by a few fp32 units over a
+// whole solve and does not feed back into A, whose rounding is what the
+// eigenvectors of close eigenvalues amplify.  D_I sits in LDS (32 KB, loaded
+// once for the workgroup's tiles, so several workgroups share a CU).  Each
+// wave takes whole strips of 64 rows x 16 columns, so no wave reads what
+// another writes and the strips need no barrier; a lane's MFMA B operands
+// are the old values of its own outputs (k-step 4 x + v loads the row of
+// result register v of block x), and the next strip's loads are issued
+// before the current strip's products.  Unrotated pairs are skipped.
 MO_DEV void apply_e_tile(uint8_t* ws, uint32_t k, uint32_t blk, double (*DI)[PW]) {
     const mo_so_header* h = so_header(ws);
     const mo_so_eig* eigs = so_eigs(ws);
@@ -629,63 +670,66 @@ MO_DEV void apply_e_tile(uint8_t* ws, uint32_t k, uint32_t blk, double (*DI)[PW]
     const int nb = 2 * P;
     const int kr = int(k % uint32_t(nb - 1));
     const int item = int(blk - eg.etile_begin);
-    const int I = item / P, cc = item % P;
+    const int ngrp = (P + int(MO_SO_ECOLS) - 1) / int(MO_SO_ECOLS);
+    const int I = item / ngrp, cc0 = (item % ngrp) * int(MO_SO_ECOLS);
     if (!reinterpret_cast<const uint32_t*>(ws + eg.off_flag)[I]) return;
     int pI, qI;
     circle_pair(nb, kr, I, pI, qI);
     const double* Dall = reinterpret_cast<const double*>(ws + eg.off_D);
-    double* E = reinterpret_cast<double*>(ws + eg.off_E);
     const int64_t ld = eg.m_pad;
-    double* Ecol = E + int64_t(cc) * PW;      // row g of the tile: Ecol[g * ld + c]
     load_d(DI, Dall, I);
     __syncthreads();
-    // acc = D_I^T X with X(k, c) = E[pair row k][64 cc + c].  The old value of
-    // this lane's output (row 32 h + 16 x + l / 16 + 4 v, column c0 + 16 y),
-    // h = w / 2, is the B operand it loads at k-step 32 h + 16 x + 4 v: it is
-    // kept from there instead of being read again (the loop is unrolled, so
-    // the register it goes to is fixed; only the wave's h is tested).
     const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int hw = w >> 1;
-    const int r0 = 32 * hw + (l & 15), c0 = 32 * (w & 1) + (l & 15);
-    f64x4 acc[2][2];
-    double own[2][2][4];
+    const int nstrip = 4 * min(int(MO_SO_ECOLS), P - cc0);
+    // lane column within the strip, and the rows of the pair: row 4 kk + l / 16
+    // of the pair for k-step kk (block p for kk < 8, block q after)
+    float* Ep = reinterpret_cast<float*>(ws + eg.off_E) + (int64_t(pI) * MO_SO_BLK + (l >> 4)) * ld +
+                int64_t(cc0) * PW + (l & 15);
+    float* Eq = reinterpret_cast<float*>(ws + eg.off_E) + (int64_t(qI) * MO_SO_BLK + (l >> 4)) * ld +
+                int64_t(cc0) * PW + (l & 15);
+    float cur[16], nxt[16];
+    auto load_strip = [&](int st, float (&dst)[16]) {
 #pragma unroll
-    for (int x = 0; x < 2; ++x)
+        for (int kk = 0; kk < 16; ++kk)
+            dst[kk] = (kk < 8 ? Ep : Eq)[int64_t(4 * (kk & 7)) * ld + 16 * st];
+    };
+    if (w < nstrip) load_strip(w, cur);
+#pragma unroll 1
+    for (int st = w; st < nstrip; st += 4) {
+        // D_I is read from LDS again for every strip: kept in registers across
+        // strips it would take 128 of them and most of the CU's waves
+        asm volatile("" ::: "memory");
+        if (st + 4 < nstrip) load_strip(st + 4, nxt);
+        f64x4 acc[4];
 #pragma unroll
-        for (int y = 0; y < 2; ++y) acc[x][y] = f64x4{0.0, 0.0, 0.0, 0.0};
+        for (int x = 0; x < 4; ++x) acc[x] = f64x4{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-    for (int k0 = 0; k0 < PW; k0 += 4) {
-        const int kq = k0 + (l >> 4);
-        const double* xrow = Ecol + pair_index(pI, qI, kq) * ld;
-        double a[2], b[2];
+        for (int kk = 0; kk < 16; ++kk) {
+            const int kq = 4 * kk + (l >> 4);
+            const double b = double(cur[kk]);
 #pragma unroll
-        for (int x = 0; x < 2; ++x) a[x] = DI[kq][r0 + 16 * x];
-#pragma unroll
-        for (int y = 0; y < 2; ++y) b[y] = xrow[c0 + 16 * y];
-        if (hw == (k0 >> 5)) {
-#pragma unroll
-            for (int y = 0; y < 2; ++y) own[(k0 >> 4) & 1][y][(k0 >> 2) & 3] = b[y];
+            for (int x = 0; x < 4; ++x)
+                acc[x] = __builtin_amdgcn_mfma_f64_16x16x4f64(DI[kq][16 * x + (l & 15)], b, acc[x], 0, 0, 0);
         }
+        // block x, register v: pair row 16 x + l / 16 + 4 v, loaded at k-step 4 x + v
 #pragma unroll
-        for (int x = 0; x < 2; ++x)
-#pragma unroll
-            for (int y = 0; y < 2; ++y) acc[x][y] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[x], b[y], acc[x][y], 0, 0, 0);
-    }
-    // every wave has read every row it needs before any row is replaced
-    __syncthreads();
-#pragma unroll
-    for (int x = 0; x < 2; ++x)
-#pragma unroll
-        for (int y = 0; y < 2; ++y)
+        for (int x = 0; x < 4; ++x)
 #pragma unroll
             for (int v = 0; v < 4; ++v)
-                Ecol[pair_index(pI, qI, mfma_row(x, v)) * ld + mfma_col(y)] = own[x][y][v] + acc[x][y][v];
+                (x < 2 ? Ep : Eq)[int64_t(16 * (x & 1) + 4 * v) * ld + 16 * st] =
+                    float(double(cur[4 * x + v]) + acc[x][v]);
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) cur[kk] = nxt[kk];
+    }
 }
 
 // All rotations of round k in one launch: workgroups 0 .. n_apply_items - 1
 // take the upper tiles of A (the heavier items, dispatched first), the rest
-// the tiles of E.  Both keep one 64 x 64 fp64 tile in LDS.
-__global__ __launch_bounds__(SO_THREADS) void so_jac_rotate_kernel(uint8_t* ws, uint32_t k) {
+// the tiles of E.  Both keep one 64 x 64 fp64 tile in LDS (33 KB: four
+// workgroups per CU), and the registers are held to four waves per SIMD to
+// match.
+__global__ __launch_bounds__(SO_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
+void so_jac_rotate_kernel(uint8_t* ws, uint32_t k) {
     __shared__ __align__(16) double buf[PW * (PW + 1)];
     const uint32_t na = so_header(ws)->n_apply_items;
     if (blockIdx.x < na) apply_a_tile(ws, k, blockIdx.x, reinterpret_cast<double (*)[PW + 1]>(buf));
@@ -739,13 +783,13 @@ __global__ __launch_bounds__(SO_THREADS) void so_eig_gather_kernel(uint8_t* ws, 
     if (idx >= int64_t(eg.m_pad) * eg.m_pad) return;
     const int64_t r = idx / eg.m_pad, c = idx % eg.m_pad;
     const int* perm = reinterpret_cast<const int*>(ws + eg.off_perm);
-    const double* E = reinterpret_cast<const double*>(ws + eg.off_E);
+    const float* E = reinterpret_cast<const float*>(ws + eg.off_E);
     // the permutation is total (see the rank kernel); the row read is bounded
     // all the same
     float v = 0.f;
     if (r < eg.m) {
         const int64_t pr = perm[r];
-        v = (pr >= 0 && pr < eg.m_pad) ? float(E[pr * eg.m_pad + c]) : __builtin_nanf("");
+        v = (pr >= 0 && pr < eg.m_pad) ? E[pr * eg.m_pad + c] : __builtin_nanf("");
     }
     reinterpret_cast<float*>(ws + eg.off_E32)[idx] = v;
 }

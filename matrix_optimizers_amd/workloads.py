@@ -323,24 +323,28 @@ def soap_jacobi_flops(m: int, sweeps: int) -> dict:
     """Flops of the blocked Jacobi eigensolver on one side m as built: per round,
     every upper 64 x 64 tile pair of A takes two 64^3 products (C = X + X D_J,
     A' = C + D_I^T C) and every 64 x 64 tile of E one; the pair problems take
-    INNER (3) scalar sweeps of 63 steps over a 64 x 64 matrix, each step about
-    6 flops per element of S and of D (counted as 12 * 64^2 per step)."""
+    one scalar sweep of 63 steps over a 64 x 64 matrix, each step about 6 flops
+    per element of S and of D (counted as 12 * 64^2 per step)."""
     P = (m + 63) // 64
     rounds = sweeps * (2 * P - 1)
     t3 = 2.0 * 64 ** 3
     apply = rounds * P * (P + 1) / 2 * 2 * t3
     etile = rounds * P * P * t3
-    solve = rounds * P * 3 * 63 * 12.0 * 64 * 64
+    solve = rounds * P * 63 * 12.0 * 64 * 64
     return {"apply": apply, "etile": etile, "solve": solve, "rounds": rounds}
 
 
 def soap_jacobi_bytes(m: int, sweeps: int) -> dict:
     """Algorithmic HBM bytes of the rotation launches on one side m: every round
-    reads and writes A (fp64, m_pad x m_pad) and E (the same), 32 m_pad^2 bytes
-    (the pair rotations D, 64 x 64 each, are small and L2-resident)."""
+    reads and writes the upper 32 x 32 blocks of A (fp64, 2P (2P + 1) / 2
+    blocks) and all of E (fp32, m_pad x m_pad); the pair rotations D, 64 x 64
+    each, are small and L2-resident."""
     P = (m + 63) // 64
-    rounds = sweeps * (2 * P - 1)
-    return {"per_round": 32.0 * (64 * P) ** 2, "rounds": rounds}
+    nb = 2 * P
+    rounds = sweeps * (nb - 1)
+    a_bytes = nb * (nb + 1) / 2 * 32 * 32 * 8
+    e_bytes = (64.0 * P) ** 2 * 4
+    return {"per_round": 2 * (a_bytes + e_bytes), "rounds": rounds}
 
 
 def soap_product_flops(rows: int, cols: int) -> float:

@@ -69,11 +69,12 @@ def test_workspace_checks_and_size():
     d = [desc(100, 70)]
     hp = mo.soap_hparams()
     need = mo.soap_workspace_bytes(d, hp)
-    # per matrix four fp32 r_pad x c_pad buffers; per side two fp64 and one fp32
-    # m_pad^2 buffer, m_pad / 64 fp64 pair rotations of 64 x 64, the permutation
-    # and the final-sweep rotation flags (one word per pair slot, 256-aligned)
+    # per matrix four fp32 r_pad x c_pad buffers; per side one fp64 and two fp32
+    # m_pad^2 buffers (A; the accumulated and the sorted eigenvectors), m_pad / 64
+    # fp64 pair rotations of 64 x 64, the permutation and the final-sweep
+    # rotation flags (one word per pair slot, 256-aligned)
     mats = 4 * 128 * 128 * 4
-    side = lambda m: (2 * m * m * 8 + (m // 64) * 64 * 64 * 8 + m * m * 4 + max(m * 4, 256)
+    side = lambda m: (m * m * 8 + 2 * m * m * 4 + (m // 64) * 64 * 64 * 8 + max(m * 4, 256)
                       + max((m // 64) * 4, 256))
     assert need >= mats + 2 * side(128)
     assert need <= mats + 2 * side(128) + 4096
