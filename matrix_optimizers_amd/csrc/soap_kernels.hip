@@ -344,22 +344,26 @@ __global__ __launch_bounds__(SV_THREADS) void so_jac_solve_kernel(uint8_t* ws, u
     const int t = threadIdx.x;
     // the four 32 x 32 blocks of the pair problem, each from where A keeps it
     // (upper blocks only: a lower block is the transpose of its mirror)
+    static_assert(MO_SO_BLK * MO_SO_BLK / 2 == SV_THREADS, "one 16-byte piece per block and thread");
+    f64x2 piece[4];
+    const int pi = t / (MO_SO_BLK / 2), pj = 2 * (t % (MO_SO_BLK / 2));
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {   // all four loads first
+        const int x = (b >> 1) ? bq : bp, y = (b & 1) ? bq : bp;
+        const double* src = x <= y ? A + int64_t(x) * MO_SO_BLK * ld + int64_t(y) * MO_SO_BLK
+                                   : A + int64_t(y) * MO_SO_BLK * ld + int64_t(x) * MO_SO_BLK;
+        piece[b] = *reinterpret_cast<const f64x2*>(src + pi * ld + pj);
+    }
+#pragma unroll
     for (int b = 0; b < 4; ++b) {
         const int ho = MO_SO_BLK * (b >> 1), vo = MO_SO_BLK * (b & 1);
         const int x = (b >> 1) ? bq : bp, y = (b & 1) ? bq : bp;
-        const bool direct = x <= y;
-        const double* src = direct ? A + int64_t(x) * MO_SO_BLK * ld + int64_t(y) * MO_SO_BLK
-                                   : A + int64_t(y) * MO_SO_BLK * ld + int64_t(x) * MO_SO_BLK;
-        for (int q = t; q < MO_SO_BLK * MO_SO_BLK / 2; q += SV_THREADS) {
-            const int i = q / (MO_SO_BLK / 2), j = 2 * (q % (MO_SO_BLK / 2));
-            const f64x2 v = *reinterpret_cast<const f64x2*>(src + i * ld + j);
-            if (direct) {
-                S[ho + i][vo + j] = v[0];
-                S[ho + i][vo + j + 1] = v[1];
-            } else {
-                S[ho + j][vo + i] = v[0];
-                S[ho + j + 1][vo + i] = v[1];
-            }
+        if (x <= y) {
+            S[ho + pi][vo + pj] = piece[b][0];
+            S[ho + pi][vo + pj + 1] = piece[b][1];
+        } else {
+            S[ho + pj][vo + pi] = piece[b][0];
+            S[ho + pj + 1][vo + pi] = piece[b][1];
         }
     }
     for (int q = t; q < PW * PW; q += SV_THREADS) D[q / PW][q % PW] = 0.0;
@@ -460,14 +464,6 @@ __global__ __launch_bounds__(SV_THREADS) void so_jac_solve_kernel(uint8_t* ws, u
         reinterpret_cast<uint32_t*>(ws + eg.off_last)[j] = 1u;
 }
 
-// Loads the 64 x 64 pair rotation D_I of round k into LDS (16-byte accesses).
-MO_DEV void load_d(double (*Dl)[PW], const double* Dall, int I) {
-    const f32x4* src = reinterpret_cast<const f32x4*>(Dall + int64_t(I) * PW * PW);
-    f32x4* dst = reinterpret_cast<f32x4*>(&Dl[0][0]);
-    for (int q = threadIdx.x; q < PW * PW / 2; q += SO_THREADS) dst[q] = src[q];
-}
-
-
 // acc = L R for one 64 x 64 tile on fp64 MFMA (v_mfma_f64_16x16x4_f64), over
 // the 64-wide k: L(r, k) = Lm[r * ldl + k], or Lm[k * ldl + r] when LT; R(k, c)
 // = Rm[k * ldr + c].  Wave w owns rows 32 (w / 2) .. + 31 and columns
@@ -544,21 +540,35 @@ MO_DEV void apply_a_tile(uint8_t* ws, uint32_t k, uint32_t blk, double (*C)[PW +
     // which is transposed into the buffer, and as the rows of its transpose
     // (y, x) otherwise (on a diagonal tile, the diagonal blocks as stored).
     // The buffer then takes C.
+    // All eight loads of the thread are issued before the first LDS write.
+    constexpr int SQ = MO_SO_BLK * MO_SO_BLK / 2 / SO_THREADS;   // 16-byte pieces per block and thread
+    f64x2 stage[4][SQ];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const int x = (b >> 1) ? qI : pI, y = (b & 1) ? qJ : pJ;
+        const double* src = x < y ? M + int64_t(x) * MO_SO_BLK * ld + int64_t(y) * MO_SO_BLK
+                                  : M + int64_t(y) * MO_SO_BLK * ld + int64_t(x) * MO_SO_BLK;
+#pragma unroll
+        for (int u = 0; u < SQ; ++u) {
+            const int q = t + u * SO_THREADS;
+            const int i = q / (MO_SO_BLK / 2), j = 2 * (q % (MO_SO_BLK / 2));
+            stage[b][u] = *reinterpret_cast<const f64x2*>(src + i * ld + j);
+        }
+    }
+#pragma unroll
     for (int b = 0; b < 4; ++b) {
         const int ro = MO_SO_BLK * (b >> 1), co = MO_SO_BLK * (b & 1);
         const int x = (b >> 1) ? qI : pI, y = (b & 1) ? qJ : pJ;
-        const bool trans = x < y;
-        const double* src = trans ? M + int64_t(x) * MO_SO_BLK * ld + int64_t(y) * MO_SO_BLK
-                                  : M + int64_t(y) * MO_SO_BLK * ld + int64_t(x) * MO_SO_BLK;
-        for (int q = t; q < MO_SO_BLK * MO_SO_BLK / 2; q += SO_THREADS) {
+#pragma unroll
+        for (int u = 0; u < SQ; ++u) {
+            const int q = t + u * SO_THREADS;
             const int i = q / (MO_SO_BLK / 2), j = 2 * (q % (MO_SO_BLK / 2));
-            const f64x2 v = *reinterpret_cast<const f64x2*>(src + i * ld + j);
-            if (trans) {
-                C[co + j][ro + i] = v[0];
-                C[co + j + 1][ro + i] = v[1];
+            if (x < y) {
+                C[co + j][ro + i] = stage[b][u][0];
+                C[co + j + 1][ro + i] = stage[b][u][1];
             } else {
-                C[co + i][ro + j] = v[0];
-                C[co + i][ro + j + 1] = v[1];
+                C[co + i][ro + j] = stage[b][u][0];
+                C[co + i][ro + j + 1] = stage[b][u][1];
             }
         }
     }
@@ -650,18 +660,26 @@ MO_DEV void apply_a_tile(uint8_t* ws, uint32_t k, uint32_t blk, double (*C)[PW +
 }
 
 // One workgroup per pair I and MO_SO_ECOLS consecutive 64-column tiles of the
-// accumulated eigenvectors E in round k: E' = V_I^T E = X + D_I^T X.  E is
-// kept in fp32 between rounds and each round's product is taken in fp64 and
-// rounded once: the rounding moves an eigenvector by a few fp32 units over a
-// whole solve and does not feed back into A, whose rounding is what the
-// eigenvectors of close eigenvalues amplify.  D_I sits in LDS (32 KB, loaded
-// once for the workgroup's tiles, so several workgroups share a CU).  Each
-// wave takes whole strips of 64 rows x 16 columns, so no wave reads what
-// another writes and the strips need no barrier; a lane's MFMA B operands
-// are the old values of its own outputs (k-step 4 x + v loads the row of
-// result register v of block x), and the next strip's loads are issued
-// before the current strip's products.  Unrotated pairs are skipped.
-MO_DEV void apply_e_tile(uint8_t* ws, uint32_t k, uint32_t blk, double (*DI)[PW]) {
+// accumulated eigenvectors E in round k: E' = V_I^T E = X + D_I^T X, in fp32
+// (E is kept in fp32 between rounds; D_I is rounded to fp32 for the product
+// on v_mfma_f32_16x16x4f32, at twice the fp64 rate).  The rounding moves an
+// eigenvector by a few fp32 units over a whole solve and does not feed back
+// into A, whose rounding is what the eigenvectors of close eigenvalues
+// amplify; the rotations themselves stay fp64.  D_I sits in LDS (fp32, rows
+// padded to ED floats so that the four row groups of a read fall in separate
+// banks; loaded once for the workgroup's tiles).  Each wave takes whole
+// strips of 64 rows x 16 columns, so no wave reads what another writes and
+// the strips need no barrier; the next strip's loads are issued before the
+// current strip's products.  In this instruction lane l holds result row
+// 4 (l / 16) + v of a 16 x 16 block in register v (read off the instruction
+// with one-hot operands), so the sum over the pair's 64 rows is taken in the
+// order k-step kk, lane group g -> pair row 16 (kk / 4) + 4 g + kk % 4: the B
+// operand a lane loads at k-step 4 x + v is then the old value of its result
+// register v of block x, kept instead of read again.  Unrotated pairs are
+// skipped.
+constexpr int ED = PW + 4;   // LDS row of D_I in the E path (floats)
+
+MO_DEV void apply_e_tile(uint8_t* ws, uint32_t k, uint32_t blk, float (*DI)[ED]) {
     const mo_so_header* h = so_header(ws);
     const mo_so_eig* eigs = so_eigs(ws);
     const mo_so_eig& eg = eigs[find_rec(eigs, h->n_eigs, blk, &mo_so_eig::etile_begin)];
@@ -675,49 +693,57 @@ MO_DEV void apply_e_tile(uint8_t* ws, uint32_t k, uint32_t blk, double (*DI)[PW]
     if (!reinterpret_cast<const uint32_t*>(ws + eg.off_flag)[I]) return;
     int pI, qI;
     circle_pair(nb, kr, I, pI, qI);
-    const double* Dall = reinterpret_cast<const double*>(ws + eg.off_D);
     const int64_t ld = eg.m_pad;
-    load_d(DI, Dall, I);
+    {
+        const f64x2* src = reinterpret_cast<const f64x2*>(reinterpret_cast<const double*>(ws + eg.off_D) +
+                                                          int64_t(I) * PW * PW);
+        for (int q = threadIdx.x; q < PW * PW / 2; q += SO_THREADS) {
+            const f64x2 v = src[q];
+            const int r = q / (PW / 2), c = 2 * (q % (PW / 2));
+            DI[r][c] = float(v[0]);
+            DI[r][c + 1] = float(v[1]);
+        }
+    }
     __syncthreads();
     const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int g = l >> 4;
     const int nstrip = 4 * min(int(MO_SO_ECOLS), P - cc0);
-    // lane column within the strip, and the rows of the pair: row 4 kk + l / 16
-    // of the pair for k-step kk (block p for kk < 8, block q after)
-    float* Ep = reinterpret_cast<float*>(ws + eg.off_E) + (int64_t(pI) * MO_SO_BLK + (l >> 4)) * ld +
+    // row 4 g of block p and of block q, the lane's column of the item; k-step
+    // kk then reads block row 16 ((kk / 4) % 2) + kk % 4 further on, of block p
+    // for kk < 8 and of block q after
+    float* Ep = reinterpret_cast<float*>(ws + eg.off_E) + (int64_t(pI) * MO_SO_BLK + 4 * g) * ld +
                 int64_t(cc0) * PW + (l & 15);
-    float* Eq = reinterpret_cast<float*>(ws + eg.off_E) + (int64_t(qI) * MO_SO_BLK + (l >> 4)) * ld +
+    float* Eq = reinterpret_cast<float*>(ws + eg.off_E) + (int64_t(qI) * MO_SO_BLK + 4 * g) * ld +
                 int64_t(cc0) * PW + (l & 15);
     float cur[16], nxt[16];
     auto load_strip = [&](int st, float (&dst)[16]) {
 #pragma unroll
         for (int kk = 0; kk < 16; ++kk)
-            dst[kk] = (kk < 8 ? Ep : Eq)[int64_t(4 * (kk & 7)) * ld + 16 * st];
+            dst[kk] = (kk < 8 ? Ep : Eq)[int64_t(16 * ((kk >> 2) & 1) + (kk & 3)) * ld + 16 * st];
     };
     if (w < nstrip) load_strip(w, cur);
 #pragma unroll 1
     for (int st = w; st < nstrip; st += 4) {
         // D_I is read from LDS again for every strip: kept in registers across
-        // strips it would take 128 of them and most of the CU's waves
+        // strips it would take 64 of them and most of the CU's waves
         asm volatile("" ::: "memory");
         if (st + 4 < nstrip) load_strip(st + 4, nxt);
-        f64x4 acc[4];
+        f32x4 acc[4];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) acc[x] = f64x4{0.0, 0.0, 0.0, 0.0};
+        for (int x = 0; x < 4; ++x) acc[x] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < 16; ++kk) {
-            const int kq = 4 * kk + (l >> 4);
-            const double b = double(cur[kk]);
+            const int kq = 16 * (kk >> 2) + 4 * g + (kk & 3);
 #pragma unroll
             for (int x = 0; x < 4; ++x)
-                acc[x] = __builtin_amdgcn_mfma_f64_16x16x4f64(DI[kq][16 * x + (l & 15)], b, acc[x], 0, 0, 0);
+                acc[x] = __builtin_amdgcn_mfma_f32_16x16x4f32(DI[kq][16 * x + (l & 15)], cur[kk], acc[x], 0, 0, 0);
         }
-        // block x, register v: pair row 16 x + l / 16 + 4 v, loaded at k-step 4 x + v
+        // block x, register v: pair row 16 x + 4 g + v, loaded at k-step 4 x + v
 #pragma unroll
         for (int x = 0; x < 4; ++x)
 #pragma unroll
             for (int v = 0; v < 4; ++v)
-                (x < 2 ? Ep : Eq)[int64_t(16 * (x & 1) + 4 * v) * ld + 16 * st] =
-                    float(double(cur[4 * x + v]) + acc[x][v]);
+                (x < 2 ? Ep : Eq)[int64_t(16 * (x & 1) + v) * ld + 16 * st] = cur[4 * x + v] + acc[x][v];
 #pragma unroll
         for (int kk = 0; kk < 16; ++kk) cur[kk] = nxt[kk];
     }
@@ -731,9 +757,12 @@ MO_DEV void apply_e_tile(uint8_t* ws, uint32_t k, uint32_t blk, double (*DI)[PW]
 __global__ __launch_bounds__(SO_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
 void so_jac_rotate_kernel(uint8_t* ws, uint32_t k) {
     __shared__ __align__(16) double buf[PW * (PW + 1)];
-    const uint32_t na = so_header(ws)->n_apply_items;
-    if (blockIdx.x < na) apply_a_tile(ws, k, blockIdx.x, reinterpret_cast<double (*)[PW + 1]>(buf));
-    else apply_e_tile(ws, k, blockIdx.x - na, reinterpret_cast<double (*)[PW]>(buf));
+    const mo_so_header* h = so_header(ws);
+    const uint64_t ne = h->n_etile_items, tot = uint64_t(h->n_apply_items) + ne;
+    const uint64_t b = blockIdx.x;
+    const uint64_t e0 = b * ne / tot, e1 = (b + 1) * ne / tot;
+    if (e1 > e0) apply_e_tile(ws, k, uint32_t(e0), reinterpret_cast<float (*)[ED]>(buf));
+    else apply_a_tile(ws, k, uint32_t(b - e0), reinterpret_cast<double (*)[PW + 1]>(buf));
 }
 
 // The eigenvalues in ascending order, as a permutation: lam[i] = A[i][i] for
