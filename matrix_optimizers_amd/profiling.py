@@ -9,9 +9,9 @@ subdirectory per ``--pmc`` pass (FETCH_SIZE/, WRITE_SIZE/) of the same command;
 COPY_DIR holds the same two passes over ``bench.py --copy-calibration`` (the
 library's plain copy of a known number of bytes), which fixes the factor
 between each counter and true bytes.  The summary states the per-kernel
-durations, per-launch HBM bytes, and the SHA-256 of the kernel sources the
-counters were taken on; bench.py reports the traffic only while that hash
-still matches the sources.
+durations, per-launch HBM bytes, and the SHA-256 of the kernel sources (of the
+workload's optimizer) the counters were taken on; bench.py reports the traffic
+only while that hash still matches the sources.
 """
 from __future__ import annotations
 
@@ -25,18 +25,33 @@ from collections import defaultdict
 from typing import Dict, Optional
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-# What decides the kernels' memory traffic: the device code and the host code
-# that builds the work lists (tile order); the upload and timing helpers
-# (host_common.*) do not.
-KERNEL_SOURCES = ["csrc/ns_kernels.hip", "csrc/tail_kernels.hip", "csrc/device_common.h", "csrc/gemm_core8.h",
-                  "csrc/mo_worklist.h", "csrc/host.cpp", "csrc/gemm_core.h", "csrc/tile_dispatch.h",
-                  "csrc/shampoo_kernels.hip", "csrc/sh_worklist.h", "csrc/shampoo.cpp",
-                  "csrc/soap_kernels.hip", "csrc/so_worklist.h", "csrc/soap.cpp"]
+# What decides each optimizer's kernels and their memory traffic: the device
+# code and the host code that builds its work lists (tile order); the upload
+# and timing helpers (host_common.*) do not.  A summary is stamped with the
+# hash of its own optimizer's sources, so that a change to one optimizer's
+# kernels leaves the others' summaries standing.
+FAMILY_SOURCES = {
+    "muon": ["csrc/ns_kernels.hip", "csrc/tail_kernels.hip", "csrc/device_common.h", "csrc/mo_worklist.h",
+             "csrc/gemm_core.h", "csrc/gemm_core8.h", "csrc/tile_dispatch.h", "csrc/host.cpp"],
+    "shampoo": ["csrc/shampoo_kernels.hip", "csrc/sh_worklist.h", "csrc/shampoo.cpp", "csrc/device_common.h",
+                "csrc/mo_worklist.h", "csrc/gemm_core.h", "csrc/tile_dispatch.h"],
+    "soap": ["csrc/soap_kernels.hip", "csrc/so_worklist.h", "csrc/soap.cpp", "csrc/device_common.h",
+             "csrc/mo_worklist.h"],
+}
 
 
-def sources_sha256() -> str:
+def family_of(workload: str) -> str:
+    """The optimizer a profiled workload runs: SOAP and Shampoo workloads carry
+    the optimizer's name as a prefix, every other workload is a Muon bucket."""
+    for fam in ("soap", "shampoo"):
+        if workload.startswith(fam + "_"):
+            return fam
+    return "muon"
+
+
+def sources_sha256(family: str) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in FAMILY_SOURCES[family]:
         with open(os.path.join(HERE, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -142,7 +157,7 @@ def summarize(trace_dir, counter_dir, copy_dirs, out_md, command, workload, copi
     lines = [f"# rocprofv3 summary: {workload}", "",
              "Commands (run from the repository root on one MI355X):", "",
              "```", command, "```", "",
-             f"Kernel sources SHA-256: `{sources_sha256()}`", ""] + ([note, ""] if note else []) + [
+             f"Kernel sources SHA-256 ({family_of(workload)}): `{sources_sha256(family_of(workload))}`", ""] + ([note, ""] if note else []) + [
              f"Byte-counter calibration with the library's copy kernel ({copied_mib} MiB read + written): "
              f"FETCH_SIZE x {ff:.4g} B, WRITE_SIZE x {wf:.4g} B.", "",
              "| phase | launches | avg (us) | total (ms) | HBM read / launch (MB) | HBM write / launch (MB) |",
@@ -158,7 +173,7 @@ def summarize(trace_dir, counter_dir, copy_dirs, out_md, command, workload, copi
         rd, wr = fetch.get(name), write.get(name)
         if rd is not None and wr is not None:
             lines.append(f"traffic {workload} {name} {rd * ff:.0f} {wr * wf:.0f} {d['avg_ns']:.0f} "
-                         f"{sources_sha256()}")
+                         f"{sources_sha256(family_of(workload))}")
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
     return out_md
@@ -183,7 +198,7 @@ def trace_summary(trace_dir, out_md, command, workload, note=""):
 def read_traffic(profiles_dir: str, workload: str, phase: str) -> Optional[dict]:
     """HBM bytes per launch of `phase` measured on the current kernel sources,
     or None if no summary matches them."""
-    sha = sources_sha256()
+    sha = sources_sha256(family_of(workload))
     for f in sorted(glob.glob(os.path.join(profiles_dir, "*.md"))):
         for line in open(f):
             p = line.split()
@@ -219,7 +234,7 @@ def counters_summary(pass_dirs, trace_dir, out_md, command, workload, flops_per_
                     vals.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
     mean = {k: {c: sum(v) / len(v) for c, v in d.items()} for k, d in vals.items()}
     lines = [f"# rocprofv3 counters: {workload}", "", "Commands (run from the repository root on one MI355X):", "",
-             "```", command, "```", "", f"Kernel sources SHA-256: `{sources_sha256()}`", "",
+             "```", command, "```", "", f"Kernel sources SHA-256 ({family_of(workload)}): `{sources_sha256(family_of(workload))}`", "",
              "Per launch, averaged over the profiled launches. GRBM_GUI_ACTIVE counts GPU-busy cycles per XCD "
              f"(summed over {XCDS}); dividing by the traced duration gives the shader clock under load. "
              f"SQ_VALU_MFMA_BUSY_CYCLES is summed over the {SIMDS} SIMDs.", "",
@@ -238,7 +253,7 @@ def counters_summary(pass_dirs, trace_dir, out_md, command, workload, flops_per_
         lat = c.get("TCP_TCC_READ_REQ_LATENCY_sum", 0.0) / max(c.get("TCP_TCC_READ_REQ_sum", 0.0), 1.0)
         lines.append(f"| {name} | {avg_ns / 1e3 if avg_ns else float('nan'):.1f} | {c['SQ_INSTS_MFMA']:.4g} | "
                      f"{busy:.3f} | {clock:.2f} | {hit:.3f} | {lat:.0f} |")
-        machine.append(f"executed {workload} {name} {busy:.4f} {clock:.3f} {sources_sha256()}")
+        machine.append(f"executed {workload} {name} {busy:.4f} {clock:.3f} {sources_sha256(family_of(workload))}")
     lines += ["", "Machine-readable (bench.py reads these lines: phase, MFMA busy share, clock in GHz):", ""]
     lines += machine
     with open(out_md, "w") as f:
@@ -252,7 +267,7 @@ def read_executed(profiles_dir: str, workload: str, phase: str) -> Optional[dict
     path = os.path.join(profiles_dir, f"counters_{workload}.md")
     if not os.path.exists(path):
         return None
-    cur = sources_sha256()
+    cur = sources_sha256(family_of(workload))
     for line in open(path):
         f = line.split()
         if len(f) == 6 and f[0] == "executed" and f[1] == workload and f[2] == phase and f[5] == cur:
