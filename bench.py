@@ -455,7 +455,7 @@ def soap_main(args):
                    "sweeps": hp.sweeps, "stat_eps": hp.stat_eps, "w_dtype": wl.w_dtype,
                    "state": "warm: statistics of 10 earlier gradients, M and V drawn, t from 10",
                    "g_dtype": wl.g_dtype, "parallelism": "none (one owner's bucket)"},
-        "flops_per_step": {"jacobi_apply_f64": jac["apply"], "jacobi_etile_f64": jac["etile"],
+        "flops_per_step": {"jacobi_apply_f64": jac["apply"], "jacobi_etile_f32": jac["etile"],
                            "jacobi_solve_f64": jac["solve"], "products_f32": prod,
                            "note": "Jacobi counts are the work of every round as if no pair had converged; "
                                    "pairs converged to fp64 resolution are skipped in late sweeps"},
@@ -477,31 +477,47 @@ def soap_main(args):
                 f = wlmod.soap_jacobi_flops(m, 2)
                 f2["apply"] += f["apply"]
                 f2["etile"] += f["etile"]
-        # One launch per round applies the rotations to the A tiles and the E
-        # tiles.  Every round reads and writes the upper blocks of A (fp64) and
-        # all of E (fp32), about 16 m_pad^2 bytes per decomposition still
-        # rotating; the roofline is HBM, and the fp64 rate is reported beside.
+        # One launch per round applies the rotations: the A tiles on fp64 MFMA,
+        # the E items on fp32 MFMA.  Its roofline is the MFMA time, each product
+        # at its own peak (the flop-weighted peak below); the HBM rate of the
+        # bytes it must move (the upper blocks of A in fp64 and E in fp32, read
+        # and written once per round) is reported beside.
         tot, cnt = p2.get("so_apply", (0.0, 0))
         if cnt:
-            flops = f2["apply"] + f2["etile"]
             nbytes = 0.0
             for sp in wl.matrices:
                 for m in (sp.rows, sp.cols):
                     b = wlmod.soap_jacobi_bytes(m, 2)
                     nbytes += b["per_round"] * b["rounds"]
-            gbs = nbytes / (tot * 1e-3) / 1e9
+            t_s = tot * 1e-3
+            flops = f2["apply"] + f2["etile"]
+            t_min = f2["apply"] / (PEAK_F64_TFLOPS * 1e12) + f2["etile"] / (PEAK_F32_TFLOPS * 1e12)
+            peak = flops / t_min / 1e12
+            achieved = flops / t_s / 1e12
+            gbs = nbytes / t_s / 1e9
             # HBM bytes per launch from the committed rocprofv3 summary (a mean over
             # the whole step's launches), only if taken on the current sources
             from matrix_optimizers_amd import profiling
             tr = profiling.read_traffic(os.path.join(ROOT, "profiles"), wl.key, "so_rotate_tiles")
+            ex = profiling.read_executed(os.path.join(ROOT, "profiles"), wl.key, "so_rotate_tiles")
             out["roofline"] = {
-                "kernel": "so_jac_rotate_kernel", "bound": "hbm", "achieved": round(gbs, 1),
-                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                "kernel": "so_jac_rotate_kernel", "bound": "mfma", "achieved": round(achieved, 2),
+                "peak": round(peak, 2), "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": None if tr is None else round(tr["read_bytes"] + tr["write_bytes"]),
-                "algorithmic_per_launch": f"{nbytes / cnt:.4e} B (upper blocks of A in fp64 and E in fp32, read and written once per round, "
-                                          f"mean over the {cnt} launches of a two-sweep pass, avg {tot / cnt:.3f} ms)",
-                "fp64_TFLOPs": round(flops / (tot * 1e-3) / 1e12, 3),
-                "fp64_frac": round(flops / (tot * 1e-3) / 1e12 / PEAK_F64_TFLOPS, 4)}
+                "algorithmic_per_launch": f"{flops / cnt:.4e} flop ({f2['apply'] / cnt:.3e} fp64 for A, "
+                                          f"{f2['etile'] / cnt:.3e} fp32 for E), mean over the {cnt} launches "
+                                          f"of a two-sweep pass, avg {tot / cnt:.3f} ms",
+                "peak_note": f"flop-weighted: the A products at the fp64 peak ({PEAK_F64_TFLOPS}) and the E "
+                             f"products at the fp32 peak ({PEAK_F32_TFLOPS}) take {t_min / cnt * 1e3:.3f} ms "
+                             f"per launch",
+                "hbm_GBps": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+                "hbm_bytes_per_launch": f"{nbytes / cnt:.4e} B (upper blocks of A in fp64 and E in fp32, "
+                                        f"read and written once per round)"}
+            if ex is not None:
+                out["roofline"]["executed"] = {"mfma_busy": ex["mfma_busy"], "clock_ghz": ex["clock_ghz"],
+                                               "profile": ex["source"],
+                                               "note": "MFMA-busy share of SIMD cycles and shader clock from "
+                                                       "the counter profile, mean over a whole step"}
             if tr is not None:
                 out["roofline"]["traffic_detail"] = {
                     "read_bytes": round(tr["read_bytes"]), "write_bytes": round(tr["write_bytes"]),
