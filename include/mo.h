@@ -313,12 +313,14 @@ mo_status shampoo_owner_step(const mo_shampoo_matrix* mats, int32_t n_mats,
  *               V' = b2 V + (1 - b2) G~^2 in the eigenbasis
  *   update      N = (M~ / (1 - b1^t)) / (sqrt(V' / (1 - b2^t)) + eps);
  *               W' = (1 - lr wd) W - lr Q_L N Q_R^T
- * The eigenvectors come from a two-sided blocked Jacobi method in fp64
- * (`sweeps` sweeps of all block pairs, rotations in Rutishauser's form; an
- * off-diagonal entry at or below 2^-48 ||L'||_F (or ||R'||_F) is left
- * unrotated, which moves an eigenvector by at most that over its eigenvalue
- * gap); the
- * statistics, moments and products are fp32.  Sides are at most 16384. */
+ * The eigenvectors come from a two-sided blocked Jacobi method whose
+ * rotations and rotated matrix are fp64 (`sweeps` sweeps of all block pairs,
+ * rotations in Rutishauser's form; an off-diagonal entry at or below
+ * 2^-48 ||L'||_F (or ||R'||_F) is left unrotated, which moves an eigenvector
+ * by at most that over its eigenvalue gap); the accumulated eigenvectors are
+ * kept and updated in fp32, whose rounding moves them by a few fp32 units and
+ * does not feed back into the rotations.  The statistics, moments and
+ * products are fp32.  Sides are at most 16384. */
 
 /* One whole matrix with its SOAP state.
  *   W          rows x cols, w_dtype, row stride ld_w; updated in place
