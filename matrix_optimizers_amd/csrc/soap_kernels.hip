@@ -744,8 +744,10 @@ MO_DEV void apply_e_tile(uint8_t* ws, uint32_t k, uint32_t blk, float (*DI)[ED])
 #pragma unroll
             for (int v = 0; v < 4; ++v)
                 (x < 2 ? Ep : Eq)[int64_t(16 * (x & 1) + v) * ld + 16 * st] = cur[4 * x + v] + acc[x][v];
+        if (st + 4 < nstrip) {
 #pragma unroll
-        for (int kk = 0; kk < 16; ++kk) cur[kk] = nxt[kk];
+            for (int kk = 0; kk < 16; ++kk) cur[kk] = nxt[kk];
+        }
     }
 }
 
