@@ -206,6 +206,39 @@ def test_two_steps_carry_state(gpu):
     assert rel(L.cpu().numpy(), o2[1]) <= 1e-6
 
 
+def test_chained_steps_stay_at_the_floor(gpu):
+    """Six chained steps on a ragged shape, a fresh gradient each time: every
+    step's update stays within the bar of its own fp32 floor against the fp64
+    oracle chained on its own state, so nothing builds up across steps (the
+    eigenvectors are recomputed each step, E accumulated in fp32 within it)."""
+    import torch
+    import matrix_optimizers_amd as mo
+    st = warm_state(71, 130, 200)
+    dev = torch.device("cuda:0")
+    t = lambda x: torch.tensor(np.asarray(x, F32), device=dev).contiguous()
+    W, G, L, R, M, V = (t(st[k]) for k in ("W", "G", "L", "R", "M", "V"))
+    U = torch.empty_like(W)
+    step = mo.SoapOwnerStep([(W, G, L, R, M, V)], update_out=[U], sweeps=14, **HP)
+    ref = dict(st)
+    errs = []
+    for k in range(6):
+        if k:
+            rng = seeded(71, 3 + k)
+            ref["G"] = np.asarray(rng.normal(0, 1e-3, st["G"].shape), F32).astype(np.float64)
+            G.copy_(t(ref["G"]))
+        step(10 + k)
+        torch.cuda.synchronize()
+        o = osoap.soap_step(ref["W"], ref["G"], ref["L"], ref["R"], ref["M"], ref["V"], 10 + k, HP["lr"],
+                            HP["beta1"], HP["beta2"], HP["eps"], HP["weight_decay"])
+        floor = rel(fp32_floor(ref, 10 + k, HP), o[5])
+        err = rel(U.cpu().numpy(), o[5])
+        errs.append(err)
+        print(f"chained step {k}: update {err:.2e} (fp32 floor {floor:.2e})", flush=True)
+        assert err <= max(2e-4, 8 * floor)
+        ref = dict(W=o[0], G=ref["G"], L=o[1], R=o[2], M=o[3], V=o[4])
+    assert rel(L.cpu().numpy(), ref["L"]) <= 1e-6 and rel(R.cpu().numpy(), ref["R"]) <= 1e-6
+
+
 def test_deterministic(gpu):
     st = warm_state(61, 100, 100)
     a = run_gpu([st], 10, HP)[0]
