@@ -321,12 +321,22 @@ MO_DEV bool jacobi_rotation(double app, double aqq, double apq, double thr, doub
     return true;
 }
 
+// Entry (i, j) of a symmetric 64 x 64 matrix kept as its packed upper triangle
+// (row i holds columns i .. 63; 2080 entries).
+MO_DEV int tri(int i, int j) {
+    const int a = min(i, j), b = max(i, j);
+    return a * PW - (a * (a - 1)) / 2 + (b - a);
+}
+
 // One workgroup per (decomposition, block pair) of round k: diagonalise the
 // 64 x 64 pair problem S = A[pair][pair] by at most INNER_SWEEPS scalar cyclic
 // sweeps (it stops after a sweep without a rotation) and store its rotation as
-// D = V - I (V^T S V ~ diagonal), and whether it rotated at all.
+// D = V - I (V^T S V ~ diagonal), and whether it rotated at all.  S is kept as
+// its packed upper triangle (17 KB; with D, three workgroups fit a CU), and
+// each step updates it in place: every entry is read and written by one
+// thread only.
 __global__ __launch_bounds__(SV_THREADS) void so_jac_solve_kernel(uint8_t* ws, uint32_t k) {
-    __shared__ double S[PW][PW + 1];
+    __shared__ double S[PW * (PW + 1) / 2];
     __shared__ double D[PW][PW + 1];
     __shared__ double rs[PW / 2], rtau[PW / 2], rt[PW / 2], rapq[PW / 2];
     __shared__ int ra[PW / 2], rb[PW / 2];
@@ -356,14 +366,13 @@ __global__ __launch_bounds__(SV_THREADS) void so_jac_solve_kernel(uint8_t* ws, u
     }
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
+        if (b == 2) continue;   // the lower off-diagonal block: the transpose of block 1
         const int ho = MO_SO_BLK * (b >> 1), vo = MO_SO_BLK * (b & 1);
         const int x = (b >> 1) ? bq : bp, y = (b & 1) ? bq : bp;
-        if (x <= y) {
-            S[ho + pi][vo + pj] = piece[b][0];
-            S[ho + pi][vo + pj + 1] = piece[b][1];
-        } else {
-            S[ho + pj][vo + pi] = piece[b][0];
-            S[ho + pj + 1][vo + pi] = piece[b][1];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int r = x <= y ? ho + pi : ho + pj + e, c = x <= y ? vo + pj + e : vo + pi;
+            if (r <= c) S[tri(r, c)] = piece[b][e];
         }
     }
     for (int q = t; q < PW * PW; q += SV_THREADS) D[q / PW][q % PW] = 0.0;
@@ -376,7 +385,7 @@ __global__ __launch_bounds__(SV_THREADS) void so_jac_solve_kernel(uint8_t* ws, u
     const double thr = reinterpret_cast<const double*>(ws + eg.off_norm)[eg.m_pad];
     for (int q = t; q < PW * PW; q += SV_THREADS) {
         const int r = q / PW, c = q % PW;
-        if (r != c && fabs(S[r][c]) > thr) rotated[1] = 1;
+        if (r < c && fabs(S[tri(r, c)]) > thr) rotated[1] = 1;
     }
     __syncthreads();
     const int n_sweeps = rotated[1] ? INNER_SWEEPS : 0;
@@ -387,8 +396,8 @@ __global__ __launch_bounds__(SV_THREADS) void so_jac_solve_kernel(uint8_t* ws, u
                 int a, b;
                 circle_pair(PW, step, t, a, b);
                 double tt, s, tau;
-                const double apq = S[a][b];
-                if (jacobi_rotation(S[a][a], S[b][b], apq, thr, tt, s, tau)) rotated[sweep & 1] = 1;
+                const double apq = S[tri(a, b)];
+                if (jacobi_rotation(S[tri(a, a)], S[tri(b, b)], apq, thr, tt, s, tau)) rotated[sweep & 1] = 1;
                 ra[t] = a; rb[t] = b; rs[t] = s; rtau[t] = tau; rt[t] = tt; rapq[t] = apq;
             }
             // Clear the other parity's flag for the next sweep.  Every thread
@@ -404,7 +413,8 @@ __global__ __launch_bounds__(SV_THREADS) void so_jac_solve_kernel(uint8_t* ws, u
                 const int u = t >> 4, dv = t & 15, v = (u + 1 + dv) & 31;
                 const bool on = dv != 15 || u < 16;
                 const int au = ra[u], bu = rb[u], av = ra[v], bv = rb[v];
-                const double x00 = S[au][av], x01 = S[au][bv], x10 = S[bu][av], x11 = S[bu][bv];
+                const int i00 = tri(au, av), i01 = tri(au, bv), i10 = tri(bu, av), i11 = tri(bu, bv);
+                const double x00 = S[i00], x01 = S[i01], x10 = S[i10], x11 = S[i11];
                 const double su = rs[u], tu = rtau[u], sv = rs[v], tv = rtau[v];
                 // rows: J_u^T
                 const double y00 = x00 - su * (x10 + tu * x00), y10 = x10 + su * (x00 - tu * x10);
@@ -413,17 +423,15 @@ __global__ __launch_bounds__(SV_THREADS) void so_jac_solve_kernel(uint8_t* ws, u
                 const double z00 = y00 - sv * (y01 + tv * y00), z01 = y01 + sv * (y00 - tv * y01);
                 const double z10 = y10 - sv * (y11 + tv * y10), z11 = y11 + sv * (y10 - tv * y11);
                 if (on) {
-                    S[au][av] = z00; S[au][bv] = z01; S[bu][av] = z10; S[bu][bv] = z11;
-                    S[av][au] = z00; S[bv][au] = z01; S[av][bu] = z10; S[bv][bu] = z11;
+                    S[i00] = z00; S[i01] = z01; S[i10] = z10; S[i11] = z11;
                 }
                 // the diagonal blocks: the rotated 2 x 2 problem itself
                 if (t < PW / 2 && rs[t] != 0.0) {   // not rotated: S[a][b] stays
                     const int a2 = ra[t], b2 = rb[t];
                     const double tt = rt[t], apq = rapq[t];
-                    S[a2][a2] -= tt * apq;
-                    S[b2][b2] += tt * apq;
-                    S[a2][b2] = 0.0;
-                    S[b2][a2] = 0.0;
+                    S[tri(a2, a2)] -= tt * apq;
+                    S[tri(b2, b2)] += tt * apq;
+                    S[tri(a2, b2)] = 0.0;
                 }
             }
             // D <- D J + (J - I): thread t takes pair u = t % 32 in rows t / 32 + 16 i
