@@ -5,7 +5,7 @@
 // whole matrices it owns, with no collective.  Per matrix (the readings are
 // stated with the C entry point):
 //   L' = L + G G^T,  R' = R + G^T G                      fp32 statistics
-//   Q_L, Q_R = eigenvectors of L', R', ascending          fp64 blocked Jacobi
+//   Q_L, Q_R = eigenvectors of L', R', ascending          blocked Jacobi (fp64 A)
 //   M' = b1 M + (1 - b1) G
 //   G~ = Q_L^T G Q_R,  M~ = Q_L^T M' Q_R                  fp32 products
 //   V' = b2 V + (1 - b2) G~^2
@@ -21,9 +21,11 @@
 // Every rotation is applied in Rutishauser's form (the new value is the old
 // one plus a correction proportional to sin), and the pair rotations are kept
 // as V - I, so rounding scales with the correction, not with the matrix.  The
-// arithmetic is fp64: an fp32 version of the same scheme builds up a backward
-// error of a few hundred units over its rounds, which the eigenvectors of
-// closely spaced eigenvalues turn into large angle errors.
+// rotations and the rotated matrix A are fp64: an fp32 A builds up a backward
+// error of a few hundred units over the rounds, which the eigenvectors of
+// closely spaced eigenvalues turn into large angle errors.  The accumulated
+// eigenvectors E are fp32 (their rounding does not feed back into A; see the
+// E path).
 #include "device_common.h"
 #include "so_worklist.h"
 #include "mo_kernels.h"
@@ -472,40 +474,13 @@ __global__ __launch_bounds__(SV_THREADS) void so_jac_solve_kernel(uint8_t* ws, u
         reinterpret_cast<uint32_t*>(ws + eg.off_last)[j] = 1u;
 }
 
-// acc = L R for one 64 x 64 tile on fp64 MFMA (v_mfma_f64_16x16x4_f64), over
-// the 64-wide k: L(r, k) = Lm[r * ldl + k], or Lm[k * ldl + r] when LT; R(k, c)
-// = Rm[k * ldr + c].  Wave w owns rows 32 (w / 2) .. + 31 and columns
-// 32 (w % 2) .. + 31 as 2 x 2 blocks of 16 x 16.  Per instruction, lane l
-// supplies A(l % 16, l / 16) and B(l / 16, l % 16) of the 16 x 4 and 4 x 16
-// operands and holds results (l / 16 + 4 v, l % 16) in its registers v = 0..3
-// (the layout read off the instruction with one-hot operands).
-template <bool LT>
-MO_DEV void mfma_tile(const double* Lm, int ldl, const double* Rm, int ldr, f64x4 (&acc)[2][2]) {
-    const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int r0 = 32 * (w >> 1) + (l & 15), c0 = 32 * (w & 1) + (l & 15);
-#pragma unroll
-    for (int x = 0; x < 2; ++x)
-#pragma unroll
-        for (int y = 0; y < 2; ++y) acc[x][y] = f64x4{0.0, 0.0, 0.0, 0.0};
-#pragma unroll 4
-    for (int k0 = 0; k0 < PW; k0 += 4) {
-        const int kq = k0 + (l >> 4);
-        double a[2], b[2];
-#pragma unroll
-        for (int x = 0; x < 2; ++x) {
-            const int r = r0 + 16 * x;
-            a[x] = LT ? Lm[kq * ldl + r] : Lm[r * ldl + kq];
-        }
-#pragma unroll
-        for (int y = 0; y < 2; ++y) b[y] = Rm[kq * ldr + c0 + 16 * y];
-#pragma unroll
-        for (int x = 0; x < 2; ++x)
-#pragma unroll
-            for (int y = 0; y < 2; ++y) acc[x][y] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[x], b[y], acc[x][y], 0, 0, 0);
-    }
-}
-
-// Tile row and column of result register v of block (x, y) in this lane.
+// The A path's products on fp64 MFMA (v_mfma_f64_16x16x4_f64): wave w owns
+// rows 32 (w / 2) .. + 31 and columns 32 (w % 2) .. + 31 of the 64 x 64 tile
+// as 2 x 2 blocks of 16 x 16, over 16 k-steps of 4.  Per instruction, lane l
+// supplies A(l % 16, l / 16) and B(l / 16, l % 16) and holds results
+// (l / 16 + 4 v, l % 16) in its registers v = 0..3 (the layout read off the
+// instruction with one-hot operands).  Tile row and column of result register
+// v of block (x, y) in this lane:
 MO_DEV int mfma_row(int x, int v) { return 32 * (threadIdx.x >> 7) + 16 * x + ((threadIdx.x & 63) >> 4) + 4 * v; }
 MO_DEV int mfma_col(int y) { return 32 * ((threadIdx.x >> 6) & 1) + 16 * y + (threadIdx.x & 15); }
 
@@ -670,10 +645,11 @@ MO_DEV void apply_a_tile(uint8_t* ws, uint32_t k, uint32_t blk, double (*C)[PW +
 // One workgroup per pair I and MO_SO_ECOLS consecutive 64-column tiles of the
 // accumulated eigenvectors E in round k: E' = V_I^T E = X + D_I^T X, in fp32
 // (E is kept in fp32 between rounds; D_I is rounded to fp32 for the product
-// on v_mfma_f32_16x16x4f32, at twice the fp64 rate).  The rounding moves an
-// eigenvector by a few fp32 units over a whole solve and does not feed back
-// into A, whose rounding is what the eigenvectors of close eigenvalues
-// amplify; the rotations themselves stay fp64.  D_I sits in LDS (fp32, rows
+// on v_mfma_f32_16x16x4f32, at twice the fp64 rate).  Each round's rounding
+// moves an eigenvector by about an fp32 unit, a random walk of a few 1e-6
+// over the longest solves, and none of it feeds back into A, whose rounding
+// is what the eigenvectors of close eigenvalues amplify; the rotations
+// themselves stay fp64.  D_I sits in LDS (fp32, rows
 // padded to ED floats so that the four row groups of a read fall in separate
 // banks; loaded once for the workgroup's tiles).  Each wave takes whole
 // strips of 64 rows x 16 columns, so no wave reads what another writes and
@@ -759,11 +735,12 @@ MO_DEV void apply_e_tile(uint8_t* ws, uint32_t k, uint32_t blk, float (*DI)[ED])
     }
 }
 
-// All rotations of round k in one launch: workgroups 0 .. n_apply_items - 1
-// take the upper tiles of A (the heavier items, dispatched first), the rest
-// the tiles of E.  Both keep one 64 x 64 fp64 tile in LDS (33 KB: four
-// workgroups per CU), and the registers are held to four waves per SIMD to
-// match.
+// All rotations of round k in one launch: the upper tiles of A and the E
+// items, interleaved in block order in proportion to their counts, so that
+// the fp64-MFMA-heavy A tiles and the memory-heavy E items share the CUs.
+// The A path keeps one 64 x 64 fp64 tile in LDS (33 KB: four workgroups per
+// CU), the E path an fp32 pair rotation (17 KB), and the registers are held
+// to four waves per SIMD to match.
 __global__ __launch_bounds__(SO_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
 void so_jac_rotate_kernel(uint8_t* ws, uint32_t k) {
     __shared__ __align__(16) double buf[PW * (PW + 1)];
