@@ -355,7 +355,7 @@ typedef struct mo_soap_hparams {
 
 /* Bytes of device workspace soap_owner_step needs: per matrix four fp32
  * buffers of r_pad x c_pad; per side of size m three m_pad x m_pad buffers
- * (two fp64, one fp32) and m_pad / 64 fp64 pair rotations of 64 x 64
+ * (one fp64, two fp32) and m_pad / 64 fp64 pair rotations of 64 x 64
  * (x_pad = x rounded up to 64); plus the work list and 256 bytes of slack. */
 mo_status soap_workspace_bytes(const mo_soap_matrix* mats, int32_t n_mats,
                                const mo_soap_hparams* hp, size_t* bytes);
