@@ -523,6 +523,39 @@ def soap_main(args):
                     "read_bytes": round(tr["read_bytes"]), "write_bytes": round(tr["write_bytes"]),
                     "profile": tr["source"], "profile_avg_ms": round(tr["avg_ns"] / 1e6, 5),
                     "note": "mean over the launches of a whole step, converged late sweeps included"}
+    if not args.profile_only:
+        # The same bucket with the eigensolver warm-started from the previous
+        # step's bases (warm_start=1 from the second call on): one untimed cold
+        # call, then the timed steps, each warm.  Every step draws a fresh
+        # gradient (on the device, inside the timed step), as in training: with
+        # one gradient repeated, successive statistics would differ by the same
+        # G G^T and the bases would barely move.
+        wstep = mo.SoapOwnerStep(mats, lr=hp.lr, beta1=hp.beta1, beta2=hp.beta2, eps=hp.eps,
+                                 weight_decay=hp.weight_decay, sweeps=hp.sweeps, warm_start=True)
+        wcount = {"t": counter["t"]}
+        wgen = torch.Generator(device=dev)
+        wgen.manual_seed(wl.seed + 4242)
+
+        def wone():
+            wcount["t"] += 1
+            for m in mats:
+                m[1].copy_(torch.randn(m[1].shape, device=dev, generator=wgen) * wl.g_std)
+            wstep(wcount["t"])
+        wone()
+        torch.cuda.synchronize()
+        wms = timed_steps(wone, args.steps)
+        print(f"[bench] warm start: {wms:.3f} ms/step", file=sys.stderr, flush=True)
+        warm = {"ms_per_step": round(wms, 3),
+                "note": "eigensolver started from the previous step's eigenbases (warm_start=1), the same "
+                        "eigendecomposition by fewer rotating sweeps; a fresh gradient each step (drawn on "
+                        "the device inside the timed step); state carried on from the steps above"}
+        if not args.no_phase_timing:
+            wprof, _ = event_timed_steps(wone, args.steps)
+            warm["phases"] = {name: round(tot / args.steps, 3) for name, (tot, cnt) in wprof.items()
+                              if cnt and name in ("so_warm", "so_solve", "so_apply", "so_products")}
+            warm["phases_unit"] = "ms per step"
+        warm["rotating_pairs_after"] = wstep.rotating_pairs()
+        out["warm_start"] = warm
     if not args.no_cpu_baseline and not args.profile_only:
         print("[bench] cpu_baseline (fp64 oracle on host)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = soap_cpu_baseline(wl)

@@ -208,7 +208,8 @@ const char* mo_status_string(mo_status status);
 #define MO_PHASE_SO_APPLY   18  /* SOAP: one round's rotations applied to A (both sides) and E */
 #define MO_PHASE_SO_SORT    19  /* SOAP: E = I, eigenvalue sort, sorted fp32 eigenvectors */
 #define MO_PHASE_SO_PRODUCTS 20 /* SOAP: the six eigenbasis products, V', N and W written */
-#define MO_PHASE_COUNT    21
+#define MO_PHASE_SO_WARM    21  /* SOAP: a warm start's four products per eigendecomposition */
+#define MO_PHASE_COUNT    22
 
 /* Enable (1) or disable (0) per-launch timing on the calling thread.  While
  * enabled, every kernel launch is bracketed by HIP events on its own stream;
@@ -348,9 +349,19 @@ typedef struct mo_soap_matrix {
 
 /* Adam hyperparameters, the step number t (>= 1) of the bias corrections, and
  * the number of outer Jacobi sweeps (1 .. 100). */
+/* warm_start: 0, the eigensolver starts from the identity (each step on its
+ * own); 1, it starts from the eigenbases the previous step of this bucket
+ * left in this workspace.  The caller guarantees that such a step ran, with
+ * the same bucket and workspace, and that nothing else used the workspace
+ * since (the reusable step objects of the binding pass 1 from their second
+ * call on).  The previous bases are made orthonormal again by one
+ * Newton-Schulz polar step, the new statistics are rotated into them, and
+ * the sweeps start from that nearly diagonal matrix: the result is the same
+ * eigendecomposition, to the sweeps' convergence, and fewer of the sweeps
+ * still rotate. */
 typedef struct mo_soap_hparams {
     float   lr, beta1, beta2, eps, weight_decay;
-    int32_t step, sweeps;
+    int32_t step, sweeps, warm_start;
 } mo_soap_hparams;
 
 /* Bytes of device workspace soap_owner_step needs: per matrix four fp32
@@ -367,7 +378,8 @@ mo_status soap_workspace_bytes(const mo_soap_matrix* mats, int32_t n_mats,
  * a few launches per matrix.  Workspace, stream and error conventions as
  * muon_owner_step: MO_ERR_INVALID_ARG (null pointer with numel > 0, negative
  * size, a stride below its row length, step < 1, sweeps outside 1 .. 100,
- * non-finite lr, betas, eps or weight decay, betas outside [0, 1), eps < 0),
+ * warm_start not 0 or 1, non-finite lr, betas, eps or weight decay, betas
+ * outside [0, 1), eps < 0),
  * MO_ERR_UNSUPPORTED (dtype not MO_F32/MO_BF16, a side longer than 16384, more
  * than 2^30 rotation tiles of 64 x 64 over the bucket's sides),
  * MO_ERR_WORKSPACE_TOO_SMALL, MO_ERR_ALIAS (a written tensor overlaps any

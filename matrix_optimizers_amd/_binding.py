@@ -29,7 +29,7 @@ LR_ADJUST = {"original": 0, "match_rms_adamw": 1, "none": 2}
 
 PHASES = ["momentum", "norm", "gram", "poly", "update", "apply", "adamw", "copy", "update_last",
           "sh_layout", "sh_stats", "sh_rootprep", "sh_root", "sh_left", "sh_right",
-          "so_prep", "so_stats", "so_solve", "so_apply", "so_sort", "so_products"]
+          "so_prep", "so_stats", "so_solve", "so_apply", "so_sort", "so_products", "so_warm"]
 
 
 class MoError(RuntimeError):
@@ -85,7 +85,7 @@ class MoSoapHParams(ctypes.Structure):
     """mo_soap_hparams of include/mo.h."""
     _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
                 ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float), ("step", ctypes.c_int32),
-                ("sweeps", ctypes.c_int32)]
+                ("sweeps", ctypes.c_int32), ("warm_start", ctypes.c_int32)]
 
 
 _lib = None
@@ -505,9 +505,10 @@ def shampoo_owner_step(mats: Sequence[Tuple], *, update_out: Optional[Sequence] 
 # ---------------------------------------------------------------------------
 
 def soap_hparams(lr: float = 1e-3, beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,
-                 weight_decay: float = 0.0, step: int = 1, sweeps: int = 14) -> MoSoapHParams:
+                 weight_decay: float = 0.0, step: int = 1, sweeps: int = 14,
+                 warm_start: int = 0) -> MoSoapHParams:
     return MoSoapHParams(lr=lr, beta1=beta1, beta2=beta2, eps=eps, weight_decay=weight_decay,
-                         step=int(step), sweeps=int(sweeps))
+                         step=int(step), sweeps=int(sweeps), warm_start=int(warm_start))
 
 
 def soap_descriptor(rows: int, cols: int, W: int = 0, G: int = 0, L: int = 0, R: int = 0, M: int = 0,
@@ -568,13 +569,18 @@ class SoapOwnerStep:
     descriptors and workspace are prepared once; ``__call__(step)`` launches
     one step (W, L, R, M, V updated in place) on the current (or given)
     stream.  Every call uses the one workspace: calls on different streams
-    must not overlap in time."""
+    must not overlap in time.  With ``warm_start=True`` every call after the
+    first starts the eigensolver from the eigenbases the previous call left
+    in the workspace (the same eigendecomposition, by fewer rotating sweeps)."""
 
-    def __init__(self, mats: Sequence[Tuple], update_out: Optional[Sequence] = None, **hp_kwargs):
+    def __init__(self, mats: Sequence[Tuple], update_out: Optional[Sequence] = None,
+                 warm_start: bool = False, **hp_kwargs):
         torch = _torch()
         self.lib = load_library()
         self.hp_kwargs = dict(hp_kwargs)
         self.hp = soap_hparams(**hp_kwargs)
+        self.warm_start = bool(warm_start)
+        self._has_bases = False
         ups = list(update_out) if update_out is not None else [None] * len(mats)
         self.descs = [soap_tensor_descriptor(*mat, u) for mat, u in zip(mats, ups)]
         self.arr, self.n = _so_array(self.descs)
@@ -588,11 +594,14 @@ class SoapOwnerStep:
         if step is not None:
             self.hp.step = int(step)
         _record_launch_stream(self.workspace, self._alloc_stream, stream)
+        self.hp.warm_start = int(self.warm_start and self._has_bases)
+        self._has_bases = False   # until this call has returned without error
         _check(self.lib.soap_owner_step(self.arr, self.n, ctypes.byref(self.hp),
                                         ctypes.c_void_p(self.workspace.data_ptr()),
                                         self.workspace.numel(),
                                         ctypes.c_void_p(_stream_handle(stream))),
                "soap_owner_step")
+        self._has_bases = True
 
     def rotating_pairs(self, stream=None) -> List[Tuple[int, int]]:
         """(L', R') per matrix: pair slots that still rotated in the last

@@ -42,7 +42,8 @@ struct mo_so_mat;
 struct mo_so_eig;
 hipError_t mo_launch_so_prep(const mo_so_mat& mt, uint8_t* ws, uint32_t mi, hipStream_t s);
 hipError_t mo_launch_so_gemm(const mo_so_mat& mt, uint8_t* ws, uint32_t mi, int kind, hipStream_t s);
-hipError_t mo_launch_so_eig_init(const mo_so_eig& eg, uint8_t* ws, uint32_t ei, hipStream_t s);
+hipError_t mo_launch_so_eig_init(const mo_so_eig& eg, uint8_t* ws, uint32_t ei, int warm, hipStream_t s);
+hipError_t mo_launch_so_warm(const mo_so_eig& eg, uint8_t* ws, uint32_t ei, int kind, hipStream_t s);
 hipError_t mo_launch_so_norm(const mo_so_eig& eg, uint8_t* ws, uint32_t ei, hipStream_t s);
 hipError_t mo_launch_so_solve(const mo_so_header& h, uint8_t* ws, uint32_t k, hipStream_t s);
 hipError_t mo_launch_so_rotate(const mo_so_header& h, uint8_t* ws, uint32_t k, hipStream_t s);

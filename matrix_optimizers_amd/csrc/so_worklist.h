@@ -10,7 +10,7 @@
 #include <stdint.h>
 
 #define MO_SO_MAGIC   0x4F534F4Du  // "MOSO"
-#define MO_SO_VERSION 3u
+#define MO_SO_VERSION 4u
 #define MO_SO_ECOLS 4u     // 64-column tiles of E per rotation work item (one D_I load each)
 
 #define MO_SO_PAD    64   // padding of every side (the eigensolver's pair of 32-wide blocks)
@@ -27,6 +27,13 @@
 #define MO_SOK_BACK_L  6   // T = Q_L N
 #define MO_SOK_BACK_R  7   // D = T Q_R^T; W <- (1 - lr wd) W - lr D
 #define MO_SOK_COUNT   8
+
+// fp32 products of a warm start, per eigendecomposition (m_pad x m_pad; E32
+// holds the previous step's sorted eigenvectors as rows)
+#define MO_SOW_P 0   // Pm = E32 E32^T - I                  (fp32, into the A region)
+#define MO_SOW_E 1   // E0 = E32 - Pm E32 / 2: one polar Newton-Schulz step (into E)
+#define MO_SOW_T 2   // T = L' E0^T, L' the caller's statistics (into E32)
+#define MO_SOW_A 3   // A0 = E0 T, the starting matrix of the sweeps (fp64, into A)
 
 #define MO_SOF_W_BF16     0x1u
 #define MO_SOF_G_BF16     0x2u

@@ -41,6 +41,7 @@ mo_status validate_hp(const mo_soap_hparams* hp) {
     if (hp->beta1 < 0.f || hp->beta1 >= 1.f || hp->beta2 < 0.f || hp->beta2 >= 1.f || hp->eps < 0.f)
         return MO_ERR_INVALID_ARG;
     if (hp->step < 1 || hp->sweeps < 1 || hp->sweeps > kMaxSweeps) return MO_ERR_INVALID_ARG;
+    if (hp->warm_start != 0 && hp->warm_start != 1) return MO_ERR_INVALID_ARG;
     return MO_OK;
 }
 
@@ -249,8 +250,14 @@ mo_status soap_owner_step(const mo_soap_matrix* mats, int32_t n, const mo_soap_h
         if (!ok(MO_PHASE_SO_STATS, [&] { return mo_launch_so_gemm(mt, ws, i, MO_SOK_STATS_R, s); }))
             return MO_ERR_HIP;
     }
+    const int warm = hp->warm_start;
     for (uint32_t e = 0; e < h.n_eigs; ++e) {
-        if (!ok(MO_PHASE_SO_SORT, [&] { return mo_launch_so_eig_init(plan.eigs[e], ws, e, s); })) return MO_ERR_HIP;
+        if (warm)
+            for (int kind : {MO_SOW_P, MO_SOW_E, MO_SOW_T, MO_SOW_A})
+                if (!ok(MO_PHASE_SO_WARM, [&] { return mo_launch_so_warm(plan.eigs[e], ws, e, kind, s); }))
+                    return MO_ERR_HIP;
+        if (!ok(MO_PHASE_SO_SORT, [&] { return mo_launch_so_eig_init(plan.eigs[e], ws, e, warm, s); }))
+            return MO_ERR_HIP;
         if (!ok(MO_PHASE_SO_SORT, [&] { return mo_launch_so_norm(plan.eigs[e], ws, e, s); })) return MO_ERR_HIP;
     }
     for (uint32_t k = 0; k < h.max_rounds; ++k) {

@@ -100,6 +100,7 @@ struct SoProd {
     const float* B;
     int64_t b_k, b_j;
     int K;
+    int64_t a_lim = 0;   // > 0: A is the caller's unpadded a_lim x a_lim matrix (zero outside, any stride)
 };
 
 MO_DEV SoProd so_prod(uint8_t* ws, const mo_so_mat& mt, int kind) {
@@ -184,20 +185,26 @@ MO_DEV void so_epilogue(uint8_t* ws, const mo_so_mat& mt, int kind, int64_t i, i
     for (int e = 0; e < 4; ++e) T[i * cp + j + e] = v[e];
 }
 
-__global__ __launch_bounds__(SO_THREADS) void so_gemm_kernel(uint8_t* ws, uint32_t mi, int kind) {
-    __shared__ __align__(16) float As[GK][GB + 4];
-    __shared__ __align__(16) float Bs[GK][GB + 4];
-    const mo_so_mat& mt = so_mats(ws)[mi];
-    const SoProd p = so_prod(ws, mt, kind);
+// One 64 x 64 tile of C = op(A) op(B) with fp64 accumulation: K runs up to the
+// long side (16384), where a sequential fp32 sum drops the small terms that
+// follow a large partial sum, always the same way.  ep(i, j, v) receives the
+// fp64 sums of row i, columns j .. j + 3.
+template <class Ep>
+MO_DEV void so_tile(const SoProd& p, int64_t i0, int64_t j0, float (*As)[GB + 4], float (*Bs)[GB + 4],
+                    const Ep& ep) {
     const int t = threadIdx.x;
-    const int64_t i0 = int64_t(blockIdx.y) * GB, j0 = int64_t(blockIdx.x) * GB;
     const int r0 = (t / 16) * 4, c0 = (t % 16) * 4;
-    // fp64 accumulation: K runs up to the long side (16384), where a sequential
-    // fp32 sum drops the small terms that follow a large partial sum, always
-    // the same way; each result is rounded to fp32 once
     double acc[4][4] = {};
     for (int k0 = 0; k0 < p.K; k0 += GK) {
-        if (p.a_k == 1) {   // 4 consecutive k of one row i
+        if (p.a_lim > 0) {  // the caller's matrix: element loads, zero outside it
+            const int i = t / 4, kk = (t % 4) * 4;
+            const int64_t gi = i0 + i;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t gk = k0 + kk + e;
+                As[kk + e][i] = (gi < p.a_lim && gk < p.a_lim) ? p.A[gi * p.a_i + gk] : 0.f;
+            }
+        } else if (p.a_k == 1) {   // 4 consecutive k of one row i
             const int i = t / 4, kk = (t % 4) * 4;
             const f32x4 a = *reinterpret_cast<const f32x4*>(p.A + (i0 + i) * p.a_i + k0 + kk);
 #pragma unroll
@@ -230,12 +237,66 @@ __global__ __launch_bounds__(SO_THREADS) void so_gemm_kernel(uint8_t* ws, uint32
         __syncthreads();
     }
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-        const float v[4] = {float(acc[x][0]), float(acc[x][1]), float(acc[x][2]), float(acc[x][3])};
-        so_epilogue(ws, mt, kind, i0 + r0 + x, j0 + c0, v);
-    }
+    for (int x = 0; x < 4; ++x) ep(i0 + r0 + x, j0 + c0, acc[x]);
 }
 
+__global__ __launch_bounds__(SO_THREADS) void so_gemm_kernel(uint8_t* ws, uint32_t mi, int kind) {
+    __shared__ __align__(16) float As[GK][GB + 4];
+    __shared__ __align__(16) float Bs[GK][GB + 4];
+    const mo_so_mat& mt = so_mats(ws)[mi];
+    so_tile(so_prod(ws, mt, kind), int64_t(blockIdx.y) * GB, int64_t(blockIdx.x) * GB, As, Bs,
+            [&](int64_t i, int64_t j, const double* a) {
+                // each result is rounded to fp32 once
+                const float v[4] = {float(a[0]), float(a[1]), float(a[2]), float(a[3])};
+                so_epilogue(ws, mt, kind, i, j, v);
+            });
+}
+
+// The products of a warm start (MO_SOW_*), one launch each per
+// eigendecomposition ei, m_pad / 64 x m_pad / 64 tiles.  E32 holds the
+// previous step's sorted eigenvectors as rows (zero below row m); the polar
+// step E0 = E32 - (E32 E32^T - I) E32 / 2 makes them orthonormal again to
+// fp32 rounding (its error is quadratic in their deviation, a few fp32 units
+// after a step), so the deviations of successive steps do not add up; the
+// difference Pm is formed in fp64 and kept, not the product, so that its few
+// units survive the rounding.  A0 = E0 L' E0^T is then the new statistics in
+// the previous basis, nearly diagonal, and E0 the sweeps' starting E.  T is
+// rounded to fp32, so the two orientations of A0 differ by fp32 rounding;
+// the sweeps need a symmetric matrix (the lower half of a diagonal block
+// would otherwise carry that difference, far above the rotation threshold,
+// from round to round), so each upper entry is written with its mirror and
+// the lower results are dropped.
+__global__ __launch_bounds__(SO_THREADS) void so_warm_kernel(uint8_t* ws, uint32_t ei, int kind) {
+    __shared__ __align__(16) float As[GK][GB + 4];
+    __shared__ __align__(16) float Bs[GK][GB + 4];
+    const mo_so_eig& eg = so_eigs(ws)[ei];
+    const int64_t mp = eg.m_pad;
+    float* E32 = reinterpret_cast<float*>(ws + eg.off_E32);
+    float* E = reinterpret_cast<float*>(ws + eg.off_E);
+    float* Pm = reinterpret_cast<float*>(ws + eg.off_A);   // the A region, before A0 replaces it
+    double* A = reinterpret_cast<double*>(ws + eg.off_A);
+    SoProd p;
+    switch (kind) {
+    case MO_SOW_P: p = {E32, mp, 1, E32, 1, mp, int(mp)}; break;
+    case MO_SOW_E: p = {Pm, mp, 1, E32, mp, 1, int(mp)}; break;
+    case MO_SOW_T: p = {reinterpret_cast<const float*>(eg.ext), eg.ld_ext, 1, E, 1, mp, int(mp), eg.m}; break;
+    default:       p = {E, mp, 1, E32, mp, 1, int(mp)}; break;   // MO_SOW_A: E0 T (T in E32)
+    }
+    so_tile(p, int64_t(blockIdx.y) * GB, int64_t(blockIdx.x) * GB, As, Bs,
+            [&](int64_t i, int64_t j, const double* v) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int64_t o = i * mp + j + e;
+                    if (kind == MO_SOW_P) Pm[o] = float(v[e] - ((i == j + e && i < eg.m) ? 1.0 : 0.0));
+                    else if (kind == MO_SOW_E) E[o] = float(double(E32[o]) - 0.5 * v[e]);
+                    else if (kind == MO_SOW_T) E32[o] = float(v[e]);
+                    else if (i <= j + e) {   // A0 exactly symmetric: the upper value and its mirror
+                        A[o] = v[e];
+                        A[(j + e) * mp + i] = v[e];
+                    }
+                }
+            });
+}
 // ============================================================================
 // eigensolver
 // ============================================================================
@@ -255,12 +316,13 @@ MO_DEV int64_t pair_index(int p, int q, int l) {
     return l < MO_SO_BLK ? int64_t(p) * MO_SO_BLK + l : int64_t(q) * MO_SO_BLK + (l - MO_SO_BLK);
 }
 
-// E = identity on the true diagonal (padding stays zero), one thread per element.
-__global__ __launch_bounds__(SO_THREADS) void so_eig_init_kernel(uint8_t* ws, uint32_t ei) {
+// E = identity on the true diagonal (padding stays zero), one thread per
+// element, unless a warm start has put its E0 there.
+__global__ __launch_bounds__(SO_THREADS) void so_eig_init_kernel(uint8_t* ws, uint32_t ei, int warm) {
     const mo_so_eig& eg = so_eigs(ws)[ei];
     const int64_t idx = int64_t(blockIdx.x) * SO_THREADS + threadIdx.x;
     if (idx < int64_t(eg.P)) reinterpret_cast<uint32_t*>(ws + eg.off_last)[idx] = 0u;   // final-sweep flags
-    if (idx >= int64_t(eg.m_pad) * eg.m_pad) return;
+    if (warm || idx >= int64_t(eg.m_pad) * eg.m_pad) return;   // a warm start's E0 is in place
     const int64_t i = idx / eg.m_pad, j = idx % eg.m_pad;
     reinterpret_cast<float*>(ws + eg.off_E)[idx] = (i == j && i < eg.m) ? 1.f : 0.f;
 }
@@ -831,10 +893,16 @@ hipError_t mo_launch_so_gemm(const mo_so_mat& mt, uint8_t* ws, uint32_t mi, int 
     return hipGetLastError();
 }
 
-hipError_t mo_launch_so_eig_init(const mo_so_eig& eg, uint8_t* ws, uint32_t ei, hipStream_t s) {
+hipError_t mo_launch_so_eig_init(const mo_so_eig& eg, uint8_t* ws, uint32_t ei, int warm, hipStream_t s) {
     const int64_t total = int64_t(eg.m_pad) * eg.m_pad;
     hipLaunchKernelGGL(so_eig_init_kernel, dim3(unsigned((total + SO_THREADS - 1) / SO_THREADS)),
-                       dim3(SO_THREADS), 0, s, ws, ei);
+                       dim3(SO_THREADS), 0, s, ws, ei, warm);
+    return hipGetLastError();
+}
+
+hipError_t mo_launch_so_warm(const mo_so_eig& eg, uint8_t* ws, uint32_t ei, int kind, hipStream_t s) {
+    const unsigned n = unsigned(eg.m_pad / GB);
+    hipLaunchKernelGGL(so_warm_kernel, dim3(n, n), dim3(SO_THREADS), 0, s, ws, ei, kind);
     return hipGetLastError();
 }
 

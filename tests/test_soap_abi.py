@@ -37,6 +37,7 @@ def test_noop_cases_return_ok_without_hip():
 
 
 @pytest.mark.parametrize("kw", [dict(sweeps=0), dict(sweeps=101), dict(step=0), dict(step=-2),
+                                dict(warm_start=2), dict(warm_start=-1),
                                 dict(lr=math.nan), dict(weight_decay=math.inf), dict(beta1=1.0),
                                 dict(beta2=-0.1), dict(eps=-1e-8), dict(eps=math.nan)])
 def test_bad_hyperparameters(kw):

@@ -239,6 +239,79 @@ def test_chained_steps_stay_at_the_floor(gpu):
     assert rel(L.cpu().numpy(), ref["L"]) <= 1e-6 and rel(R.cpu().numpy(), ref["R"]) <= 1e-6
 
 
+def test_warm_start_chained_steps(gpu):
+    """Steps after the first start the eigensolver from the previous step's
+    bases: six chained steps on a ragged shape, every one within the bar of
+    its own fp32 floor against the fp64 oracle (which recomputes each
+    eigendecomposition from scratch), and every step converged."""
+    import torch
+    import matrix_optimizers_amd as mo
+    st = warm_state(73, 130, 200)
+    dev = torch.device("cuda:0")
+    t = lambda x: torch.tensor(np.asarray(x, F32), device=dev).contiguous()
+    W, G, L, R, M, V = (t(st[k]) for k in ("W", "G", "L", "R", "M", "V"))
+    U = torch.empty_like(W)
+    step = mo.SoapOwnerStep([(W, G, L, R, M, V)], update_out=[U], warm_start=True, sweeps=14, **HP)
+    ref = dict(st)
+    for k in range(6):
+        if k:
+            rng = seeded(73, 3 + k)
+            ref["G"] = np.asarray(rng.normal(0, 1e-3, st["G"].shape), F32).astype(np.float64)
+            G.copy_(t(ref["G"]))
+        step(10 + k)
+        assert step.hp.warm_start == (1 if k else 0)
+        torch.cuda.synchronize()
+        o = osoap.soap_step(ref["W"], ref["G"], ref["L"], ref["R"], ref["M"], ref["V"], 10 + k, HP["lr"],
+                            HP["beta1"], HP["beta2"], HP["eps"], HP["weight_decay"])
+        floor = rel(fp32_floor(ref, 10 + k, HP), o[5])
+        err = rel(U.cpu().numpy(), o[5])
+        print(f"warm chained step {k}: update {err:.2e} (fp32 floor {floor:.2e})", flush=True)
+        assert err <= max(2e-4, 8 * floor)
+        assert step.rotating_pairs() == [(0, 0)]
+        ref = dict(W=o[0], G=ref["G"], L=o[1], R=o[2], M=o[3], V=o[4])
+
+
+def test_warm_start_full_size(gpu):
+    """A 2048 x 2048 and a 5632 x 2048 matrix of the decoder-layer shapes: a
+    cold step, then a warm one on a fresh gradient, the warm step against the
+    oracle on the state the cold one left, at its fp32 floor; both converged."""
+    import torch
+    import matrix_optimizers_amd as mo
+    dev = torch.device("cuda:0")
+    mats = []
+    for i, (r, c) in enumerate(((2048, 2048), (5632, 2048))):
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(7100 + i)
+        rnd = lambda std: torch.randn((r, c), device=dev, generator=gen) * std
+        W, G = rnd(0.02), rnd(1e-3)
+        L = torch.eye(r, device=dev) * 1e-6
+        R = torch.eye(c, device=dev) * 1e-6
+        for _ in range(10):
+            Gp = rnd(1e-3)
+            L += Gp @ Gp.T
+            R += Gp.T @ Gp
+        mats.append((W, G, L, R, rnd(1e-3), rnd(1e-3) ** 2))
+    ups = [torch.empty_like(m[0]) for m in mats]
+    hp = dict(HP, weight_decay=0.01)
+    step = mo.SoapOwnerStep(mats, update_out=ups, warm_start=True, sweeps=14, **hp)
+    step(10)
+    assert step.rotating_pairs() == [(0, 0), (0, 0)]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7200)
+    for m in mats:
+        m[1].copy_(torch.randn(m[1].shape, device=dev, generator=gen) * 1e-3)
+    torch.cuda.synchronize()
+    host = [{k: m[j].double().cpu().numpy() for j, k in enumerate(("W", "G", "L", "R", "M", "V"))}
+            for m in mats]
+    step(11)
+    assert step.hp.warm_start == 1
+    assert step.rotating_pairs() == [(0, 0), (0, 0)]
+    for i, label in enumerate(("warm 2048x2048", "warm 5632x2048")):
+        out = {k: mats[i][j].double().cpu().numpy() for j, k in enumerate(("W", "G", "L", "R", "M", "V"))}
+        out["U"] = ups[i].double().cpu().numpy()
+        check(host[i], out, 11, hp, label)
+
+
 def test_deterministic(gpu):
     st = warm_state(61, 100, 100)
     a = run_gpu([st], 10, HP)[0]
