@@ -351,10 +351,11 @@ typedef struct mo_soap_matrix {
  * the number of outer Jacobi sweeps (1 .. 100). */
 /* warm_start: 0, the eigensolver starts from the identity (each step on its
  * own); 1, it starts from the eigenbases the previous step of this bucket
- * left in this workspace.  The caller guarantees that such a step ran, with
- * the same bucket and workspace, and that nothing else used the workspace
- * since (the reusable step objects of the binding pass 1 from their second
- * call on).  The previous bases are made orthonormal again by one
+ * left in this workspace (the reusable step objects of the binding pass 1
+ * from their second call on).  A side whose workspace region does not hold
+ * bases written by a step (the word the sort writes beside them) runs cold;
+ * bases that some other step of the same shapes left there are orthonormal
+ * and still a valid start, only a slower one.  The previous bases are made orthonormal again by one
  * Newton-Schulz polar step, the new statistics are rotated into them, and
  * the sweeps start from that nearly diagonal matrix: the result is the same
  * eigendecomposition, to the sweeps' convergence, and fewer of the sweeps

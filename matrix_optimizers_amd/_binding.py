@@ -634,7 +634,9 @@ def soap_owner_step(mats: Sequence[Tuple], *, update_out: Optional[Sequence] = N
     """One SOAP step over a bucket of (W, G, L, R, M, V) tensors, in place.
 
     hp_kwargs: lr, beta1, beta2, eps, weight_decay, step (t of the bias
-    corrections), sweeps (outer Jacobi sweeps).  L and R are the float32
+    corrections), sweeps (outer Jacobi sweeps), warm_start (1: start the
+    eigensolver from the bases the previous step of this bucket left in
+    ``workspace``; a workspace without them runs cold).  L and R are the float32
     statistics (started by the caller at eps I), M the first moment in the
     weight's frame and V the second moment in the eigenbasis (float32, zeros
     at the start).

@@ -10,7 +10,7 @@
 #include <stdint.h>
 
 #define MO_SO_MAGIC   0x4F534F4Du  // "MOSO"
-#define MO_SO_VERSION 4u
+#define MO_SO_VERSION 5u
 #define MO_SO_ECOLS 4u     // 64-column tiles of E per rotation work item (one D_I load each)
 
 #define MO_SO_PAD    64   // padding of every side (the eigensolver's pair of 32-wide blocks)
@@ -72,7 +72,9 @@ struct mo_so_mat {
 // rotation threshold 2^-48 ||A||_F (fp64); last one word per pair slot: set
 // when that slot's pair problem rotated in some round of the final sweep
 // (all zero: the final sweep rotated nothing, so A was diagonal to the
-// threshold, the convergence test of cyclic Jacobi).
+// threshold, the convergence test of cyclic Jacobi).  valid is one word the gather writes
+// after E32 (MO_SO_MAGIC ^ m_pad): a warm start uses E32 only when it holds it,
+// so a workspace that never held this side's bases runs cold.
 struct mo_so_eig {
     uint64_t off_A, off_E, off_D, off_E32, off_perm, off_flag, off_norm, off_last;
     uint64_t ext;                         // caller statistics (L or R), m x m fp32, row stride ld_ext
@@ -81,8 +83,9 @@ struct mo_so_eig {
     uint32_t rounds;                      // sweeps x (2P - 1)
     uint32_t solve_begin, apply_begin;    // first item of this decomposition in each grouped launch
     uint32_t etile_begin;
+    uint64_t off_valid;                   // one word: MO_SO_MAGIC ^ m_pad once the sort has written E32
 };
 
 static_assert(sizeof(mo_so_header) == 80, "header layout");
 static_assert(sizeof(mo_so_mat) == 176, "matrix record layout");
-static_assert(sizeof(mo_so_eig) == 112, "eig record layout");
+static_assert(sizeof(mo_so_eig) == 120, "eig record layout");

@@ -196,6 +196,7 @@ void build_plan(const mo_soap_matrix* mats, int32_t n, const mo_soap_hparams* hp
         e.off_flag = take(uint64_t(e.P) * 4);
         e.off_last = take(uint64_t(e.P) * 4);
         e.off_norm = take(uint64_t(e.m_pad + 1) * 8);
+        e.off_valid = take(8);
     }
     h.ws_bytes = off;
     plan->header = h;

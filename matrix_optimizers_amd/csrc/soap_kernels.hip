@@ -52,6 +52,16 @@ MO_DEV const mo_so_eig* so_eigs(const uint8_t* ws) {
     return reinterpret_cast<const mo_so_eig*>(ws + so_header(ws)->eigs_offset);
 }
 
+// What the sort's gather writes beside the sorted eigenvectors E32, and what a
+// warm start requires before it uses them: a workspace that never held this
+// side's bases (fresh memory) does not hold this word, and such a step runs
+// cold.  Any orthonormal bases would still give the right result, only by more
+// sweeps; the word keeps uninitialised memory out of the polar step.
+MO_DEV uint32_t valid_word(const mo_so_eig& eg) { return MO_SO_MAGIC ^ eg.m_pad; }
+MO_DEV bool bases_valid(const uint8_t* ws, const mo_so_eig& eg) {
+    return *reinterpret_cast<const uint32_t*>(ws + eg.off_valid) == valid_word(eg);
+}
+
 // Round k (0 .. n - 2) of the circle ordering over n (even) indices: pair j
 // (0 .. n/2 - 1).  Index 0 stays put and the others turn one place per round,
 // so that every pair meets exactly once in n - 1 rounds.
@@ -270,6 +280,7 @@ __global__ __launch_bounds__(SO_THREADS) void so_warm_kernel(uint8_t* ws, uint32
     __shared__ __align__(16) float As[GK][GB + 4];
     __shared__ __align__(16) float Bs[GK][GB + 4];
     const mo_so_eig& eg = so_eigs(ws)[ei];
+    if (!bases_valid(ws, eg)) return;   // no previous bases here: the step runs cold
     const int64_t mp = eg.m_pad;
     float* E32 = reinterpret_cast<float*>(ws + eg.off_E32);
     float* E = reinterpret_cast<float*>(ws + eg.off_E);
@@ -322,7 +333,8 @@ __global__ __launch_bounds__(SO_THREADS) void so_eig_init_kernel(uint8_t* ws, ui
     const mo_so_eig& eg = so_eigs(ws)[ei];
     const int64_t idx = int64_t(blockIdx.x) * SO_THREADS + threadIdx.x;
     if (idx < int64_t(eg.P)) reinterpret_cast<uint32_t*>(ws + eg.off_last)[idx] = 0u;   // final-sweep flags
-    if (warm || idx >= int64_t(eg.m_pad) * eg.m_pad) return;   // a warm start's E0 is in place
+    if ((warm && bases_valid(ws, eg)) || idx >= int64_t(eg.m_pad) * eg.m_pad)
+        return;   // a warm start's E0 is in place
     const int64_t i = idx / eg.m_pad, j = idx % eg.m_pad;
     reinterpret_cast<float*>(ws + eg.off_E)[idx] = (i == j && i < eg.m) ? 1.f : 0.f;
 }
@@ -870,6 +882,7 @@ __global__ __launch_bounds__(SO_THREADS) void so_eig_gather_kernel(uint8_t* ws, 
         v = (pr >= 0 && pr < eg.m_pad) ? E[pr * eg.m_pad + c] : __builtin_nanf("");
     }
     reinterpret_cast<float*>(ws + eg.off_E32)[idx] = v;
+    if (idx == 0) *reinterpret_cast<uint32_t*>(ws + eg.off_valid) = valid_word(eg);
 }
 
 }  // namespace

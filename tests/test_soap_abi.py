@@ -72,11 +72,12 @@ def test_workspace_checks_and_size():
     need = mo.soap_workspace_bytes(d, hp)
     # per matrix four fp32 r_pad x c_pad buffers; per side one fp64 and two fp32
     # m_pad^2 buffers (A; the accumulated and the sorted eigenvectors), m_pad / 64
-    # fp64 pair rotations of 64 x 64, the permutation and the final-sweep
-    # rotation flags (one word per pair slot, 256-aligned)
+    # fp64 pair rotations of 64 x 64, the permutation, the final-sweep rotation
+    # flags (one word per pair slot) and the word that marks E32 as written
+    # (each region 256-aligned)
     mats = 4 * 128 * 128 * 4
     side = lambda m: (m * m * 8 + 2 * m * m * 4 + (m // 64) * 64 * 64 * 8 + max(m * 4, 256)
-                      + max((m // 64) * 4, 256))
+                      + max((m // 64) * 4, 256) + 256)
     assert need >= mats + 2 * side(128)
     assert need <= mats + 2 * side(128) + 4096
     assert step(d, ws_bytes=need - 1) == WS_SMALL

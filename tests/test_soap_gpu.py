@@ -312,6 +312,39 @@ def test_warm_start_full_size(gpu):
         check(host[i], out, 11, hp, label)
 
 
+def test_warm_start_without_previous_bases(gpu):
+    """warm_start=1 on a workspace that never held this bucket's bases (bytes
+    of 0xFF) runs cold; on one holding another matrix's bases of the same
+    size, those orthonormal bases are a valid start too.  Both match the
+    oracle at the floor and converge."""
+    import torch
+    import matrix_optimizers_amd as mo
+    dev = torch.device("cuda:0")
+    t = lambda x: torch.tensor(np.asarray(x, F32), device=dev).contiguous()
+    st = warm_state(77, 150, 90)
+    other = warm_state(78, 150, 90)
+
+    def mats_of(s):
+        return [tuple(t(s[k]) for k in ("W", "G", "L", "R", "M", "V"))]
+    ref = mats_of(st)
+    need = mo.soap_workspace_bytes([mo.soap_tensor_descriptor(*ref[0])], mo.soap_hparams())
+    for label, ws in (("fresh workspace", None), ("another matrix's bases", "other")):
+        if ws is None:
+            ws = torch.full((need,), 255, dtype=torch.uint8, device=dev)
+        else:
+            ostep = mo.SoapOwnerStep(mats_of(other), sweeps=14, **HP)
+            ostep(10)
+            ws = ostep.workspace
+        mats = mats_of(st)
+        U = torch.empty_like(mats[0][0])
+        mo.soap_owner_step(mats, update_out=[U], workspace=ws, step=10, sweeps=14, warm_start=1, **HP)
+        torch.cuda.synchronize()
+        assert mo.soap_converged(mats, ws, step=10, sweeps=14, **HP) == [(0, 0)], label
+        out = {k: mats[0][j].double().cpu().numpy() for j, k in enumerate(("W", "G", "L", "R", "M", "V"))}
+        out["U"] = U.double().cpu().numpy()
+        check(st, out, 10, HP, f"warm start, {label}")
+
+
 def test_deterministic(gpu):
     st = warm_state(61, 100, 100)
     a = run_gpu([st], 10, HP)[0]
