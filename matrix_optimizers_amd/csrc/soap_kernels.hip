@@ -40,7 +40,6 @@ constexpr int SV_THREADS = 512;        // the pair solve: one slot of 2 x 2 bloc
 constexpr int GB = 64;                 // GEMM tile
 constexpr int GK = 16;                 // GEMM K chunk
 constexpr int PW = 2 * MO_SO_BLK;      // pair width (64)
-constexpr int INNER_SWEEPS = 1;        // scalar sweeps per pair problem
 
 MO_DEV const mo_so_header* so_header(const uint8_t* ws) {
     return reinterpret_cast<const mo_so_header*>(ws);
@@ -274,13 +273,15 @@ __global__ __launch_bounds__(SO_THREADS) void so_gemm_kernel(uint8_t* ws, uint32
 // rounded to fp32, so the two orientations of A0 differ by fp32 rounding;
 // the sweeps need a symmetric matrix (the lower half of a diagonal block
 // would otherwise carry that difference, far above the rotation threshold,
-// from round to round), so each upper entry is written with its mirror and
-// the lower results are dropped.
+// from round to round), so each upper entry is written with its mirror.  The
+// difference Pm is symmetric too (each entry and its mirror sum the same
+// products in the same order), so for both only the upper tiles run.
 __global__ __launch_bounds__(SO_THREADS) void so_warm_kernel(uint8_t* ws, uint32_t ei, int kind) {
     __shared__ __align__(16) float As[GK][GB + 4];
     __shared__ __align__(16) float Bs[GK][GB + 4];
     const mo_so_eig& eg = so_eigs(ws)[ei];
     if (!bases_valid(ws, eg)) return;   // no previous bases here: the step runs cold
+    if ((kind == MO_SOW_P || kind == MO_SOW_A) && blockIdx.y > blockIdx.x) return;   // symmetric results
     const int64_t mp = eg.m_pad;
     float* E32 = reinterpret_cast<float*>(ws + eg.off_E32);
     float* E = reinterpret_cast<float*>(ws + eg.off_E);
@@ -298,10 +299,14 @@ __global__ __launch_bounds__(SO_THREADS) void so_warm_kernel(uint8_t* ws, uint32
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int64_t o = i * mp + j + e;
-                    if (kind == MO_SOW_P) Pm[o] = float(v[e] - ((i == j + e && i < eg.m) ? 1.0 : 0.0));
-                    else if (kind == MO_SOW_E) E[o] = float(double(E32[o]) - 0.5 * v[e]);
+                    if (kind == MO_SOW_E) E[o] = float(double(E32[o]) - 0.5 * v[e]);
                     else if (kind == MO_SOW_T) E32[o] = float(v[e]);
-                    else if (i <= j + e) {   // A0 exactly symmetric: the upper value and its mirror
+                    else if (i > j + e) continue;   // a symmetric result: the upper value and its mirror
+                    else if (kind == MO_SOW_P) {
+                        const float d = float(v[e] - ((i == j + e && i < eg.m) ? 1.0 : 0.0));
+                        Pm[o] = d;
+                        Pm[(j + e) * mp + i] = d;
+                    } else {
                         A[o] = v[e];
                         A[(j + e) * mp + i] = v[e];
                     }
@@ -404,19 +409,46 @@ MO_DEV int tri(int i, int j) {
     return a * PW - (a * (a - 1)) / 2 + (b - a);
 }
 
+// Slot of 2 x 2 blocks that thread t updates in a step (a bijection of
+// 0 .. 511).  Slot s is the unordered pair {u, v} of the step's 32 rotations
+// with u = s / 16, v = u + 1 + s % 16 (mod 32); the pairs 16 apart come up
+// twice and the copy from the higher u is idle.  The circle ordering turns
+// one place per step, so pair j of step k + 1 joins one element of each of
+// two pairs of step k, the same two at every step: pairs j - 1 and j + 1 for
+// 1 <= j <= 30, 0 and 1 for j = 0, 30 and 31 for j = 31.  The block of those
+// two pairs holds the next pivot S[a'][b'], and slot solve_slot(j) of thread
+// j (0 .. 31, all in wave 0) is that block; the 29 slots this displaces from
+// threads 2 .. 31 go, in order, to the threads whose own slot was taken.
+MO_DEV int solve_slot(int t) {
+    if (t < PW / 2) return t == 0 ? 0 : t == PW / 2 - 1 ? 480 : 16 * (t - 1) + 1;
+    if (t == 480) return 31;
+    if ((t & 15) == 1 && t <= 465) {
+        const int i = (t >> 4) - 2;
+        return i <= 14 ? i + 2 : i + 3;
+    }
+    return t;
+}
+
 // One workgroup per (decomposition, block pair) of round k: diagonalise the
-// 64 x 64 pair problem S = A[pair][pair] by at most INNER_SWEEPS scalar cyclic
-// sweeps (it stops after a sweep without a rotation) and store its rotation as
-// D = V - I (V^T S V ~ diagonal), and whether it rotated at all.  S is kept as
-// its packed upper triangle (17 KB; with D, three workgroups fit a CU), and
-// each step updates it in place: every entry is read and written by one
-// thread only.
+// 64 x 64 pair problem S = A[pair][pair] by one scalar cyclic sweep (63 steps
+// of 32 disjoint rotations; none if it is already diagonal to the threshold)
+// and store its rotation as D = V - I (V^T S V ~ diagonal), and whether it
+// rotated at all.  S is kept as its packed upper triangle (17 KB; with D, three
+// workgroups fit a CU) and is updated in place: in a step every entry is read
+// and written by one thread only.  A step is one barrier: threads 0 .. 31
+// update the blocks that hold the next step's pivots, apply the two diagonal
+// updates each next pivot needs and compute the next step's rotations into the
+// other parameter buffer, while the other threads update the other blocks and
+// waves 1 .. 7 accumulate D with the current rotations.  Every rounding of the
+// updates is written out (fma, or a rounded product where one is shared), so
+// the results do not depend on which contractions the compiler chooses.
 __global__ __launch_bounds__(SV_THREADS) void so_jac_solve_kernel(uint8_t* ws, uint32_t k) {
+    constexpr int NP = PW / 2;   // rotations per step
     __shared__ double S[PW * (PW + 1) / 2];
     __shared__ double D[PW][PW + 1];
-    __shared__ double rs[PW / 2], rtau[PW / 2], rt[PW / 2], rapq[PW / 2];
-    __shared__ int ra[PW / 2], rb[PW / 2];
-    __shared__ int rotated[2];   // per sweep parity: a rotation happened
+    __shared__ double rs[2][NP], rtau[2][NP], rt[2][NP], rapq[2][NP];   // by step parity
+    __shared__ int ra[2][NP], rb[2][NP];
+    __shared__ int flags[2];   // [0] an off-diagonal entry above the threshold, [1] a rotation happened
     const mo_so_header* h = so_header(ws);
     const mo_so_eig* eigs = so_eigs(ws);
     const mo_so_eig& eg = eigs[find_rec(eigs, h->n_eigs, blockIdx.x, &mo_so_eig::solve_begin)];
@@ -452,91 +484,102 @@ __global__ __launch_bounds__(SV_THREADS) void so_jac_solve_kernel(uint8_t* ws, u
         }
     }
     for (int q = t; q < PW * PW; q += SV_THREADS) D[q / PW][q % PW] = 0.0;
-    if (t == 0) rotated[0] = rotated[1] = 0;
+    if (t == 0) flags[0] = flags[1] = 0;
     __syncthreads();
     // Already diagonal to the rotation threshold (every off-diagonal entry at or
-    // below it): no sweep would rotate, D stays zero.  The test uses
-    // flag 1, which sweep 0 first clears at its step 1, after every thread has
-    // passed step 0's barrier and so has read it here.
+    // below it): no step would rotate, D stays zero.
     const double thr = reinterpret_cast<const double*>(ws + eg.off_norm)[eg.m_pad];
     for (int q = t; q < PW * PW; q += SV_THREADS) {
         const int r = q / PW, c = q % PW;
-        if (r < c && fabs(S[tri(r, c)]) > thr) rotated[1] = 1;
+        if (r < c && fabs(S[tri(r, c)]) > thr) flags[0] = 1;
     }
     __syncthreads();
-    const int n_sweeps = rotated[1] ? INNER_SWEEPS : 0;
-    bool any = false;
-    for (int sweep = 0; sweep < n_sweeps; ++sweep) {
+    if (flags[0]) {   // uniform
+        if (t < NP) {   // the rotations of step 0
+            int a, b;
+            circle_pair(PW, 0, t, a, b);
+            double tt, s, tau;
+            const double apq = S[tri(a, b)];
+            if (jacobi_rotation(S[tri(a, a)], S[tri(b, b)], apq, thr, tt, s, tau)) flags[1] = 1;
+            ra[0][t] = a; rb[0][t] = b; rs[0][t] = s; rtau[0][t] = tau; rt[0][t] = tt; rapq[0][t] = apq;
+        }
+        __syncthreads();
+        const int sl = solve_slot(t);
+        const int u = sl >> 4, dv = sl & 15, v = (u + 1 + dv) & 31;
+        const bool on = dv != 15 || u < 16;
         for (int step = 0; step < PW - 1; ++step) {
-            if (t < PW / 2) {
-                int a, b;
-                circle_pair(PW, step, t, a, b);
-                double tt, s, tau;
-                const double apq = S[tri(a, b)];
-                if (jacobi_rotation(S[tri(a, a)], S[tri(b, b)], apq, thr, tt, s, tau)) rotated[sweep & 1] = 1;
-                ra[t] = a; rb[t] = b; rs[t] = s; rtau[t] = tau; rt[t] = tt; rapq[t] = apq;
+            const int cur = step & 1, nxt = cur ^ 1;
+            // Two-sided update of this thread's off-diagonal 2 x 2 block (rows
+            // a_u, b_u by J_u^T, then columns a_v, b_v by J_v, each in
+            // Rutishauser's form), loads issued before the arithmetic.
+            const int au = ra[cur][u], bu = rb[cur][u], av = ra[cur][v], bv = rb[cur][v];
+            const int i00 = tri(au, av), i01 = tri(au, bv), i10 = tri(bu, av), i11 = tri(bu, bv);
+            const double x00 = S[i00], x01 = S[i01], x10 = S[i10], x11 = S[i11];
+            const double su = rs[cur][u], tu = rtau[cur][u], sv = rs[cur][v], tv = rtau[cur][v];
+            const double y00 = fma(-su, fma(tu, x00, x10), x00), y10 = fma(su, fma(-tu, x10, x00), x10);
+            const double y01 = fma(-su, fma(tu, x01, x11), x01), y11 = fma(su, fma(-tu, x11, x01), x11);
+            const double z00 = fma(-sv, fma(tv, y00, y01), y00), z01 = fma(sv, fma(-tv, y01, y00), y01);
+            const double z10 = fma(-sv, fma(tv, y10, y11), y10), z11 = fma(sv, fma(-tv, y11, y10), y11);
+            if (on) {
+                S[i00] = z00; S[i01] = z01; S[i10] = z10; S[i11] = z11;
             }
-            // Clear the other parity's flag for the next sweep.  Every thread
-            // read it (the stop test of the previous sweep) before the barrier
-            // of this sweep's step 0, so the clear waits for step 1.
-            if (t == 0 && step == 1) rotated[(sweep + 1) & 1] = 0;
-            __syncthreads();
-            // Two-sided update of the off-diagonal 2 x 2 blocks, each unordered
-            // pair {u, v} once, mirrored: slot t (0 .. 511) is u = t / 16 with
-            // v = u + 1 + t % 16 (mod 32); the pairs 16 apart come up twice and
-            // run from the lower u only.  Loads are issued before the arithmetic.
-            {
-                const int u = t >> 4, dv = t & 15, v = (u + 1 + dv) & 31;
-                const bool on = dv != 15 || u < 16;
-                const int au = ra[u], bu = rb[u], av = ra[v], bv = rb[v];
-                const int i00 = tri(au, av), i01 = tri(au, bv), i10 = tri(bu, av), i11 = tri(bu, bv);
-                const double x00 = S[i00], x01 = S[i01], x10 = S[i10], x11 = S[i11];
-                const double su = rs[u], tu = rtau[u], sv = rs[v], tv = rtau[v];
-                // rows: J_u^T
-                const double y00 = x00 - su * (x10 + tu * x00), y10 = x10 + su * (x00 - tu * x10);
-                const double y01 = x01 - su * (x11 + tu * x01), y11 = x11 + su * (x01 - tu * x11);
-                // columns: J_v
-                const double z00 = y00 - sv * (y01 + tv * y00), z01 = y01 + sv * (y00 - tv * y01);
-                const double z10 = y10 - sv * (y11 + tv * y10), z11 = y11 + sv * (y10 - tv * y11);
-                if (on) {
-                    S[i00] = z00; S[i01] = z01; S[i10] = z10; S[i11] = z11;
+            if (t < NP) {
+                // Rotation t of this step is done: its pivot becomes zero (the
+                // diagonal updates are applied below, by the thread whose next
+                // pivot needs them).
+                if (rs[cur][t] != 0.0) S[tri(ra[cur][t], rb[cur][t])] = 0.0;
+                // Pair t of the next step: a' from one of this block's pairs,
+                // b' from the other; every diagonal entry is in exactly one of
+                // them, so every diagonal update is applied once.
+                int a2, b2;
+                circle_pair(PW, (step + 1) % (PW - 1), t, a2, b2);
+                const bool a_in_u = a2 == au || a2 == bu;
+                const int xa = a_in_u ? a2 : b2, ya = a_in_u ? b2 : a2;   // row of the block, column
+                const double apq2 = xa == au ? (ya == av ? z00 : z01) : (ya == av ? z10 : z11);
+                const int wa = a_in_u ? u : v, wb = a_in_u ? v : u;
+                double app2 = S[tri(a2, a2)], aqq2 = S[tri(b2, b2)];
+                if (rs[cur][wa] != 0.0)   // the first index of a rotation loses t apq, the second gains it
+                    app2 = fma(a2 == ra[cur][wa] ? -rt[cur][wa] : rt[cur][wa], rapq[cur][wa], app2);
+                if (rs[cur][wb] != 0.0)
+                    aqq2 = fma(b2 == ra[cur][wb] ? -rt[cur][wb] : rt[cur][wb], rapq[cur][wb], aqq2);
+                S[tri(a2, a2)] = app2;
+                S[tri(b2, b2)] = aqq2;
+                if (step + 1 < PW - 1) {
+                    double tt, s, tau;
+                    if (jacobi_rotation(app2, aqq2, apq2, thr, tt, s, tau)) flags[1] = 1;
+                    ra[nxt][t] = a2; rb[nxt][t] = b2; rs[nxt][t] = s; rtau[nxt][t] = tau; rt[nxt][t] = tt;
+                    rapq[nxt][t] = apq2;
                 }
-                // the diagonal blocks: the rotated 2 x 2 problem itself
-                if (t < PW / 2 && rs[t] != 0.0) {   // not rotated: S[a][b] stays
-                    const int a2 = ra[t], b2 = rb[t];
-                    const double tt = rt[t], apq = rapq[t];
-                    S[tri(a2, a2)] -= tt * apq;
-                    S[tri(b2, b2)] += tt * apq;
-                    S[tri(a2, b2)] = 0.0;
-                }
-            }
-            // D <- D J + (J - I): thread t takes pair u = t % 32 in rows t / 32 + 16 i
-            {
-                const int u = t & 31, a2 = ra[u], b2 = rb[u];
-                const double s2 = rs[u], tau = rtau[u];
-                constexpr int NR = PW * (PW / 2) / SV_THREADS;
+            } else if (t >= 64) {
+                // D <- D J + (J - I) on waves 1 .. 7: item q is pair q % 32 in row q / 32.
+                constexpr int NT = SV_THREADS - 64, NR = (PW * NP + NT - 1) / NT;
+                int a3[NR], b3[NR], r3[NR];
                 double da[NR], db[NR];
 #pragma unroll
                 for (int i = 0; i < NR; ++i) {
-                    const int r = (t >> 5) + (SV_THREADS / 32) * i;
-                    da[i] = D[r][a2];
-                    db[i] = D[r][b2];
+                    const int q = (t - 64) + NT * i;
+                    const int w = q & (NP - 1);
+                    r3[i] = q >> 5; a3[i] = ra[cur][w]; b3[i] = rb[cur][w];
+                    if (q < PW * NP) { da[i] = D[r3[i]][a3[i]]; db[i] = D[r3[i]][b3[i]]; }
                 }
 #pragma unroll
                 for (int i = 0; i < NR; ++i) {
-                    const int r = (t >> 5) + (SV_THREADS / 32) * i;
-                    double na = da[i] - s2 * (db[i] + tau * da[i]), nb2 = db[i] + s2 * (da[i] - tau * db[i]);
-                    if (r == a2) { na -= s2 * tau; nb2 += s2; }
-                    if (r == b2) { na -= s2; nb2 -= s2 * tau; }
-                    D[r][a2] = na;
-                    D[r][b2] = nb2;
+                    const int q = (t - 64) + NT * i;
+                    if (q >= PW * NP) break;
+                    const int w = q & (NP - 1), r = r3[i];
+                    const double s2 = rs[cur][w], tau = rtau[cur][w], st = __dmul_rn(s2, tau);
+                    double na = fma(-s2, fma(tau, da[i], db[i]), da[i]);
+                    double nb2 = fma(s2, fma(-tau, db[i], da[i]), db[i]);
+                    if (r == a3[i]) { na = __dsub_rn(na, st); nb2 = __dadd_rn(nb2, s2); }
+                    if (r == b3[i]) { na = __dsub_rn(na, s2); nb2 = __dsub_rn(nb2, st); }
+                    D[r][a3[i]] = na;
+                    D[r][b3[i]] = nb2;
                 }
             }
             __syncthreads();
         }
-        if (!rotated[sweep & 1]) break;   // uniform: read after the barrier
-        any = true;
     }
+    const bool any = flags[1];   // read after the last barrier
     double* Dout = reinterpret_cast<double*>(ws + eg.off_D) + int64_t(j) * PW * PW;
     for (int q = t; q < PW * PW / 2; q += SV_THREADS) {
         const int r = q / (PW / 2), c = 2 * (q % (PW / 2));
