@@ -353,9 +353,10 @@ typedef struct mo_soap_matrix {
  * own); 1, it starts from the eigenbases the previous step of this bucket
  * left in this workspace (the reusable step objects of the binding pass 1
  * from their second call on).  A side whose workspace region does not hold
- * bases written by a step (the word the sort writes beside them) runs cold;
- * bases that some other step of the same shapes left there are orthonormal
- * and still a valid start, only a slower one.  The previous bases are made orthonormal again by one
+ * bases that a step wrote for a side of the same size m (the word the sort
+ * writes beside them names m and its padding) runs cold; bases of another
+ * matrix's side of that size are orthonormal and still a valid start, only a
+ * slower one.  The previous bases are made orthonormal again by one
  * Newton-Schulz polar step, the new statistics are rotated into them, and
  * the sweeps start from that nearly diagonal matrix: the result is the same
  * eigendecomposition, to the sweeps' convergence, and fewer of the sweeps

@@ -10,12 +10,12 @@
 #include <stdint.h>
 
 #define MO_SO_MAGIC   0x4F534F4Du  // "MOSO"
-#define MO_SO_VERSION 5u
+#define MO_SO_VERSION 6u
 #define MO_SO_ECOLS 4u     // 64-column tiles of E per rotation work item (one D_I load each)
 
 #define MO_SO_PAD    64   // padding of every side (the eigensolver's pair of 32-wide blocks)
 #define MO_SO_BLK    32   // Jacobi block width
-#define MO_SO_MAXSIDE 16384  // the paper's MLP side; each side holds 5 m_pad^2 fp64-equivalents of workspace
+#define MO_SO_MAXSIDE 16384  // the paper's MLP side; each side holds 16 bytes of workspace per m_pad^2 (A fp64, E and E32 fp32)
 
 // fp32 products of the step (C = op(A) op(B), 64 x 64 tiles)
 #define MO_SOK_STATS_L 0   // L' = L + G G^T: caller L and the fp64 copy the eigensolver works on
@@ -73,8 +73,9 @@ struct mo_so_mat {
 // when that slot's pair problem rotated in some round of the final sweep
 // (all zero: the final sweep rotated nothing, so A was diagonal to the
 // threshold, the convergence test of cyclic Jacobi).  valid is one word the gather writes
-// after E32 (MO_SO_MAGIC ^ m_pad): a warm start uses E32 only when it holds it,
-// so a workspace that never held this side's bases runs cold.
+// after E32 (MO_SO_MAGIC ^ (m_pad | m << 16)): a warm start uses E32 only when
+// it holds it, so a workspace that never held bases of a side of this size
+// runs cold.
 struct mo_so_eig {
     uint64_t off_A, off_E, off_D, off_E32, off_perm, off_flag, off_norm, off_last;
     uint64_t ext;                         // caller statistics (L or R), m x m fp32, row stride ld_ext
@@ -83,7 +84,7 @@ struct mo_so_eig {
     uint32_t rounds;                      // sweeps x (2P - 1)
     uint32_t solve_begin, apply_begin;    // first item of this decomposition in each grouped launch
     uint32_t etile_begin;
-    uint64_t off_valid;                   // one word: MO_SO_MAGIC ^ m_pad once the sort has written E32
+    uint64_t off_valid;                   // one word: MO_SO_MAGIC ^ (m_pad | m << 16) once the sort has written E32
 };
 
 static_assert(sizeof(mo_so_header) == 80, "header layout");

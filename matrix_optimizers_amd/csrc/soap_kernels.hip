@@ -52,11 +52,15 @@ MO_DEV const mo_so_eig* so_eigs(const uint8_t* ws) {
 }
 
 // What the sort's gather writes beside the sorted eigenvectors E32, and what a
-// warm start requires before it uses them: a workspace that never held this
-// side's bases (fresh memory) does not hold this word, and such a step runs
-// cold.  Any orthonormal bases would still give the right result, only by more
-// sweeps; the word keeps uninitialised memory out of the polar step.
-MO_DEV uint32_t valid_word(const mo_so_eig& eg) { return MO_SO_MAGIC ^ eg.m_pad; }
+// warm start requires before it uses them: a workspace that never held bases
+// of a side of this size (fresh memory, or another bucket's side whose size
+// pads to the same m_pad) does not hold this word, and such a step runs cold.
+// Any orthonormal basis of the m-dimensional side would still give the right
+// result, only by more sweeps; bases of a smaller side lack directions the
+// polar step cannot restore, and uninitialised memory is no basis at all.
+// Sides are at most 16384 (15 bits), so m_pad and m do not overlap.
+static_assert(MO_SO_MAXSIDE < (1 << 15), "m_pad and m share the validity word");
+MO_DEV uint32_t valid_word(const mo_so_eig& eg) { return MO_SO_MAGIC ^ (eg.m_pad | (eg.m << 16)); }
 MO_DEV bool bases_valid(const uint8_t* ws, const mo_so_eig& eg) {
     return *reinterpret_cast<const uint32_t*>(ws + eg.off_valid) == valid_word(eg);
 }

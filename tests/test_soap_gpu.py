@@ -315,24 +315,30 @@ def test_warm_start_full_size(gpu):
 def test_warm_start_without_previous_bases(gpu):
     """warm_start=1 on a workspace that never held this bucket's bases (bytes
     of 0xFF) runs cold; on one holding another matrix's bases of the same
-    size, those orthonormal bases are a valid start too.  Both match the
-    oracle at the floor and converge."""
+    size, those orthonormal bases are a valid start too; on one holding the
+    bases of a smaller matrix whose sides pad to the same sizes (so the same
+    workspace layout), those lack directions and the step runs cold.  All
+    match the oracle at the floor and converge."""
     import torch
     import matrix_optimizers_amd as mo
     dev = torch.device("cuda:0")
     t = lambda x: torch.tensor(np.asarray(x, F32), device=dev).contiguous()
     st = warm_state(77, 150, 90)
     other = warm_state(78, 150, 90)
+    smaller = warm_state(79, 140, 70)   # sides 140 and 70 pad to 192 and 128, as 150 and 90 do
 
     def mats_of(s):
         return [tuple(t(s[k]) for k in ("W", "G", "L", "R", "M", "V"))]
     ref = mats_of(st)
     need = mo.soap_workspace_bytes([mo.soap_tensor_descriptor(*ref[0])], mo.soap_hparams())
-    for label, ws in (("fresh workspace", None), ("another matrix's bases", "other")):
-        if ws is None:
+    for label, prev in (("fresh workspace", None), ("another matrix's bases", other),
+                        ("a smaller matrix's bases", smaller)):
+        if prev is None:
             ws = torch.full((need,), 255, dtype=torch.uint8, device=dev)
         else:
-            ostep = mo.SoapOwnerStep(mats_of(other), sweeps=14, **HP)
+            pmats = mats_of(prev)
+            assert mo.soap_workspace_bytes([mo.soap_tensor_descriptor(*pmats[0])], mo.soap_hparams()) == need
+            ostep = mo.SoapOwnerStep(pmats, sweeps=14, **HP)
             ostep(10)
             ws = ostep.workspace
         mats = mats_of(st)
