@@ -162,10 +162,42 @@ def check_tail(device, seed, n, a: wlmod.AdamWHP):
 
 
 # 517 and 2051: a last partial group of 16-byte accesses plus ragged elements;
-# 2^25 + 4099: more elements than one grid-stride pass covers at the grid cap.
+# 2^25 + 4099: a grid of 16387 workgroups with both.
 @pytest.mark.parametrize("n", [0, 1, 3, 4, 517, 1023, 2051, 4096, 32768, 1 << 20, (1 << 25) + 4099])
 def test_adamw_tail(gpu, n):
     check_tail(gpu, 40 + n % 7, n, wlmod.AdamWHP())
+
+
+def test_adamw_tail_beyond_one_pass(gpu):
+    """More elements than one pass of the largest grid covers (131072
+    workgroups of 2048 elements, 2^28): the first workgroups loop once more,
+    one ends in a partial 16-byte group, and the last n % 4 elements take the
+    element-wise path.  Inputs are drawn on the device; AdamW is elementwise,
+    so the oracle evaluated on sampled elements (both ends, both sides of the
+    pass boundary, and random ones), from their inputs as stored, is exact for
+    those elements."""
+    import torch
+    import matrix_optimizers_amd as mo
+    n = (1 << 28) + (1 << 20) + 4099
+    gen = torch.Generator(device=gpu).manual_seed(71)
+    p = torch.randn(n, device=gpu, generator=gen) * 0.02
+    g = torch.randn(n, device=gpu, generator=gen) * 1e-3
+    m = torch.randn(n, device=gpu, generator=gen) * 1e-3
+    v = (torch.randn(n, device=gpu, generator=gen) * 1e-3) ** 2
+    edge = 1 << 28
+    idx = torch.cat([torch.arange(0, 8192), torch.arange(edge - 8192, edge + 8192), torch.arange(n - 16384, n),
+                     torch.randint(0, n, (200000,), generator=torch.Generator().manual_seed(72))]).unique()
+    idx_d = idx.to(gpu)
+    before = [t[idx_d].double().cpu().numpy() for t in (p, g, m, v)]
+    a = wlmod.AdamWHP()
+    mo.adamw_tail_step(p, g, m, v, a.step, lr=a.lr, beta1=a.beta1, beta2=a.beta2, eps=a.eps,
+                       weight_decay=a.weight_decay)
+    after = [t[idx_d].double().cpu().numpy() for t in (p, m, v)]
+    f = lambda x: float(np.float32(x))
+    want = oadamw.adamw_step(*before, a.step, f(a.lr), f(a.beta1), f(a.beta2), f(a.eps), f(a.weight_decay))
+    errs = [rel(x, w) for x, w in zip(after, want)]
+    print("adamw beyond one pass", n, len(idx), errs)
+    assert max(errs) <= 1e-6, errs
 
 
 @pytest.mark.parametrize("step", [1, 2, 1000])
