@@ -224,10 +224,13 @@ def test_adamw_misaligned_views(gpu):
     assert rel(to_host(views[0]), po) <= 1e-6
 
 
-@pytest.mark.parametrize("nbytes", [16, 48, 4096 + 16, 3 * 4096 * 16 + 1008, (64 << 20) + 4080])
+# (2 << 30) + (64 << 20) + 4080: more than one pass of the largest grid (2 GiB)
+@pytest.mark.parametrize("nbytes", [16, 48, 4096 + 16, 3 * 4096 * 16 + 1008, (64 << 20) + 4080,
+                                    (2 << 30) + (64 << 20) + 4080])
 def test_device_copy(gpu, nbytes):
     """The copy that calibrates the byte counters copies every byte, including
-    a last partial group of 16-byte accesses."""
+    a last partial group of 16-byte accesses and, past 2 GiB, a second pass of
+    the grid."""
     import torch
     import matrix_optimizers_amd as mo
     gen = torch.Generator(device=gpu).manual_seed(nbytes % 1000)
