@@ -34,6 +34,7 @@ namespace {
 
 typedef double f64x2 __attribute__((ext_vector_type(2)));
 typedef double f64x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int SO_THREADS = 256;
 constexpr int SV_THREADS = 512;        // the pair solve: one slot of 2 x 2 blocks per thread
@@ -773,15 +774,16 @@ MO_DEV void apply_a_tile(uint8_t* ws, uint32_t k, uint32_t blk, double (*C)[PW +
 // themselves stay fp64.  D_I sits in LDS (fp32, rows
 // padded to ED floats so that the four row groups of a read fall in separate
 // banks; loaded once for the workgroup's tiles).  Each wave takes whole
-// strips of 64 rows x 16 columns, so no wave reads what another writes and
-// the strips need no barrier; the next strip's loads are issued before the
-// current strip's products.  In this instruction lane l holds result row
-// 4 (l / 16) + v of a 16 x 16 block in register v (read off the instruction
-// with one-hot operands), so the sum over the pair's 64 rows is taken in the
-// order k-step kk, lane group g -> pair row 16 (kk / 4) + 4 g + kk % 4: the B
-// operand a lane loads at k-step 4 x + v is then the old value of its result
-// register v of block x, kept instead of read again.  Unrotated pairs are
-// skipped.
+// strips of 64 rows x 32 columns, so no wave reads what another writes and
+// the strips need no barrier.  A lane holds two adjacent columns of a row (one
+// 8-byte access; 16 lanes cover a 128-byte line) and runs two column sets of
+// products with each D_I value it reads.  In this instruction lane l holds
+// result row 4 (l / 16) + v of a 16 x 16 block in register v (read off the
+// instruction with one-hot operands), so the sum over the pair's 64 rows is
+// taken in the order k-step kk, lane group g -> pair row 16 (kk / 4) + 4 g +
+// kk % 4: the B operand a lane loads at k-step 4 x + v is then the old value
+// of its result register v of block x, kept instead of read again.  Unrotated
+// pairs are skipped.
 constexpr int ED = PW + 4;   // LDS row of D_I in the E path (floats)
 
 MO_DEV void apply_e_tile(uint8_t* ws, uint32_t k, uint32_t blk, float (*DI)[ED]) {
@@ -812,47 +814,50 @@ MO_DEV void apply_e_tile(uint8_t* ws, uint32_t k, uint32_t blk, float (*DI)[ED])
     __syncthreads();
     const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int g = l >> 4;
-    const int nstrip = 4 * min(int(MO_SO_ECOLS), P - cc0);
-    // row 4 g of block p and of block q, the lane's column of the item; k-step
-    // kk then reads block row 16 ((kk / 4) % 2) + kk % 4 further on, of block p
-    // for kk < 8 and of block q after
-    float* Ep = reinterpret_cast<float*>(ws + eg.off_E) + (int64_t(pI) * MO_SO_BLK + 4 * g) * ld +
-                int64_t(cc0) * PW + (l & 15);
-    float* Eq = reinterpret_cast<float*>(ws + eg.off_E) + (int64_t(qI) * MO_SO_BLK + 4 * g) * ld +
-                int64_t(cc0) * PW + (l & 15);
-    float cur[16], nxt[16];
-    auto load_strip = [&](int st, float (&dst)[16]) {
-#pragma unroll
-        for (int kk = 0; kk < 16; ++kk)
-            dst[kk] = (kk < 8 ? Ep : Eq)[int64_t(16 * ((kk >> 2) & 1) + (kk & 3)) * ld + 16 * st];
+    const int nstrip = 2 * min(int(MO_SO_ECOLS), P - cc0);
+    // Row 4 g of block p and of block q, the lane's two columns of the strip;
+    // k-step kk then reads block row 16 ((kk / 4) % 2) + kk % 4 further on, of
+    // block p for kk < 8 and of block q after.  Byte offsets from the E region
+    // (at most 16384^2 x 4 bytes = 2^30), so each access takes the region's
+    // uniform base plus one 32-bit lane offset.
+    uint8_t* Eb = ws + eg.off_E;
+    const uint32_t ldb = uint32_t(ld) * 4u;
+    const uint32_t op = (uint32_t(pI) * MO_SO_BLK + 4u * g) * ldb + uint32_t(cc0) * PW * 4u + 8u * (l & 15);
+    const uint32_t oq = (uint32_t(qI) * MO_SO_BLK + 4u * g) * ldb + uint32_t(cc0) * PW * 4u + 8u * (l & 15);
+    auto at = [&](int kk, int st) -> f32x2* {   // k-step kk's row (or register v = kk % 4 of block kk / 4)
+        return reinterpret_cast<f32x2*>(Eb + ((kk < 8 ? op : oq) + uint32_t(16 * ((kk >> 2) & 1) + (kk & 3)) * ldb +
+                                              uint32_t(st) * 128u));
     };
-    if (w < nstrip) load_strip(w, cur);
+    f32x2 cur[16];
 #pragma unroll 1
     for (int st = w; st < nstrip; st += 4) {
-        // D_I is read from LDS again for every strip: kept in registers across
-        // strips it would take 64 of them and most of the CU's waves
-        asm volatile("" ::: "memory");
-        if (st + 4 < nstrip) load_strip(st + 4, nxt);
-        f32x4 acc[4];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) acc[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int kk = 0; kk < 16; ++kk) cur[kk] = *at(kk, st);
+        f32x4 acc[4][2];
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) acc[x][h] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < 16; ++kk) {
             const int kq = 16 * (kk >> 2) + 4 * g + (kk & 3);
 #pragma unroll
-            for (int x = 0; x < 4; ++x)
-                acc[x] = __builtin_amdgcn_mfma_f32_16x16x4f32(DI[kq][16 * x + (l & 15)], cur[kk], acc[x], 0, 0, 0);
+            for (int x = 0; x < 4; ++x) {
+                const float d = DI[kq][16 * x + (l & 15)];
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    acc[x][h] = __builtin_amdgcn_mfma_f32_16x16x4f32(d, cur[kk][h], acc[x][h], 0, 0, 0);
+            }
+            // this k-step's D_I reads stay with its products: hoisted over the
+            // whole strip they would take 64 more registers and spill
+            __builtin_amdgcn_sched_barrier(0);
         }
         // block x, register v: pair row 16 x + 4 g + v, loaded at k-step 4 x + v
 #pragma unroll
         for (int x = 0; x < 4; ++x)
 #pragma unroll
             for (int v = 0; v < 4; ++v)
-                (x < 2 ? Ep : Eq)[int64_t(16 * (x & 1) + v) * ld + 16 * st] = cur[4 * x + v] + acc[x][v];
-        if (st + 4 < nstrip) {
-#pragma unroll
-            for (int kk = 0; kk < 16; ++kk) cur[kk] = nxt[kk];
-        }
+                *at(4 * x + v, st) = f32x2{cur[4 * x + v][0] + acc[x][0][v], cur[4 * x + v][1] + acc[x][1][v]};
     }
 }
 
