@@ -138,77 +138,65 @@ MO_DEV SoProd so_prod(uint8_t* ws, const mo_so_mat& mt, int kind) {
 }
 
 // The epilogue of one row of four results: row i, columns j .. j + 3.
-MO_DEV void so_epilogue(uint8_t* ws, const mo_so_mat& mt, int kind, int64_t i, int64_t j, const float* v) {
-    const int64_t rp = mt.r_pad, cp = mt.c_pad;
+MO_DEV void so_epilogue(uint8_t* ws, const mo_so_mat& mt, int kind, int64_t i, int64_t j, float v) {
+    const int64_t cp = mt.c_pad;
     if (kind == MO_SOK_STATS_L || kind == MO_SOK_STATS_R) {
         const mo_so_eig& eg = so_eigs(ws)[kind == MO_SOK_STATS_L ? mt.eig_l : mt.eig_r];
         float* ext = reinterpret_cast<float*>(eg.ext);
         double* A = reinterpret_cast<double*>(ws + eg.off_A);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            float s = 0.f;
-            if (i < eg.m && j + e < eg.m) {
-                s = ext[i * eg.ld_ext + j + e] + v[e];
-                ext[i * eg.ld_ext + j + e] = s;
-            }
-            A[i * eg.m_pad + j + e] = double(s);
+        float s = 0.f;
+        if (i < eg.m && j < eg.m) {
+            s = ext[i * eg.ld_ext + j] + v;
+            ext[i * eg.ld_ext + j] = s;
         }
+        A[i * eg.m_pad + j] = double(s);
         return;
     }
     if (kind == MO_SOK_RIGHT_G) {
-        if (i >= mt.rows) return;
-        float* V = reinterpret_cast<float*>(mt.V);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (j + e < mt.cols) {
-                float& x = V[i * mt.ld_v + j + e];
-                x = mt.beta2 * x + (1.0f - mt.beta2) * v[e] * v[e];
-            }
+        if (i < mt.rows && j < mt.cols) {
+            float& x = reinterpret_cast<float*>(mt.V)[i * mt.ld_v + j];
+            x = mt.beta2 * x + (1.0f - mt.beta2) * v * v;
+        }
         return;
     }
     if (kind == MO_SOK_RIGHT_M) {
         const float* V = reinterpret_cast<const float*>(mt.V);
-        float* N = reinterpret_cast<float*>(ws + mt.off_N);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            float n = 0.f;
-            if (i < mt.rows && j + e < mt.cols)
-                n = (v[e] * mt.ibc1) / (sqrtf(V[i * mt.ld_v + j + e] * mt.ibc2) + mt.eps);
-            N[i * cp + j + e] = n;
-        }
+        float n = 0.f;
+        if (i < mt.rows && j < mt.cols) n = (v * mt.ibc1) / (sqrtf(V[i * mt.ld_v + j] * mt.ibc2) + mt.eps);
+        reinterpret_cast<float*>(ws + mt.off_N)[i * cp + j] = n;
         return;
     }
     if (kind == MO_SOK_BACK_R) {
-        if (i >= mt.rows) return;
-        const bool wbf = mt.flags & MO_SOF_W_BF16;
-        void* W = reinterpret_cast<void*>(mt.W);
-        float* U = reinterpret_cast<float*>(mt.U);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (j + e < mt.cols) {
-                const int64_t wi = i * mt.ld_w + j + e;
-                store_elem(W, wi, mt.decay * load_elem(W, wi, wbf) - mt.lr * v[e], wbf);
-                if (U) U[i * mt.ld_u + j + e] = mt.lr * v[e];
-            }
+        if (i < mt.rows && j < mt.cols) {
+            const bool wbf = mt.flags & MO_SOF_W_BF16;
+            void* W = reinterpret_cast<void*>(mt.W);
+            const int64_t wi = i * mt.ld_w + j;
+            store_elem(W, wi, mt.decay * load_elem(W, wi, wbf) - mt.lr * v, wbf);
+            if (mt.U) reinterpret_cast<float*>(mt.U)[i * mt.ld_u + j] = mt.lr * v;
+        }
         return;
     }
     // LEFT_G, LEFT_M, BACK_L: the padded scratch product
-    float* T = reinterpret_cast<float*>(ws + mt.off_T);
-    (void)rp;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) T[i * cp + j + e] = v[e];
+    reinterpret_cast<float*>(ws + mt.off_T)[i * cp + j] = v;
 }
 
 // One 64 x 64 tile of C = op(A) op(B) with fp64 accumulation: K runs up to the
 // long side (16384), where a sequential fp32 sum drops the small terms that
-// follow a large partial sum, always the same way.  ep(i, j, v) receives the
-// fp64 sums of row i, columns j .. j + 3.
+// follow a large partial sum, always the same way.  The fp32 operands are
+// staged in LDS and widened (exactly) for v_mfma_f64_16x16x4_f64; each wave
+// owns a 32 x 32 quarter as 2 x 2 blocks of 16 x 16 (the lane layout of the
+// A path below).  ep(i, j, v) receives the fp64 sum of element (i, j).
 template <class Ep>
 MO_DEV void so_tile(const SoProd& p, int64_t i0, int64_t j0, float (*As)[GB + 4], float (*Bs)[GB + 4],
                     const Ep& ep) {
     const int t = threadIdx.x;
-    const int r0 = (t / 16) * 4, c0 = (t % 16) * 4;
-    double acc[4][4] = {};
+    const int l = t & 63, w = t >> 6;
+    const int rw = 32 * (w >> 1), cw = 32 * (w & 1);   // this wave's 32 x 32 quarter of the tile
+    f64x4 acc[2][2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) acc[x][y] = f64x4{0.0, 0.0, 0.0, 0.0};
     for (int k0 = 0; k0 < p.K; k0 += GK) {
         if (p.a_lim > 0) {  // the caller's matrix: element loads, zero outside it
             const int i = t / 4, kk = (t % 4) * 4;
@@ -240,18 +228,27 @@ MO_DEV void so_tile(const SoProd& p, int64_t i0, int64_t j0, float (*As)[GB + 4]
         }
         __syncthreads();
 #pragma unroll
-        for (int kk = 0; kk < GK; ++kk) {
-            const f32x4 a = *reinterpret_cast<const f32x4*>(&As[kk][r0]);
-            const f32x4 b = *reinterpret_cast<const f32x4*>(&Bs[kk][c0]);
+        for (int kk = 0; kk < GK; kk += 4) {   // lane l: A(l % 16, l / 16), B(l / 16, l % 16)
+            double a[2], b[2];
 #pragma unroll
-            for (int x = 0; x < 4; ++x)
+            for (int x = 0; x < 2; ++x) a[x] = double(As[kk + (l >> 4)][rw + 16 * x + (l & 15)]);
 #pragma unroll
-                for (int y = 0; y < 4; ++y) acc[x][y] = fma(double(a[x]), double(b[y]), acc[x][y]);
+            for (int y = 0; y < 2; ++y) b[y] = double(Bs[kk + (l >> 4)][cw + 16 * y + (l & 15)]);
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int y = 0; y < 2; ++y) acc[x][y] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[x], b[y], acc[x][y], 0, 0, 0);
         }
         __syncthreads();
     }
+    // register v of block (x, y): row 16 x + l / 16 + 4 v, column 16 y + l % 16 of the quarter
 #pragma unroll
-    for (int x = 0; x < 4; ++x) ep(i0 + r0 + x, j0 + c0, acc[x]);
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                ep(i0 + rw + 16 * x + (l >> 4) + 4 * v, j0 + cw + 16 * y + (l & 15), acc[x][y][v]);
 }
 
 __global__ __launch_bounds__(SO_THREADS) void so_gemm_kernel(uint8_t* ws, uint32_t mi, int kind) {
@@ -259,10 +256,8 @@ __global__ __launch_bounds__(SO_THREADS) void so_gemm_kernel(uint8_t* ws, uint32
     __shared__ __align__(16) float Bs[GK][GB + 4];
     const mo_so_mat& mt = so_mats(ws)[mi];
     so_tile(so_prod(ws, mt, kind), int64_t(blockIdx.y) * GB, int64_t(blockIdx.x) * GB, As, Bs,
-            [&](int64_t i, int64_t j, const double* a) {
-                // each result is rounded to fp32 once
-                const float v[4] = {float(a[0]), float(a[1]), float(a[2]), float(a[3])};
-                so_epilogue(ws, mt, kind, i, j, v);
+            [&](int64_t i, int64_t j, double a) {
+                so_epilogue(ws, mt, kind, i, j, float(a));   // each result is rounded to fp32 once
             });
 }
 
@@ -300,21 +295,18 @@ __global__ __launch_bounds__(SO_THREADS) void so_warm_kernel(uint8_t* ws, uint32
     default:       p = {E, mp, 1, E32, mp, 1, int(mp)}; break;   // MO_SOW_A: E0 T (T in E32)
     }
     so_tile(p, int64_t(blockIdx.y) * GB, int64_t(blockIdx.x) * GB, As, Bs,
-            [&](int64_t i, int64_t j, const double* v) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int64_t o = i * mp + j + e;
-                    if (kind == MO_SOW_E) E[o] = float(double(E32[o]) - 0.5 * v[e]);
-                    else if (kind == MO_SOW_T) E32[o] = float(v[e]);
-                    else if (i > j + e) continue;   // a symmetric result: the upper value and its mirror
-                    else if (kind == MO_SOW_P) {
-                        const float d = float(v[e] - ((i == j + e && i < eg.m) ? 1.0 : 0.0));
-                        Pm[o] = d;
-                        Pm[(j + e) * mp + i] = d;
-                    } else {
-                        A[o] = v[e];
-                        A[(j + e) * mp + i] = v[e];
-                    }
+            [&](int64_t i, int64_t j, double v) {
+                const int64_t o = i * mp + j;
+                if (kind == MO_SOW_E) E[o] = float(double(E32[o]) - 0.5 * v);
+                else if (kind == MO_SOW_T) E32[o] = float(v);
+                else if (i > j) return;   // a symmetric result: the upper value and its mirror
+                else if (kind == MO_SOW_P) {
+                    const float d = float(v - ((i == j && i < eg.m) ? 1.0 : 0.0));
+                    Pm[o] = d;
+                    Pm[j * mp + i] = d;
+                } else {
+                    A[o] = v;
+                    A[j * mp + i] = v;
                 }
             });
 }
