@@ -377,25 +377,44 @@ __global__ __launch_bounds__(SO_THREADS) void so_norm_final_kernel(uint8_t* ws, 
     if (threadIdx.x == 0) nrm[eg.m_pad] = 0x1p-48 * sqrt(red[0]);
 }
 
+// 1/x and 1/sqrt(x) for normal x > 0: the hardware estimate refined by two
+// Newton steps, to within a unit or two of fp64 rounding (not correctly
+// rounded; the rotation below needs accuracy and consistency, not IEEE
+// division, whose scaling and fix-up steps dominated the pair solve).
+MO_DEV double rcp_nr(double x) {
+    double y = __builtin_amdgcn_rcp(x);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) y = fma(y, fma(-x, y, 1.0), y);
+    return y;
+}
+MO_DEV double rsq_nr(double x) {
+    double y = __builtin_amdgcn_rsq(x);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) y = fma(y, fma(-(x * y), 0.5 * y, 0.5), y);   // y (3 - x y^2) / 2
+    return y;
+}
+
 // Rotation that zeroes S[a][b] of the symmetric 2 x 2 problem (app, apq; apq, aqq):
-// t = tan, s = sin, tau = sin / (1 + cos) (Rutishauser's formulas).  An
-// off-diagonal entry at or below the threshold is left as it is (no
-// rotation).  Returns whether it rotates.
+// t = tan, s = sin, tau = sin / (1 + cos) (Rutishauser's formulas).  With
+// d = aqq - app and e = 2 apq, t = sign(d e) |e| / (|d| + hypot(d, e)) (the
+// smaller of the two angles, +1 at d = 0), cos = 1 / sqrt(1 + t^2), s = t cos.
+// The entries are statistics of fp32 data, at most about 1e81 in magnitude,
+// and a rotated |apq| is above the threshold 2^-48 ||A||_F, so d^2 + e^2 stays
+// far from fp64 overflow and underflow.  An off-diagonal entry at or below the
+// threshold is left as it is (no rotation).  Returns whether it rotates.
 MO_DEV bool jacobi_rotation(double app, double aqq, double apq, double thr, double& t, double& s,
                             double& tau) {
     if (fabs(apq) <= thr) {
         t = s = tau = 0.0;
         return false;
     }
-    const double theta = (aqq - app) / (2.0 * apq);
-    if (fabs(theta) > 1e150) {
-        t = 0.5 / theta;
-    } else {
-        t = (theta >= 0.0 ? 1.0 : -1.0) / (fabs(theta) + sqrt(theta * theta + 1.0));
-    }
-    const double c = 1.0 / sqrt(t * t + 1.0);
+    const double d = aqq - app, e = 2.0 * apq;
+    const double x = fma(d, d, e * e);
+    const double r = x * rsq_nr(x);   // hypot(d, e)
+    t = (d * e >= 0.0 ? fabs(e) : -fabs(e)) * rcp_nr(fabs(d) + r);
+    const double c = rsq_nr(fma(t, t, 1.0));
     s = t * c;
-    tau = s / (1.0 + c);
+    tau = s * rcp_nr(1.0 + c);
     return true;
 }
 
@@ -513,6 +532,17 @@ __global__ __launch_bounds__(SV_THREADS) void so_jac_solve_kernel(uint8_t* ws, u
             const int i00 = tri(au, av), i01 = tri(au, bv), i10 = tri(bu, av), i11 = tri(bu, bv);
             const double x00 = S[i00], x01 = S[i01], x10 = S[i10], x11 = S[i11];
             const double su = rs[cur][u], tu = rtau[cur][u], sv = rs[cur][v], tv = rtau[cur][v];
+            // Threads 0 .. 31 also load, with the block, what the next pivot needs:
+            // its two diagonal entries (written by no other thread in this step)
+            // and the tan and pivot of this block's two rotations.
+            int a2 = 0, b2 = 0;
+            double da = 0.0, db = 0.0, tU = 0.0, pU = 0.0, tV = 0.0, pV = 0.0;
+            if (t < NP) {
+                circle_pair(PW, (step + 1) % (PW - 1), t, a2, b2);
+                da = S[tri(a2, a2)];
+                db = S[tri(b2, b2)];
+                tU = rt[cur][u]; pU = rapq[cur][u]; tV = rt[cur][v]; pV = rapq[cur][v];
+            }
             const double y00 = fma(-su, fma(tu, x00, x10), x00), y10 = fma(su, fma(-tu, x10, x00), x10);
             const double y01 = fma(-su, fma(tu, x01, x11), x01), y11 = fma(su, fma(-tu, x11, x01), x11);
             const double z00 = fma(-sv, fma(tv, y00, y01), y00), z01 = fma(sv, fma(-tv, y01, y00), y01);
@@ -528,17 +558,17 @@ __global__ __launch_bounds__(SV_THREADS) void so_jac_solve_kernel(uint8_t* ws, u
                 // Pair t of the next step: a' from one of this block's pairs,
                 // b' from the other; every diagonal entry is in exactly one of
                 // them, so every diagonal update is applied once.
-                int a2, b2;
-                circle_pair(PW, (step + 1) % (PW - 1), t, a2, b2);
                 const bool a_in_u = a2 == au || a2 == bu;
                 const int xa = a_in_u ? a2 : b2, ya = a_in_u ? b2 : a2;   // row of the block, column
                 const double apq2 = xa == au ? (ya == av ? z00 : z01) : (ya == av ? z10 : z11);
-                const int wa = a_in_u ? u : v, wb = a_in_u ? v : u;
-                double app2 = S[tri(a2, a2)], aqq2 = S[tri(b2, b2)];
-                if (rs[cur][wa] != 0.0)   // the first index of a rotation loses t apq, the second gains it
-                    app2 = fma(a2 == ra[cur][wa] ? -rt[cur][wa] : rt[cur][wa], rapq[cur][wa], app2);
-                if (rs[cur][wb] != 0.0)
-                    aqq2 = fma(b2 == ra[cur][wb] ? -rt[cur][wb] : rt[cur][wb], rapq[cur][wb], aqq2);
+                const double s_a = a_in_u ? su : sv, t_a = a_in_u ? tU : tV, p_a = a_in_u ? pU : pV;
+                const double s_b = a_in_u ? sv : su, t_b = a_in_u ? tV : tU, p_b = a_in_u ? pV : pU;
+                const int first_a = a_in_u ? au : av, first_b = a_in_u ? av : au;
+                double app2 = da, aqq2 = db;
+                if (s_a != 0.0)   // the first index of a rotation loses t apq, the second gains it
+                    app2 = fma(a2 == first_a ? -t_a : t_a, p_a, app2);
+                if (s_b != 0.0)
+                    aqq2 = fma(b2 == first_b ? -t_b : t_b, p_b, aqq2);
                 S[tri(a2, a2)] = app2;
                 S[tri(b2, b2)] = aqq2;
                 if (step + 1 < PW - 1) {
