@@ -232,17 +232,31 @@ def cpu_baseline(wl, args):
     if est > CPU_BUDGET_S and hp.ns_steps > 1:
         k = max(1, int(hp.ns_steps * CPU_BUDGET_S / est))
         hp = dataclasses.replace(hp, ns_steps=k)
-    flops = 0.0
     inputs = [wlmod.matrix_inputs(wl, i) for i in sample]
-    t0 = time.perf_counter()
-    for i, x in zip(sample, inputs):
-        omuon.muon_step(x.W, x.G, x.M, hp)
-        flops += per(i, hp.ns_steps)
-    if wl.tail_numel:
-        t = wlmod.tail_inputs(wl.seed, wl.tail_numel)
-        a = wl.adamw
-        oadamw.adamw_step(t.p, t.g, t.m, t.v, a.step, a.lr, a.beta1, a.beta2, a.eps, a.weight_decay)
-    dt = time.perf_counter() - t0
+    tail = wlmod.tail_inputs(wl.seed, wl.tail_numel) if wl.tail_numel else None
+    flops = sum(per(i, hp.ns_steps) for i in sample)
+
+    def run_sample():
+        t0 = time.perf_counter()
+        for x in inputs:
+            omuon.muon_step(x.W, x.G, x.M, hp)
+        if tail is not None:
+            a = wl.adamw
+            oadamw.adamw_step(tail.p, tail.g, tail.m, tail.v, a.step, a.lr, a.beta1, a.beta2, a.eps,
+                              a.weight_decay)
+        return time.perf_counter() - t0
+
+    dt = run_sample()
+    single = None
+    if wl.key in SINGLE_CORE_WORKLOADS:   # the small buckets: the same sample on one core as well
+        try:
+            import threadpoolctl
+            with threadpoolctl.threadpool_limits(limits=1):
+                dt1 = run_sample()
+            single = {"value": flops / dt1 / 1e12, "unit": "TFLOP/s", "cores": 1, "seconds": round(dt1, 2),
+                      "note": "the same sample with the BLAS pool limited to one thread"}
+        except Exception as e:   # no BLAS pool control: say so instead of guessing
+            single = {"value": None, "note": f"not measured: {type(e).__name__}"}
     desc = ", ".join(f"{wl.matrices[i].rows}x{wl.matrices[i].cols}" for i in sample)
     if len(sample) == len(shapes) and hp.ns_steps == wl.hp.ns_steps:
         what = f"one whole matrix of each distinct shape ({desc}), full step"
@@ -250,12 +264,38 @@ def cpu_baseline(wl, args):
         what = (f"{len(sample)} whole matrix{'es' if len(sample) > 1 else ''} of the bucket ({desc}): "
                 f"momentum, normalisation and {hp.ns_steps} of the {wl.hp.ns_steps} Newton-Schulz steps")
     total = sum(wlmod.ns_flops_nominal(m.rows, m.cols, wl.hp.ns_steps) for m in wl.matrices)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": what
-                      + (f" + the {wl.tail_numel}-element AdamW tail" if wl.tail_numel else "")
-                      + f"; fp64 numpy, {dt:.2f} s; rate = nominal NS flops of what ran / time",
-            "projected_full_step_s": round(dt * total / flops, 1),
-            "projection_note": "the whole bucket at the sample's rate (a projection, not a measurement)"}
+    out = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+           "sample": what
+                     + (f" + the {wl.tail_numel}-element AdamW tail" if wl.tail_numel else "")
+                     + f"; fp64 numpy, {dt:.2f} s; rate = nominal NS flops of what ran / time",
+           "projected_full_step_s": round(dt * total / flops, 1),
+           "projection_note": "the whole bucket at the sample's rate (a projection, not a measurement)",
+           "host": host_cpu()}
+    if single is not None:
+        out["single_core"] = single
+    return out
+
+
+# Buckets small enough to time the oracle sample on one core too.
+SINGLE_CORE_WORKLOADS = ("single_256x512_f32", "decoder_layer_h2048")
+
+
+def host_cpu():
+    """The host's CPU model and the CPUs this process may use."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"cpu_model": model, "usable_cpus": usable, "os_cpu_count": os.cpu_count()}
 
 
 SHAMPOO_METRIC = "Shampoo owner-step ms + fp32 TFLOP/s (algorithmic, % fp32 MFMA peak), 1 MI355X"
