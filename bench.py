@@ -158,8 +158,9 @@ def event_timed_steps(fn, steps, per_step=None):
 
 
 def machine_info():
-    """ROCm / HIP version, gfx target and the shader clock that rocm-smi reports
-    right after the timed region (best effort: None where a tool is missing)."""
+    """ROCm / HIP version, gfx target and the shader clock and package power that
+    rocm-smi reports right after the timed region (best effort: None where a tool
+    is missing)."""
     import subprocess
     import torch
     info = {"hip": getattr(torch.version, "hip", None), "torch": torch.__version__}
@@ -181,6 +182,13 @@ def machine_info():
         info["mclk_after_run"] = card.get("mclk clock speed:")
     except Exception:
         info["sclk_after_run"] = None
+    try:   # package power and its cap, as rocm-smi names them
+        out = subprocess.run(["rocm-smi", "--showpower", "--showmaxpower", "--json"], capture_output=True,
+                             text=True, timeout=20).stdout
+        card = next(iter(json.loads(out).values()))
+        info["power_after_run"] = {k: v for k, v in card.items() if "ower" in k} or None
+    except Exception:
+        info["power_after_run"] = None
     return info
 
 
