@@ -11,7 +11,7 @@
 
 #define MO_SO_MAGIC   0x4F534F4Du  // "MOSO"
 #define MO_SO_VERSION 6u
-#define MO_SO_ECOLS 4u     // 64-column tiles of E per rotation work item (one D_I load each)
+#define MO_SO_ECOLS 8u     // 64-column tiles of E per rotation work item (one D_I load each)
 
 #define MO_SO_PAD    64   // padding of every side (the eigensolver's pair of 32-wide blocks)
 #define MO_SO_BLK    32   // Jacobi block width
