@@ -321,7 +321,8 @@ mo_status shampoo_owner_step(const mo_shampoo_matrix* mats, int32_t n_mats,
  * by at most that over its eigenvalue gap); the accumulated eigenvectors are
  * kept and updated in fp32, whose rounding moves them by a few fp32 units and
  * does not feed back into the rotations.  The statistics, moments and
- * products are fp32.  Sides are at most 16384. */
+ * products are stored in fp32; the products (and the statistics' G G^T)
+ * take their sums in fp64.  Sides are at most 16384. */
 
 /* One whole matrix with its SOAP state.
  *   W          rows x cols, w_dtype, row stride ld_w; updated in place
