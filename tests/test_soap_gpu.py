@@ -133,6 +133,22 @@ def test_warm_step(gpu, shape):
     check(st, out, 10, HP, f"warm {shape}")
 
 
+@pytest.mark.parametrize("log2s", [40, -40])
+def test_statistics_scale(gpu, log2s):
+    """The eigensolver's rotations hold far from fp64's range ends: a gradient
+    scaled by s (moments and Adam eps with it, statistics by s^2) gives, in
+    exact arithmetic, the same update; the step must match the oracle there as
+    at unit scale, and the scaled update must equal the unscaled one to the bar."""
+    s = 2.0 ** log2s
+    base = warm_state(23, 96, 160)
+    st = dict(base, G=base["G"] * s, M=base["M"] * s, L=base["L"] * s * s, R=base["R"] * s * s,
+              V=base["V"] * s * s)
+    hp = dict(HP, eps=HP["eps"] * s)
+    out, ref = run_gpu([st], 10, hp)[0], run_gpu([base], 10, HP)[0]
+    check(st, out, 10, hp, f"scale 2^{log2s}")
+    assert rel(out["U"], ref["U"]) <= 2e-4
+
+
 def test_mixed_bucket_with_empty_shard(gpu):
     """One launch sequence over several shapes; each matrix's result is the one
     it gets alone (rows = 0 marks a skipped shard)."""
