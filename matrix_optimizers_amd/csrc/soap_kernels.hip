@@ -80,6 +80,10 @@ MO_DEV void circle_pair(int n, int k, int j, int& a, int& b) {
     }
 }
 
+// The same index one step later in the pair solve's 64-index circle ordering:
+// 0 stays, 1 .. 62 move up by one, 63 wraps to 1.
+MO_DEV int advance_circle(int i) { return i == 0 ? 0 : i == PW - 1 ? 1 : i + 1; }
+
 // ============================================================================
 // prep: padded G and M' = b1 M + (1 - b1) G (the caller's M updated)
 // ============================================================================
@@ -377,31 +381,38 @@ __global__ __launch_bounds__(SO_THREADS) void so_norm_final_kernel(uint8_t* ws, 
     if (threadIdx.x == 0) nrm[eg.m_pad] = 0x1p-48 * sqrt(red[0]);
 }
 
-// 1/x and 1/sqrt(x) for normal x > 0: the hardware estimate refined by two
-// Newton steps, to within a unit or two of fp64 rounding (not correctly
-// rounded; the rotation below needs accuracy and consistency, not IEEE
-// division, whose scaling and fix-up steps dominated the pair solve).
+// 1/x and 1/sqrt(x) for normal x > 0: the hardware estimate (relative error
+// about 2^-24) refined by one third-order step, to within two or three units
+// of fp64 rounding (not correctly rounded; the rotation below needs accuracy
+// and consistency, not IEEE division, whose scaling and fix-up steps dominated
+// the pair solve).  With e the estimate's residual, 1/x = y / (1 - e) and
+// 1/sqrt(x) = y / sqrt(1 - e), each taken to its e^2 term: three dependent
+// operations after the estimate for 1/x and four for 1/sqrt(x), against four
+// and six for two Newton steps.
 MO_DEV double rcp_nr(double x) {
-    double y = __builtin_amdgcn_rcp(x);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) y = fma(y, fma(-x, y, 1.0), y);
-    return y;
+    const double y = __builtin_amdgcn_rcp(x);
+    const double e = fma(-x, y, 1.0);              // 1 - x y
+    return fma(y, fma(e, e, e), y);                // y (1 + e + e^2)
 }
 MO_DEV double rsq_nr(double x) {
-    double y = __builtin_amdgcn_rsq(x);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) y = fma(y, fma(-(x * y), 0.5 * y, 0.5), y);   // y (3 - x y^2) / 2
-    return y;
+    const double y = __builtin_amdgcn_rsq(x);
+    const double e = fma(-(x * y), y, 1.0);        // 1 - x y^2
+    return fma(y * e, fma(0.375, e, 0.5), y);      // y (1 + e/2 + 3 e^2/8)
 }
 
 // Rotation that zeroes S[a][b] of the symmetric 2 x 2 problem (app, apq; apq, aqq):
-// t = tan, s = sin, tau = sin / (1 + cos) (Rutishauser's formulas).  With
-// d = aqq - app and e = 2 apq, t = sign(d e) |e| / (|d| + hypot(d, e)) (the
-// smaller of the two angles, +1 at d = 0), cos = 1 / sqrt(1 + t^2), s = t cos.
+// t = tan, s = sin, tau = sin / (1 + cos) (Rutishauser's formulas), the smaller
+// of the two angles.  With d = aqq - app, e = 2 apq, r = hypot(d, e) and
+// w = |d| + r: t = sign(d e) |e| / w (+1 at d = 0), and since
+// 1 + t^2 = 2 r / w, one reciprocal square root q = 1 / sqrt(2 r w) gives
+// cos = w q and sin = sign(d e) |e| q; tau = sign(d e) |e| / (w + sqrt(2 r w)),
+// with sqrt(2 r w) = 2 r w q.  The chain from the pivot to tau is then about
+// twenty dependent operations, which sets the pair solve's step time.
 // The entries are statistics of fp32 data, at most about 1e81 in magnitude,
-// and a rotated |apq| is above the threshold 2^-48 ||A||_F, so d^2 + e^2 stays
-// far from fp64 overflow and underflow.  An off-diagonal entry at or below the
-// threshold is left as it is (no rotation).  Returns whether it rotates.
+// and a rotated |apq| is above the threshold 2^-48 ||A||_F, so d^2 + e^2 and
+// 2 r w (between 2 r^2 and 4 r^2) stay far from fp64 overflow and underflow.
+// An off-diagonal entry at or below the threshold is left as it is (no
+// rotation).  Returns whether it rotates.
 MO_DEV bool jacobi_rotation(double app, double aqq, double apq, double thr, double& t, double& s,
                             double& tau) {
     if (fabs(apq) <= thr) {
@@ -409,12 +420,16 @@ MO_DEV bool jacobi_rotation(double app, double aqq, double apq, double thr, doub
         return false;
     }
     const double d = aqq - app, e = 2.0 * apq;
+    const double se = d * e >= 0.0 ? fabs(e) : -fabs(e);
     const double x = fma(d, d, e * e);
-    const double r = x * rsq_nr(x);   // hypot(d, e)
-    t = (d * e >= 0.0 ? fabs(e) : -fabs(e)) * rcp_nr(fabs(d) + r);
-    const double c = rsq_nr(fma(t, t, 1.0));
-    s = t * c;
-    tau = s * rcp_nr(1.0 + c);
+    const double y = rsq_nr(x);
+    const double r = x * y;                        // hypot(d, e)
+    const double w = fma(x, y, fabs(d));
+    const double p = (r + r) * w;                  // 2 r w = w^2 + e^2
+    const double q = rsq_nr(p);
+    t = se * rcp_nr(w);
+    s = se * q;
+    tau = se * rcp_nr(fma(p, q, w));
     return true;
 }
 
@@ -422,7 +437,8 @@ MO_DEV bool jacobi_rotation(double app, double aqq, double apq, double thr, doub
 // (row i holds columns i .. 63; 2080 entries).
 MO_DEV int tri(int i, int j) {
     const int a = min(i, j), b = max(i, j);
-    return a * PW - (a * (a - 1)) / 2 + (b - a);
+    // row a starts at a PW - a (a - 1) / 2 - a = a (2 PW - 1 - a) / 2 (an even product)
+    return int(__umul24(unsigned(a), unsigned(2 * PW - 1 - a)) >> 1) + b;
 }
 
 // Slot of 2 x 2 blocks that thread t updates in a step (a bijection of
@@ -456,14 +472,13 @@ MO_DEV int solve_slot(int t) {
 // updates each next pivot needs and compute the next step's rotations into the
 // other parameter buffer, while the other threads update the other blocks and
 // waves 1 .. 7 accumulate D with the current rotations.  Every rounding of the
-// updates is written out (fma, or a rounded product where one is shared), so
-// the results do not depend on which contractions the compiler chooses.
+// updates is written out as an fma, so the results do not depend on which
+// contractions the compiler chooses.
 __global__ __launch_bounds__(SV_THREADS) void so_jac_solve_kernel(uint8_t* ws, uint32_t k) {
     constexpr int NP = PW / 2;   // rotations per step
     __shared__ double S[PW * (PW + 1) / 2];
     __shared__ double D[PW][PW + 1];
     __shared__ double rs[2][NP], rtau[2][NP], rt[2][NP], rapq[2][NP];   // by step parity
-    __shared__ int ra[2][NP], rb[2][NP];
     __shared__ int flags[2];   // [0] an off-diagonal entry above the threshold, [1] a rotation happened
     const mo_so_header* h = so_header(ws);
     const mo_so_eig* eigs = so_eigs(ws);
@@ -511,34 +526,50 @@ __global__ __launch_bounds__(SV_THREADS) void so_jac_solve_kernel(uint8_t* ws, u
     }
     __syncthreads();
     if (flags[0]) {   // uniform
-        if (t < NP) {   // the rotations of step 0
-            int a, b;
-            circle_pair(PW, 0, t, a, b);
-            double tt, s, tau;
-            const double apq = S[tri(a, b)];
-            if (jacobi_rotation(S[tri(a, a)], S[tri(b, b)], apq, thr, tt, s, tau)) flags[1] = 1;
-            ra[0][t] = a; rb[0][t] = b; rs[0][t] = s; rtau[0][t] = tau; rt[0][t] = tt; rapq[0][t] = apq;
-        }
-        __syncthreads();
+        // Pair j of step k is circle_pair(PW, k, j).  From one step to the next
+        // every index but 0 moves one place along 1 .. 63, so the indices a
+        // thread needs are kept in registers and advanced (no LDS round trip
+        // before a step's loads).
         const int sl = solve_slot(t);
         const int u = sl >> 4, dv = sl & 15, v = (u + 1 + dv) & 31;
         const bool on = dv != 15 || u < 16;
+        int au, bu, av, bv;
+        circle_pair(PW, 0, u, au, bu);
+        circle_pair(PW, 0, v, av, bv);
+        // D items of threads 64 .. 511: pair w in rows r0 + 14 i (the stride
+        // 448 of the items is a multiple of 32, so every item has the same pair)
+        constexpr int NT = SV_THREADS - 64, NR = (PW * NP + NT - 1) / NT;
+        static_assert(NT % NP == 0, "one pair per D thread");
+        const int w = (t - 64) & (NP - 1), r0 = (t - 64) >> 5;
+        int aw, bw;
+        circle_pair(PW, 0, w, aw, bw);
+        // rotation t of the current step (threads 0 .. 31 compute it a step ahead)
+        int at = 0, bt = 0;
+        bool rot_t = false;
+        if (t < NP) {   // the rotations of step 0
+            circle_pair(PW, 0, t, at, bt);
+            double tt, s, tau;
+            const double apq = S[tri(at, bt)];
+            rot_t = jacobi_rotation(S[tri(at, at)], S[tri(bt, bt)], apq, thr, tt, s, tau);
+            if (rot_t) flags[1] = 1;
+            rs[0][t] = s; rtau[0][t] = tau; rt[0][t] = tt; rapq[0][t] = apq;
+        }
+        __syncthreads();
         for (int step = 0; step < PW - 1; ++step) {
             const int cur = step & 1, nxt = cur ^ 1;
             // Two-sided update of this thread's off-diagonal 2 x 2 block (rows
             // a_u, b_u by J_u^T, then columns a_v, b_v by J_v, each in
             // Rutishauser's form), loads issued before the arithmetic.
-            const int au = ra[cur][u], bu = rb[cur][u], av = ra[cur][v], bv = rb[cur][v];
             const int i00 = tri(au, av), i01 = tri(au, bv), i10 = tri(bu, av), i11 = tri(bu, bv);
             const double x00 = S[i00], x01 = S[i01], x10 = S[i10], x11 = S[i11];
             const double su = rs[cur][u], tu = rtau[cur][u], sv = rs[cur][v], tv = rtau[cur][v];
             // Threads 0 .. 31 also load, with the block, what the next pivot needs:
             // its two diagonal entries (written by no other thread in this step)
-            // and the tan and pivot of this block's two rotations.
-            int a2 = 0, b2 = 0;
+            // and the tan and pivot of this block's two rotations.  Pair t of the
+            // next step is (a2, b2).
+            const int a2 = advance_circle(at), b2 = advance_circle(bt);
             double da = 0.0, db = 0.0, tU = 0.0, pU = 0.0, tV = 0.0, pV = 0.0;
             if (t < NP) {
-                circle_pair(PW, (step + 1) % (PW - 1), t, a2, b2);
                 da = S[tri(a2, a2)];
                 db = S[tri(b2, b2)];
                 tU = rt[cur][u]; pU = rapq[cur][u]; tV = rt[cur][v]; pV = rapq[cur][v];
@@ -554,7 +585,7 @@ __global__ __launch_bounds__(SV_THREADS) void so_jac_solve_kernel(uint8_t* ws, u
                 // Rotation t of this step is done: its pivot becomes zero (the
                 // diagonal updates are applied below, by the thread whose next
                 // pivot needs them).
-                if (rs[cur][t] != 0.0) S[tri(ra[cur][t], rb[cur][t])] = 0.0;
+                if (rot_t) S[tri(at, bt)] = 0.0;
                 // Pair t of the next step: a' from one of this block's pairs,
                 // b' from the other; every diagonal entry is in exactly one of
                 // them, so every diagonal update is applied once.
@@ -564,45 +595,41 @@ __global__ __launch_bounds__(SV_THREADS) void so_jac_solve_kernel(uint8_t* ws, u
                 const double s_a = a_in_u ? su : sv, t_a = a_in_u ? tU : tV, p_a = a_in_u ? pU : pV;
                 const double s_b = a_in_u ? sv : su, t_b = a_in_u ? tV : tU, p_b = a_in_u ? pV : pU;
                 const int first_a = a_in_u ? au : av, first_b = a_in_u ? av : au;
-                double app2 = da, aqq2 = db;
-                if (s_a != 0.0)   // the first index of a rotation loses t apq, the second gains it
-                    app2 = fma(a2 == first_a ? -t_a : t_a, p_a, app2);
-                if (s_b != 0.0)
-                    aqq2 = fma(b2 == first_b ? -t_b : t_b, p_b, aqq2);
+                // the first index of a rotation loses t apq, the second gains it
+                const double app2 = s_a != 0.0 ? fma(a2 == first_a ? -t_a : t_a, p_a, da) : da;
+                const double aqq2 = s_b != 0.0 ? fma(b2 == first_b ? -t_b : t_b, p_b, db) : db;
                 S[tri(a2, a2)] = app2;
                 S[tri(b2, b2)] = aqq2;
-                if (step + 1 < PW - 1) {
-                    double tt, s, tau;
-                    if (jacobi_rotation(app2, aqq2, apq2, thr, tt, s, tau)) flags[1] = 1;
-                    ra[nxt][t] = a2; rb[nxt][t] = b2; rs[nxt][t] = s; rtau[nxt][t] = tau; rt[nxt][t] = tt;
-                    rapq[nxt][t] = apq2;
-                }
+                double tt, s, tau;
+                rot_t = jacobi_rotation(app2, aqq2, apq2, thr, tt, s, tau) && step + 1 < PW - 1;
+                if (rot_t) flags[1] = 1;
+                rs[nxt][t] = s; rtau[nxt][t] = tau; rt[nxt][t] = tt; rapq[nxt][t] = apq2;
             } else if (t >= 64) {
-                // D <- D J + (J - I) on waves 1 .. 7: item q is pair q % 32 in row q / 32.
-                constexpr int NT = SV_THREADS - 64, NR = (PW * NP + NT - 1) / NT;
-                int a3[NR], b3[NR], r3[NR];
-                double da[NR], db[NR];
+                // D <- D J + (J - I) on waves 1 .. 7: item i is row r0 + 14 i of pair w.
+                const double s2 = rs[cur][w], tau = rtau[cur][w];
+                double dA[NR], dB[NR];
 #pragma unroll
                 for (int i = 0; i < NR; ++i) {
-                    const int q = (t - 64) + NT * i;
-                    const int w = q & (NP - 1);
-                    r3[i] = q >> 5; a3[i] = ra[cur][w]; b3[i] = rb[cur][w];
-                    if (q < PW * NP) { da[i] = D[r3[i]][a3[i]]; db[i] = D[r3[i]][b3[i]]; }
+                    const int r = r0 + (NT / NP) * i;
+                    if (r < PW) { dA[i] = D[r][aw]; dB[i] = D[r][bw]; }
                 }
+                // With V = I + D, entry (r, a) of V J - I is
+                // D[r][a] - s (V[r][b] + tau V[r][a]) and entry (r, b) is
+                // D[r][b] + s (V[r][a] - tau V[r][b]): the rotation's products
+                // take V's entries (D plus 1 in rows a and b), the sums keep D.
 #pragma unroll
                 for (int i = 0; i < NR; ++i) {
-                    const int q = (t - 64) + NT * i;
-                    if (q >= PW * NP) break;
-                    const int w = q & (NP - 1), r = r3[i];
-                    const double s2 = rs[cur][w], tau = rtau[cur][w], st = __dmul_rn(s2, tau);
-                    double na = fma(-s2, fma(tau, da[i], db[i]), da[i]);
-                    double nb2 = fma(s2, fma(-tau, db[i], da[i]), db[i]);
-                    if (r == a3[i]) { na = __dsub_rn(na, st); nb2 = __dadd_rn(nb2, s2); }
-                    if (r == b3[i]) { na = __dsub_rn(na, s2); nb2 = __dsub_rn(nb2, st); }
-                    D[r][a3[i]] = na;
-                    D[r][b3[i]] = nb2;
+                    const int r = r0 + (NT / NP) * i;
+                    if (r >= PW) break;
+                    const double va = dA[i] + (r == aw ? 1.0 : 0.0), vb = dB[i] + (r == bw ? 1.0 : 0.0);
+                    D[r][aw] = fma(-s2, fma(tau, va, vb), dA[i]);
+                    D[r][bw] = fma(s2, fma(-tau, vb, va), dB[i]);
                 }
             }
+            at = a2; bt = b2;
+            au = advance_circle(au); bu = advance_circle(bu);
+            av = advance_circle(av); bv = advance_circle(bv);
+            aw = advance_circle(aw); bw = advance_circle(bw);
             __syncthreads();
         }
     }

@@ -9,7 +9,8 @@ checked here:
 
   * the circle ordering turns one place per step, so pair j of step k + 1
     takes one element from pair j - 1 and one from pair j + 1 of step k (0 and 1
-    for j = 0, 30 and 31 for j = 31), at every step;
+    for j = 0, 30 and 31 for j = 31), at every step, and each index the kernel
+    keeps in a register follows it by one update (0 stays, 63 wraps to 1);
   * the slot map is a bijection of the 512 threads onto the 512 block slots,
     and threads 0 .. 31 hold exactly those 32 blocks;
   * the one-barrier order gives the same S and D, bit for bit, as steps that
@@ -31,6 +32,11 @@ PW, NP, THREADS = 64, 32, 512
 def circle_pair(n, k, j):
     f = lambda i: (i + k) % (n - 1) + 1
     return (0, f(0)) if j == 0 else (f(j), f(n - 1 - j))
+
+
+def advance_circle(i):
+    """The kernel's index update from one step to the next."""
+    return 0 if i == 0 else 1 if i == PW - 1 else i + 1
 
 
 def next_sources(j):
@@ -84,15 +90,10 @@ def block(x, su, tu, sv, tv):
 
 
 def d_update(D, r, a, b, s, tau):
+    """Row r of D <- D J + (J - I): the rotation's products take V = I + D."""
     da, db = D[r][a], D[r][b]
-    na, nb = da - s * (db + tau * da), db + s * (da - tau * db)
-    if r == a:
-        na -= s * tau
-        nb += s
-    if r == b:
-        na -= s
-        nb -= s * tau
-    return na, nb
+    va, vb = da + (1.0 if r == a else 0.0), db + (1.0 if r == b else 0.0)
+    return da - s * (vb + tau * va), db + s * (va - tau * vb)
 
 
 def key(i, j):
@@ -211,6 +212,15 @@ def test_next_pivots_come_from_neighbouring_pairs():
             assert sorted((where[a2], where[b2])) == sorted(next_sources(j))
 
 
+def test_indices_advance_with_the_circle():
+    """The kernel keeps each pair's indices in registers and advances them; that
+    gives circle_pair at every step, through the wrap from step 62 to step 0."""
+    for k in range(PW - 1):
+        for j in range(NP):
+            a, b = circle_pair(PW, k, j)
+            assert (advance_circle(a), advance_circle(b)) == circle_pair(PW, (k + 1) % (PW - 1), j)
+
+
 def test_slot_map_is_a_bijection_with_the_pivot_blocks_first():
     slots = [solve_slot(t) for t in range(THREADS)]
     assert sorted(slots) == list(range(512))
@@ -241,3 +251,15 @@ def test_one_barrier_order_equals_two_barrier_steps(case):
     off0 = np.linalg.norm(S0 - np.diag(np.diag(S0)))
     R = V.T @ S0 @ V
     assert np.linalg.norm(R - np.diag(np.diag(R))) <= off0
+
+
+def test_packed_triangle_index():
+    """The kernel's packed index of (i, j), min(i, j) (2 PW - 1 - min) / 2 + max,
+    is row-major order over the upper triangle: a bijection onto 0 .. 2079."""
+    def tri(i, j):
+        a, b = min(i, j), max(i, j)
+        assert a * (2 * PW - 1 - a) % 2 == 0
+        return a * (2 * PW - 1 - a) // 2 + b
+    order = [tri(i, j) for i in range(PW) for j in range(i, PW)]
+    assert order == list(range(PW * (PW + 1) // 2))
+    assert all(tri(i, j) == tri(j, i) for i in range(PW) for j in range(PW))
