@@ -81,8 +81,14 @@ MO_DEV void circle_pair(int n, int k, int j, int& a, int& b) {
 }
 
 // The same index one step later in the pair solve's 64-index circle ordering:
-// 0 stays, 1 .. 62 move up by one, 63 wraps to 1.
-MO_DEV int advance_circle(int i) { return i == 0 ? 0 : i == PW - 1 ? 1 : i + 1; }
+// 1 .. 62 move up by one, 63 wraps to 1, and index 0, the first of pair 0,
+// stays.  keep is PW - 1 for an index that moves and 0 for that fixed one,
+// so the update is three integer operations with no compare.
+static_assert(PW == 64, "the wrap below is PW = 64");
+MO_DEV int advance_circle(int i, int keep = PW - 1) {
+    const int x = i + 1;
+    return (x & keep) | (x >> 6);
+}
 
 // ============================================================================
 // prep: padded G and M' = b1 M + (1 - b1) G (the caller's M updated)
@@ -435,11 +441,13 @@ MO_DEV bool jacobi_rotation(double app, double aqq, double apq, double thr, doub
 
 // Entry (i, j) of a symmetric 64 x 64 matrix kept as its packed upper triangle
 // (row i holds columns i .. 63; 2080 entries).
-MO_DEV int tri(int i, int j) {
+// Row a starts at a PW - a (a - 1) / 2 - a = a (2 PW - 1 - a) / 2 (an even
+// product), so the byte offset of (i, j) is 4 a (2 PW - 1 - a) + 8 b.
+MO_DEV int tri_off(int i, int j) {
     const int a = min(i, j), b = max(i, j);
-    // row a starts at a PW - a (a - 1) / 2 - a = a (2 PW - 1 - a) / 2 (an even product)
-    return int(__umul24(unsigned(a), unsigned(2 * PW - 1 - a)) >> 1) + b;
+    return int(__umul24(unsigned(a), unsigned(4 * (2 * PW - 1) - 4 * a))) + 8 * b;
 }
+MO_DEV int tri(int i, int j) { return tri_off(i, j) >> 3; }
 
 // Slot of 2 x 2 blocks that thread t updates in a step (a bijection of
 // 0 .. 511).  Slot s is the unordered pair {u, v} of the step's 32 rotations
@@ -536,6 +544,10 @@ __global__ __launch_bounds__(SV_THREADS) void so_jac_solve_kernel(uint8_t* ws, u
         int au, bu, av, bv;
         circle_pair(PW, 0, u, au, bu);
         circle_pair(PW, 0, v, av, bv);
+        // S by byte offset (tri_off), and the keep masks of advance_circle: the
+        // first index of pair 0 is the one that never moves
+        auto Sb = [&](int off) -> double& { return *reinterpret_cast<double*>(reinterpret_cast<uint8_t*>(S) + off); };
+        const int keep_u = u == 0 ? 0 : PW - 1, keep_v = v == 0 ? 0 : PW - 1;
         // D items of threads 64 .. 511: pair w in rows r0 + 14 i (the stride
         // 448 of the items is a multiple of 32, so every item has the same pair)
         constexpr int NT = SV_THREADS - 64, NR = (PW * NP + NT - 1) / NT;
@@ -543,6 +555,7 @@ __global__ __launch_bounds__(SV_THREADS) void so_jac_solve_kernel(uint8_t* ws, u
         const int w = (t - 64) & (NP - 1), r0 = (t - 64) >> 5;
         int aw, bw;
         circle_pair(PW, 0, w, aw, bw);
+        const int keep_w = w == 0 ? 0 : PW - 1, keep_t = t == 0 ? 0 : PW - 1;
         // rotation t of the current step (threads 0 .. 31 compute it a step ahead)
         int at = 0, bt = 0;
         bool rot_t = false;
@@ -560,18 +573,18 @@ __global__ __launch_bounds__(SV_THREADS) void so_jac_solve_kernel(uint8_t* ws, u
             // Two-sided update of this thread's off-diagonal 2 x 2 block (rows
             // a_u, b_u by J_u^T, then columns a_v, b_v by J_v, each in
             // Rutishauser's form), loads issued before the arithmetic.
-            const int i00 = tri(au, av), i01 = tri(au, bv), i10 = tri(bu, av), i11 = tri(bu, bv);
-            const double x00 = S[i00], x01 = S[i01], x10 = S[i10], x11 = S[i11];
+            const int i00 = tri_off(au, av), i01 = tri_off(au, bv), i10 = tri_off(bu, av), i11 = tri_off(bu, bv);
+            const double x00 = Sb(i00), x01 = Sb(i01), x10 = Sb(i10), x11 = Sb(i11);
             const double su = rs[cur][u], tu = rtau[cur][u], sv = rs[cur][v], tv = rtau[cur][v];
             // Threads 0 .. 31 also load, with the block, what the next pivot needs:
             // its two diagonal entries (written by no other thread in this step)
             // and the tan and pivot of this block's two rotations.  Pair t of the
             // next step is (a2, b2).
-            const int a2 = advance_circle(at), b2 = advance_circle(bt);
+            const int a2 = advance_circle(at, keep_t), b2 = advance_circle(bt);
             double da = 0.0, db = 0.0, tU = 0.0, pU = 0.0, tV = 0.0, pV = 0.0;
             if (t < NP) {
-                da = S[tri(a2, a2)];
-                db = S[tri(b2, b2)];
+                da = Sb(tri_off(a2, a2));
+                db = Sb(tri_off(b2, b2));
                 tU = rt[cur][u]; pU = rapq[cur][u]; tV = rt[cur][v]; pV = rapq[cur][v];
             }
             const double y00 = fma(-su, fma(tu, x00, x10), x00), y10 = fma(su, fma(-tu, x10, x00), x10);
@@ -579,13 +592,13 @@ __global__ __launch_bounds__(SV_THREADS) void so_jac_solve_kernel(uint8_t* ws, u
             const double z00 = fma(-sv, fma(tv, y00, y01), y00), z01 = fma(sv, fma(-tv, y01, y00), y01);
             const double z10 = fma(-sv, fma(tv, y10, y11), y10), z11 = fma(sv, fma(-tv, y11, y10), y11);
             if (on) {
-                S[i00] = z00; S[i01] = z01; S[i10] = z10; S[i11] = z11;
+                Sb(i00) = z00; Sb(i01) = z01; Sb(i10) = z10; Sb(i11) = z11;
             }
             if (t < NP) {
                 // Rotation t of this step is done: its pivot becomes zero (the
                 // diagonal updates are applied below, by the thread whose next
                 // pivot needs them).
-                if (rot_t) S[tri(at, bt)] = 0.0;
+                if (rot_t) Sb(tri_off(at, bt)) = 0.0;
                 // Pair t of the next step: a' from one of this block's pairs,
                 // b' from the other; every diagonal entry is in exactly one of
                 // them, so every diagonal update is applied once.
@@ -598,8 +611,8 @@ __global__ __launch_bounds__(SV_THREADS) void so_jac_solve_kernel(uint8_t* ws, u
                 // the first index of a rotation loses t apq, the second gains it
                 const double app2 = s_a != 0.0 ? fma(a2 == first_a ? -t_a : t_a, p_a, da) : da;
                 const double aqq2 = s_b != 0.0 ? fma(b2 == first_b ? -t_b : t_b, p_b, db) : db;
-                S[tri(a2, a2)] = app2;
-                S[tri(b2, b2)] = aqq2;
+                Sb(tri_off(a2, a2)) = app2;
+                Sb(tri_off(b2, b2)) = aqq2;
                 double tt, s, tau;
                 rot_t = jacobi_rotation(app2, aqq2, apq2, thr, tt, s, tau) && step + 1 < PW - 1;
                 if (rot_t) flags[1] = 1;
@@ -627,9 +640,9 @@ __global__ __launch_bounds__(SV_THREADS) void so_jac_solve_kernel(uint8_t* ws, u
                 }
             }
             at = a2; bt = b2;
-            au = advance_circle(au); bu = advance_circle(bu);
-            av = advance_circle(av); bv = advance_circle(bv);
-            aw = advance_circle(aw); bw = advance_circle(bw);
+            au = advance_circle(au, keep_u); bu = advance_circle(bu);
+            av = advance_circle(av, keep_v); bv = advance_circle(bv);
+            aw = advance_circle(aw, keep_w); bw = advance_circle(bw);
             __syncthreads();
         }
     }

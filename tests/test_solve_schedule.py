@@ -34,9 +34,11 @@ def circle_pair(n, k, j):
     return (0, f(0)) if j == 0 else (f(j), f(n - 1 - j))
 
 
-def advance_circle(i):
-    """The kernel's index update from one step to the next."""
-    return 0 if i == 0 else 1 if i == PW - 1 else i + 1
+def advance_circle(i, keep=PW - 1):
+    """The kernel's index update from one step to the next: keep is 0 for the
+    first index of pair 0 (which never moves), PW - 1 for every other."""
+    x = i + 1
+    return (x & keep) | (x >> 6)
 
 
 def next_sources(j):
@@ -218,7 +220,8 @@ def test_indices_advance_with_the_circle():
     for k in range(PW - 1):
         for j in range(NP):
             a, b = circle_pair(PW, k, j)
-            assert (advance_circle(a), advance_circle(b)) == circle_pair(PW, (k + 1) % (PW - 1), j)
+            keep_a = 0 if j == 0 else PW - 1
+            assert (advance_circle(a, keep_a), advance_circle(b)) == circle_pair(PW, (k + 1) % (PW - 1), j)
 
 
 def test_slot_map_is_a_bijection_with_the_pivot_blocks_first():
@@ -255,7 +258,8 @@ def test_one_barrier_order_equals_two_barrier_steps(case):
 
 def test_packed_triangle_index():
     """The kernel's packed index of (i, j), min(i, j) (2 PW - 1 - min) / 2 + max,
-    is row-major order over the upper triangle: a bijection onto 0 .. 2079."""
+    is row-major order over the upper triangle: a bijection onto 0 .. 2079,
+    and its byte offset is eight times that."""
     def tri(i, j):
         a, b = min(i, j), max(i, j)
         assert a * (2 * PW - 1 - a) % 2 == 0
@@ -263,3 +267,8 @@ def test_packed_triangle_index():
     order = [tri(i, j) for i in range(PW) for j in range(i, PW)]
     assert order == list(range(PW * (PW + 1) // 2))
     assert all(tri(i, j) == tri(j, i) for i in range(PW) for j in range(PW))
+    # the byte offset the step loop uses: 4 a (2 PW - 1 - a) + 8 b
+    for i in range(PW):
+        for j in range(PW):
+            a, b = min(i, j), max(i, j)
+            assert 4 * a * (2 * PW - 1 - a) + 8 * b == 8 * tri(i, j)
