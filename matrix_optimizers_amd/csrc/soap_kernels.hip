@@ -647,11 +647,14 @@ __global__ __launch_bounds__(SV_THREADS) void so_jac_solve_kernel(uint8_t* ws, u
         }
     }
     const bool any = flags[1];   // read after the last barrier
+    // D of a pair that did not rotate is zero and is never read (its A and E
+    // products are skipped on the flag word), so it is not stored.
     double* Dout = reinterpret_cast<double*>(ws + eg.off_D) + int64_t(j) * PW * PW;
-    for (int q = t; q < PW * PW / 2; q += SV_THREADS) {
-        const int r = q / (PW / 2), c = 2 * (q % (PW / 2));
-        *reinterpret_cast<f64x2*>(Dout + r * PW + c) = f64x2{D[r][c], D[r][c + 1]};
-    }
+    if (any)
+        for (int q = t; q < PW * PW / 2; q += SV_THREADS) {
+            const int r = q / (PW / 2), c = 2 * (q % (PW / 2));
+            *reinterpret_cast<f64x2*>(Dout + r * PW + c) = f64x2{D[r][c], D[r][c + 1]};
+        }
     if (t == 0) reinterpret_cast<uint32_t*>(ws + eg.off_flag)[j] = any ? 1u : 0u;
     // rounds of the final sweep: mark this pair slot if its problem rotated
     if (t == 0 && any && k + uint32_t(nb - 1) >= eg.rounds)
@@ -690,7 +693,10 @@ MO_DEV void apply_a_tile(uint8_t* ws, uint32_t k, uint32_t blk, double (*C)[PW +
     while (item >= P - I) { item -= P - I; ++I; }
     const int J = I + item;
     const uint32_t* flag = reinterpret_cast<const uint32_t*>(ws + eg.off_flag);
-    if (!flag[I] && !flag[J]) return;
+    // A pair that did not rotate has D = 0 (not stored): its product would add
+    // exact zeros and is skipped (both: the tile stays as it is).
+    const bool rot_I = flag[I] != 0, rot_J = flag[J] != 0;
+    if (!rot_I && !rot_J) return;
     int pI, qI, pJ, qJ;
     circle_pair(nb, kr, I, pI, qI);
     circle_pair(nb, kr, J, pJ, qJ);
@@ -741,69 +747,77 @@ MO_DEV void apply_a_tile(uint8_t* ws, uint32_t k, uint32_t blk, double (*C)[PW +
     }
     __syncthreads();
     f64x4 acc[2][2];
-#pragma unroll
-    for (int x = 0; x < 2; ++x)
-#pragma unroll
-        for (int y = 0; y < 2; ++y) acc[x][y] = f64x4{0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-    for (int k0 = 0; k0 < PW; k0 += 4) {   // X D_J
-        const int kq = k0 + (l >> 4);
-        double a[2], b[2];
-#pragma unroll
-        for (int x = 0; x < 2; ++x) a[x] = C[kq][r0 + 16 * x];   // X[r][kq] = X^T[kq][r]
-#pragma unroll
-        for (int y = 0; y < 2; ++y) b[y] = DJ[kq * PW + c0 + 16 * y];
-#pragma unroll
-        for (int x = 0; x < 2; ++x)
-#pragma unroll
-            for (int y = 0; y < 2; ++y) acc[x][y] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[x], b[y], acc[x][y], 0, 0, 0);
-    }
     double own[2][2][4];
-#pragma unroll
-    for (int x = 0; x < 2; ++x)
-#pragma unroll
-        for (int y = 0; y < 2; ++y)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) own[x][y][v] = C[mfma_col(y)][mfma_row(x, v)] + acc[x][y][v];
-    __syncthreads();                          // X^T fully read: C replaces it
-#pragma unroll
-    for (int x = 0; x < 2; ++x)
-#pragma unroll
-        for (int y = 0; y < 2; ++y)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) C[mfma_row(x, v)][mfma_col(y)] = own[x][y][v];
-    __syncthreads();
-#pragma unroll
-    for (int x = 0; x < 2; ++x)
-#pragma unroll
-        for (int y = 0; y < 2; ++y) acc[x][y] = f64x4{0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-    for (int k0 = 0; k0 < PW; k0 += 4) {   // D_I^T C
-        const int kq = k0 + (l >> 4);
-        double a[2], b[2];
-#pragma unroll
-        for (int x = 0; x < 2; ++x) a[x] = DI[kq * PW + r0 + 16 * x];
-#pragma unroll
-        for (int y = 0; y < 2; ++y) b[y] = C[kq][c0 + 16 * y];
+    if (rot_J) {   // uniform
 #pragma unroll
         for (int x = 0; x < 2; ++x)
 #pragma unroll
-            for (int y = 0; y < 2; ++y) acc[x][y] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[x], b[y], acc[x][y], 0, 0, 0);
+            for (int y = 0; y < 2; ++y) acc[x][y] = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int k0 = 0; k0 < PW; k0 += 4) {   // X D_J
+            const int kq = k0 + (l >> 4);
+            double a[2], b[2];
+#pragma unroll
+            for (int x = 0; x < 2; ++x) a[x] = C[kq][r0 + 16 * x];   // X[r][kq] = X^T[kq][r]
+#pragma unroll
+            for (int y = 0; y < 2; ++y) b[y] = DJ[kq * PW + c0 + 16 * y];
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int y = 0; y < 2; ++y) acc[x][y] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[x], b[y], acc[x][y], 0, 0, 0);
+        }
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int y = 0; y < 2; ++y)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) own[x][y][v] = C[mfma_col(y)][mfma_row(x, v)] + acc[x][y][v];
+        __syncthreads();                          // X^T fully read: C replaces it
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int y = 0; y < 2; ++y)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) C[mfma_row(x, v)][mfma_col(y)] = own[x][y][v];
+        __syncthreads();
     }
+    // C is in the buffer by rows, or (D_J = 0) C = X is still there as X^T,
+    // read transposed below.
+    if (rot_I) {   // uniform
+        const bool ct = !rot_J;
 #pragma unroll
-    for (int x = 0; x < 2; ++x)
+        for (int x = 0; x < 2; ++x)
 #pragma unroll
-        for (int y = 0; y < 2; ++y)
+            for (int y = 0; y < 2; ++y) acc[x][y] = f64x4{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-            for (int v = 0; v < 4; ++v) own[x][y][v] = C[mfma_row(x, v)][mfma_col(y)] + acc[x][y][v];
-    __syncthreads();                          // C fully read: the result replaces it
+        for (int k0 = 0; k0 < PW; k0 += 4) {   // D_I^T C
+            const int kq = k0 + (l >> 4);
+            double a[2], b[2];
 #pragma unroll
-    for (int x = 0; x < 2; ++x)
+            for (int x = 0; x < 2; ++x) a[x] = DI[kq * PW + r0 + 16 * x];
 #pragma unroll
-        for (int y = 0; y < 2; ++y)
+            for (int y = 0; y < 2; ++y) b[y] = ct ? C[c0 + 16 * y][kq] : C[kq][c0 + 16 * y];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) C[mfma_row(x, v)][mfma_col(y)] = own[x][y][v];
-    __syncthreads();
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int y = 0; y < 2; ++y) acc[x][y] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[x], b[y], acc[x][y], 0, 0, 0);
+        }
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int y = 0; y < 2; ++y)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    own[x][y][v] = (ct ? C[mfma_col(y)][mfma_row(x, v)] : C[mfma_row(x, v)][mfma_col(y)]) + acc[x][y][v];
+        __syncthreads();                          // C fully read: the result replaces it
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int y = 0; y < 2; ++y)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) C[mfma_row(x, v)][mfma_col(y)] = own[x][y][v];
+        __syncthreads();
+    }
     // each block of the result goes to where A keeps it: an upper block by
     // rows, a lower one as its transpose; on a diagonal tile the lower one of
     // the two off-diagonal blocks is the mirror of the other and is not written
