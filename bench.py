@@ -157,10 +157,12 @@ def event_timed_steps(fn, steps, per_step=None):
     return mo.profile_read(), ms
 
 
-def machine_info():
+def machine_info(query_smi=True):
     """ROCm / HIP version, gfx target and the shader clock and package power that
     rocm-smi reports right after the timed region (best effort: None where a tool
-    is missing)."""
+    is missing).  With query_smi False (--profile-only runs) no subprocess is
+    started: under a profiler every child process initialises the GPU too, and
+    rocm-smi, a script, would then be started by exec from such a child."""
     import subprocess
     import torch
     info = {"hip": getattr(torch.version, "hip", None), "torch": torch.__version__}
@@ -173,6 +175,9 @@ def machine_info():
             info["rocm"] = f.read().strip()
     except OSError:
         info["rocm"] = None
+    if not query_smi:
+        info["sclk_after_run"] = info["power_after_run"] = None
+        return info
     try:
         out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
                              timeout=20).stdout
@@ -770,7 +775,7 @@ def main():
                                       "algorithmic_per_launch": f"{algo_b} B ({es_g + 8 + es_x} B/elem)",
                                       "moved_GBps": round(moved_b / t / 1e9, 1),
                                       "moved_per_launch": f"{moved_b} B"}
-    out["machine"] = machine_info()
+    out["machine"] = machine_info(query_smi=not args.profile_only)
     if not args.no_cpu_baseline and not args.profile_only:
         print("[bench] cpu_baseline (fp64 oracle on host)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, args)

@@ -114,6 +114,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -m matrix_optimizers_amd.build`"
                            " (there is no non-HIP fallback)")
+    # The binding hands torch's device memory and streams to the library, so
+    # both must run on one HIP runtime.  torch ships its own, under the same
+    # soname as the system's that libmo.so is linked against: whichever loads
+    # first serves the process.  Loaded before torch, libmo.so would put torch
+    # on the system runtime, where the step's launches fail; torch goes first.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     P = ctypes.POINTER
     lib.muon_workspace_bytes.argtypes = [P(MoMatrix), ctypes.c_int32, P(MoMuonHParams),

@@ -47,6 +47,25 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     B.load_library()
 
 
+def test_library_shares_torchs_hip_runtime():
+    """torch ships its own HIP runtime under the system runtime's soname, and the
+    first one loaded serves the whole process.  Loading the library through the
+    binding, even before anything else imports torch, leaves exactly one
+    libamdhip64 mapped, torch's, so the two cannot end up on different runtimes."""
+    import subprocess
+    import sys
+    code = ("from matrix_optimizers_amd import _binding\n"
+            "_binding.load_library()\n"
+            "import os, torch\n"
+            "tl = os.path.realpath(os.path.join(os.path.dirname(torch.__file__), 'lib'))\n"
+            "maps = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}\n"
+            "print(len(maps), all(os.path.realpath(m).startswith(tl) for m in maps))\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.split()[-2:] == ["1", "True"], out.stdout
+
+
 GiB = 1 << 30
 BASE = 1 << 44
 
