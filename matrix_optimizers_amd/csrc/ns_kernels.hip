@@ -35,11 +35,11 @@ namespace {
 constexpr int MOM_THREADS = 256;
 
 // Streaming (non-temporal) 16-byte loads: G and M are read once per step.
-// Stores stay ordinary: the transposed tile is written in 16-byte pieces of
-// 128-byte rows, which L2 merges before they reach HBM (non-temporal stores
-// measured 10-14 % slower).
+// Stores stay ordinary 16-byte stores: non-temporal ones measured slower for
+// this kernel (10-14 % while the transposed tile went out in pieces of 64
+// rows, still 2-18 % with every store a whole 128-byte line).
 MO_DEV u32x4 ld_nt(const void* p) { return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)); }
-MO_DEV void st_nt(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
+MO_DEV void st16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
 MO_DEV void unpack_bf16x8(const u32x4& raw, f32x8& o) {
     const bf16x8 b = __builtin_bit_cast(bf16x8, raw);
 #pragma unroll
@@ -63,16 +63,16 @@ MO_DEV void store8_stream(bf16_t* p, const f32x8& o) {
     __builtin_nontemporal_store(__builtin_bit_cast(u32x4, b), reinterpret_cast<u32x4*>(p));
 }
 MO_DEV void store8_stream(float* p, const f32x8& o) { store8(p, o); }
-template <typename T> MO_DEV void st8_nt(T* p, const f32x8& v);
-template <> MO_DEV void st8_nt<bf16_t>(bf16_t* p, const f32x8& v) {
+template <typename T> MO_DEV void st8v(T* p, const f32x8& v);
+template <> MO_DEV void st8v<bf16_t>(bf16_t* p, const f32x8& v) {
     bf16x8 b;
 #pragma unroll
     for (int e = 0; e < 8; ++e) b[e] = (bf16_t)v.v[e];
-    st_nt(p, __builtin_bit_cast(u32x4, b));
+    st16(p, __builtin_bit_cast(u32x4, b));
 }
-template <> MO_DEV void st8_nt<float>(float* p, const f32x8& v) {
-    st_nt(p, __builtin_bit_cast(u32x4, f32x4{v.v[0], v.v[1], v.v[2], v.v[3]}));
-    st_nt(p + 4, __builtin_bit_cast(u32x4, f32x4{v.v[4], v.v[5], v.v[6], v.v[7]}));
+template <> MO_DEV void st8v<float>(float* p, const f32x8& v) {
+    st16(p, __builtin_bit_cast(u32x4, f32x4{v.v[0], v.v[1], v.v[2], v.v[3]}));
+    st16(p + 4, __builtin_bit_cast(u32x4, f32x4{v.v[4], v.v[5], v.v[6], v.v[7]}));
 }
 
 template <typename XT>
@@ -154,13 +154,13 @@ __global__ __launch_bounds__(MOM_THREADS) void momentum_kernel(uint8_t* ws, floa
             tile[r][cc * 8 + e] = u.v[e];
         }
         if (fast[i]) {
-            st8_nt<float>(M + row * mt.ld_m + col0, mn);
+            st8v<float>(M + row * mt.ld_m + col0, mn);
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 if (row < rows && col0 + e < cols) M[row * mt.ld_m + col0 + e] = mn.v[e];
         }
-        st8_nt<XT>(direct + row * ld_direct + col0, u);
+        st8v<XT>(direct + row * ld_direct + col0, u);
     }
     __syncthreads();
 #pragma unroll
@@ -172,7 +172,7 @@ __global__ __launch_bounds__(MOM_THREADS) void momentum_kernel(uint8_t* ws, floa
         f32x8 o;
 #pragma unroll
         for (int e = 0; e < 8; ++e) o.v[e] = tile[rr * 8 + e][c];
-        st8_nt<XT>(transp + (C0 + c) * ld_transp + R0 + rr * 8, o);
+        st8v<XT>(transp + (C0 + c) * ld_transp + R0 + rr * 8, o);
     }
     const float tot = block_sum<MOM_THREADS>(sq, red);
     if (threadIdx.x == 0) reinterpret_cast<float*>(ws + mt.off_partials)[t] = tot;
